@@ -1,0 +1,104 @@
+"""The CPU oracle against its pins (closed forms, invariants, brute force, a hand-worked
+example), plus a check that the pins have teeth: plausible mistakes planted in copies
+of the oracle source (on the CPU) must each make at least one pin fail."""
+import os
+import shutil
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins
+from gated_deltanet_recurrence_gdn_amd import inputs
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin(oracle.load())
+
+
+# Planted mistakes: (name, exact source text, replacement).  Each must apply once.
+MUTANTS = [
+    ("erase_sign", "double *sij = &S[(size_t)i * dk + j];\n                *sij = at * (*sij - bt * u[i] * kt[j]) + bt * vt[i] * kt[j];",
+     "double *sij = &S[(size_t)i * dk + j];\n                *sij = at * (*sij + bt * u[i] * kt[j]) + bt * vt[i] * kt[j];"),
+    ("write_decayed", "double *sij = &S[(size_t)i * dk + j];\n                *sij = at * (*sij - bt * u[i] * kt[j]) + bt * vt[i] * kt[j];",
+     "double *sij = &S[(size_t)i * dk + j];\n                *sij = at * (*sij - bt * u[i] * kt[j] + bt * vt[i] * kt[j]);"),
+    ("erase_dropped", "double *sij = &S[(size_t)i * dk + j];\n                *sij = at * (*sij - bt * u[i] * kt[j]) + bt * vt[i] * kt[j];",
+     "double *sij = &S[(size_t)i * dk + j];\n                *sij = at * (*sij) + bt * vt[i] * kt[j];"),
+    ("erase_undecayed", "double *sij = &S[(size_t)i * dk + j];\n                *sij = at * (*sij - bt * u[i] * kt[j]) + bt * vt[i] * kt[j];",
+     "double *sij = &S[(size_t)i * dk + j];\n                *sij = at * *sij - bt * u[i] * kt[j] + bt * vt[i] * kt[j];"),
+    ("output_reads_k", "            for (int j = 0; j < dk; ++j) acc += S[(size_t)i * dk + j] * qt[j];\n            if (accumulate)",
+     "            for (int j = 0; j < dk; ++j) acc += S[(size_t)i * dk + j] * kt[j];\n            if (accumulate)"),
+    ("scale_dv", "const double scale = 1.0 / sqrt((double)dk);\n    if (state_in)",
+     "const double scale = 1.0 / sqrt((double)dv);\n    if (state_in)"),
+    ("gates_swapped", "const double bt = beta[gate(b, t, h, T, H)];\n        const double at = decay[gate(b, t, h, T, H)];\n        double *ot",
+     "const double bt = decay[gate(b, t, h, T, H)];\n        const double at = beta[gate(b, t, h, T, H)];\n        double *ot"),
+    ("state_in_ignored", "    if (state_in) {\n        memcpy(S, state_in + ((size_t)b * H + h) * dv * dk,\n               (size_t)dv * dk * sizeof(double));\n    }\n    for (long s = 0;",
+     "    for (long s = 0;"),
+    ("value_lagged", "const double *vt = v + tok(b, t, h, T, H, dv);\n        const double bt = beta",
+     "const double *vt = v + tok(b, t > 0 ? t - 1 : 0, h, T, H, dv);\n        const double bt = beta"),
+    ("half_erase", "            u[i] = acc;\n        }\n        /* S = a",
+     "            u[i] = 0.5 * acc;\n        }\n        /* S = a"),
+    ("reverse_ignored", "const long t = reverse ? T - 1 - s : s;", "const long t = s;"),
+    ("chunk_decay_offset", "G[i * C + j] = G[i * C + j + 1] * DECAY(j + 1);",
+     "G[i * C + j] = G[i * C + j + 1] * DECAY(j);"),
+    ("chunk_A_beta_col", "A[i * C + j] = (j < i) ? BETA(i) * G", "A[i * C + j] = (j < i) ? BETA(j) * G"),
+    ("chunk_W_no_gamma", "BETA(j) * gam[j] * KROW(j)[e]", "BETA(j) * KROW(j)[e]"),
+    ("chunk_state_no_decay", "Snew[(size_t)e * dk + f] = gam[n - 1] * S[(size_t)e * dk + f] + acc;",
+     "Snew[(size_t)e * dk + f] = S[(size_t)e * dk + f] + acc;"),
+    ("chunk_P_strict", "P[i * C + j] = (j <= i) ? G[i * C + j] * qk", "P[i * C + j] = (j < i) ? G[i * C + j] * qk"),
+    ("chunk_inter_no_gamma", "ot[e] = (gam[i] * inter + intra) * scale;", "ot[e] = (inter + intra) * scale;"),
+    ("dense_sign", "Mt[i * dk + j] = at * ((i == j ? 1.0 : 0.0) - bt * kt[i] * kt[j]);",
+     "Mt[i * dk + j] = at * ((i == j ? 1.0 : 0.0) + bt * kt[i] * kt[j]);"),
+    ("dense_order", "for (int l = 0; l < dk; ++l) acc += Pr[i * dk + l] * Mr[l * dk + j];",
+     "for (int l = 0; l < dk; ++l) acc += Mr[i * dk + l] * Pr[l * dk + j];"),
+]
+
+
+@pytest.fixture(scope="module")
+def mutant_dir():
+    d = tempfile.mkdtemp(prefix="gdn_mutants_")
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(name, old, new, mutant_dir):
+    with open(os.path.join(os.path.dirname(oracle.__file__), "gdn_oracle.c")) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/present"
+    path = os.path.join(mutant_dir, f"{name}.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = oracle.load(oracle.build(path, os.path.join(mutant_dir, f"lib{name}.so")))
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake {name}"
+
+
+def test_fp32_floor_on_tiny_config():
+    """The fp32 instance of the sequential loop lands ~1e-7 from the f64 oracle on the
+    tiny fp32 workload, so a 1e-5 bar for fp32 I/O is reachable."""
+    x = inputs.make_workload("causal_fp32_tiny")
+    o64, s64 = oracle.forward(**x)
+    o32, s32 = oracle.forward_f32(**x)
+    assert oracle.rel_l2(o32, o64) < 1e-6
+    assert oracle.rel_l2(s32, s64) < 1e-6
+
+
+def test_generator_distributions():
+    x = inputs.make_inputs(1, 200, 4, 32, 32, "bf16", seed=0)
+    kn = np.linalg.norm(x["k"].float().numpy(), axis=-1)
+    assert np.allclose(kn, 1.0, atol=1e-2)
+    assert 0.0 < float(x["beta"].min()) and float(x["beta"].max()) < 1.0
+    assert 0.0 < float(x["decay"].min()) and float(x["decay"].max()) < 1.0
+    # same seed, same bytes; prefix of a longer draw is not required (shapes differ)
+    assert inputs.sha256(x) == inputs.sha256(inputs.make_inputs(1, 200, 4, 32, 32, "bf16", seed=0))
+    # the strong-decay workload: a = exp(-softplus(N(2,1))) has mean ~0.13
+    y = inputs.make_inputs(1, 500, 4, 16, 16, "bf16", seed=0, a_mean=2.0)
+    assert 0.08 < float(y["decay"].mean()) < 0.2
