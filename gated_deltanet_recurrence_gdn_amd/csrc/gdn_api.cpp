@@ -1,0 +1,349 @@
+// gdn_api.cpp -- the C ABI (include/gdn.h): handle lifetime, validation,
+// dispatch to the HIP kernels on the caller's stream.
+//
+// The create/forward/free handle pattern, a NULL handle plus one stderr line on
+// a failed create, and building the object completely before publishing the
+// handle follow the librediffusion PR #21 page (sections "What's added" and the
+// review of librediffusion_sana_create).  An unavailable path is an error,
+// never a silent fallback (the sglang SANA-WM record raises when a forced GDN
+// backend fails its prechecks).
+#include "gdn.h"
+#include "gdn_launch.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+struct gdn_ctx {
+    gdn_config cfg{};
+    std::string err;
+    float *scratch = nullptr;  // fp32 [B, max_T, H, d_v] partial for the bidirectional form
+    size_t scratch_bytes = 0;
+};
+
+namespace {
+
+thread_local std::string g_create_err;
+
+int set_err(std::string &dst, int code, const char *fmt, va_list ap) {
+    char buf[512];
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    dst = buf;
+    return code;
+}
+
+int fail(gdn_ctx *h, int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    set_err(h->err, code, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int fail_create(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    set_err(g_create_err, code, fmt, ap);
+    va_end(ap);
+    fprintf(stderr, "gdn_create failed: %s\n", g_create_err.c_str());
+    return code;
+}
+
+bool valid_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+struct Range {
+    const char *name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(const Range &a, const Range &b) {
+    return a.hi > a.lo && b.hi > b.lo && a.lo < b.hi && b.lo < a.hi;
+}
+
+Range rng(const char *name, const void *p, size_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{name, lo, p ? lo + bytes : lo};
+}
+
+// Checks that p is device memory of `device` (not host memory, which would
+// fault on the GPU).  Skipped for dry-run handles.
+int check_device_ptr(gdn_ctx *h, const char *name, const void *p) {
+    if (!p || h->cfg.device < 0) return GDN_OK;
+    hipPointerAttribute_t attr;
+    hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(h, GDN_ERR_ARG, "%s: not a HIP allocation (%s)", name, hipGetErrorString(e));
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+        return fail(h, GDN_ERR_ARG, "%s: not device memory", name);
+    if (attr.device != h->cfg.device)
+        return fail(h, GDN_ERR_ARG, "%s: lives on device %d, handle is on device %d", name,
+                    attr.device, h->cfg.device);
+    return GDN_OK;
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    bool changed = false;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) == hipSuccess && prev != dev) {
+            changed = hipSetDevice(dev) == hipSuccess;
+        }
+    }
+    ~DeviceGuard() {
+        if (changed) (void)hipSetDevice(prev);
+    }
+};
+
+// Shared validation of the token tensors.  Fills sizes.
+int validate_tokens(gdn_ctx *h, const void *q, const void *k, const void *v, const float *beta,
+                    const float *decay, const void *out, long long T, size_t *qk_bytes,
+                    size_t *v_bytes, size_t *g_bytes) {
+    const gdn_config &c = h->cfg;
+    if (T < 0) return fail(h, GDN_ERR_ARG, "T = %lld is negative", T);
+    if (T > c.max_T) return fail(h, GDN_ERR_ARG, "T = %lld exceeds max_T = %lld", T, c.max_T);
+    const size_t es = c.io_dtype == GDN_BF16 ? 2 : 4;
+    const size_t tok = (size_t)c.B * (size_t)T * (size_t)c.H;
+    *qk_bytes = tok * c.d_k * es;
+    *v_bytes = tok * c.d_v * es;
+    *g_bytes = tok * sizeof(float);
+    if (T > 0) {
+        if (!q || !k || !v || !beta || !decay || !out)
+            return fail(h, GDN_ERR_ARG, "q, k, v, beta, decay and out must be non-NULL when T > 0");
+        const void *a16[] = {q, k, v, out};
+        const char *n16[] = {"q", "k", "v", "out"};
+        for (int i = 0; i < 4; ++i)
+            if (reinterpret_cast<uintptr_t>(a16[i]) % 16)
+                return fail(h, GDN_ERR_ALIGN, "%s is not 16-byte aligned", n16[i]);
+        if (reinterpret_cast<uintptr_t>(beta) % 4 || reinterpret_cast<uintptr_t>(decay) % 4)
+            return fail(h, GDN_ERR_ALIGN, "beta/decay are not 4-byte aligned");
+    }
+    return GDN_OK;
+}
+
+int check_aliasing(gdn_ctx *h, const Range *outs, int n_out, const Range *ins, int n_in,
+                   const void *state_in, const void *state_out) {
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlap(outs[i], outs[j]))
+                return fail(h, GDN_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+        for (int j = 0; j < n_in; ++j) {
+            if (overlap(outs[i], ins[j])) {
+                const bool inplace_state = state_out && state_in == state_out &&
+                                           outs[i].lo == reinterpret_cast<uintptr_t>(state_out) &&
+                                           ins[j].lo == reinterpret_cast<uintptr_t>(state_in);
+                if (!inplace_state)
+                    return fail(h, GDN_ERR_ALIAS, "%s overlaps input %s", outs[i].name, ins[j].name);
+            }
+        }
+    }
+    return GDN_OK;
+}
+
+int launch_status(gdn_ctx *h, hipError_t e, const char *what) {
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(h, GDN_ERR_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+    }
+    return GDN_OK;
+}
+
+int resolve_chunk(gdn_ctx *h, int chunk_len, int *C) {
+    if (chunk_len == 0) chunk_len = 64;
+    if (chunk_len == 1) {
+        *C = 1;
+        return GDN_OK;
+    }
+    if (!gdn::chunk_supported(chunk_len, h->cfg.d_k, h->cfg.d_v, h->cfg.io_dtype == GDN_BF16))
+        return fail(h, GDN_ERR_UNSUPPORTED,
+                    "chunk_len = %d is not supported for d_k = %d, d_v = %d, io_dtype = %d "
+                    "(use 1 for the sequential scan, 0 or 64 for the chunked form)",
+                    chunk_len, h->cfg.d_k, h->cfg.d_v, h->cfg.io_dtype);
+    *C = chunk_len;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_version(void) { return "0.1.0"; }
+
+int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
+    if (out_h) *out_h = nullptr;
+    if (!cfg || !out_h) return fail_create(GDN_ERR_ARG, "cfg and out_h must be non-NULL");
+    const gdn_config c = *cfg;
+    if (c.B < 1 || c.H < 1) return fail_create(GDN_ERR_ARG, "B = %d and H = %d must be >= 1", c.B, c.H);
+    if (!valid_dim(c.d_k) || !valid_dim(c.d_v))
+        return fail_create(GDN_ERR_UNSUPPORTED, "d_k = %d, d_v = %d: each must be 16, 32, 64 or 128",
+                           c.d_k, c.d_v);
+    if (c.io_dtype != GDN_F32 && c.io_dtype != GDN_BF16)
+        return fail_create(GDN_ERR_UNSUPPORTED, "io_dtype = %d is not GDN_F32 or GDN_BF16", c.io_dtype);
+    if (c.max_T < 0) return fail_create(GDN_ERR_ARG, "max_T = %lld is negative", c.max_T);
+    if (c.device < -1) return fail_create(GDN_ERR_ARG, "device = %d", c.device);
+    if (c.flags & ~GDN_FLAG_BIDI) return fail_create(GDN_ERR_ARG, "unknown flags 0x%x", c.flags);
+    // Element count guard: B*T*H*d must fit comfortably in 64-bit byte offsets.
+    const double elems = (double)c.B * (double)c.max_T * (double)c.H * 128.0 * 4.0;
+    if (elems > 9.0e18) return fail_create(GDN_ERR_ARG, "B*max_T*H is too large");
+
+    size_t scratch_bytes = 0;
+    if (c.flags & GDN_FLAG_BIDI) scratch_bytes = (size_t)c.B * (size_t)c.max_T * c.H * c.d_v * sizeof(float);
+
+    float *scratch = nullptr;
+    if (c.device >= 0) {
+        int n = 0;
+        hipError_t e = hipGetDeviceCount(&n);
+        if (e != hipSuccess || n == 0) {
+            (void)hipGetLastError();
+            return fail_create(GDN_ERR_DEVICE, "no HIP device available (%s)",
+                               e != hipSuccess ? hipGetErrorString(e) : "0 devices");
+        }
+        if (c.device >= n) return fail_create(GDN_ERR_DEVICE, "device %d does not exist (%d devices)", c.device, n);
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, c.device);
+        if (e != hipSuccess) return fail_create(GDN_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+            return fail_create(GDN_ERR_DEVICE, "device %d is %s; this library is built for gfx950",
+                               c.device, prop.gcnArchName);
+        if (scratch_bytes) {
+            DeviceGuard g(c.device);
+            e = hipMalloc(reinterpret_cast<void **>(&scratch), scratch_bytes);
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                return fail_create(GDN_ERR_OOM, "hipMalloc(%zu bytes) for the bidirectional partial: %s",
+                                   scratch_bytes, hipGetErrorString(e));
+            }
+        }
+    }
+    gdn_ctx *h = new (std::nothrow) gdn_ctx;
+    if (!h) {
+        if (scratch) (void)hipFree(scratch);
+        return fail_create(GDN_ERR_OOM, "out of host memory");
+    }
+    h->cfg = c;
+    h->scratch = scratch;
+    h->scratch_bytes = scratch_bytes;
+    *out_h = h;
+    g_create_err.clear();
+    return GDN_OK;
+}
+
+void gdn_free(gdn_handle h) {
+    if (!h) return;
+    if (h->scratch) {
+        DeviceGuard g(h->cfg.device);
+        (void)hipFree(h->scratch);
+    }
+    delete h;
+}
+
+const char *gdn_last_error(gdn_handle h) { return h ? h->err.c_str() : g_create_err.c_str(); }
+
+int gdn_forward(gdn_handle h, const void *q, const void *k, const void *v, const float *beta,
+                const float *decay, const float *state_in, float *state_out, void *out, long long T,
+                int chunk_len, void *hip_stream) {
+    if (!h) {
+        g_create_err = "gdn_forward: NULL handle";
+        return GDN_ERR_ARG;
+    }
+    h->err.clear();
+    const gdn_config &c = h->cfg;
+    size_t qk_bytes, v_bytes, g_bytes;
+    int st = validate_tokens(h, q, k, v, beta, decay, out, T, &qk_bytes, &v_bytes, &g_bytes);
+    if (st) return st;
+    int C = 0;
+    if ((st = resolve_chunk(h, chunk_len, &C))) return st;
+    const size_t s_bytes = (size_t)c.B * c.H * c.d_v * c.d_k * sizeof(float);
+    if ((state_in && reinterpret_cast<uintptr_t>(state_in) % 16) ||
+        (state_out && reinterpret_cast<uintptr_t>(state_out) % 16))
+        return fail(h, GDN_ERR_ALIGN, "state_in/state_out are not 16-byte aligned");
+    const bool tok = T > 0;
+    Range outs[2];
+    int n_out = 0;
+    if (tok) outs[n_out++] = rng("out", out, v_bytes);
+    if (state_out) outs[n_out++] = rng("state_out", state_out, s_bytes);
+    Range ins[6];
+    int n_in = 0;
+    if (tok) {
+        ins[n_in++] = rng("q", q, qk_bytes);
+        ins[n_in++] = rng("k", k, qk_bytes);
+        ins[n_in++] = rng("v", v, v_bytes);
+        ins[n_in++] = rng("beta", beta, g_bytes);
+        ins[n_in++] = rng("decay", decay, g_bytes);
+    }
+    if (state_in) ins[n_in++] = rng("state_in", state_in, s_bytes);
+    if ((st = check_aliasing(h, outs, n_out, ins, n_in, state_in, state_out))) return st;
+    if (c.device < 0) return GDN_OK;  // dry run: validated, nothing launched
+
+    const void *ptrs[] = {q, k, v, beta, decay, state_in, state_out, out};
+    const char *names[] = {"q", "k", "v", "beta", "decay", "state_in", "state_out", "out"};
+    for (int i = 0; i < 8; ++i) {
+        if (!tok && i != 5 && i != 6) continue;
+        if ((st = check_device_ptr(h, names[i], ptrs[i]))) return st;
+    }
+    if (!tok && !state_out) return GDN_OK;  // nothing to compute or write
+
+    DeviceGuard g(c.device);
+    gdn::PassArgs a{};
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.decay = decay;
+    a.state_in = state_in; a.state_out = state_out; a.out = out; a.partial = nullptr;
+    a.B = c.B; a.H = c.H; a.dk = c.d_k; a.dv = c.d_v; a.T = T;
+    a.io_bf16 = c.io_dtype == GDN_BF16; a.reverse = 0; a.out_mode = gdn::OUT_STORE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+    hipError_t e = (C == 1) ? gdn::launch_scan(a, s) : gdn::launch_chunk(a, C, s);
+    return launch_status(h, e, C == 1 ? "scan" : "chunked");
+}
+
+int gdn_forward_bidi(gdn_handle h, const void *q, const void *k, const void *v, const float *beta,
+                     const float *decay, void *out, long long T, int chunk_len, void *hip_stream) {
+    if (!h) {
+        g_create_err = "gdn_forward_bidi: NULL handle";
+        return GDN_ERR_ARG;
+    }
+    h->err.clear();
+    const gdn_config &c = h->cfg;
+    if (!(c.flags & GDN_FLAG_BIDI))
+        return fail(h, GDN_ERR_ARG, "gdn_forward_bidi needs a handle created with GDN_FLAG_BIDI");
+    size_t qk_bytes, v_bytes, g_bytes;
+    int st = validate_tokens(h, q, k, v, beta, decay, out, T, &qk_bytes, &v_bytes, &g_bytes);
+    if (st) return st;
+    int C = 0;
+    if ((st = resolve_chunk(h, chunk_len, &C))) return st;
+    if (T == 0) return GDN_OK;
+    Range outs[1] = {rng("out", out, v_bytes)};
+    Range ins[5] = {rng("q", q, qk_bytes), rng("k", k, qk_bytes), rng("v", v, v_bytes),
+                    rng("beta", beta, g_bytes), rng("decay", decay, g_bytes)};
+    if ((st = check_aliasing(h, outs, 1, ins, 5, nullptr, nullptr))) return st;
+    if (c.device < 0) return GDN_OK;
+    const void *ptrs[] = {q, k, v, beta, decay, out};
+    const char *names[] = {"q", "k", "v", "beta", "decay", "out"};
+    for (int i = 0; i < 6; ++i)
+        if ((st = check_device_ptr(h, names[i], ptrs[i]))) return st;
+
+    DeviceGuard g(c.device);
+    gdn::PassArgs a{};
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.decay = decay;
+    a.state_in = nullptr; a.state_out = nullptr; a.out = out; a.partial = h->scratch;
+    a.B = c.B; a.H = c.H; a.dk = c.d_k; a.dv = c.d_v; a.T = T;
+    a.io_bf16 = c.io_dtype == GDN_BF16;
+    hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+    // Forward direction into the fp32 partial, then the reverse direction adds
+    // its own output, rounding the sum once.
+    a.reverse = 0;
+    a.out_mode = gdn::OUT_PARTIAL;
+    hipError_t e = (C == 1) ? gdn::launch_scan(a, s) : gdn::launch_chunk(a, C, s);
+    if ((st = launch_status(h, e, "bidirectional forward pass"))) return st;
+    a.reverse = 1;
+    a.out_mode = gdn::OUT_COMBINE;
+    e = (C == 1) ? gdn::launch_scan(a, s) : gdn::launch_chunk(a, C, s);
+    return launch_status(h, e, "bidirectional reverse pass");
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// gdn_common.h -- small device helpers shared by the GDN kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest even
+// (NaN stays NaN).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Cross-lane data movement inside a row of 16 lanes (DPP).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of L consecutive lanes (L in {1, 2, 4, 8, 16}); every
+// lane of the group receives the group sum.
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(L == 1 || L == 2 || L == 4 || L == 8 || L == 16, "group size");
+    if constexpr (L >= 2) x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (L >= 4) x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (L >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror: other quad of the 8
+    if constexpr (L >= 16) x += dpp_mov<0x140>(x); // row_mirror: other half of the 16
+    return x;
+}
+
+}  // namespace gdn

@@ -1,0 +1,136 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated-Delta-Net recurrence library.
+ *
+ * The operation.  Per batch element b and head h, independently, over tokens
+ * t = 0 .. T-1 with a d_v x d_k fp32 state S:
+ *
+ *     S_t = a_t * S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T
+ *     o_t = S_t q_t / sqrt(d_k)
+ *
+ * This is the GDN (Gated-Delta-Net) linear-attention recurrence of the SANA
+ * video DiTs: the librediffusion PR #21 page ("feat(sana): in-tree
+ * SANA-Streaming V2V DiT (GDN linear-attention) + C-API", section "What's
+ * added") ships it as a CUDA kernel behind a C API, and the sglang SANA-WM
+ * record (errors.standardbeagle.com page, field sourceCode) names its inputs
+ * q, k, v, beta, decay.  The state carried from call to call is the "causal
+ * linear attention KV cache" of the diffusers LongSANA PR page (section
+ * "PR feature"); the bidirectional form is the full-sequence SANA-WM variant
+ * of the FlashDreams "SANA-WM" page (section "Bidirectional variant").  The
+ * pages do not print the update; the formula above is the gated delta rule.
+ *
+ * beta (b_t) and decay (a_t) are plain values in [0, 1], one per token and
+ * head -- not logits, not log-decays.  The library does not normalise q or k
+ * and applies no gate activation; callers do that beforehand.
+ *
+ * Layouts.  Every tensor pointer is a DEVICE pointer to a contiguous,
+ * row-major array on the handle's device:
+ *     q, k       [B, T, H, d_k]   io_dtype
+ *     v, out     [B, T, H, d_v]   io_dtype
+ *     beta,decay [B, T, H]        float32
+ *     state      [B, H, d_v, d_k] float32  (row i is output channel i: o = S q)
+ * q, k, v, out and the states must be 16-byte aligned; beta and decay 4-byte.
+ *
+ * Ownership.  The caller owns every tensor and the stream.  The library owns
+ * the handle and its device scratch, allocated once in gdn_create and freed in
+ * gdn_free.  gdn_forward and gdn_forward_bidi allocate nothing, never
+ * synchronise and never copy between host and device: they validate, enqueue
+ * kernels on the given stream and return.  Device faults surface at the
+ * caller's next synchronisation, as with any HIP launch.  A handle must be
+ * used by one host thread at a time; separate handles are independent.
+ *
+ * Errors.  Every call returns GDN_OK (0) or a negative gdn_status; nothing is
+ * thrown across this boundary and no call silently falls back to another
+ * algorithm.  Validation happens before any launch, so a rejected call leaves
+ * out and state_out untouched.  gdn_last_error() describes the last failure.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gdn_ctx *gdn_handle; /* opaque; hides every HIP type */
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_ARG = -1,         /* NULL pointer, bad size, T > max_T, ...        */
+    GDN_ERR_UNSUPPORTED = -2, /* d_k/d_v not in {16,32,64,128}, dtype, chunk_len */
+    GDN_ERR_ALIGN = -3,       /* pointer alignment (see Layouts)               */
+    GDN_ERR_ALIAS = -4,       /* an output overlaps an input or another output */
+    GDN_ERR_DEVICE = -5,      /* no such device, not gfx950, HIP runtime error  */
+    GDN_ERR_OOM = -6,         /* scratch allocation failed in gdn_create        */
+    GDN_ERR_LAUNCH = -7       /* kernel launch was rejected                     */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Request the scratch that gdn_forward_bidi needs (B * max_T * H * d_v fp32). */
+#define GDN_FLAG_BIDI 1u
+
+typedef struct {
+    int device;        /* HIP device ordinal; -1 = dry run (validate only, no GPU) */
+    int B, H;          /* batch and heads, >= 1                                   */
+    int d_k, d_v;      /* head dims, each in {16, 32, 64, 128}                    */
+    int io_dtype;      /* gdn_dtype of q, k, v and out                            */
+    long long max_T;   /* largest T any call on this handle will pass, >= 0       */
+    unsigned flags;    /* GDN_FLAG_* bits                                         */
+} gdn_config;
+
+/*
+ * Create a handle.  On success *out_h holds it and GDN_OK is returned.  On
+ * failure *out_h is set to NULL, a negative status is returned and one line
+ * is printed to stderr (gdn_last_error(NULL) repeats it).  device = -1 gives
+ * a dry-run handle: every call is fully validated and then returns GDN_OK
+ * without touching a GPU.
+ */
+int gdn_create(const gdn_config *cfg, gdn_handle *out_h);
+
+/*
+ * Causal recurrence over T tokens (0 <= T <= max_T), starting from state_in
+ * and leaving the final state in state_out.
+ *   state_in   NULL = zero initial state; never written unless it is state_out.
+ *   state_out  NULL = final state discarded; may equal state_in (in-place carry).
+ *   chunk_len  1 = sequential scan; 64 = chunked form with 64-token chunks;
+ *              0 = default (64).  Others return GDN_ERR_UNSUPPORTED.
+ *   hip_stream a hipStream_t (NULL = the null stream of the handle's device).
+ * Streaming: calling with consecutive token ranges and state_out of one call
+ * as state_in of the next reproduces a single call over the whole range.
+ * With chunk_len = 1 the result is bit-identical to the single call; with the
+ * chunked form it is bit-identical when every call but the last is a multiple
+ * of chunk_len long, and equal within rounding otherwise.
+ * T = 0 is valid: state_out receives state_in (or zeros); out is untouched.
+ */
+int gdn_forward(gdn_handle h, const void *q, const void *k, const void *v,
+                const float *beta, const float *decay,
+                const float *state_in, float *state_out, void *out,
+                long long T, int chunk_len, void *hip_stream);
+
+/*
+ * Bidirectional form over one full sequence:
+ *     out = fwd(x; S = 0) + R(fwd(R x; S = 0)),
+ * R reversing the token axis; token t is counted by both directions.  The two
+ * directions' outputs are summed in fp32 and rounded once to io_dtype.  The
+ * reverse pass places its chunk grid from token T-1 downwards, so reversing the
+ * inputs reverses the output exactly.  Needs a handle created with
+ * GDN_FLAG_BIDI.  No state is read or returned.
+ */
+int gdn_forward_bidi(gdn_handle h, const void *q, const void *k, const void *v,
+                     const float *beta, const float *decay, void *out,
+                     long long T, int chunk_len, void *hip_stream);
+
+/* Release the handle and its scratch.  NULL is a no-op. */
+void gdn_free(gdn_handle h);
+
+/* Message of the last failed call on h (NULL: last gdn_create failure on
+ * this thread).  Never NULL; "" when there was none.  Valid until the next
+ * call on the same handle. */
+const char *gdn_last_error(gdn_handle h);
+
+/* Library version, "major.minor.patch". */
+const char *gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

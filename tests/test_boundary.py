@@ -1,0 +1,156 @@
+"""The C ABI without a GPU: the library loads, exports every symbol include/gdn.h
+declares, and validates arguments on dry-run handles (device = -1), which check
+everything and launch nothing.  Pointers here are fake, well-separated addresses;
+a dry-run handle never dereferences them."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_recurrence_gdn_amd import binding as gb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "gdn.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) >= {"gdn_create", "gdn_forward", "gdn_forward_bidi", "gdn_free",
+                          "gdn_last_error", "gdn_version"}
+    lib = ctypes.CDLL(gb.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in gdn.h but not exported"
+
+
+def test_version():
+    assert re.fullmatch(r"\d+\.\d+\.\d+", gb.gdn_version())
+
+
+# Fake device addresses: 1 GiB apart, 256-byte aligned.
+BASE = 1 << 40
+GiB = 1 << 30
+ADDR = {n: BASE + i * GiB for i, n in enumerate(["q", "k", "v", "beta", "decay", "s_in", "s_out", "out"])}
+
+
+@pytest.fixture
+def dry():
+    st, h = gb.gdn_create(-1, 2, 3, 64, 32, gb.GDN_BF16, 1000, gb.GDN_FLAG_BIDI)
+    assert st == gb.GDN_OK and h
+    yield h
+    gb.gdn_free(h)
+
+
+def fwd(h, T=100, chunk=1, **over):
+    a = dict(ADDR)
+    a.update(over)
+    return gb.gdn_forward(h, a["q"], a["k"], a["v"], a["beta"], a["decay"], a["s_in"], a["s_out"],
+                          a["out"], T, chunk)
+
+
+def test_dry_run_valid_calls(dry):
+    assert fwd(dry) == gb.GDN_OK
+    assert fwd(dry, s_in=None, s_out=None) == gb.GDN_OK
+    assert fwd(dry, s_out=ADDR["s_in"]) == gb.GDN_OK  # in-place carry
+    assert fwd(dry, T=1000) == gb.GDN_OK
+    assert fwd(dry, T=0, q=None, k=None, v=None, beta=None, decay=None, out=None) == gb.GDN_OK
+    assert gb.gdn_last_error(dry) == ""
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(T=1001), gb.GDN_ERR_ARG),
+    (dict(T=-1), gb.GDN_ERR_ARG),
+    (dict(q=None), gb.GDN_ERR_ARG),
+    (dict(out=None), gb.GDN_ERR_ARG),
+    (dict(decay=None), gb.GDN_ERR_ARG),
+    (dict(chunk=7), gb.GDN_ERR_UNSUPPORTED),
+    (dict(chunk=-1), gb.GDN_ERR_UNSUPPORTED),
+    (dict(q=ADDR["q"] + 8), gb.GDN_ERR_ALIGN),
+    (dict(out=ADDR["out"] + 2), gb.GDN_ERR_ALIGN),
+    (dict(beta=ADDR["beta"] + 2), gb.GDN_ERR_ALIGN),
+    (dict(s_in=ADDR["s_in"] + 4), gb.GDN_ERR_ALIGN),
+    (dict(out=ADDR["q"]), gb.GDN_ERR_ALIAS),
+    (dict(out=ADDR["v"] + 4096), gb.GDN_ERR_ALIAS),
+    (dict(s_out=ADDR["s_in"] + 64), gb.GDN_ERR_ALIAS),
+    (dict(s_out=ADDR["out"] + 256), gb.GDN_ERR_ALIAS),
+    (dict(s_out=ADDR["k"]), gb.GDN_ERR_ALIAS),
+])
+def test_dry_run_rejections(dry, over, code):
+    assert fwd(dry, **over) == code
+    assert gb.gdn_last_error(dry) != ""
+
+
+def test_beta_unaligned_to_16_is_accepted(dry):
+    # gates only need 4-byte alignment (a streaming call can start at any token)
+    assert fwd(dry, beta=ADDR["beta"] + 4, decay=ADDR["decay"] + 12) == gb.GDN_OK
+
+
+def test_alias_edges(dry):
+    # out ends exactly where q begins: adjacent, not overlapping
+    out_bytes = 2 * 100 * 3 * 32 * 2
+    assert fwd(dry, out=ADDR["q"] - out_bytes) == gb.GDN_OK
+    assert fwd(dry, out=ADDR["q"] - out_bytes + 16) == gb.GDN_ERR_ALIAS
+
+
+def test_bidi_dry_run(dry):
+    a = ADDR
+    assert gb.gdn_forward_bidi(dry, a["q"], a["k"], a["v"], a["beta"], a["decay"], a["out"], 100, 1) == gb.GDN_OK
+    assert gb.gdn_forward_bidi(dry, a["q"], a["k"], a["v"], a["beta"], a["decay"], a["q"], 100, 1) == gb.GDN_ERR_ALIAS
+    st, h = gb.gdn_create(-1, 1, 1, 16, 16, gb.GDN_F32, 10, 0)
+    assert gb.gdn_forward_bidi(h, a["q"], a["k"], a["v"], a["beta"], a["decay"], a["out"], 5, 1) == gb.GDN_ERR_ARG
+    assert "GDN_FLAG_BIDI" in gb.gdn_last_error(h)
+    gb.gdn_free(h)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 0, 1, 16, 16, gb.GDN_F32, 10, 0), gb.GDN_ERR_ARG),
+    ((-1, 1, 0, 16, 16, gb.GDN_F32, 10, 0), gb.GDN_ERR_ARG),
+    ((-1, 1, 1, 24, 16, gb.GDN_F32, 10, 0), gb.GDN_ERR_UNSUPPORTED),
+    ((-1, 1, 1, 16, 256, gb.GDN_F32, 10, 0), gb.GDN_ERR_UNSUPPORTED),
+    ((-1, 1, 1, 16, 16, 7, 10, 0), gb.GDN_ERR_UNSUPPORTED),
+    ((-1, 1, 1, 16, 16, gb.GDN_F32, -1, 0), gb.GDN_ERR_ARG),
+    ((-1, 1, 1, 16, 16, gb.GDN_F32, 10, 8), gb.GDN_ERR_ARG),
+    ((-2, 1, 1, 16, 16, gb.GDN_F32, 10, 0), gb.GDN_ERR_ARG),
+])
+def test_create_rejections(args, code, capfd):
+    st, h = gb.gdn_create(*args)
+    assert st == code and h is None
+    assert gb.gdn_last_error(None) != ""
+    assert "gdn_create failed" in capfd.readouterr().err
+
+
+def test_create_null_args():
+    lib = gb.library()
+    assert lib.gdn_create(None, None) == gb.GDN_ERR_ARG
+    cfg = gb.gdn_config(-1, 1, 1, 16, 16, 0, 1, 0)
+    assert lib.gdn_create(ctypes.byref(cfg), None) == gb.GDN_ERR_ARG
+
+
+def test_free_null_and_null_handle_calls():
+    gb.gdn_free(None)
+    assert isinstance(gb.gdn_last_error(None), str)
+    assert gb.gdn_forward(None, 0, 0, 0, 0, 0, None, None, 0, 0, 1) == gb.GDN_ERR_ARG
+
+
+def test_create_without_gpu_is_device_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st, h = gb.gdn_create(0, 1, 1, 16, 16, gb.GDN_F32, 10, 0)
+    assert st == gb.GDN_ERR_DEVICE and h is None
+
+
+def test_torch_wrapper_checks_shapes():
+    import torch
+    g = gb.GDN(1, 2, 16, 16, "fp32", max_T=10, device=-1)
+    x = torch.zeros(1, 4, 2, 16)
+    with pytest.raises(ValueError):
+        g.forward(x, x, x, torch.zeros(1, 4, 3), torch.zeros(1, 4, 2), out=x, state_out=None,
+                  return_state=False)
+    g.close()
