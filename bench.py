@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the GDN recurrence library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one gdn_forward call of the chunked causal form (64-token chunks, bf16
+MFMA) with the fp32 state carried in and out, over the batched d=128 workload:
+B=2 (guidance pair), H=32, T=32760 (21 latent frames x 30x52 tokens),
+d_k=d_v=128, bf16 q/k/v/out, fp32 beta/decay/state, decay a = exp(-softplus(N(2,1))).
+Inputs are seeded synthetic data (see gated_deltanet_recurrence_gdn_amd/inputs.py),
+resident in HBM before timing starts.
+
+Prints ONE JSON line: throughput in token*heads/s, the dominant kernel's HBM
+roofline (algorithmic bytes / average kernel time from HIP events on the launch
+stream), its MFMA utilisation, the float64 CPU oracle timed on a bounded sample of
+the same inputs, and secondary measurements of the other forms (sequential scan,
+5-call streaming, bidirectional).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+FP32_VALU_PEAK_TFS = 157.3   # MI355X fp32 vector (published, packed)
+CHUNK_KERNEL = "chunk_kernel"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def algorithmic_bytes(B, T, H, dk, dv, es=2):
+    """q, k, v read and out written in the I/O dtype, beta and decay read in fp32, the
+    fp32 state read once and written once."""
+    return B * T * H * ((2 * dk + 2 * dv) * es + 8) + 2 * B * H * dk * dv * 4
+
+
+def chunk_flops(B, T, H, dk, dv, C=64):
+    """Dense-tile flop count of the chunked form per token*head:
+    6 dk dv (K S^T, Q S^T and the state update) + 2C(3dk + 2dv) (K K^T, Q K^T, T R, P N
+    and the chunk-local products) + C^2/3 (the triangular inverse)."""
+    return B * T * H * (6 * dk * dv + 2 * C * (3 * dk + 2 * dv) + C * C / 3.0)
+
+
+def scan_flops(B, T, H, dk, dv):
+    """Two dot products and one rank-1 update per state row: 6 dk dv per token*head."""
+    return B * T * H * 6 * dk * dv
+
+
+def src_hash(name):
+    p = os.path.join(ROOT, "gated_deltanet_recurrence_gdn_amd", "csrc", name)
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per launch of the chunked kernel from the committed rocprofv3 --pmc
+    summary, if it was taken on the current kernel source; else None."""
+    p = os.path.join(PROFILES, f"chunk_kernel_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha256_16") != src_hash("gdn_chunk.hip"):
+        return None
+    return t
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192,
+                    help="tokens per head of the oracle's CPU sample (prefix of the same inputs)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-forms", action="store_true", help="skip the secondary forms")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the per-head recurrence shards over (b, h) with no exchange, but no "
+              "multi-GPU path is built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_deltanet_recurrence_gdn_amd import inputs
+    from gated_deltanet_recurrence_gdn_amd import binding as gb
+
+    w = inputs.WORKLOADS["batched_bf16_d128"]
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    t0 = time.time()
+    x = inputs.make_workload(w)
+    gen_s = time.time() - t0
+    d = {k_: v_.cuda() for k_, v_ in x.items()}
+    s_in = torch.zeros((B, H, dv, dk), dtype=torch.float32, device="cuda")
+    s_out = torch.empty_like(s_in)
+    out = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device="cuda")
+    g = gb.GDN(B, H, dk, dv, "bf16", max_T=T)
+    stream = gb.current_stream()
+
+    def step():
+        st = gb.gdn_forward(g.h, d["q"], d["k"], d["v"], d["beta"], d["decay"], s_in, s_out, out, T, 64,
+                            stream)
+        if st != gb.GDN_OK:
+            raise gb.GDNError(st, gb.gdn_last_error(g.h))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = ev0.elapsed_time(ev1) / args.steps  # one kernel launch per step
+    ms_per_step = wall * 1000.0 / args.steps
+    th = B * H * T
+    value = th / (ms_per_step / 1000.0)
+
+    abytes = algorithmic_bytes(B, T, H, dk, dv)
+    achieved = abytes / (kern_ms / 1000.0) / 1e9
+    flops = chunk_flops(B, T, H, dk, dv)
+    mfma_tfs = flops / (kern_ms / 1000.0) / 1e12
+    traffic = load_traffic(w.name)
+
+    result = {
+        "metric": "GDN tokens*heads/sec at d=128 (chunked causal form) + achieved HBM GB/s and MFMA % of peak",
+        "value": value,
+        "unit": "token*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; inputs.py recipe)",
+        "config": {"workload": w.name, "B": B, "H": H, "T": T, "d_k": dk, "d_v": dv, "chunk_len": 64,
+                   "form": "chunked causal, fp32 state in/out", "decay": "exp(-softplus(N(2,1)))"},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": CHUNK_KERNEL,
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": (traffic["bytes_per_launch"] if traffic else None),
+            "algorithmic_bytes_per_launch": abytes,
+            "kernel_ms": kern_ms,
+        },
+        "mfma": {"achieved": mfma_tfs, "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                 "frac": mfma_tfs / BF16_MFMA_PEAK_TFS, "flops_per_launch": flops},
+    }
+
+    if not args.no_forms:
+        result["forms"] = measure_forms(torch, gb, inputs, d, g, x)
+    g.close()
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(x, args.cpu_sample_tokens)
+    result["input_gen_s"] = round(gen_s, 2)
+    print(json.dumps(result), flush=True)
+
+
+def timed(torch, fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def measure_forms(torch, gb, inputs, d, g, x):
+    forms = {}
+    B, T, H, dk = d["q"].shape
+    dv = d["v"].shape[-1]
+    stream = gb.current_stream()
+    out = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device="cuda")
+
+    # Sequential scan form on the same inputs.
+    def scan():
+        assert gb.gdn_forward(g.h, d["q"], d["k"], d["v"], d["beta"], d["decay"], None, None, out, T, 1,
+                              stream) == 0
+    ms = timed(torch, scan, 3)
+    fl = scan_flops(B, T, H, dk, dv)
+    forms["scan_batched_bf16_d128"] = {
+        "ms": ms, "token_heads_per_s": B * H * T / (ms / 1e3), "bound": "alu",
+        "achieved_tflops": fl / (ms / 1e3) / 1e12, "peak_tflops": FP32_VALU_PEAK_TFS,
+        "hbm_gbs": algorithmic_bytes(B, T, H, dk, dv) / (ms / 1e3) / 1e9}
+
+    # 5-call streaming (state carried) vs one call over the same 23400 tokens.
+    w = inputs.WORKLOADS["streaming_bf16_d128"]
+    xs = {k_: v_.cuda() for k_, v_ in inputs.make_workload(w).items()}
+    gs = gb.GDN(w.B, w.H, w.dk, w.dv, "bf16", max_T=w.T)
+    n = w.T // w.calls
+    parts = [{k_: v_[:, i * n:(i + 1) * n].contiguous() for k_, v_ in xs.items()} for i in range(w.calls)]
+    state = torch.zeros((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
+    outs = [torch.empty((w.B, n, w.H, w.dv), dtype=torch.bfloat16, device="cuda") for _ in range(w.calls)]
+    out1 = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
+    per_call = []
+    for i in range(w.calls):
+        pi = parts[i]
+        per_call.append(timed(torch, lambda: gb.gdn_forward(gs.h, pi["q"], pi["k"], pi["v"], pi["beta"],
+                                                            pi["decay"], state, state, outs[i], n, 64, stream), 5))
+    one = timed(torch, lambda: gb.gdn_forward(gs.h, xs["q"], xs["k"], xs["v"], xs["beta"], xs["decay"], None,
+                                              state, out1, w.T, 64, stream), 5)
+    forms["streaming_bf16_d128"] = {"per_call_ms": per_call, "sum_ms": sum(per_call), "one_shot_ms": one,
+                                    "token_heads_per_s": w.B * w.H * w.T / (sum(per_call) / 1e3)}
+    gs.close()
+    del xs, parts
+
+    # Bidirectional form, 21 frames.
+    wb = inputs.WORKLOADS["bidi_bf16_d128"]
+    xb = {k_: v_.cuda() for k_, v_ in inputs.make_workload(wb).items()}
+    gbd = gb.GDN(wb.B, wb.H, wb.dk, wb.dv, "bf16", max_T=wb.T, bidi=True)
+    ob = torch.empty((wb.B, wb.T, wb.H, wb.dv), dtype=torch.bfloat16, device="cuda")
+    ms = timed(torch, lambda: gb.gdn_forward_bidi(gbd.h, xb["q"], xb["k"], xb["v"], xb["beta"], xb["decay"],
+                                                  ob, wb.T, 64, stream), 5)
+    forms["bidi_bf16_d128"] = {"ms": ms, "token_heads_per_s": wb.B * wb.H * wb.T / (ms / 1e3),
+                               "design": "two passes through an fp32 partial"}
+    gbd.close()
+    return forms
+
+
+def cpu_baseline(x, tokens):
+    import oracle
+    Ts = min(tokens, x["q"].shape[1])
+    sample = {k_: v_[:, :Ts].contiguous() for k_, v_ in x.items()}
+    B, _, H, _ = sample["q"].shape
+    t0 = time.perf_counter()
+    oracle.forward(**sample)
+    dt = time.perf_counter() - t0
+    th = B * H * Ts
+    return {"value": th / dt, "unit": "token*heads/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"float64 sequential oracle on the first {Ts} tokens of every head of the same "
+                      f"inputs (B={B}, H={H}): {th} token*heads, including the bf16->f64 widening"}
+
+
+if __name__ == "__main__":
+    main()
