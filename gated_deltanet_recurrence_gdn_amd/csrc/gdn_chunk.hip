@@ -1,7 +1,7 @@
 // gdn_chunk.hip -- chunked (UT-transform) form of the GDN recurrence on bf16 MFMA.
 //
 // Within a chunk of C tokens starting from state S0 (d_v x d_k), with
-// g_i = sum_{r<=i} log a_r, gam_i = e^{g_i}, G_ij = e^{g_i - g_j} (j <= i):
+// g_i = sum_{r<=i} log2 a_r, gam_i = 2^{g_i}, G_ij = 2^{g_i - g_j} (j <= i):
 //
 //   A  = strict_lower(diag(b) (K K^T .* G))             C x C
 //   Tm = (I + A)^{-1}                                   unit lower triangular
@@ -12,35 +12,56 @@
 //
 // This is the sequential recurrence S_t = a_t S_{t-1}(I - b_t k_t k_t^T) +
 // b_t v_t k_t^T rewritten over a block of tokens (the chunkwise WY/UT form; the
-// sglang SANA-WM record names its Triton kernel cam_scan_bidi_chunkwise).  The
-// C x C and C x d products are dense contractions and run on
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
+// sglang SANA-WM record names its Triton kernel cam_scan_bidi_chunkwise).  Every
+// C x C and C x d product runs on MFMA (bf16 operands, fp32 accumulation).
 //
 // Parallel decomposition.  Rows of S are independent, so a block owns one
-// (b, h) and a 32-wide tile of d_v and walks the head's chunks in order,
-// holding its 32 x d_k slice of S in fp32 accumulator registers for the whole
-// call.  The S-independent per-chunk work (Gram products, decay factors, the
-// triangular inverse) is recomputed by each of the d_v/32 tiles of a head:
-// that costs MFMA time but keeps HBM traffic at one read of q/k (the tiles of
-// a head are placed on the same XCD so the repeats hit its L2) and buys the
-// CU count the sequential chunk chain needs.
+// (b, h) and a 32-wide tile of d_v and walks the head's chunks in order, with
+// its 32 x d_k slice of S in fp32 accumulator registers for the whole call.
+// The S-independent per-chunk work (decay factors, Gram products, the
+// triangular inverse) is recomputed by each d_v tile of a head: that costs MFMA
+// time but keeps HBM traffic at one read of q/k per head (the tiles of a head
+// are placed on one XCD so the repeats hit its L2) and buys the CU count the
+// sequential chunk chain needs.
 //
-// Operand layouts.  A 32x32 MFMA accumulator holds 4 consecutive ROWS per
-// lane, so every product is arranged so that its output rows are the K
-// dimension of the product that consumes it:
-//   K K^T, K Q^T are computed as (keys x queries): A and P land row-major;
-//   K S^T, Q S^T  (tokens x d_v): R lands as R^T [d_v][token];
-//   N = Tm R      (tokens x d_v): N^T [d_v][token];
-//   S^T += K^T N~ (d_k x d_v): the state lands as S [d_v][d_k].
-// Only K needs a transposed copy in LDS (for the state update).
+// Software pipeline.  Iteration c runs the state chain of chunk c and prepares
+// chunk c+1, in three barrier-separated phases:
+//   phase 1: X = [K;Q] S^T (8 MFMA per wave), R = diag(b)(V - diag(gam) K S^T);
+//            off-diagonal blocks of Tm for chunk c; decay factors of chunk c+1;
+//            global loads for chunk c+2 issued
+//   phase 2: N = Tm R;  Gram products K K^T, K Q^T of chunk c+1 -> A, P
+//   phase 3: O = diag(gam) Q S^T + P N (stored);  S update;  16x16 diagonal
+//            blocks of Tm for chunk c+1;  chunk c+2 staged into LDS
+// Each wave owns one 32-token row block of K or Q (wave 0: K rows 0-31, 1: K
+// rows 32-63, 2: Q rows 0-31, 3: Q rows 32-63), loaded from HBM straight into
+// registers in MFMA operand layout and prefetched two chunks ahead; the same
+// registers serve the Gram products of chunk c+1 and the state products of
+// chunk c+1.  K is also kept token-major in LDS (three chunk buffers) and read
+// transposed with ds_read_b64_tr_b16 where a product contracts over tokens.
 //
-// Decay numerics: g is accumulated in float64 from log a (a = 0 is clamped to
-// log a = -1000, which makes every factor across that token exactly 0 in
-// fp32), and only e^{g_i - g_j} for j <= i is ever formed, so nothing
-// overflows however strong the decay.
+// Operand layouts.  A 32x32 MFMA accumulator holds 4 consecutive rows per
+// lane, so products are oriented so that accumulator rows are the contraction
+// index of the consumer, or the output is contiguous in memory:
+//   K K^T, K Q^T as (keys x queries): A and P land row-major;
+//   K S^T (tokens x d_v): R lands as R^T [d_v][token];
+//   N = Tm R (tokens x d_v): N^T [d_v][token];
+//   O^T = S Q^T + N^T P^T (d_v x tokens): 4 consecutive d_v per lane -> 8-byte stores;
+//   S^T += K^T N~ (d_k x d_v): the state lands as S [d_v][d_k] for the next X.
+// For the 16x16x16 MFMA the accumulator layout equals the B-operand layout, so
+// the triangular-inverse chains pass blocks from one product to the next in
+// registers.
 //
-// A final chunk shorter than C is padded with k = q = v = 0, b = 0, a = 1,
-// which leaves every product exact for the real tokens.
+// Triangular inverse.  Tm's four 16x16 diagonal blocks are inverted in fp32
+// on the VALU (one row per lane, backward substitution on (I + A)^T); the
+// off-diagonal blocks follow block column by block column,
+//   T_rc = -T_rr * sum_{k=c}^{r-1} A_rk T_kc,
+// on 16x16x16 bf16 MFMA, one block column per wave.
+//
+// Decay numerics: log2 a is accumulated in float64 (a = 0 is clamped to
+// log2 a = -1e4, which makes every factor across that token exactly 0), and
+// only 2^{g_i - g_j} for j <= i is ever formed, so nothing overflows however
+// strong the decay.  A final chunk shorter than C is padded with k = q = v = 0,
+// b = 0, a = 1, which leaves every product exact for the real tokens.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -48,11 +69,15 @@ namespace gdn {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;     // chunk length
 constexpr int NT = 256;   // threads per block: 4 waves
 constexpr int DVT = 32;   // d_v columns per block
+constexpr int LC = C + 8; // padded bf16 row pitch of C-long rows
+constexpr int LV = DVT + 8;
 
 struct ChunkParams {
     const uint16_t *q, *k, *v;
@@ -62,95 +87,128 @@ struct ChunkParams {
     void *out;
     float *partial;
     long long T;
-    int H, dv, ntile, nblocks;
+    int H, dv, ntile;
     int reverse, out_mode, xcd_remap;
     float scale;
 };
 
-__device__ __forceinline__ f32x16_t mfma(const bf16x8_t a, const bf16x8_t b, f32x16_t c) {
+template <int DK>
+struct __align__(16) Smem {
+    static constexpr int LK = DK + 8;  // padded bf16 row pitch of d_k-long rows
+    uint16_t Ks[3][C][LK];   // K, token-major, three chunk buffers
+    uint16_t Qs[C][LK];      // Q of the chunk being prepared
+    uint16_t Vs[C][LV];      // V tile of the next chunk, token-major
+    uint16_t Sb[DVT][LK];    // bf16 copy of the state tile, [d_v][d_k]
+    uint16_t Rt[DVT][LC];    // R^T
+    uint16_t Nt[DVT][LC];    // N^T
+    uint16_t Nd[DVT][LC];    // (diag(G_{C-1,.}) N)^T
+    uint16_t Pb[2][C][LC];   // P, row-major, zero above the diagonal
+    uint16_t Tb[C][LC];      // Tm, row-major, zero above the diagonal
+    uint16_t Ab[C][LC];      // A (its off-diagonal 16x16 blocks are read)
+    float AdT[4][16][20];    // A's diagonal 16x16 blocks, transposed, fp32
+    double g[2][C];          // cumulative log2 decay
+    float gam[2][C];         // 2^{g_i}
+    float glast[2][C];       // 2^{g_{C-1} - g_i}
+    float bet[2][C];
+    float rawdec[C], rawbet[C];
+};
+
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4_t mfma16(s16x4_t a, s16x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
 
-__device__ __forceinline__ bf16x8_t ld8(const uint16_t *p) {
+__device__ __forceinline__ bf16x8_t lds16(const uint16_t *p) {
     bf16x8_t r;
     __builtin_memcpy(&r, p, 16);
     return r;
 }
-
-// acc += A[arow0 .. +32][k] * B[brow0 .. +32][k]^T over k in [k0, k1), where
-// both operands are row-major bf16 with the contraction index contiguous.
-__device__ __forceinline__ f32x16_t mma_nt(const uint16_t *A, int lda, int arow0, const uint16_t *B,
-                                           int ldb, int brow0, int k0, int k1, f32x16_t acc, int lane) {
-    const uint16_t *pa = A + (arow0 + (lane & 31)) * lda + 8 * (lane >> 5);
-    const uint16_t *pb = B + (brow0 + (lane & 31)) * ldb + 8 * (lane >> 5);
-    for (int k = k0; k < k1; k += 16) acc = mfma(ld8(pa + k), ld8(pb + k), acc);
-    return acc;
+__device__ __forceinline__ s16x4_t lds8(const uint16_t *p) {
+    s16x4_t r;
+    __builtin_memcpy(&r, p, 8);
+    return r;
 }
-
-// Row index (within a 32x32 accumulator tile) of element r of lane `lane`.
-__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
-
+// Transposed LDS read: within each 16-lane group, result lane i slot s is the
+// element at position i%4 of the 4 addressed by lane 4s + i/4.
+__device__ __forceinline__ s16x4_t lds_tr(const uint16_t *p) {
+    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+}
+__device__ __forceinline__ bf16x8_t join(s16x4_t a, s16x4_t b) {
+    bf16x8_t r;
+    __builtin_memcpy(&r, &a, 8);
+    __builtin_memcpy(reinterpret_cast<char *>(&r) + 8, &b, 8);
+    return r;
+}
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+    return make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+}
+__device__ __forceinline__ s16x4_t pack4s(float a, float b, float c, float d) {
+    const uint2 u = pack4(a, b, c, d);
+    s16x4_t r;
+    __builtin_memcpy(&r, &u, 8);
+    return r;
+}
 __device__ __forceinline__ f32x16_t zero16() {
     f32x16_t z;
 #pragma unroll
     for (int r = 0; r < 16; ++r) z[r] = 0.f;
     return z;
 }
-
-template <bool BF16>
-__device__ __forceinline__ void store_elem(void *out, size_t e, float x) {
-    if constexpr (BF16)
-        reinterpret_cast<uint16_t *>(out)[e] = (uint16_t)f32_to_bf16_bits(x);
-    else
-        reinterpret_cast<float *>(out)[e] = x;
+__device__ __forceinline__ f32x4_t zero4() {
+    f32x4_t z;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[r] = 0.f;
+    return z;
 }
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int DK>
-struct __align__(16) Smem {
-    static constexpr int LK = DK + 8;  // padded row length (bf16) of d_k-long rows
-    static constexpr int LC = C + 8;   // padded row length (bf16) of C-long rows
-    static constexpr int LF = C + 4;   // padded row length (fp32) of C-long rows
-    uint16_t Ks[C][LK];     // K, token-major
-    uint16_t Qs[C][LK];     // Q, token-major
-    uint16_t Kt[DK][LC];    // K^T
-    uint16_t Vt[DVT][LC];   // V tile, transposed
-    uint16_t Sb[DVT][LK];   // bf16 copy of the state tile, row-major [d_v][d_k]
-    float Af[C][LF];        // A (lower part read only)
-    float Tf[C][LF];        // (I + A)^-1 in fp32
-    uint16_t Tb[C][LC];     // (I + A)^-1 in bf16, zero above the diagonal
-    uint16_t Pb[C][LC];     // P, zero above the diagonal
-    uint16_t Rt[DVT][LC];   // R^T
-    uint16_t Nt[DVT][LC];   // N^T
-    uint16_t Nd[DVT][LC];   // (diag(G_{C-1,.}) N)^T
-    double g[C];            // cumulative log decay
-    float gam[C];           // e^{g_i}
-    float glast[C];         // e^{g_{C-1} - g_i}
-    float bet[C];
-    float dec[C];
-    float Y[3][16][16];     // triangular-inverse temporaries
-};
+// Off-diagonal blocks of block column CB of Tm = (I + A)^{-1}, walking down:
+//   T_rc = -T_rr * sum_{k=c}^{r-1} A_rk T_kc   (16x16 blocks, bf16 16x16x16 MFMA).
+// The diagonal blocks are already in Tb; the column's blocks are passed from one
+// product to the next in registers (accumulator layout == B-operand layout).
+template <int CB>
+__device__ __forceinline__ void tm_column(uint16_t (*Tb)[LC], const uint16_t (*Ab)[LC], int l16, int g16) {
+    s16x4_t tcol[4];
+    tcol[CB] = lds_tr(&Tb[16 * CB + 4 * g16 + (l16 >> 2)][16 * CB + 4 * (l16 & 3)]);
+#pragma unroll
+    for (int rb = CB + 1; rb < 4; ++rb) {
+        f32x4_t y = zero4();
+#pragma unroll
+        for (int kb = CB; kb < rb; ++kb) y = mfma16(lds8(&Ab[16 * rb + l16][16 * kb + 4 * g16]), tcol[kb], y);
+        const f32x4_t t = mfma16(lds8(&Tb[16 * rb + l16][16 * rb + 4 * g16]), pack4s(y[0], y[1], y[2], y[3]), zero4());
+        tcol[rb] = pack4s(-t[0], -t[1], -t[2], -t[3]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Tb[16 * rb + 4 * g16 + r][16 * CB + l16] = (uint16_t)f32_to_bf16_bits(-t[r]);
+    }
+}
 
 template <int DK, bool BF16>
 __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
-    static_assert(DK % 32 == 0, "d_k must be a multiple of 32");
+    static_assert(DK % 32 == 0 && DK <= 128, "d_k must be 32, 64 or 128");
     using SM = Smem<DK>;
-    constexpr int LK = SM::LK, LC = SM::LC;
-    constexpr int NSB = DK / 32;  // 32-row blocks of S^T (d_k rows)
+    constexpr int NKS = DK / 16;  // 16-wide contraction steps over d_k
+    constexpr int NSB = DK / 32;  // 32-row blocks of S^T held by waves 0 .. NSB-1
     __shared__ SM sm;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wid = tid >> 6;
-    const int col = lane & 31;    // accumulator column
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+    const int l16 = lane & 15;
+    const int g16 = lane >> 4;
 
     // Block -> (b, h, d_v tile).  With the XCD remap, the ntile blocks of one head
     // get linear ids that differ by multiples of 8, i.e. land on one XCD.
-    int L = blockIdx.x;
+    const int L = blockIdx.x;
     int head, tile;
     if (p.xcd_remap) {
-        const int xcd = L & 7, slot = L >> 3;
+        const int slot = L >> 3;
         tile = slot % p.ntile;
-        head = (slot / p.ntile) * 8 + xcd;
+        head = (slot / p.ntile) * 8 + (L & 7);
     } else {
         tile = L % p.ntile;
         head = L / p.ntile;
@@ -161,292 +219,343 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     const int dv = p.dv;
     const int dv0 = tile * DVT;
     const long long T = p.T;
+    const long long nchunks = (T + C - 1) / C;
 
-    // fp32 state S^T block (d_k rows 32*wid .., d_v cols dv0 + col), waves < NSB.
-    f32x16_t st = zero16();
-    const size_t sbase = ((size_t)(b * H + h) * dv + dv0 + col) * DK;
+    auto ntok = [&](long long c) -> int { return (int)((T - c * C) < C ? (T - c * C) : C); };
+    auto tok = [&](long long c, int j) -> long long {
+        const long long s = c * C + j;
+        return p.reverse ? T - 1 - s : s;
+    };
+
+    // This wave's row block: K rows (wid & 1)*32 .. (waves 0, 1) or Q rows (waves 2, 3).
+    const uint16_t *blk_src = (wid < 2) ? p.k : p.q;
+    const int blk_row = 32 * (wid & 1) + l32;
+    auto load_block = [&](long long c, bf16x8_t *dst) {
+        const bool ok = c < nchunks && blk_row < ntok(c);
+        const uint16_t *src = blk_src;
+        if (ok) src += ((size_t)(b * T + tok(c, blk_row)) * H + h) * DK + 8 * hi;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            uint4 w = make_uint4(0, 0, 0, 0);
+            if (ok) w = *reinterpret_cast<const uint4 *>(src + 16 * s);
+            __builtin_memcpy(&dst[s], &w, 16);
+        }
+    };
+    auto store_block = [&](long long c, const bf16x8_t *src) {
+        uint16_t *row = (wid < 2) ? &sm.Ks[c % 3][blk_row][8 * hi] : &sm.Qs[blk_row][8 * hi];
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) __builtin_memcpy(row + 16 * s, &src[s], 16);
+    };
+    // V tile of chunk c: 64 tokens x 32 d_v = 256 16-byte vectors, one per thread.
+    const int v_tok = tid >> 2, v_part = tid & 3;
+    auto load_v = [&](long long c) -> uint4 {
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (c < nchunks && v_tok < ntok(c))
+            w = *reinterpret_cast<const uint4 *>(p.v + ((size_t)(b * T + tok(c, v_tok)) * H + h) * dv + dv0 + 8 * v_part);
+        return w;
+    };
+    auto load_gates = [&](long long c, float &bb, float &aa) {
+        bb = 0.f;
+        aa = 1.f;
+        if (tid < C && c < nchunks && tid < ntok(c)) {
+            const size_t g = (size_t)(b * T + tok(c, tid)) * H + h;
+            bb = p.beta[g];
+            aa = p.decay[g];
+        }
+    };
+
+    // ---- initial state: S^T block (d_k rows 32*wid.., d_v cols dv0 + l32) ----
+    f32x16_t sacc = zero16();
+    const size_t sbase = ((size_t)(b * H + h) * dv + dv0 + l32) * DK;
     if (wid < NSB) {
         if (p.state_in) {
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int dk = 32 * wid + 8 * r4 + 4 * (lane >> 5);
-                const float4 s4 = *reinterpret_cast<const float4 *>(p.state_in + sbase + dk);
-                st[4 * r4 + 0] = s4.x; st[4 * r4 + 1] = s4.y; st[4 * r4 + 2] = s4.z; st[4 * r4 + 3] = s4.w;
+            for (int rb = 0; rb < 4; ++rb) {
+                const float4 s4 = *reinterpret_cast<const float4 *>(p.state_in + sbase + 32 * wid + 8 * rb + 4 * hi);
+                sacc[4 * rb + 0] = s4.x; sacc[4 * rb + 1] = s4.y; sacc[4 * rb + 2] = s4.z; sacc[4 * rb + 3] = s4.w;
             }
         }
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int dk = 32 * wid + 8 * r4 + 4 * (lane >> 5);
-            uint2 w;
-            w.x = pack_bf16x2(st[4 * r4 + 0], st[4 * r4 + 1]);
-            w.y = pack_bf16x2(st[4 * r4 + 2], st[4 * r4 + 3]);
-            *reinterpret_cast<uint2 *>(&sm.Sb[col][dk]) = w;
+        for (int rb = 0; rb < 4; ++rb)
+            *reinterpret_cast<uint2 *>(&sm.Sb[l32][32 * wid + 8 * rb + 4 * hi]) =
+                pack4(sacc[4 * rb], sacc[4 * rb + 1], sacc[4 * rb + 2], sacc[4 * rb + 3]);
+    }
+
+    // ---- pre-step: chunk 0 staged, its row blocks in registers ---------------
+    bf16x8_t cur[NKS], nxt[NKS], pf[NKS];
+    uint4 vpf = make_uint4(0, 0, 0, 0);
+    float bpf = 0.f, apf = 1.f;
+    if (nchunks > 0) {
+        load_block(0, nxt);
+        float bb, aa;
+        load_gates(0, bb, aa);
+        store_block(0, nxt);
+        if (tid < C) {
+            sm.rawbet[tid] = bb;
+            sm.rawdec[tid] = aa;
         }
     }
     __syncthreads();
 
-    const long long nchunks = (T + C - 1) / C;
-    for (long long ci = 0; ci < nchunks; ++ci) {
-        const long long s0 = ci * C;  // first sequence index of the chunk
-        const int n = (int)((T - s0) < C ? (T - s0) : C);
-        auto tok = [&](int j) -> long long { return p.reverse ? T - 1 - (s0 + j) : s0 + j; };
+    // Iteration c: state chain of chunk c (c >= 0), preparation of chunk c+1.
+    for (long long c = -1; c < nchunks; ++c) {
+        const bool chain = c >= 0;
+        const bool prep = c + 1 < nchunks;
+        const int cb = (int)((c + 3) % 2);      // gate buffer of chunk c (c >= -1)
+        const int nb = (int)((c + 1 + 3) % 2);  // gate buffer of chunk c+1
+        const int n = chain ? ntok(c) : 0;
 
-        // ---- P0: stage K, Q, V tile, b, a --------------------------------------
-        {
-            constexpr int VPR = DK / 8;  // 16-byte vectors per q/k row
-#pragma unroll
-            for (int i = 0; i < (C * VPR) / NT; ++i) {
-                const int vi = tid + i * NT;
-                const int j = vi / VPR, seg = vi % VPR;
-                uint4 kw = make_uint4(0, 0, 0, 0), qw = make_uint4(0, 0, 0, 0);
-                if (j < n) {
-                    const size_t e = ((size_t)(b * T + tok(j)) * H + h) * DK + seg * 8;
-                    kw = *reinterpret_cast<const uint4 *>(p.k + e);
-                    qw = *reinterpret_cast<const uint4 *>(p.q + e);
-                }
-                *reinterpret_cast<uint4 *>(&sm.Ks[j][seg * 8]) = kw;
-                *reinterpret_cast<uint4 *>(&sm.Qs[j][seg * 8]) = qw;
-                const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sm.Kt[seg * 8 + 2 * e][j] = (uint16_t)(kk[e] & 0xffffu);
-                    sm.Kt[seg * 8 + 2 * e + 1][j] = (uint16_t)(kk[e] >> 16);
-                }
-            }
-            {
-                // V tile: C tokens x 32 d_v = 256 vectors, one per thread.
-                const int j = tid >> 2, part = tid & 3;
-                uint4 vw = make_uint4(0, 0, 0, 0);
-                if (j < n)
-                    vw = *reinterpret_cast<const uint4 *>(p.v + ((size_t)(b * T + tok(j)) * H + h) * dv + dv0 + part * 8);
-                const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sm.Vt[part * 8 + 2 * e][j] = (uint16_t)(vv[e] & 0xffffu);
-                    sm.Vt[part * 8 + 2 * e + 1][j] = (uint16_t)(vv[e] >> 16);
-                }
-            }
-            if (tid < C) {
-                float bb = 0.f, aa = 1.f;
-                if (tid < n) {
-                    const size_t g = (size_t)(b * T + tok(tid)) * H + h;
-                    bb = p.beta[g];
-                    aa = p.decay[g];
-                }
-                sm.bet[tid] = bb;
-                sm.dec[tid] = aa;
-            }
-        }
-        __syncthreads();
+        // ===== phase 1 ======================================================
+        // loads for later chunks
+        load_block(c + 2, pf);
+        vpf = load_v(c + 1);
+        load_gates(c + 2, bpf, apf);
 
-        // ---- P1: decay factors (wave 0) ------------------------------------------
-        if (wid == 0) {
-            const float a = sm.dec[lane];
-            double x = a > 0.f ? log((double)a) : -1000.0;
-            if (x < -1000.0) x = -1000.0;
+        // decay factors of chunk c+1 (wave 3)
+        if (prep && wid == 3) {
+            const float a = sm.rawdec[lane];
+            float l2 = __builtin_amdgcn_logf(a);  // log2
+            if (!(l2 > -1.0e4f)) l2 = -1.0e4f;
+            double x = (double)l2;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const double y = __shfl_up(x, off, 64);
                 if (lane >= off) x += y;
             }
-            sm.g[lane] = x;
-            const double glast = __shfl(x, 63, 64);
-            sm.gam[lane] = expf((float)x);
-            sm.glast[lane] = expf((float)(glast - x));
+            const double xl = __shfl(x, 63, 64);
+            sm.g[nb][lane] = x;
+            sm.gam[nb][lane] = exp2_fast((float)x);
+            sm.glast[nb][lane] = exp2_fast((float)(xl - x));
+            sm.bet[nb][lane] = sm.rawbet[lane];
+        }
+
+        f32x16_t xacc = zero16();
+        if (chain) {
+            // off-diagonal 16x16 blocks of Tm for chunk c: block column `wid`
+            if (wid == 0) tm_column<0>(sm.Tb, sm.Ab, l16, g16);
+            else if (wid == 1) tm_column<1>(sm.Tb, sm.Ab, l16, g16);
+            else if (wid == 2) tm_column<2>(sm.Tb, sm.Ab, l16, g16);
+            // X: waves 0,1 K S^T (tokens x d_v); waves 2,3 (Q S^T)^T (d_v x tokens)
+            if (wid < 2) {
+#pragma unroll
+                for (int s = 0; s < NKS; ++s) xacc = mfma32(cur[s], lds16(&sm.Sb[l32][16 * s + 8 * hi]), xacc);
+            } else {
+#pragma unroll
+                for (int s = 0; s < NKS; ++s) xacc = mfma32(lds16(&sm.Sb[l32][16 * s + 8 * hi]), cur[s], xacc);
+            }
+            if (wid < 2) {
+                // R = diag(b)(V - diag(gam) K S^T) -> R^T
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    const int i0 = 32 * wid + 8 * rb + 4 * hi;
+                    const s16x4_t vv = lds_tr(&sm.Vs[i0 + (l16 >> 2)][16 * (g16 & 1) + 4 * (l16 & 3)]);
+                    const uint2 vu = *reinterpret_cast<const uint2 *>(&vv);
+                    const float4 bt = *reinterpret_cast<const float4 *>(&sm.bet[cb][i0]);
+                    const float4 gm = *reinterpret_cast<const float4 *>(&sm.gam[cb][i0]);
+                    const float r0 = bt.x * (bf16_lo(vu.x) - gm.x * xacc[4 * rb + 0]);
+                    const float r1 = bt.y * (bf16_hi(vu.x) - gm.y * xacc[4 * rb + 1]);
+                    const float r2 = bt.z * (bf16_lo(vu.y) - gm.z * xacc[4 * rb + 2]);
+                    const float r3 = bt.w * (bf16_hi(vu.y) - gm.w * xacc[4 * rb + 3]);
+                    *reinterpret_cast<uint2 *>(&sm.Rt[l32][i0]) = pack4(r0, r1, r2, r3);
+                }
+            } else {
+                const float gq = sm.gam[cb][32 * (wid - 2) + l32];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xacc[r] *= gq;
+            }
         }
         __syncthreads();
 
-        // ---- P2: Gram blocks -> A, P;  K S^T -> R;  Q S^T kept for O ------------
-        // Tiles are (key block jb, query block ib): A[i][j] and P[i][j] need j <= i.
-        f32x16_t xo = zero16();  // waves 2, 3: Q S^T for token block (wid - 2)
-        {
-            auto gram_to_A = [&](int jb, int ib) {
-                f32x16_t acc = mma_nt(&sm.Ks[0][0], LK, 32 * jb, &sm.Ks[0][0], LK, 32 * ib, 0, DK, zero16(), lane);
-                const int i = 32 * ib + col;
-                const double gi = sm.g[i];
-                const float bi = sm.bet[i];
+        // ===== phase 2 ======================================================
+        if (chain && wid < 2) {
+            // N = Tm R for token block wid (Tm lower triangular: keys < 32*(wid+1))
+            f32x16_t nacc = zero16();
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int j0 = 32 * jb + 8 * r4 + 4 * (lane >> 5);
-                    float4 o;
-                    float *op = &o.x;
+            for (int k = 0; k < 64; k += 16) {
+                if (k >= 32 * (wid + 1)) break;
+                nacc = mfma32(lds16(&sm.Tb[32 * wid + l32][k + 8 * hi]), lds16(&sm.Rt[l32][k + 8 * hi]), nacc);
+            }
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int i0 = 32 * wid + 8 * rb + 4 * hi;
+                const float4 gl = *reinterpret_cast<const float4 *>(&sm.glast[cb][i0]);
+                *reinterpret_cast<uint2 *>(&sm.Nt[l32][i0]) =
+                    pack4(nacc[4 * rb], nacc[4 * rb + 1], nacc[4 * rb + 2], nacc[4 * rb + 3]);
+                *reinterpret_cast<uint2 *>(&sm.Nd[l32][i0]) =
+                    pack4(gl.x * nacc[4 * rb], gl.y * nacc[4 * rb + 1], gl.z * nacc[4 * rb + 2], gl.w * nacc[4 * rb + 3]);
+            }
+        }
+        if (prep) {
+            // Gram products of chunk c+1, computed as (keys x queries):
+            //   wave 0: K_a K_a^T, K_a K_b^T   wave 1: K_b K_b^T, K_b Q_b^T
+            //   wave 2: K_a Q_a^T              wave 3: K_a Q_b^T
+            const int kb3 = (int)((c + 1) % 3);
+            f32x16_t g0 = zero16(), g1 = zero16();
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) {
+                const int ko = 16 * s + 8 * hi;
+                if (wid == 0) {
+                    g0 = mfma32(nxt[s], nxt[s], g0);
+                    g1 = mfma32(nxt[s], lds16(&sm.Ks[kb3][32 + l32][ko]), g1);
+                } else if (wid == 1) {
+                    g0 = mfma32(nxt[s], nxt[s], g0);
+                    g1 = mfma32(nxt[s], lds16(&sm.Qs[32 + l32][ko]), g1);
+                } else {
+                    g0 = mfma32(lds16(&sm.Ks[kb3][l32][ko]), nxt[s], g0);
+                }
+            }
+            // Epilogues: element (key j, query i); factor 2^{g_i - g_j} for j <= i.
+            const double *gg = sm.g[nb];
+            auto epi = [&](const f32x16_t &acc, int jb, int ib, bool is_k) {
+                const int i = 32 * ib + l32;
+                const double gi = gg[i];
+                const float bi = sm.bet[nb][i];
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    const int j0 = 32 * jb + 8 * rb + 4 * hi;
+                    float v4[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int j = j0 + e;
-                        op[e] = (j < i) ? bi * expf((float)(gi - sm.g[j])) * acc[4 * r4 + e] : 0.f;
+                        const float f = exp2_fast((float)(gi - gg[j]));
+                        const float val = acc[4 * rb + e] * f;
+                        v4[e] = is_k ? ((j < i) ? bi * val : 0.f) : ((j <= i) ? val : 0.f);
                     }
-                    *reinterpret_cast<float4 *>(&sm.Af[i][j0]) = o;
-                }
-            };
-            auto gram_to_P = [&](int jb, int ib) {
-                f32x16_t acc = mma_nt(&sm.Ks[0][0], LK, 32 * jb, &sm.Qs[0][0], LK, 32 * ib, 0, DK, zero16(), lane);
-                const int i = 32 * ib + col;
-                const double gi = sm.g[i];
+                    if (!is_k) {
+                        *reinterpret_cast<uint2 *>(&sm.Pb[nb][i][j0]) = pack4(v4[0], v4[1], v4[2], v4[3]);
+                    } else if ((i >> 4) == (j0 >> 4)) {
+                        float *d = &sm.AdT[i >> 4][j0 & 15][i & 15];
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int j0 = 32 * jb + 8 * r4 + 4 * (lane >> 5);
-                    float pv[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int j = j0 + e;
-                        pv[e] = (j <= i) ? expf((float)(gi - sm.g[j])) * acc[4 * r4 + e] : 0.f;
+                        for (int e = 0; e < 4; ++e) d[20 * e] = v4[e];
+                    } else if ((i >> 4) > (j0 >> 4)) {
+                        *reinterpret_cast<uint2 *>(&sm.Ab[i][j0]) = pack4(v4[0], v4[1], v4[2], v4[3]);
                     }
-                    uint2 w;
-                    w.x = pack_bf16x2(pv[0], pv[1]);
-                    w.y = pack_bf16x2(pv[2], pv[3]);
-                    *reinterpret_cast<uint2 *>(&sm.Pb[i][j0]) = w;
-                }
-            };
-            auto ks_to_R = [&](int tb) {
-                f32x16_t acc = mma_nt(&sm.Ks[0][0], LK, 32 * tb, &sm.Sb[0][0], LK, 0, 0, DK, zero16(), lane);
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int i0 = 32 * tb + 8 * r4 + 4 * (lane >> 5);
-                    const uint2 vw = *reinterpret_cast<const uint2 *>(&sm.Vt[col][i0]);
-                    const float vv[4] = {bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y)};
-                    float rv[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = i0 + e;
-                        rv[e] = sm.bet[i] * (vv[e] - sm.gam[i] * acc[4 * r4 + e]);
-                    }
-                    uint2 w;
-                    w.x = pack_bf16x2(rv[0], rv[1]);
-                    w.y = pack_bf16x2(rv[2], rv[3]);
-                    *reinterpret_cast<uint2 *>(&sm.Rt[col][i0]) = w;
                 }
             };
             if (wid == 0) {
-                gram_to_A(0, 0);
-                gram_to_P(0, 0);
-                ks_to_R(0);
+                epi(g0, 0, 0, true);
+                epi(g1, 0, 1, true);
             } else if (wid == 1) {
-                gram_to_A(0, 1);
-                gram_to_P(0, 1);
-                ks_to_R(1);
+                epi(g0, 1, 1, true);
+                epi(g1, 1, 1, false);
+            } else if (wid == 2) {
+                epi(g0, 0, 0, false);
             } else {
+                epi(g0, 0, 1, false);
+            }
+        }
+        __syncthreads();
+
+        // ===== phase 3 ======================================================
+        if (chain) {
+            if (wid >= 2) {
+                // O^T = gam (Q S^T)^T + N^T P^T for query block tb, keys < 32*(tb+1)
                 const int tb = wid - 2;
-                if (wid == 2) gram_to_A(1, 1);
-                else gram_to_P(1, 1);
-                xo = mma_nt(&sm.Qs[0][0], LK, 32 * tb, &sm.Sb[0][0], LK, 0, 0, DK, zero16(), lane);
+                const int pbuf = cb;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) xo[r] *= sm.gam[32 * tb + acc_row(r, lane)];
-            }
-            // P[i][j] for the (query block a, key block b) tile is never read: the
-            // O product for query block a stops at key 31.
-        }
-        __syncthreads();
-
-        // ---- P3: Tm = (I + A)^-1 ----------------------------------------------------
-        // 16x16 diagonal blocks by forward substitution (one wave each, lane = column),
-        // then the off-diagonal blocks by distance from the diagonal:
-        // T_rc = -T_rr * sum_{k=c}^{r-1} A_rk T_kc.
-        if (lane < 16) {
-            const int base = 16 * wid, c = lane;
-            float x[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float s = (i == c) ? 1.f : 0.f;
-#pragma unroll
-                for (int j = 0; j < i; ++j) s -= sm.Af[base + i][base + j] * x[j];
-                x[i] = s;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sm.Tf[base + i][base + c] = x[i];
-        }
-        __syncthreads();
-        {
-            const int ti = tid >> 4, tj = tid & 15;
-            for (int d = 1; d < 4; ++d) {
-                const int nb = 4 - d;
-                for (int cb = 0; cb < nb; ++cb) {
-                    const int rb = cb + d;
-                    float y = 0.f;
-                    for (int kb = cb; kb < rb; ++kb) {
-#pragma unroll
-                        for (int m = 0; m < 16; ++m)
-                            y += sm.Af[16 * rb + ti][16 * kb + m] * sm.Tf[16 * kb + m][16 * cb + tj];
-                    }
-                    sm.Y[cb][ti][tj] = y;
+                for (int k = 0; k < 64; k += 16) {
+                    if (k >= 32 * (tb + 1)) break;
+                    xacc = mfma32(lds16(&sm.Nt[l32][k + 8 * hi]), lds16(&sm.Pb[pbuf][32 * tb + l32][k + 8 * hi]), xacc);
                 }
-                __syncthreads();
-                for (int cb = 0; cb < nb; ++cb) {
-                    const int rb = cb + d;
-                    float t = 0.f;
-#pragma unroll
-                    for (int m = 0; m < 16; ++m) t += sm.Tf[16 * rb + ti][16 * rb + m] * sm.Y[cb][m][tj];
-                    sm.Tf[16 * rb + ti][16 * cb + tj] = -t;
-                }
-                __syncthreads();
-            }
-        }
-        // bf16 copy with zeros above the diagonal.
-        for (int idx = tid; idx < C * C / 2; idx += NT) {
-            const int i = idx / (C / 2), j = 2 * (idx % (C / 2));
-            const float t0 = (j <= i) ? sm.Tf[i][j] : 0.f;
-            const float t1 = (j + 1 <= i) ? sm.Tf[i][j + 1] : 0.f;
-            *reinterpret_cast<uint32_t *>(&sm.Tb[i][j]) = pack_bf16x2(t0, t1);
-        }
-        __syncthreads();
-
-        // ---- P4: N = Tm R (waves 0, 1: token block wid) ---------------------------
-        if (wid < 2) {
-            const f32x16_t acc = mma_nt(&sm.Tb[0][0], LC, 32 * wid, &sm.Rt[0][0], LC, 0, 0, 32 * (wid + 1),
-                                        zero16(), lane);
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int i0 = 32 * wid + 8 * r4 + 4 * (lane >> 5);
-                uint2 w, wd;
-                w.x = pack_bf16x2(acc[4 * r4 + 0], acc[4 * r4 + 1]);
-                w.y = pack_bf16x2(acc[4 * r4 + 2], acc[4 * r4 + 3]);
-                wd.x = pack_bf16x2(sm.glast[i0 + 0] * acc[4 * r4 + 0], sm.glast[i0 + 1] * acc[4 * r4 + 1]);
-                wd.y = pack_bf16x2(sm.glast[i0 + 2] * acc[4 * r4 + 2], sm.glast[i0 + 3] * acc[4 * r4 + 3]);
-                *reinterpret_cast<uint2 *>(&sm.Nt[col][i0]) = w;
-                *reinterpret_cast<uint2 *>(&sm.Nd[col][i0]) = wd;
-            }
-        }
-        __syncthreads();
-
-        // ---- P5: outputs (waves 2, 3) and the state update (waves < NSB) ---------
-        if (wid >= 2) {
-            const int tb = wid - 2;
-            xo = mma_nt(&sm.Pb[0][0], LC, 32 * tb, &sm.Nt[0][0], LC, 0, 0, 32 * (tb + 1), xo, lane);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = 32 * tb + acc_row(r, lane);
+                const int i = 32 * tb + l32;
                 if (i < n) {
-                    const size_t e = ((size_t)(b * T + tok(i)) * H + h) * dv + dv0 + col;
-                    const float o = xo[r] * p.scale;
-                    if (p.out_mode == OUT_PARTIAL) p.partial[e] = o;
-                    else if (p.out_mode == OUT_COMBINE) store_elem<BF16>(p.out, e, p.partial[e] + o);
-                    else store_elem<BF16>(p.out, e, o);
+                    const size_t e0 = ((size_t)(b * T + tok(c, i)) * H + h) * dv + dv0;
+#pragma unroll
+                    for (int rb = 0; rb < 4; ++rb) {
+                        const size_t e = e0 + 8 * rb + 4 * hi;
+                        float o0 = xacc[4 * rb] * p.scale, o1 = xacc[4 * rb + 1] * p.scale;
+                        float o2 = xacc[4 * rb + 2] * p.scale, o3 = xacc[4 * rb + 3] * p.scale;
+                        if (p.out_mode == OUT_PARTIAL) {
+                            *reinterpret_cast<float4 *>(p.partial + e) = make_float4(o0, o1, o2, o3);
+                        } else {
+                            if (p.out_mode == OUT_COMBINE) {
+                                const float4 pr = *reinterpret_cast<const float4 *>(p.partial + e);
+                                o0 = pr.x + o0; o1 = pr.y + o1; o2 = pr.z + o2; o3 = pr.w + o3;
+                            }
+                            if constexpr (BF16)
+                                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.out) + e) = pack4(o0, o1, o2, o3);
+                            else
+                                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.out) + e) = make_float4(o0, o1, o2, o3);
+                        }
+                    }
+                }
+            }
+            if (wid < NSB) {
+                // S^T <- gam_{C-1} S^T + K^T N~  (K^T read transposed from the token-major K)
+                const float gl = sm.gam[cb][C - 1];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[r] *= gl;
+                const int kb3 = (int)(c % 3);
+                const int dcol = 32 * wid + 16 * (g16 & 1) + 4 * (l16 & 3);
+#pragma unroll
+                for (int t = 0; t < 64; t += 16) {
+                    const int t0 = t + 8 * hi + (l16 >> 2);
+                    const bf16x8_t a = join(lds_tr(&sm.Ks[kb3][t0][dcol]), lds_tr(&sm.Ks[kb3][t0 + 4][dcol]));
+                    sacc = mfma32(a, lds16(&sm.Nd[l32][t + 8 * hi]), sacc);
+                }
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb)
+                    *reinterpret_cast<uint2 *>(&sm.Sb[l32][32 * wid + 8 * rb + 4 * hi]) =
+                        pack4(sacc[4 * rb], sacc[4 * rb + 1], sacc[4 * rb + 2], sacc[4 * rb + 3]);
+            }
+        }
+        if (prep && wid < 2) {
+            // 16x16 diagonal blocks of Tm for chunk c+1: lane l16 of half g16 (0/1)
+            // owns row l16 of block 2*wid + g16.  Row i of (I + A_kk)^{-1} is the
+            // solution of (I + A_kk)^T y = e_i, found by backward substitution.
+            if (g16 < 2) {
+                const int kb = 2 * wid + g16;
+                const int i = l16;
+                float y[16];
+#pragma unroll
+                for (int m = 15; m >= 0; --m) {
+                    float s = (m == i) ? 1.f : 0.f;
+                    if (m < 15) {
+                        const float *col = &sm.AdT[kb][m][0];  // A[j][m] for j = 0..15
+                        float av[16];
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const float4 f = *reinterpret_cast<const float4 *>(col + 4 * q4);
+                            av[4 * q4] = f.x; av[4 * q4 + 1] = f.y; av[4 * q4 + 2] = f.z; av[4 * q4 + 3] = f.w;
+                        }
+#pragma unroll
+                        for (int j = m + 1; j < 16; ++j) s -= av[j] * y[j];
+                    }
+                    y[m] = s;
+                }
+                uint16_t *row = &sm.Tb[16 * kb + i][16 * kb];
+                const uint4 w0 = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                                            pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+                const uint4 w1 = make_uint4(pack_bf16x2(y[8], y[9]), pack_bf16x2(y[10], y[11]),
+                                            pack_bf16x2(y[12], y[13]), pack_bf16x2(y[14], y[15]));
+                *reinterpret_cast<uint4 *>(row) = w0;
+                *reinterpret_cast<uint4 *>(row + 8) = w1;
+                if ((kb & 1) == 0) {  // zero block right of the diagonal inside the 32-row block
+                    *reinterpret_cast<uint4 *>(row + 16) = make_uint4(0, 0, 0, 0);
+                    *reinterpret_cast<uint4 *>(row + 24) = make_uint4(0, 0, 0, 0);
                 }
             }
         }
-        if (wid < NSB) {
-            const float gl = sm.gam[C - 1];
+        // stage chunk c+2 (row blocks, already in pf) and chunk c+1's V tile and gates
+        if (c + 2 < nchunks) store_block(c + 2, pf);
+        if (prep) *reinterpret_cast<uint4 *>(&sm.Vs[v_tok][8 * v_part]) = vpf;
+        if (tid < C) {
+            sm.rawbet[tid] = bpf;
+            sm.rawdec[tid] = apf;
+        }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) st[r] *= gl;
-            st = mma_nt(&sm.Kt[0][0], LC, 32 * wid, &sm.Nd[0][0], LC, 0, 0, C, st, lane);
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int dk = 32 * wid + 8 * r4 + 4 * (lane >> 5);
-                uint2 w;
-                w.x = pack_bf16x2(st[4 * r4 + 0], st[4 * r4 + 1]);
-                w.y = pack_bf16x2(st[4 * r4 + 2], st[4 * r4 + 3]);
-                *reinterpret_cast<uint2 *>(&sm.Sb[col][dk]) = w;
-            }
+        for (int s = 0; s < NKS; ++s) {
+            cur[s] = nxt[s];
+            nxt[s] = pf[s];
         }
         __syncthreads();
     }
 
     if (p.state_out && wid < NSB) {
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int dk = 32 * wid + 8 * r4 + 4 * (lane >> 5);
-            *reinterpret_cast<float4 *>(p.state_out + sbase + dk) =
-                make_float4(st[4 * r4 + 0], st[4 * r4 + 1], st[4 * r4 + 2], st[4 * r4 + 3]);
-        }
+        for (int rb = 0; rb < 4; ++rb)
+            *reinterpret_cast<float4 *>(p.state_out + sbase + 32 * wid + 8 * rb + 4 * hi) =
+                make_float4(sacc[4 * rb], sacc[4 * rb + 1], sacc[4 * rb + 2], sacc[4 * rb + 3]);
     }
 }
 
@@ -461,11 +570,10 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.T = a.T; p.H = a.H; p.dv = a.dv;
     p.ntile = a.dv / DVT;
     const int heads = a.B * a.H;
-    p.nblocks = heads * p.ntile;
     p.xcd_remap = (heads % 8) == 0;
     p.reverse = a.reverse; p.out_mode = a.out_mode;
     p.scale = (float)(1.0 / __builtin_sqrt((double)DK));
-    hipLaunchKernelGGL((chunk_kernel<DK, true>), dim3(p.nblocks), dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL((chunk_kernel<DK, true>), dim3(heads * p.ntile), dim3(NT), 0, stream, p);
     return hipGetLastError();
 }
 
