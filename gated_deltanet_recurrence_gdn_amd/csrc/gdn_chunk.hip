@@ -105,8 +105,8 @@ struct __align__(16) Smem {
     uint16_t Pb[2][C][LC];   // P, row-major, zero above the diagonal
     uint16_t Tb[C][LC];      // Tm, row-major, zero above the diagonal
     uint16_t Ab[C][LC];      // A (its off-diagonal 16x16 blocks are read)
-    float AdT[4][16][20];    // A's diagonal 16x16 blocks, transposed, fp32
-    double g[2][C];          // cumulative log2 decay
+    float Ad[4][16][20];     // A's diagonal 16x16 blocks, row-major, fp32
+    float g[2][C];           // cumulative log2 decay (summed in float64)
     float gam[2][C];         // 2^{g_i}
     float glast[2][C];       // 2^{g_{C-1} - g_i}
     float bet[2][C];
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wid = tid >> 6;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int l32 = lane & 31;
     const int hi = lane >> 5;
     const int l16 = lane & 15;
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         if (prep && wid == 3) {
             const float a = sm.rawdec[lane];
             float l2 = __builtin_amdgcn_logf(a);  // log2
-            if (!(l2 > -1.0e4f)) l2 = -1.0e4f;
+            if (!(l2 > -200.0f)) l2 = -200.0f;    // a = 0: 2^-200 is 0 in fp32
             double x = (double)l2;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
                 if (lane >= off) x += y;
             }
             const double xl = __shfl(x, 63, 64);
-            sm.g[nb][lane] = x;
+            sm.g[nb][lane] = (float)x;
             sm.gam[nb][lane] = exp2_fast((float)x);
             sm.glast[nb][lane] = exp2_fast((float)(xl - x));
             sm.bet[nb][lane] = sm.rawbet[lane];
@@ -387,46 +387,52 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         }
         if (prep) {
             // Gram products of chunk c+1, computed as (keys x queries):
-            //   wave 0: K_a K_a^T, K_a K_b^T   wave 1: K_b K_b^T, K_b Q_b^T
-            //   wave 2: K_a Q_a^T              wave 3: K_a Q_b^T
+            //   wave 0: K_a K_a^T          wave 1: K_b K_b^T
+            //   wave 2: K_a Q_a^T, K_a K_b^T   wave 3: K_a Q_b^T, K_b Q_b^T
+            // (own row block from registers, the others from LDS)
             const int kb3 = (int)((c + 1) % 3);
             f32x16_t g0 = zero16(), g1 = zero16();
+            if (wid < 2) {
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) {
-                const int ko = 16 * s + 8 * hi;
-                if (wid == 0) {
-                    g0 = mfma32(nxt[s], nxt[s], g0);
-                    g1 = mfma32(nxt[s], lds16(&sm.Ks[kb3][32 + l32][ko]), g1);
-                } else if (wid == 1) {
-                    g0 = mfma32(nxt[s], nxt[s], g0);
-                    g1 = mfma32(nxt[s], lds16(&sm.Qs[32 + l32][ko]), g1);
-                } else {
+                for (int s = 0; s < NKS; ++s) g0 = mfma32(nxt[s], nxt[s], g0);
+            } else if (wid == 2) {
+#pragma unroll
+                for (int s = 0; s < NKS; ++s) {
+                    const int ko = 16 * s + 8 * hi;
+                    const bf16x8_t ka = lds16(&sm.Ks[kb3][l32][ko]);
+                    g0 = mfma32(ka, nxt[s], g0);
+                    g1 = mfma32(ka, lds16(&sm.Ks[kb3][32 + l32][ko]), g1);
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < NKS; ++s) {
+                    const int ko = 16 * s + 8 * hi;
                     g0 = mfma32(lds16(&sm.Ks[kb3][l32][ko]), nxt[s], g0);
+                    g1 = mfma32(lds16(&sm.Ks[kb3][32 + l32][ko]), nxt[s], g1);
                 }
             }
             // Epilogues: element (key j, query i); factor 2^{g_i - g_j} for j <= i.
-            const double *gg = sm.g[nb];
+            const float *gg = sm.g[nb];
             auto epi = [&](const f32x16_t &acc, int jb, int ib, bool is_k) {
                 const int i = 32 * ib + l32;
-                const double gi = gg[i];
+                const float gi = gg[i];
                 const float bi = sm.bet[nb][i];
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) {
                     const int j0 = 32 * jb + 8 * rb + 4 * hi;
+                    const float4 gj = *reinterpret_cast<const float4 *>(&gg[j0]);
+                    const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
                     float v4[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int j = j0 + e;
-                        const float f = exp2_fast((float)(gi - gg[j]));
-                        const float val = acc[4 * rb + e] * f;
+                        const float val = acc[4 * rb + e] * exp2_fast(gi - gjv[e]);
                         v4[e] = is_k ? ((j < i) ? bi * val : 0.f) : ((j <= i) ? val : 0.f);
                     }
                     if (!is_k) {
                         *reinterpret_cast<uint2 *>(&sm.Pb[nb][i][j0]) = pack4(v4[0], v4[1], v4[2], v4[3]);
                     } else if ((i >> 4) == (j0 >> 4)) {
-                        float *d = &sm.AdT[i >> 4][j0 & 15][i & 15];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) d[20 * e] = v4[e];
+                        *reinterpret_cast<float4 *>(&sm.Ad[i >> 4][i & 15][j0 & 15]) = make_float4(v4[0], v4[1], v4[2], v4[3]);
                     } else if ((i >> 4) > (j0 >> 4)) {
                         *reinterpret_cast<uint2 *>(&sm.Ab[i][j0]) = pack4(v4[0], v4[1], v4[2], v4[3]);
                     }
@@ -434,14 +440,14 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
             };
             if (wid == 0) {
                 epi(g0, 0, 0, true);
-                epi(g1, 0, 1, true);
             } else if (wid == 1) {
                 epi(g0, 1, 1, true);
-                epi(g1, 1, 1, false);
             } else if (wid == 2) {
                 epi(g0, 0, 0, false);
+                epi(g1, 0, 1, true);
             } else {
                 epi(g0, 0, 1, false);
+                epi(g1, 1, 1, false);
             }
         }
         __syncthreads();
@@ -501,27 +507,27 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         }
         if (prep && wid < 2) {
             // 16x16 diagonal blocks of Tm for chunk c+1: lane l16 of half g16 (0/1)
-            // owns row l16 of block 2*wid + g16.  Row i of (I + A_kk)^{-1} is the
-            // solution of (I + A_kk)^T y = e_i, found by backward substitution.
+            // owns row l16 of block 2*wid + g16.  Row i of (I + A_kk)^{-1} solves
+            // (I + A_kk)^T y = e_i; backward substitution, right-looking: once y_j is
+            // known, acc_m -= A[j][m] y_j for every m < j (independent FMAs).
             if (g16 < 2) {
                 const int kb = 2 * wid + g16;
                 const int i = l16;
                 float y[16];
 #pragma unroll
-                for (int m = 15; m >= 0; --m) {
-                    float s = (m == i) ? 1.f : 0.f;
-                    if (m < 15) {
-                        const float *col = &sm.AdT[kb][m][0];  // A[j][m] for j = 0..15
-                        float av[16];
+                for (int m = 0; m < 16; ++m) y[m] = (m == i) ? 1.f : 0.f;
 #pragma unroll
-                        for (int q4 = 0; q4 < 4; ++q4) {
-                            const float4 f = *reinterpret_cast<const float4 *>(col + 4 * q4);
-                            av[4 * q4] = f.x; av[4 * q4 + 1] = f.y; av[4 * q4 + 2] = f.z; av[4 * q4 + 3] = f.w;
-                        }
+                for (int j = 15; j >= 1; --j) {
+                    const float *arow = &sm.Ad[kb][j][0];  // A[j][m], m < j
+                    float av[16];
 #pragma unroll
-                        for (int j = m + 1; j < 16; ++j) s -= av[j] * y[j];
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        if (4 * q4 >= j) break;
+                        const float4 f = *reinterpret_cast<const float4 *>(arow + 4 * q4);
+                        av[4 * q4] = f.x; av[4 * q4 + 1] = f.y; av[4 * q4 + 2] = f.z; av[4 * q4 + 3] = f.w;
                     }
-                    y[m] = s;
+#pragma unroll
+                    for (int m = 0; m < j; ++m) y[m] -= av[m] * y[j];
                 }
                 uint16_t *row = &sm.Tb[16 * kb + i][16 * kb];
                 const uint4 w0 = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
