@@ -81,6 +81,9 @@ def main():
                     help="tokens per head of the oracle's CPU sample (prefix of the same inputs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-forms", action="store_true", help="skip the secondary forms")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after timing, run one plain 512 MiB device-to-device copy (a known-size "
+                         "reference dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -161,6 +164,15 @@ def main():
         "mfma": {"achieved": mfma_tfs, "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
                  "frac": mfma_tfs / BF16_MFMA_PEAK_TFS, "flops_per_launch": flops},
     }
+
+    if args.calib_copy:
+        src = torch.empty(256 * 1024 * 1024, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes"] = src.numel() * src.element_size()
+        del src, dst
 
     if not args.no_forms:
         result["forms"] = measure_forms(torch, gb, inputs, d, g, x)

@@ -6,20 +6,28 @@
 
 namespace gdn {
 
-// bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest even
-// (NaN stays NaN).
+// bf16 <-> fp32.  Widening is exact (bf16 is the top half of an fp32).
+// Narrowing is the native conversion (v_cvt_pk_bf16_f32 on gfx950): round to
+// nearest even, NaN stays NaN.
+typedef __bf16 gdn_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float gdn_f32x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const gdn_f32x2_t v = {lo, hi};
+    const gdn_bf16x2_t b = __builtin_convertvector(v, gdn_bf16x2_t);
+    uint32_t u;
+    __builtin_memcpy(&u, &b, 4);
+    return u;
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    const __bf16 b = (__bf16)f;
+    uint16_t u;
+    __builtin_memcpy(&u, &b, 2);
+    return u;
 }
 
 // Cross-lane data movement inside a row of 16 lanes (DPP).
