@@ -74,7 +74,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;     // chunk length
-constexpr int NT = 256;   // threads per block: 4 waves
+constexpr int NT = 512;   // threads per block: 4 chain waves + 4 preparation waves
 constexpr int DVT = 32;   // d_v columns per block
 constexpr int LC = C + 8; // padded bf16 row pitch of C-long rows
 constexpr int LV = DVT + 8;
@@ -96,7 +96,7 @@ template <int DK>
 struct __align__(16) Smem {
     static constexpr int LK = DK + 8;  // padded bf16 row pitch of d_k-long rows
     uint16_t Ks[3][C][LK];   // K, token-major, three chunk buffers
-    uint16_t Qs[C][LK];      // Q of the chunk being prepared
+    uint16_t Qs[2][C][LK];   // Q, token-major, two chunk buffers
     uint16_t Vs[C][LV];      // V tile of the next chunk, token-major
     uint16_t Sb[DVT][LK];    // bf16 copy of the state tile, [d_v][d_k]
     uint16_t Rt[DVT][LC];    // R^T
@@ -185,88 +185,53 @@ __device__ __forceinline__ void tm_column(uint16_t (*Tb)[LC], const uint16_t (*A
     }
 }
 
-template <int DK, bool BF16>
-__global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
-    static_assert(DK % 32 == 0 && DK <= 128, "d_k must be 32, 64 or 128");
-    using SM = Smem<DK>;
-    constexpr int NKS = DK / 16;  // 16-wide contraction steps over d_k
-    constexpr int NSB = DK / 32;  // 32-row blocks of S^T held by waves 0 .. NSB-1
-    __shared__ SM sm;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int l32 = lane & 31;
-    const int hi = lane >> 5;
-    const int l16 = lane & 15;
-    const int g16 = lane >> 4;
-
-    // Block -> (b, h, d_v tile).  With the XCD remap, the ntile blocks of one head
-    // get linear ids that differ by multiples of 8, i.e. land on one XCD.
-    const int L = blockIdx.x;
-    int head, tile;
-    if (p.xcd_remap) {
-        const int slot = L >> 3;
-        tile = slot % p.ntile;
-        head = (slot / p.ntile) * 8 + (L & 7);
-    } else {
-        tile = L % p.ntile;
-        head = L / p.ntile;
+// Per-block constants: base pointers already offset to (b, token 0, h), token
+// strides in elements, and the chunk walk.
+struct Ctx {
+    const uint16_t *q, *k, *v;  // v offset to the block's d_v tile
+    const float *beta, *decay;
+    long long T;
+    int nchunks;
+    int rs;   // q/k elements between consecutive tokens: H * d_k
+    int rsv;  // v/out elements between consecutive tokens: H * d_v
+    int H;    // gate elements between consecutive tokens
+    int reverse;
+    __device__ int ntok(int c) const {
+        const long long r = T - (long long)c * C;
+        return r < C ? (int)r : C;
     }
-    const int h = head % p.H;
-    const int b = head / p.H;
-    const int H = p.H;
-    const int dv = p.dv;
-    const int dv0 = tile * DVT;
-    const long long T = p.T;
-    const long long nchunks = (T + C - 1) / C;
+    __device__ long long tok(int c, int j) const {
+        const long long s = (long long)c * C + j;
+        return reverse ? T - 1 - s : s;
+    }
+};
 
-    auto ntok = [&](long long c) -> int { return (int)((T - c * C) < C ? (T - c * C) : C); };
-    auto tok = [&](long long c, int j) -> long long {
-        const long long s = c * C + j;
-        return p.reverse ? T - 1 - s : s;
-    };
-
-    // This wave's row block: K rows (wid & 1)*32 .. (waves 0, 1) or Q rows (waves 2, 3).
-    const uint16_t *blk_src = (wid < 2) ? p.k : p.q;
-    const int blk_row = 32 * (wid & 1) + l32;
-    auto load_block = [&](long long c, bf16x8_t *dst) {
-        const bool ok = c < nchunks && blk_row < ntok(c);
-        const uint16_t *src = blk_src;
-        if (ok) src += ((size_t)(b * T + tok(c, blk_row)) * H + h) * DK + 8 * hi;
+// Loads are unconditional: rows past the end of a final short chunk re-read
+// token n-1 (finite data; those tokens carry b = 0 and a = 1, so every product
+// they enter is multiplied by 0 or never stored).  Conditional loads into
+// zeroed registers would make the compiler wait for all earlier loads.
+template <int DK>
+__device__ __forceinline__ void load_block(const Ctx &x, int c, int role, int lane, bf16x8_t *dst) {
+    if (c >= x.nchunks) return;  // uniform
+    const int nt = x.ntok(c);
+    const int r = 32 * (role & 1) + (lane & 31);
+    const uint16_t *src = ((role < 2) ? x.k : x.q) + (size_t)x.tok(c, r < nt ? r : nt - 1) * x.rs + 8 * (lane >> 5);
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-            uint4 w = make_uint4(0, 0, 0, 0);
-            if (ok) w = *reinterpret_cast<const uint4 *>(src + 16 * s);
-            __builtin_memcpy(&dst[s], &w, 16);
-        }
-    };
-    auto store_block = [&](long long c, const bf16x8_t *src) {
-        uint16_t *row = (wid < 2) ? &sm.Ks[c % 3][blk_row][8 * hi] : &sm.Qs[blk_row][8 * hi];
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) __builtin_memcpy(row + 16 * s, &src[s], 16);
-    };
-    // V tile of chunk c: 64 tokens x 32 d_v = 256 16-byte vectors, one per thread.
-    const int v_tok = tid >> 2, v_part = tid & 3;
-    auto load_v = [&](long long c) -> uint4 {
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (c < nchunks && v_tok < ntok(c))
-            w = *reinterpret_cast<const uint4 *>(p.v + ((size_t)(b * T + tok(c, v_tok)) * H + h) * dv + dv0 + 8 * v_part);
-        return w;
-    };
-    auto load_gates = [&](long long c, float &bb, float &aa) {
-        bb = 0.f;
-        aa = 1.f;
-        if (tid < C && c < nchunks && tid < ntok(c)) {
-            const size_t g = (size_t)(b * T + tok(c, tid)) * H + h;
-            bb = p.beta[g];
-            aa = p.decay[g];
-        }
-    };
+    for (int s = 0; s < DK / 16; ++s) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(src + 16 * s);
+        __builtin_memcpy(&dst[s], &w, 16);
+    }
+}
 
-    // ---- initial state: S^T block (d_k rows 32*wid.., d_v cols dv0 + l32) ----
-    f32x16_t sacc = zero16();
-    const size_t sbase = ((size_t)(b * H + h) * dv + dv0 + l32) * DK;
+// ---- state chain: waves 0-3 -------------------------------------------------
+template <int DK, bool BF16>
+__device__ __forceinline__ void chain_loop(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int wid,
+                                           int lane, void *out_b, float *part_b, size_t sbase) {
+    constexpr int NKS = DK / 16;
+    constexpr int NSB = DK / 32;
+    const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g16 = lane >> 4;
+
+    f32x16_t sacc = zero16();  // S^T block: d_k rows 32*wid.., d_v cols l32 (waves < NSB)
     if (wid < NSB) {
         if (p.state_in) {
 #pragma unroll
@@ -280,76 +245,27 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
             *reinterpret_cast<uint2 *>(&sm.Sb[l32][32 * wid + 8 * rb + 4 * hi]) =
                 pack4(sacc[4 * rb], sacc[4 * rb + 1], sacc[4 * rb + 2], sacc[4 * rb + 3]);
     }
-
-    // ---- pre-step: chunk 0 staged, its row blocks in registers ---------------
-    bf16x8_t cur[NKS], nxt[NKS], pf[NKS];
-    uint4 vpf = make_uint4(0, 0, 0, 0);
-    float bpf = 0.f, apf = 1.f;
-    if (nchunks > 0) {
-        load_block(0, nxt);
-        float bb, aa;
-        load_gates(0, bb, aa);
-        store_block(0, nxt);
-        if (tid < C) {
-            sm.rawbet[tid] = bb;
-            sm.rawdec[tid] = aa;
-        }
-    }
     __syncthreads();
 
-    // Iteration c: state chain of chunk c (c >= 0), preparation of chunk c+1.
-    for (long long c = -1; c < nchunks; ++c) {
+    for (int c = -1; c < x.nchunks; ++c) {
         const bool chain = c >= 0;
-        const bool prep = c + 1 < nchunks;
-        const int cb = (int)((c + 3) % 2);      // gate buffer of chunk c (c >= -1)
-        const int nb = (int)((c + 1 + 3) % 2);  // gate buffer of chunk c+1
-        const int n = chain ? ntok(c) : 0;
-
-        // ===== phase 1 ======================================================
-        // loads for later chunks
-        load_block(c + 2, pf);
-        vpf = load_v(c + 1);
-        load_gates(c + 2, bpf, apf);
-
-        // decay factors of chunk c+1 (wave 3)
-        if (prep && wid == 3) {
-            const float a = sm.rawdec[lane];
-            float l2 = __builtin_amdgcn_logf(a);  // log2
-            if (!(l2 > -200.0f)) l2 = -200.0f;    // a = 0: 2^-200 is 0 in fp32
-            double x = (double)l2;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const double y = __shfl_up(x, off, 64);
-                if (lane >= off) x += y;
-            }
-            const double xl = __shfl(x, 63, 64);
-            sm.g[nb][lane] = (float)x;
-            sm.gam[nb][lane] = exp2_fast((float)x);
-            sm.glast[nb][lane] = exp2_fast((float)(xl - x));
-            sm.bet[nb][lane] = sm.rawbet[lane];
-        }
-
+        const int cb = (c + 3) & 1;  // gate/P buffer of chunk c
+        // ===== phase 1: X = [K;Q] S^T, R ===================================
+        // this wave's row block of chunk c (K rows for waves 0-1, Q rows for 2-3)
+        const uint16_t *blk = (wid < 2) ? &sm.Ks[c < 0 ? 0 : c % 3][32 * (wid & 1) + l32][8 * hi]
+                                        : &sm.Qs[c & 1][32 * (wid & 1) + l32][8 * hi];
         f32x16_t xacc = zero16();
         if (chain) {
-            // off-diagonal 16x16 blocks of Tm for chunk c: block column `wid`
-            if (wid == 0) tm_column<0>(sm.Tb, sm.Ab, l16, g16);
-            else if (wid == 1) tm_column<1>(sm.Tb, sm.Ab, l16, g16);
-            else if (wid == 2) tm_column<2>(sm.Tb, sm.Ab, l16, g16);
-            // X: waves 0,1 K S^T (tokens x d_v); waves 2,3 (Q S^T)^T (d_v x tokens)
             if (wid < 2) {
+                // K S^T (tokens x d_v), then R = diag(b)(V - diag(gam) K S^T) -> R^T
 #pragma unroll
-                for (int s = 0; s < NKS; ++s) xacc = mfma32(cur[s], lds16(&sm.Sb[l32][16 * s + 8 * hi]), xacc);
-            } else {
-#pragma unroll
-                for (int s = 0; s < NKS; ++s) xacc = mfma32(lds16(&sm.Sb[l32][16 * s + 8 * hi]), cur[s], xacc);
-            }
-            if (wid < 2) {
-                // R = diag(b)(V - diag(gam) K S^T) -> R^T
+                for (int s = 0; s < NKS; ++s) xacc = mfma32(lds16(blk + 16 * s), lds16(&sm.Sb[l32][16 * s + 8 * hi]), xacc);
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) {
                     const int i0 = 32 * wid + 8 * rb + 4 * hi;
                     const s16x4_t vv = lds_tr(&sm.Vs[i0 + (l16 >> 2)][16 * (g16 & 1) + 4 * (l16 & 3)]);
-                    const uint2 vu = *reinterpret_cast<const uint2 *>(&vv);
+                    uint2 vu;
+                    __builtin_memcpy(&vu, &vv, 8);
                     const float4 bt = *reinterpret_cast<const float4 *>(&sm.bet[cb][i0]);
                     const float4 gm = *reinterpret_cast<const float4 *>(&sm.gam[cb][i0]);
                     const float r0 = bt.x * (bf16_lo(vu.x) - gm.x * xacc[4 * rb + 0]);
@@ -359,17 +275,18 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
                     *reinterpret_cast<uint2 *>(&sm.Rt[l32][i0]) = pack4(r0, r1, r2, r3);
                 }
             } else {
+                // (Q S^T)^T (d_v x tokens), scaled by gam of the token column
+#pragma unroll
+                for (int s = 0; s < NKS; ++s) xacc = mfma32(lds16(&sm.Sb[l32][16 * s + 8 * hi]), lds16(blk + 16 * s), xacc);
                 const float gq = sm.gam[cb][32 * (wid - 2) + l32];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) xacc[r] *= gq;
             }
         }
         __syncthreads();
-
-        // ===== phase 2 ======================================================
+        // ===== phase 2: N = Tm R ==============================================
         if (chain && wid < 2) {
-            // N = Tm R for token block wid (Tm lower triangular: keys < 32*(wid+1))
-            f32x16_t nacc = zero16();
+            f32x16_t nacc = zero16();  // token block wid; Tm lower triangular: keys < 32*(wid+1)
 #pragma unroll
             for (int k = 0; k < 64; k += 16) {
                 if (k >= 32 * (wid + 1)) break;
@@ -385,33 +302,173 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
                     pack4(gl.x * nacc[4 * rb], gl.y * nacc[4 * rb + 1], gl.z * nacc[4 * rb + 2], gl.w * nacc[4 * rb + 3]);
             }
         }
-        if (prep) {
-            // Gram products of chunk c+1, computed as (keys x queries):
-            //   wave 0: K_a K_a^T          wave 1: K_b K_b^T
-            //   wave 2: K_a Q_a^T, K_a K_b^T   wave 3: K_a Q_b^T, K_b Q_b^T
-            // (own row block from registers, the others from LDS)
-            const int kb3 = (int)((c + 1) % 3);
-            f32x16_t g0 = zero16(), g1 = zero16();
-            if (wid < 2) {
+        __syncthreads();
+        // ===== phase 3: outputs, state update =================================
+        if (chain) {
+            if (wid >= 2) {
+                // O^T = gam (Q S^T)^T + N^T P^T for query block tb, keys < 32*(tb+1)
+                const int tb = wid - 2;
 #pragma unroll
-                for (int s = 0; s < NKS; ++s) g0 = mfma32(nxt[s], nxt[s], g0);
-            } else if (wid == 2) {
+                for (int k = 0; k < 64; k += 16) {
+                    if (k >= 32 * (tb + 1)) break;
+                    xacc = mfma32(lds16(&sm.Nt[l32][k + 8 * hi]), lds16(&sm.Pb[cb][32 * tb + l32][k + 8 * hi]), xacc);
+                }
+                const int i = 32 * tb + l32;
+                if (i < x.ntok(c)) {
+                    const size_t e0 = (size_t)x.tok(c, i) * x.rsv;
+#pragma unroll
+                    for (int rb = 0; rb < 4; ++rb) {
+                        const size_t e = e0 + 8 * rb + 4 * hi;
+                        float o0 = xacc[4 * rb] * p.scale, o1 = xacc[4 * rb + 1] * p.scale;
+                        float o2 = xacc[4 * rb + 2] * p.scale, o3 = xacc[4 * rb + 3] * p.scale;
+                        if (p.out_mode == OUT_PARTIAL) {
+                            *reinterpret_cast<float4 *>(part_b + e) = make_float4(o0, o1, o2, o3);
+                        } else {
+                            if (p.out_mode == OUT_COMBINE) {
+                                const float4 pr = *reinterpret_cast<const float4 *>(part_b + e);
+                                o0 = pr.x + o0; o1 = pr.y + o1; o2 = pr.z + o2; o3 = pr.w + o3;
+                            }
+                            if constexpr (BF16)
+                                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out_b) + e) = pack4(o0, o1, o2, o3);
+                            else
+                                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out_b) + e) = make_float4(o0, o1, o2, o3);
+                        }
+                    }
+                }
+            }
+            if (wid < NSB) {
+                // S^T <- gam_{C-1} S^T + K^T N~  (K^T read transposed from the token-major K)
+                const float gl = sm.gam[cb][C - 1];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[r] *= gl;
+                const int kb3 = c % 3;
+                const int dcol = 32 * wid + 16 * (g16 & 1) + 4 * (l16 & 3);
+#pragma unroll
+                for (int t = 0; t < 64; t += 16) {
+                    const int t0 = t + 8 * hi + (l16 >> 2);
+                    const bf16x8_t a = join(lds_tr(&sm.Ks[kb3][t0][dcol]), lds_tr(&sm.Ks[kb3][t0 + 4][dcol]));
+                    sacc = mfma32(a, lds16(&sm.Nd[l32][t + 8 * hi]), sacc);
+                }
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb)
+                    *reinterpret_cast<uint2 *>(&sm.Sb[l32][32 * wid + 8 * rb + 4 * hi]) =
+                        pack4(sacc[4 * rb], sacc[4 * rb + 1], sacc[4 * rb + 2], sacc[4 * rb + 3]);
+            }
+        }
+        __syncthreads();
+    }
+
+    if (p.state_out && wid < NSB) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+            *reinterpret_cast<float4 *>(p.state_out + sbase + 32 * wid + 8 * rb + 4 * hi) =
+                make_float4(sacc[4 * rb], sacc[4 * rb + 1], sacc[4 * rb + 2], sacc[4 * rb + 3]);
+    }
+}
+
+// ---- preparation: waves 4-7 (role = wid - 4) ---------------------------------
+template <int DK>
+__device__ __forceinline__ void prep_loop(const Ctx &x, Smem<DK> &sm, int role, int lane) {
+    constexpr int NKS = DK / 16;
+    const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g16 = lane >> 4;
+    const int ptid = 64 * role + lane;
+    const int v_tok = ptid >> 2, v_part = ptid & 3;  // V tile: 64 tokens x 4 16-byte vectors
+
+    auto store_block = [&](int c, const bf16x8_t *src) {
+        uint16_t *row = (role < 2) ? &sm.Ks[c % 3][32 * (role & 1) + l32][8 * hi] : &sm.Qs[c & 1][32 * (role & 1) + l32][8 * hi];
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) __builtin_memcpy(row + 16 * s, &src[s], 16);
+    };
+    auto load_v = [&](int c, uint4 &w) {
+        if (c >= x.nchunks) return;  // uniform
+        const int nt = x.ntok(c);
+        w = *reinterpret_cast<const uint4 *>(x.v + (size_t)x.tok(c, v_tok < nt ? v_tok : nt - 1) * x.rsv + 8 * v_part);
+    };
+    // gates of chunk c (role 0, lane = token); padding gets b = 0, a = 1 when stored
+    auto load_gates = [&](int c, float &bb, float &aa, bool &ok) {
+        ok = false;
+        if (c >= x.nchunks) return;  // uniform
+        const int nt = x.ntok(c);
+        ok = lane < nt;
+        const size_t g = (size_t)x.tok(c, ok ? lane : nt - 1) * x.H;
+        bb = x.beta[g];
+        aa = x.decay[g];
+    };
+
+    bf16x8_t rcur[NKS], rnext[NKS];  // this wave's row block of chunk c+1, and of chunk c+2
+    uint4 vpf = make_uint4(0, 0, 0, 0);
+    float bpf = 0.f, apf = 1.f;
+    bool gpf = false;
+    if (x.nchunks > 0) {
+        load_block<DK>(x, 0, role, lane, rcur);
+        if (role == 0) load_gates(0, bpf, apf, gpf);
+        store_block(0, rcur);
+        if (role == 0) {
+            sm.rawbet[lane] = gpf ? bpf : 0.f;
+            sm.rawdec[lane] = gpf ? apf : 1.f;
+        }
+    }
+    __syncthreads();
+
+    for (int c = -1; c < x.nchunks; ++c) {
+        const bool prep = c + 1 < x.nchunks;
+        const int nb = c & 1;  // gate/P buffer of chunk c+1 (== (c + 4) & 1)
+        f32x16_t g0 = zero16(), g1 = zero16();
+        // ===== phase 1: later chunks' loads; Tm of chunk c; Gram products of c+1
+        load_block<DK>(x, c + 2, role, lane, rnext);
+        load_v(c + 1, vpf);
+        if (role == 0) load_gates(c + 2, bpf, apf, gpf);
+        if (c >= 0) {  // off-diagonal 16x16 blocks of Tm for chunk c: block column `role`
+            if (role == 0) tm_column<0>(sm.Tb, sm.Ab, l16, g16);
+            else if (role == 1) tm_column<1>(sm.Tb, sm.Ab, l16, g16);
+            else if (role == 2) tm_column<2>(sm.Tb, sm.Ab, l16, g16);
+        }
+        if (prep) {
+            if (role == 3) {
+                // decay factors of chunk c+1: g = cumulative log2 a (summed in float64)
+                const float a = sm.rawdec[lane];
+                float l2 = __builtin_amdgcn_logf(a);  // log2
+                if (!(l2 > -200.0f)) l2 = -200.0f;    // a = 0: 2^-200 is 0 in fp32
+                double xs = (double)l2;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const double y = __shfl_up(xs, off, 64);
+                    if (lane >= off) xs += y;
+                }
+                const double xl = __shfl(xs, 63, 64);
+                sm.g[nb][lane] = (float)xs;
+                sm.gam[nb][lane] = exp2_fast((float)xs);
+                sm.glast[nb][lane] = exp2_fast((float)(xl - xs));
+                sm.bet[nb][lane] = sm.rawbet[lane];
+            }
+            // Gram products of chunk c+1, computed as (keys x queries):
+            //   role 0: K_a K_a^T          role 1: K_b K_b^T
+            //   role 2: K_a Q_a^T, K_a K_b^T   role 3: K_a Q_b^T, K_b Q_b^T
+            const int kb3 = (c + 1) % 3;
+            if (role < 2) {
+#pragma unroll
+                for (int s = 0; s < NKS; ++s) g0 = mfma32(rcur[s], rcur[s], g0);
+            } else if (role == 2) {
 #pragma unroll
                 for (int s = 0; s < NKS; ++s) {
                     const int ko = 16 * s + 8 * hi;
                     const bf16x8_t ka = lds16(&sm.Ks[kb3][l32][ko]);
-                    g0 = mfma32(ka, nxt[s], g0);
+                    g0 = mfma32(ka, rcur[s], g0);
                     g1 = mfma32(ka, lds16(&sm.Ks[kb3][32 + l32][ko]), g1);
                 }
             } else {
 #pragma unroll
                 for (int s = 0; s < NKS; ++s) {
                     const int ko = 16 * s + 8 * hi;
-                    g0 = mfma32(lds16(&sm.Ks[kb3][l32][ko]), nxt[s], g0);
-                    g1 = mfma32(lds16(&sm.Ks[kb3][32 + l32][ko]), nxt[s], g1);
+                    g0 = mfma32(lds16(&sm.Ks[kb3][l32][ko]), rcur[s], g0);
+                    g1 = mfma32(lds16(&sm.Ks[kb3][32 + l32][ko]), rcur[s], g1);
                 }
             }
-            // Epilogues: element (key j, query i); factor 2^{g_i - g_j} for j <= i.
+        }
+        __syncthreads();
+        // ===== phase 2: Gram epilogues of chunk c+1 -> A, P ===================
+        if (prep) {
+            // element (key j, query i); factor 2^{g_i - g_j} for j <= i
             const float *gg = sm.g[nb];
             auto epi = [&](const f32x16_t &acc, int jb, int ib, bool is_k) {
                 const int i = 32 * ib + l32;
@@ -438,11 +495,11 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
                     }
                 }
             };
-            if (wid == 0) {
+            if (role == 0) {
                 epi(g0, 0, 0, true);
-            } else if (wid == 1) {
+            } else if (role == 1) {
                 epi(g0, 1, 1, true);
-            } else if (wid == 2) {
+            } else if (role == 2) {
                 epi(g0, 0, 0, false);
                 epi(g1, 0, 1, true);
             } else {
@@ -451,117 +508,100 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
             }
         }
         __syncthreads();
-
-        // ===== phase 3 ======================================================
-        if (chain) {
-            if (wid >= 2) {
-                // O^T = gam (Q S^T)^T + N^T P^T for query block tb, keys < 32*(tb+1)
-                const int tb = wid - 2;
-                const int pbuf = cb;
+        // ===== phase 3: diagonal blocks of Tm for chunk c+1; staging ==========
+        if (prep && role < 2 && g16 < 2) {
+            // lane l16 of half g16 owns row l16 of block 2*role + g16.  Row i of
+            // (I + A_kk)^{-1} solves (I + A_kk)^T y = e_i; backward substitution,
+            // right-looking: once y_j is known, y_m -= A[j][m] y_j for every m < j.
+            const int kb = 2 * role + g16;
+            const int i = l16;
+            float y[16];
 #pragma unroll
-                for (int k = 0; k < 64; k += 16) {
-                    if (k >= 32 * (tb + 1)) break;
-                    xacc = mfma32(lds16(&sm.Nt[l32][k + 8 * hi]), lds16(&sm.Pb[pbuf][32 * tb + l32][k + 8 * hi]), xacc);
-                }
-                const int i = 32 * tb + l32;
-                if (i < n) {
-                    const size_t e0 = ((size_t)(b * T + tok(c, i)) * H + h) * dv + dv0;
+            for (int m = 0; m < 16; ++m) y[m] = (m == i) ? 1.f : 0.f;
 #pragma unroll
-                    for (int rb = 0; rb < 4; ++rb) {
-                        const size_t e = e0 + 8 * rb + 4 * hi;
-                        float o0 = xacc[4 * rb] * p.scale, o1 = xacc[4 * rb + 1] * p.scale;
-                        float o2 = xacc[4 * rb + 2] * p.scale, o3 = xacc[4 * rb + 3] * p.scale;
-                        if (p.out_mode == OUT_PARTIAL) {
-                            *reinterpret_cast<float4 *>(p.partial + e) = make_float4(o0, o1, o2, o3);
-                        } else {
-                            if (p.out_mode == OUT_COMBINE) {
-                                const float4 pr = *reinterpret_cast<const float4 *>(p.partial + e);
-                                o0 = pr.x + o0; o1 = pr.y + o1; o2 = pr.z + o2; o3 = pr.w + o3;
-                            }
-                            if constexpr (BF16)
-                                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.out) + e) = pack4(o0, o1, o2, o3);
-                            else
-                                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.out) + e) = make_float4(o0, o1, o2, o3);
-                        }
-                    }
+            for (int j = 15; j >= 1; --j) {
+                const float *arow = &sm.Ad[kb][j][0];  // A[j][m], m < j
+                float av[16];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    if (4 * q4 >= j) break;
+                    const float4 f = *reinterpret_cast<const float4 *>(arow + 4 * q4);
+                    av[4 * q4] = f.x; av[4 * q4 + 1] = f.y; av[4 * q4 + 2] = f.z; av[4 * q4 + 3] = f.w;
                 }
+#pragma unroll
+                for (int m = 0; m < j; ++m) y[m] -= av[m] * y[j];
             }
-            if (wid < NSB) {
-                // S^T <- gam_{C-1} S^T + K^T N~  (K^T read transposed from the token-major K)
-                const float gl = sm.gam[cb][C - 1];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[r] *= gl;
-                const int kb3 = (int)(c % 3);
-                const int dcol = 32 * wid + 16 * (g16 & 1) + 4 * (l16 & 3);
-#pragma unroll
-                for (int t = 0; t < 64; t += 16) {
-                    const int t0 = t + 8 * hi + (l16 >> 2);
-                    const bf16x8_t a = join(lds_tr(&sm.Ks[kb3][t0][dcol]), lds_tr(&sm.Ks[kb3][t0 + 4][dcol]));
-                    sacc = mfma32(a, lds16(&sm.Nd[l32][t + 8 * hi]), sacc);
-                }
-#pragma unroll
-                for (int rb = 0; rb < 4; ++rb)
-                    *reinterpret_cast<uint2 *>(&sm.Sb[l32][32 * wid + 8 * rb + 4 * hi]) =
-                        pack4(sacc[4 * rb], sacc[4 * rb + 1], sacc[4 * rb + 2], sacc[4 * rb + 3]);
+            uint16_t *row = &sm.Tb[16 * kb + i][16 * kb];
+            const uint4 w0 = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                                        pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+            const uint4 w1 = make_uint4(pack_bf16x2(y[8], y[9]), pack_bf16x2(y[10], y[11]),
+                                        pack_bf16x2(y[12], y[13]), pack_bf16x2(y[14], y[15]));
+            *reinterpret_cast<uint4 *>(row) = w0;
+            *reinterpret_cast<uint4 *>(row + 8) = w1;
+            if ((kb & 1) == 0) {  // zero block right of the diagonal inside the 32-row block
+                *reinterpret_cast<uint4 *>(row + 16) = make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4 *>(row + 24) = make_uint4(0, 0, 0, 0);
             }
         }
-        if (prep && wid < 2) {
-            // 16x16 diagonal blocks of Tm for chunk c+1: lane l16 of half g16 (0/1)
-            // owns row l16 of block 2*wid + g16.  Row i of (I + A_kk)^{-1} solves
-            // (I + A_kk)^T y = e_i; backward substitution, right-looking: once y_j is
-            // known, acc_m -= A[j][m] y_j for every m < j (independent FMAs).
-            if (g16 < 2) {
-                const int kb = 2 * wid + g16;
-                const int i = l16;
-                float y[16];
-#pragma unroll
-                for (int m = 0; m < 16; ++m) y[m] = (m == i) ? 1.f : 0.f;
-#pragma unroll
-                for (int j = 15; j >= 1; --j) {
-                    const float *arow = &sm.Ad[kb][j][0];  // A[j][m], m < j
-                    float av[16];
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        if (4 * q4 >= j) break;
-                        const float4 f = *reinterpret_cast<const float4 *>(arow + 4 * q4);
-                        av[4 * q4] = f.x; av[4 * q4 + 1] = f.y; av[4 * q4 + 2] = f.z; av[4 * q4 + 3] = f.w;
-                    }
-#pragma unroll
-                    for (int m = 0; m < j; ++m) y[m] -= av[m] * y[j];
-                }
-                uint16_t *row = &sm.Tb[16 * kb + i][16 * kb];
-                const uint4 w0 = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
-                                            pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
-                const uint4 w1 = make_uint4(pack_bf16x2(y[8], y[9]), pack_bf16x2(y[10], y[11]),
-                                            pack_bf16x2(y[12], y[13]), pack_bf16x2(y[14], y[15]));
-                *reinterpret_cast<uint4 *>(row) = w0;
-                *reinterpret_cast<uint4 *>(row + 8) = w1;
-                if ((kb & 1) == 0) {  // zero block right of the diagonal inside the 32-row block
-                    *reinterpret_cast<uint4 *>(row + 16) = make_uint4(0, 0, 0, 0);
-                    *reinterpret_cast<uint4 *>(row + 24) = make_uint4(0, 0, 0, 0);
-                }
-            }
-        }
-        // stage chunk c+2 (row blocks, already in pf) and chunk c+1's V tile and gates
-        if (c + 2 < nchunks) store_block(c + 2, pf);
+        // stage chunk c+2 (row blocks), chunk c+1's V tile and chunk c+2's gates
+        if (c + 2 < x.nchunks) store_block(c + 2, rnext);
         if (prep) *reinterpret_cast<uint4 *>(&sm.Vs[v_tok][8 * v_part]) = vpf;
-        if (tid < C) {
-            sm.rawbet[tid] = bpf;
-            sm.rawdec[tid] = apf;
+        if (role == 0 && c + 2 < x.nchunks) {
+            sm.rawbet[lane] = gpf ? bpf : 0.f;
+            sm.rawdec[lane] = gpf ? apf : 1.f;
         }
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-            cur[s] = nxt[s];
-            nxt[s] = pf[s];
-        }
+        for (int s = 0; s < NKS; ++s) rcur[s] = rnext[s];
         __syncthreads();
     }
+}
 
-    if (p.state_out && wid < NSB) {
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-            *reinterpret_cast<float4 *>(p.state_out + sbase + 32 * wid + 8 * rb + 4 * hi) =
-                make_float4(sacc[4 * rb], sacc[4 * rb + 1], sacc[4 * rb + 2], sacc[4 * rb + 3]);
+template <int DK, bool BF16>
+__global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
+    static_assert(DK % 32 == 0 && DK <= 128, "d_k must be 32, 64 or 128");
+    __shared__ Smem<DK> sm;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+
+    // Block -> (b, h, d_v tile).  With the XCD remap, the ntile blocks of one head
+    // get linear ids that differ by multiples of 8, i.e. land on one XCD.
+    const int L = blockIdx.x;
+    int head, tile;
+    if (p.xcd_remap) {
+        const int slot = L >> 3;
+        tile = slot % p.ntile;
+        head = (slot / p.ntile) * 8 + (L & 7);
+    } else {
+        tile = L % p.ntile;
+        head = L / p.ntile;
+    }
+    const int h = head % p.H;
+    const int b = head / p.H;
+    const int dv0 = tile * DVT;
+
+    Ctx x;
+    x.T = p.T;
+    x.nchunks = (int)((p.T + C - 1) / C);
+    x.rs = p.H * DK;
+    x.rsv = p.H * p.dv;
+    x.H = p.H;
+    x.reverse = p.reverse;
+    const size_t tok0 = (size_t)b * p.T * p.H + h;  // (b, token 0, h) in [B, T, H]
+    x.q = p.q + tok0 * DK;
+    x.k = p.k + tok0 * DK;
+    x.v = p.v + tok0 * p.dv + dv0;
+    x.beta = p.beta + tok0;
+    x.decay = p.decay + tok0;
+
+    if (wid < 4) {
+        void *out_b = BF16 ? (void *)(reinterpret_cast<uint16_t *>(p.out) + tok0 * p.dv + dv0)
+                           : (void *)(reinterpret_cast<float *>(p.out) + tok0 * p.dv + dv0);
+        float *part_b = p.partial ? p.partial + tok0 * p.dv + dv0 : nullptr;
+        const size_t sbase = ((size_t)(b * p.H + h) * p.dv + dv0 + (lane & 31)) * DK;
+        chain_loop<DK, BF16>(x, sm, p, wid, lane, out_b, part_b, sbase);
+    } else {
+        prep_loop<DK>(x, sm, wid - 4, lane);
     }
 }
 
