@@ -243,7 +243,7 @@ def measure_forms(torch, gb, inputs, d, g, x):
     ms = timed(torch, lambda: gb.gdn_forward_bidi(gbd.h, xb["q"], xb["k"], xb["v"], xb["beta"], xb["decay"],
                                                   ob, wb.T, 64, stream), 5)
     forms["bidi_bf16_d128"] = {"ms": ms, "token_heads_per_s": wb.B * wb.H * wb.T / (ms / 1e3),
-                               "design": "two passes through an fp32 partial"}
+                               "design": "both directions in one launch, two fp32 partials, one combine"}
     gbd.close()
     return forms
 

@@ -22,7 +22,7 @@
 struct gdn_ctx {
     gdn_config cfg{};
     std::string err;
-    float *scratch = nullptr;  // fp32 [B, max_T, H, d_v] partial for the bidirectional form
+    float *scratch = nullptr;  // two fp32 [B, max_T, H, d_v] partials for the bidirectional form
     size_t scratch_bytes = 0;
 };
 
@@ -194,7 +194,7 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
     if (elems > 9.0e18) return fail_create(GDN_ERR_ARG, "B*max_T*H is too large");
 
     size_t scratch_bytes = 0;
-    if (c.flags & GDN_FLAG_BIDI) scratch_bytes = (size_t)c.B * (size_t)c.max_T * c.H * c.d_v * sizeof(float);
+    if (c.flags & GDN_FLAG_BIDI) scratch_bytes = 2 * (size_t)c.B * (size_t)c.max_T * c.H * c.d_v * sizeof(float);
 
     float *scratch = nullptr;
     if (c.device >= 0) {
@@ -217,7 +217,7 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
             e = hipMalloc(reinterpret_cast<void **>(&scratch), scratch_bytes);
             if (e != hipSuccess) {
                 (void)hipGetLastError();
-                return fail_create(GDN_ERR_OOM, "hipMalloc(%zu bytes) for the bidirectional partial: %s",
+                return fail_create(GDN_ERR_OOM, "hipMalloc(%zu bytes) for the bidirectional partials: %s",
                                    scratch_bytes, hipGetErrorString(e));
             }
         }
@@ -330,20 +330,24 @@ int gdn_forward_bidi(gdn_handle h, const void *q, const void *k, const void *v, 
     DeviceGuard g(c.device);
     gdn::PassArgs a{};
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.decay = decay;
-    a.state_in = nullptr; a.state_out = nullptr; a.out = out; a.partial = h->scratch;
+    const size_t n_out = (size_t)c.B * (size_t)T * c.H * c.d_v;
+    a.state_in = nullptr; a.state_out = nullptr; a.out = out;
+    a.partial = h->scratch;
+    a.partial_rev = h->scratch + n_out;
     a.B = c.B; a.H = c.H; a.dk = c.d_k; a.dv = c.d_v; a.T = T;
     a.io_bf16 = c.io_dtype == GDN_BF16;
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-    // Forward direction into the fp32 partial, then the reverse direction adds
-    // its own output, rounding the sum once.
+    // Both directions in one launch, each into its own fp32 partial (the reverse
+    // direction walks the tokens from T-1 down, chunk grid anchored there), then
+    // out = round(partial + partial_rev): one rounding, and fp32 addition is
+    // commutative, so reversing the inputs reverses the output exactly.
     a.reverse = 0;
+    a.both_dirs = 1;
     a.out_mode = gdn::OUT_PARTIAL;
     hipError_t e = (C == 1) ? gdn::launch_scan(a, s) : gdn::launch_chunk(a, C, s);
-    if ((st = launch_status(h, e, "bidirectional forward pass"))) return st;
-    a.reverse = 1;
-    a.out_mode = gdn::OUT_COMBINE;
-    e = (C == 1) ? gdn::launch_scan(a, s) : gdn::launch_chunk(a, C, s);
-    return launch_status(h, e, "bidirectional reverse pass");
+    if ((st = launch_status(h, e, "bidirectional pass"))) return st;
+    e = gdn::launch_combine(out, a.partial, a.partial_rev, (long long)n_out, a.io_bf16, s);
+    return launch_status(h, e, "bidirectional combine");
 }
 
 }  // extern "C"

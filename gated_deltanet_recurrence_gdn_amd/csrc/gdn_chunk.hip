@@ -85,10 +85,10 @@ struct ChunkParams {
     const float *state_in;
     float *state_out;
     void *out;
-    float *partial;
+    float *partial, *partial_rev;
     long long T;
-    int H, dv, ntile;
-    int reverse, out_mode, xcd_remap;
+    int H, dv, ntile, nblk_dir;
+    int reverse, out_mode, xcd_remap, both_dirs;
     float scale;
 };
 
@@ -324,10 +324,6 @@ __device__ __forceinline__ void chain_loop(const Ctx &x, Smem<DK> &sm, const Chu
                         if (p.out_mode == OUT_PARTIAL) {
                             *reinterpret_cast<float4 *>(part_b + e) = make_float4(o0, o1, o2, o3);
                         } else {
-                            if (p.out_mode == OUT_COMBINE) {
-                                const float4 pr = *reinterpret_cast<const float4 *>(part_b + e);
-                                o0 = pr.x + o0; o1 = pr.y + o1; o2 = pr.z + o2; o3 = pr.w + o3;
-                            }
                             if constexpr (BF16)
                                 *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out_b) + e) = pack4(o0, o1, o2, o3);
                             else
@@ -564,18 +560,18 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     const int lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
 
-    // Block -> (b, h, d_v tile).  With the XCD remap, the ntile blocks of one head
-    // get linear ids that differ by multiples of 8, i.e. land on one XCD.
-    const int L = blockIdx.x;
-    int head, tile;
-    if (p.xcd_remap) {
-        const int slot = L >> 3;
-        tile = slot % p.ntile;
-        head = (slot / p.ntile) * 8 + (L & 7);
-    } else {
-        tile = L % p.ntile;
-        head = L / p.ntile;
+    // Block -> (direction, b, h, d_v tile).  Blocks are dispatched round-robin over
+    // the 8 XCDs (linear id mod 8); with the remap, the blocks on one XCD take
+    // consecutive (head, tile) indices, so the d_v tiles of a head share an L2.
+    int L = blockIdx.x;
+    int dir = 0;
+    if (p.both_dirs && L >= p.nblk_dir) {
+        dir = 1;
+        L -= p.nblk_dir;
     }
+    const int v = p.xcd_remap ? (L & 7) * (p.nblk_dir >> 3) + (L >> 3) : L;
+    const int tile = v % p.ntile;
+    const int head = v / p.ntile;
     const int h = head % p.H;
     const int b = head / p.H;
     const int dv0 = tile * DVT;
@@ -586,7 +582,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     x.rs = p.H * DK;
     x.rsv = p.H * p.dv;
     x.H = p.H;
-    x.reverse = p.reverse;
+    x.reverse = p.reverse ^ dir;
     const size_t tok0 = (size_t)b * p.T * p.H + h;  // (b, token 0, h) in [B, T, H]
     x.q = p.q + tok0 * DK;
     x.k = p.k + tok0 * DK;
@@ -597,7 +593,8 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     if (wid < 4) {
         void *out_b = BF16 ? (void *)(reinterpret_cast<uint16_t *>(p.out) + tok0 * p.dv + dv0)
                            : (void *)(reinterpret_cast<float *>(p.out) + tok0 * p.dv + dv0);
-        float *part_b = p.partial ? p.partial + tok0 * p.dv + dv0 : nullptr;
+        float *part = dir ? p.partial_rev : p.partial;
+        float *part_b = part ? part + tok0 * p.dv + dv0 : nullptr;
         const size_t sbase = ((size_t)(b * p.H + h) * p.dv + dv0 + (lane & 31)) * DK;
         chain_loop<DK, BF16>(x, sm, p, wid, lane, out_b, part_b, sbase);
     } else {
@@ -612,14 +609,16 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.k = static_cast<const uint16_t *>(a.k);
     p.v = static_cast<const uint16_t *>(a.v);
     p.beta = a.beta; p.decay = a.decay;
-    p.state_in = a.state_in; p.state_out = a.state_out; p.out = a.out; p.partial = a.partial;
+    p.state_in = a.state_in; p.state_out = a.state_out; p.out = a.out;
+    p.partial = a.partial; p.partial_rev = a.partial_rev;
     p.T = a.T; p.H = a.H; p.dv = a.dv;
     p.ntile = a.dv / DVT;
-    const int heads = a.B * a.H;
-    p.xcd_remap = (heads % 8) == 0;
-    p.reverse = a.reverse; p.out_mode = a.out_mode;
+    p.nblk_dir = a.B * a.H * p.ntile;
+    p.xcd_remap = (p.nblk_dir % 8) == 0;
+    p.reverse = a.reverse; p.out_mode = a.out_mode; p.both_dirs = a.both_dirs;
     p.scale = (float)(1.0 / __builtin_sqrt((double)DK));
-    hipLaunchKernelGGL((chunk_kernel<DK, true>), dim3(heads * p.ntile), dim3(NT), 0, stream, p);
+    const int nblk = p.nblk_dir * (a.both_dirs ? 2 : 1);
+    hipLaunchKernelGGL((chunk_kernel<DK, true>), dim3(nblk), dim3(NT), 0, stream, p);
     return hipGetLastError();
 }
 

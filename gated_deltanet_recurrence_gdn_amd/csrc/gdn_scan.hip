@@ -36,10 +36,10 @@ struct ScanParams {
     const float *state_in;
     float *state_out;
     void *out;
-    float *partial;
+    float *partial, *partial_rev;
     long long T;
-    int H, dv;
-    int reverse, out_mode;
+    int B, H, dv;
+    int reverse, out_mode, both_dirs;
     float scale;
 };
 
@@ -102,7 +102,12 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
     const int rloc = tid / L;          // row within the block
     const int row0 = blockIdx.x * rows;
     const int h = blockIdx.y;
-    const int b = blockIdx.z;
+    // grid.z covers (direction, b); the second direction (both_dirs) runs reversed
+    // and writes its own fp32 partial.
+    const int dir = blockIdx.z >= p.B ? 1 : 0;
+    const int b = blockIdx.z - dir * p.B;
+    const int reverse = p.reverse ^ dir;
+    float *partial = dir ? p.partial_rev : p.partial;
     const int H = p.H;
     const long long T = p.T;
     const int dv = p.dv;
@@ -135,7 +140,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
 
     auto tok_of = [&](long long st, int j) -> long long {
         const long long sidx = st * TB + j;
-        return p.reverse ? T - 1 - sidx : sidx;
+        return reverse ? T - 1 - sidx : sidx;
     };
     auto issue = [&](long long st) {
 #pragma unroll
@@ -250,9 +255,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
             const size_t e = ((size_t)(b * T + tok_of(st, j)) * H + h) * dv + row0 + r;
             const float o = of[j][r];
             if (p.out_mode == OUT_PARTIAL) {
-                p.partial[e] = o;
-            } else if (p.out_mode == OUT_COMBINE) {
-                store_out<BF16>(p.out, e, p.partial[e] + o);
+                partial[e] = o;
             } else {
                 store_out<BF16>(p.out, e, o);
             }
@@ -274,16 +277,32 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     const int rows = (NT / L) < a.dv ? (NT / L) : a.dv;
     ScanParams p;
     p.q = a.q; p.k = a.k; p.v = a.v; p.beta = a.beta; p.decay = a.decay;
-    p.state_in = a.state_in; p.state_out = a.state_out; p.out = a.out; p.partial = a.partial;
-    p.T = a.T; p.H = a.H; p.dv = a.dv; p.reverse = a.reverse; p.out_mode = a.out_mode;
+    p.state_in = a.state_in; p.state_out = a.state_out; p.out = a.out;
+    p.partial = a.partial; p.partial_rev = a.partial_rev;
+    p.T = a.T; p.B = a.B; p.H = a.H; p.dv = a.dv; p.reverse = a.reverse; p.out_mode = a.out_mode;
+    p.both_dirs = a.both_dirs;
     p.scale = (float)(1.0 / __builtin_sqrt((double)DK));
-    dim3 grid(a.dv / rows, a.H, a.B);
+    dim3 grid(a.dv / rows, a.H, a.B * (a.both_dirs ? 2 : 1));
     dim3 block(rows * L);
     if (a.io_bf16)
         hipLaunchKernelGGL((scan_kernel<DK, true>), grid, block, 0, stream, p);
     else
         hipLaunchKernelGGL((scan_kernel<DK, false>), grid, block, 0, stream, p);
     return hipGetLastError();
+}
+
+// out = round(partial + partial_rev), 4 elements per thread.
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(void *out, const float4 *pa, const float4 *pb, long long n4) {
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        const float4 x = pa[i], y = pb[i];
+        const float o0 = x.x + y.x, o1 = x.y + y.y, o2 = x.z + y.z, o3 = x.w + y.w;
+        if constexpr (BF16)
+            reinterpret_cast<uint2 *>(out)[i] = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+        else
+            reinterpret_cast<float4 *>(out)[i] = make_float4(o0, o1, o2, o3);
+    }
 }
 
 }  // namespace
@@ -297,5 +316,21 @@ hipError_t launch_scan(const PassArgs &a, hipStream_t stream) {
         default: return hipErrorInvalidValue;
     }
 }
+
+hipError_t launch_combine(void *out, const float *partial, const float *partial_rev, long long n,
+                          int io_bf16, hipStream_t stream) {
+    const long long n4 = n / 4;
+    if (n4 == 0) return hipSuccess;
+    long long nb = (n4 + 255) / 256;
+    if (nb > 256 * 64) nb = 256 * 64;
+    const float4 *pa = reinterpret_cast<const float4 *>(partial);
+    const float4 *pb = reinterpret_cast<const float4 *>(partial_rev);
+    if (io_bf16)
+        hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)nb), dim3(256), 0, stream, out, pa, pb, n4);
+    else
+        hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)nb), dim3(256), 0, stream, out, pa, pb, n4);
+    return hipGetLastError();
+}
+
 
 }  // namespace gdn
