@@ -77,8 +77,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=8192,
-                    help="tokens per head of the oracle's CPU sample (prefix of the same inputs)")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens per head of the oracle's CPU sample (prefix of the same inputs); "
+                         "0 = every token of the workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-forms", action="store_true", help="skip the secondary forms")
     ap.add_argument("--calib-copy", action="store_true",
@@ -250,7 +251,7 @@ def measure_forms(torch, gb, inputs, d, g, x):
 
 def cpu_baseline(x, tokens):
     import oracle
-    Ts = min(tokens, x["q"].shape[1])
+    Ts = x["q"].shape[1] if tokens <= 0 else min(tokens, x["q"].shape[1])
     sample = {k_: v_[:, :Ts].contiguous() for k_, v_ in x.items()}
     B, _, H, _ = sample["q"].shape
     t0 = time.perf_counter()

@@ -1,0 +1,146 @@
+"""Summarise rocprofv3 CSV output of bench.py runs into short text files under profiles/.
+
+Three rocprofv3 runs of bench.py feed it (each its own process; see the command lines
+written into the summaries):
+
+  kernel trace:  rocprofv3 --kernel-trace --stats --output-format csv -d DIR/kt -o kt -- \\
+                     python bench.py --steps 5 --warmup 1 --no-cpu --no-forms
+  fetch bytes:   rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o fetch -- \\
+                     python bench.py --steps 2 --warmup 1 --no-cpu --no-forms --calib-copy
+  write bytes:   rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o write -- \\
+                     python bench.py --steps 2 --warmup 1 --no-cpu --no-forms --calib-copy
+
+    python -m gated_deltanet_recurrence_gdn_amd.profile_summary DIR [--workload NAME]
+
+FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same counters
+read for the plain 512 MiB device copy that --calib-copy adds to the run: the copy
+reads and writes exactly 512 MiB, so scale = 512 MiB / counter.  The scaled bytes
+per launch of the chunked kernel are written to
+profiles/chunk_kernel_<workload>_traffic.json together with a hash of the kernel
+source, which bench.py checks before reporting them.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+PROFILES = os.path.join(ROOT, "profiles")
+CHUNK = "chunk_kernel"
+COPY = "copyBuffer"
+COPY_BYTES = 512 * 1024 * 1024
+
+KT_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d {d}/kt -o kt -- "
+          "python bench.py --steps 5 --warmup 1 --no-cpu --no-forms")
+PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d {d}/{n} -o {n} -- "
+           "python bench.py --steps 2 --warmup 1 --no-cpu --no-forms --calib-copy")
+
+
+def _csv(path_glob):
+    paths = glob.glob(path_glob, recursive=True)
+    if not paths:
+        raise FileNotFoundError(path_glob)
+    with open(paths[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def src_hash():
+    with open(os.path.join(PKG, "csrc", "gdn_chunk.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def kernel_stats(d):
+    rows = _csv(os.path.join(d, "kt", "**", "*kernel_stats.csv"))
+    out = []
+    for r in rows:
+        out.append((r["Name"], int(r["Calls"]), float(r["TotalDurationNs"]), float(r["AverageNs"]),
+                    float(r["Percentage"])))
+    return out
+
+
+def counter_per_dispatch(d, sub, counter):
+    rows = _csv(os.path.join(d, sub, "**", "*counter_collection.csv"))
+    vals = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    chunk = [v for k, vs in vals.items() if CHUNK in k for v in vs]
+    copy = [v for k, vs in vals.items() if COPY in k for v in vs]
+    if not chunk or not copy:
+        raise RuntimeError(f"{counter}: chunk kernel or copy dispatch missing in {d}/{sub}")
+    return statistics.mean(chunk), statistics.mean(copy), len(chunk)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("dir", help="directory holding the kt/, fetch/ and write/ rocprofv3 outputs")
+    ap.add_argument("--workload", default="batched_bf16_d128")
+    ap.add_argument("--algorithmic-bytes", type=float, default=None,
+                    help="algorithmic bytes per launch (default: bench.py's formula for the workload)")
+    a = ap.parse_args()
+    os.makedirs(PROFILES, exist_ok=True)
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    from gated_deltanet_recurrence_gdn_amd import inputs
+    w = inputs.WORKLOADS[a.workload]
+    abytes = a.algorithmic_bytes or bench.algorithmic_bytes(w.B, w.T, w.H, w.dk, w.dv)
+
+    stats = kernel_stats(a.dir)
+    chunk_avg = [s for s in stats if CHUNK in s[0]]
+    lines = [f"rocprofv3 kernel trace: chunked GDN kernel, workload {w.name}",
+             f"(B={w.B}, H={w.H}, T={w.T}, d_k={w.dk}, d_v={w.dv}, bf16 I/O, chunk_len=64, fp32 state in/out)",
+             "", "command (MI355X, repo root, TMPDIR=/tmp):", "  " + KT_CMD.format(d="gpurun_out/prof"),
+             f"kernel source sha256[:16]: {src_hash()}", "",
+             "kernel stats (durations in ns):",
+             f"  {'name':60s} {'calls':>6s} {'total_ns':>14s} {'avg_ns':>12s} {'pct':>7s}"]
+    for n, c, t, av, pc in stats:
+        lines.append(f"  {n[:60]:60s} {c:6d} {t:14.0f} {av:12.0f} {pc:7.2f}")
+    if chunk_avg:
+        av = chunk_avg[0][3]
+        lines += ["", f"chunk kernel average: {av / 1e6:.4f} ms -> algorithmic {abytes / (av * 1e-9) / 1e9:.1f} GB/s "
+                  f"({abytes:.0f} B per launch)"]
+    with open(os.path.join(PROFILES, f"chunk_kernel_{w.name}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    fetch_k, fetch_c, nf = counter_per_dispatch(a.dir, "fetch", "FETCH_SIZE")
+    write_k, write_c, nw = counter_per_dispatch(a.dir, "write", "WRITE_SIZE")
+    f_scale = COPY_BYTES / (fetch_c * 1024.0)
+    w_scale = COPY_BYTES / (write_c * 1024.0)
+    fetch_b = fetch_k * 1024.0 * f_scale
+    write_b = write_k * 1024.0 * w_scale
+    rec = {"workload": w.name, "kernel_src_sha256_16": src_hash(),
+           "bytes_per_launch": fetch_b + write_b, "fetch_bytes": fetch_b, "write_bytes": write_b,
+           "fetch_size_kib_raw": fetch_k, "write_size_kib_raw": write_k,
+           "copy_fetch_kib": fetch_c, "copy_write_kib": write_c,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "algorithmic_bytes_per_launch": abytes, "dispatches": [nf, nw]}
+    with open(os.path.join(PROFILES, f"chunk_kernel_{w.name}_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    tl = [f"rocprofv3 HBM traffic counters: chunked GDN kernel, workload {w.name}", "",
+          "commands (MI355X, repo root, TMPDIR=/tmp), one counter per run:",
+          "  " + PMC_CMD.format(c="FETCH_SIZE", d="gpurun_out/prof", n="fetch"),
+          "  " + PMC_CMD.format(c="WRITE_SIZE", d="gpurun_out/prof", n="write"),
+          f"kernel source sha256[:16]: {src_hash()}", "",
+          "scale: the run's plain 512 MiB device copy (--calib-copy) reads and writes 512 MiB;",
+          f"  FETCH_SIZE reads {fetch_c:.0f} KiB for it -> scale {f_scale:.3f}",
+          f"  WRITE_SIZE reads {write_c:.0f} KiB for it -> scale {w_scale:.3f}", "",
+          f"chunk kernel per launch (mean of {nf} / {nw} dispatches):",
+          f"  FETCH_SIZE {fetch_k:.0f} KiB raw -> {fetch_b / 1e9:.4f} GB",
+          f"  WRITE_SIZE {write_k:.0f} KiB raw -> {write_b / 1e9:.4f} GB",
+          f"  total {(fetch_b + write_b) / 1e9:.4f} GB vs algorithmic {abytes / 1e9:.4f} GB "
+          f"({(fetch_b + write_b) / abytes:.3f}x)"]
+    with open(os.path.join(PROFILES, f"chunk_kernel_{w.name}_traffic.txt"), "w") as f:
+        f.write("\n".join(tl) + "\n")
+    print("\n".join(lines + [""] + tl))
+
+
+if __name__ == "__main__":
+    main()
