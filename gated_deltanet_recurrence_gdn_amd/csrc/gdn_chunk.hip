@@ -57,11 +57,14 @@
 //   T_rc = -T_rr * sum_{k=c}^{r-1} A_rk T_kc,
 // on 16x16x16 bf16 MFMA, one block column per wave.
 //
-// Decay numerics: log2 a is accumulated in float64 (a = 0 is clamped to
-// log2 a = -1e4, which makes every factor across that token exactly 0), and
-// only 2^{g_i - g_j} for j <= i is ever formed, so nothing overflows however
-// strong the decay.  A final chunk shorter than C is padded with k = q = v = 0,
-// b = 0, a = 1, which leaves every product exact for the real tokens.
+// Decay numerics: log2 a is accumulated in float64 (log2 a is clamped at
+// -200, and 2^-200 is 0 in fp32, so a = 0 makes every factor across that token
+// exactly 0), and only 2^{g_i - g_j} for j <= i is ever formed, so nothing
+// overflows however strong the decay.  A final chunk of n < C tokens is padded
+// with rows that re-read token n-1 (finite values, no out-of-bounds access)
+// and get b = 0, a = 1: their corrected writes N are exactly 0 and the decay of
+// the real rows is unchanged, so every product is exact for the real tokens;
+// padded outputs are not stored.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
