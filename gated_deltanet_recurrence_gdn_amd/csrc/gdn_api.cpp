@@ -164,7 +164,7 @@ int resolve_chunk(gdn_ctx *h, int chunk_len, int *C) {
     if (!gdn::chunk_supported(chunk_len, h->cfg.d_k, h->cfg.d_v, h->cfg.io_dtype == GDN_BF16))
         return fail(h, GDN_ERR_UNSUPPORTED,
                     "chunk_len = %d is not supported for d_k = %d, d_v = %d, io_dtype = %d "
-                    "(use 1 for the sequential scan, 0 or 64 for the chunked form)",
+                    "(use 1 for the sequential scan, 16, 32, 64 or 128 (0 = 64) for the chunked form)",
                     chunk_len, h->cfg.d_k, h->cfg.d_v, h->cfg.io_dtype);
     *C = chunk_len;
     return GDN_OK;

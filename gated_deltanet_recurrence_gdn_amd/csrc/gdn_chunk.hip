@@ -627,13 +627,13 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-bool chunk_supported(int C_, int dk, int dv, int io_bf16) {
+bool chunk_mfma_supported(int C_, int dk, int dv, int io_bf16) {
     const bool dims = (dk == 32 || dk == 64 || dk == 128) && (dv == 32 || dv == 64 || dv == 128);
     return C_ == C && dims && io_bf16;
 }
 
-hipError_t launch_chunk(const PassArgs &a, int C_, hipStream_t stream) {
-    if (!chunk_supported(C_, a.dk, a.dv, a.io_bf16)) return hipErrorInvalidValue;
+hipError_t launch_chunk_mfma(const PassArgs &a, int C_, hipStream_t stream) {
+    if (!chunk_mfma_supported(C_, a.dk, a.dv, a.io_bf16)) return hipErrorInvalidValue;
     switch (a.dk) {
         case 32: return launch_dk<32>(a, stream);
         case 64: return launch_dk<64>(a, stream);

@@ -36,15 +36,28 @@ struct PassArgs {
 // Sequential per-token scan (the chunk_len = 1 form).
 hipError_t launch_scan(const PassArgs &a, hipStream_t stream);
 
-// Chunked (UT-transform) form with chunk length C.  Returns
-// hipErrorInvalidValue for a (C, dk, dv, dtype) it has no kernel for.
-hipError_t launch_chunk(const PassArgs &a, int C, hipStream_t stream);
+// Chunked (UT-transform) form, bf16 MFMA kernel: C = 64, bf16 I/O,
+// d_k, d_v in {32, 64, 128}.
+bool chunk_mfma_supported(int C, int dk, int dv, int io_bf16);
+hipError_t launch_chunk_mfma(const PassArgs &a, int C, hipStream_t stream);
+
+// Chunked form, general fp32 kernel: C, d_k, d_v in {16, 32, 64, 128}, fp32 or
+// bf16 I/O.
+bool chunk_general_supported(int C, int dk, int dv);
+hipError_t launch_chunk_general(const PassArgs &a, int C, hipStream_t stream);
 
 // out[e] = round(partial[e] + partial_rev[e]) over n elements (n % 4 == 0).
 hipError_t launch_combine(void *out, const float *partial, const float *partial_rev, long long n,
                           int io_bf16, hipStream_t stream);
 
-// Whether launch_chunk has a kernel for this shape.
-bool chunk_supported(int C, int dk, int dv, int io_bf16);
+// Chunked form with chunk length C: the MFMA kernel where it applies, else the
+// general one.  hipErrorInvalidValue for a (C, dk, dv, dtype) neither covers.
+inline bool chunk_supported(int C, int dk, int dv, int io_bf16) {
+    return chunk_mfma_supported(C, dk, dv, io_bf16) || chunk_general_supported(C, dk, dv);
+}
+inline hipError_t launch_chunk(const PassArgs &a, int C, hipStream_t stream) {
+    if (chunk_mfma_supported(C, a.dk, a.dv, a.io_bf16)) return launch_chunk_mfma(a, C, stream);
+    return launch_chunk_general(a, C, stream);
+}
 
 }  // namespace gdn

@@ -91,8 +91,12 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h);
  * and leaving the final state in state_out.
  *   state_in   NULL = zero initial state; never written unless it is state_out.
  *   state_out  NULL = final state discarded; may equal state_in (in-place carry).
- *   chunk_len  1 = sequential scan; 64 = chunked form with 64-token chunks;
- *              0 = default (64).  Others return GDN_ERR_UNSUPPORTED.
+ *   chunk_len  1 = sequential scan; 16, 32, 64 or 128 = chunked (UT-transform)
+ *              form with chunks of that many tokens; 0 = default (64).  Others
+ *              return GDN_ERR_UNSUPPORTED.  bf16 I/O with chunk_len 64 and
+ *              d_k, d_v >= 32 runs on bf16 MFMA with fp32 accumulation; every
+ *              other chunked request (fp32 I/O, other chunk lengths, d = 16)
+ *              runs a kernel that computes in fp32 throughout.
  *   hip_stream a hipStream_t (NULL = the null stream of the handle's device).
  * Streaming: calling with consecutive token ranges and state_out of one call
  * as state_in of the next reproduces a single call over the whole range.

@@ -59,6 +59,8 @@ def test_dry_run_valid_calls(dry):
     assert fwd(dry, s_in=None, s_out=None) == gb.GDN_OK
     assert fwd(dry, s_out=ADDR["s_in"]) == gb.GDN_OK  # in-place carry
     assert fwd(dry, T=1000) == gb.GDN_OK
+    for chunk in (0, 1, 16, 32, 64, 128):
+        assert fwd(dry, chunk=chunk) == gb.GDN_OK
     assert fwd(dry, T=0, q=None, k=None, v=None, beta=None, decay=None, out=None) == gb.GDN_OK
     assert gb.gdn_last_error(dry) == ""
 
@@ -71,6 +73,9 @@ def test_dry_run_valid_calls(dry):
     (dict(decay=None), gb.GDN_ERR_ARG),
     (dict(chunk=7), gb.GDN_ERR_UNSUPPORTED),
     (dict(chunk=-1), gb.GDN_ERR_UNSUPPORTED),
+    (dict(chunk=8), gb.GDN_ERR_UNSUPPORTED),
+    (dict(chunk=48), gb.GDN_ERR_UNSUPPORTED),
+    (dict(chunk=256), gb.GDN_ERR_UNSUPPORTED),
     (dict(q=ADDR["q"] + 8), gb.GDN_ERR_ALIGN),
     (dict(out=ADDR["out"] + 2), gb.GDN_ERR_ALIGN),
     (dict(beta=ADDR["beta"] + 2), gb.GDN_ERR_ALIGN),

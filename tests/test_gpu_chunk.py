@@ -139,13 +139,3 @@ def test_state_in_untouched_and_inplace():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s_in, st1)
     g.close()
-
-
-def test_fp32_io_chunked_is_rejected():
-    g = gb.GDN(1, 1, 64, 64, "fp32", max_T=10)
-    x = dev(inputs.make_inputs(1, 10, 1, 64, 64, "fp32"))
-    out = torch.empty((1, 10, 1, 64), device="cuda")
-    st = gb.gdn_forward(g.h, x["q"], x["k"], x["v"], x["beta"], x["decay"], None, None, out, 10, 64,
-                        gb.current_stream())
-    assert st == gb.GDN_ERR_UNSUPPORTED
-    g.close()
