@@ -16,46 +16,38 @@
 // C x C and C x d product runs on MFMA (bf16 operands, fp32 accumulation).
 //
 // Parallel decomposition.  Rows of S are independent, so a block owns one
-// (b, h) and a 32-wide tile of d_v and walks the head's chunks in order, with
-// its 32 x d_k slice of S in fp32 accumulator registers for the whole call.
-// The S-independent per-chunk work (decay factors, Gram products, the
-// triangular inverse) is recomputed by each d_v tile of a head: that costs MFMA
-// time but keeps HBM traffic at one read of q/k per head (the tiles of a head
-// are placed on one XCD so the repeats hit its L2) and buys the CU count the
-// sequential chunk chain needs.
+// (b, h) and a 32-wide tile of d_v and walks the head's chunks in order.  The
+// S-independent per-chunk work (decay factors, Gram products, the triangular
+// inverse) is recomputed by each d_v tile of a head: that costs MFMA time, not
+// HBM traffic, because the tiles of a head are placed on one XCD and share q/k
+// through its L2, and it buys the CU count the sequential chunk chain needs.
 //
-// Software pipeline.  Iteration c runs the state chain of chunk c and prepares
-// chunk c+1, in three barrier-separated phases:
-//   phase 1: X = [K;Q] S^T (8 MFMA per wave), R = diag(b)(V - diag(gam) K S^T);
-//            off-diagonal blocks of Tm for chunk c; decay factors of chunk c+1;
-//            global loads for chunk c+2 issued
-//   phase 2: N = Tm R;  Gram products K K^T, K Q^T of chunk c+1 -> A, P
-//   phase 3: O = diag(gam) Q S^T + P N (stored);  S update;  16x16 diagonal
-//            blocks of Tm for chunk c+1;  chunk c+2 staged into LDS
-// Each wave owns one 32-token row block of K or Q (wave 0: K rows 0-31, 1: K
-// rows 32-63, 2: Q rows 0-31, 3: Q rows 32-63), loaded from HBM straight into
-// registers in MFMA operand layout and prefetched two chunks ahead; the same
-// registers serve the Gram products of chunk c+1 and the state products of
-// chunk c+1.  K is also kept token-major in LDS (three chunk buffers) and read
-// transposed with ds_read_b64_tr_b16 where a product contracts over tokens.
-//
-// Operand layouts.  A 32x32 MFMA accumulator holds 4 consecutive rows per
-// lane, so products are oriented so that accumulator rows are the contraction
-// index of the consumer, or the output is contiguous in memory:
-//   K K^T, K Q^T as (keys x queries): A and P land row-major;
-//   K S^T (tokens x d_v): R lands as R^T [d_v][token];
-//   N = Tm R (tokens x d_v): N^T [d_v][token];
-//   O^T = S Q^T + N^T P^T (d_v x tokens): 4 consecutive d_v per lane -> 8-byte stores;
-//   S^T += K^T N~ (d_k x d_v): the state lands as S [d_v][d_k] for the next X.
-// For the 16x16x16 MFMA the accumulator layout equals the B-operand layout, so
-// the triangular-inverse chains pass blocks from one product to the next in
-// registers.
-//
-// Triangular inverse.  Tm's four 16x16 diagonal blocks are inverted in fp32
-// on the VALU (one row per lane, backward substitution on (I + A)^T); the
-// off-diagonal blocks follow block column by block column,
-//   T_rc = -T_rr * sum_{k=c}^{r-1} A_rk T_kc,
-// on 16x16x16 bf16 MFMA, one block column per wave.
+// Roles.  Eight waves; waves w and w + 4 share a SIMD.  One workgroup barrier
+// per chunk period.  In period c:
+//   wave 0     the state chain of chunk c.  S^T (d_k x 32) lives in fp32 MFMA
+//              accumulators for the whole call; X = K S^T, R, N = Tm R and the
+//              update S^T = gam_{C-1} S^T + K^T N~ hand their results from one
+//              product to the next in registers: a 32x32 accumulator becomes the
+//              next product's bf16 operand with one v_permlane32_swap per two
+//              rows (the 32x32x16 A and B operands share one lane layout), so
+//              the chain has no barrier and no LDS round trip of its own.  It
+//              publishes bf16 copies of S (for the next period's outputs) and of
+//              N (behind an LDS flag, for this period's outputs).
+//   wave 4     (light work beside the chain) V tile of chunk c+1 into LDS; gate
+//              vectors of chunk c+2 (float64 prefix sum of log2 a, 2^g,
+//              2^{g_last - g}, b).
+//   waves 3, 7 outputs of chunk c, one 32-token half each:
+//              O^T = gam .* (S Q^T) + N^T P^T, written as 8-byte row segments.
+//   waves 1, 2, 5, 6  chunk c+1 (preparation roles 0-3; a K-row wave shares its
+//              SIMD with a Q-row wave): their K or Q row block (HBM -> registers -> LDS),
+//              the Gram products K K^T and K Q^T, the A and P epilogues, and
+//              Tm -- 16x16 diagonal blocks by fp32 substitution, the other
+//              blocks by 16x16x16 MFMA -- with two LDS-counter syncs among
+//              themselves.
+// Global loads run two periods ahead (K/Q/V of chunk c+3, gates of c+4, in
+// alternating register sets), so their latency hides behind two periods; a
+// register set is refilled right after it has been stored to LDS, and no
+// product reads it, so no wait on an in-flight load lands inside a period.
 //
 // Decay numerics: log2 a is accumulated in float64 (log2 a is clamped at
 // -200, and 2^-200 is 0 in fp32, so a = 0 makes every factor across that token
@@ -75,12 +67,14 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;     // chunk length
-constexpr int NT = 512;   // threads per block: 4 chain waves + 4 preparation waves
+constexpr int NT = 512;   // threads per block: 8 waves
 constexpr int DVT = 32;   // d_v columns per block
 constexpr int LC = C + 8; // padded bf16 row pitch of C-long rows
 constexpr int LV = DVT + 8;
+constexpr int SPIN_LIMIT = 1 << 20;  // bound on any LDS-flag wait (never reached in a correct run)
 
 struct ChunkParams {
     const uint16_t *q, *k, *v;
@@ -98,22 +92,21 @@ struct ChunkParams {
 template <int DK>
 struct __align__(16) Smem {
     static constexpr int LK = DK + 8;  // padded bf16 row pitch of d_k-long rows
-    uint16_t Ks[3][C][LK];   // K, token-major, three chunk buffers
-    uint16_t Qs[2][C][LK];   // Q, token-major, two chunk buffers
-    uint16_t Vs[C][LV];      // V tile of the next chunk, token-major
-    uint16_t Sb[DVT][LK];    // bf16 copy of the state tile, [d_v][d_k]
-    uint16_t Rt[DVT][LC];    // R^T
-    uint16_t Nt[DVT][LC];    // N^T
-    uint16_t Nd[DVT][LC];    // (diag(G_{C-1,.}) N)^T
+    uint16_t Ks[2][C][LK];   // K, token-major (chunk parity)
+    uint16_t Qs[2][C][LK];   // Q, token-major
+    uint16_t Vs[2][C][LV];   // V tile, token-major
+    uint16_t Sb[2][DVT][LK]; // bf16 state tile at the start of a chunk, [d_v][d_k]
+    uint16_t Nt[DVT][LC];    // N^T of the current chunk
     uint16_t Pb[2][C][LC];   // P, row-major, zero above the diagonal
-    uint16_t Tb[C][LC];      // Tm, row-major, zero above the diagonal
+    uint16_t Tb[2][C][LC];   // Tm, row-major, zero above the diagonal
     uint16_t Ab[C][LC];      // A (its off-diagonal 16x16 blocks are read)
-    float Ad[4][16][20];     // A's diagonal 16x16 blocks, row-major, fp32
-    float g[2][C];           // cumulative log2 decay (summed in float64)
-    float gam[2][C];         // 2^{g_i}
-    float glast[2][C];       // 2^{g_{C-1} - g_i}
-    float bet[2][C];
-    float rawdec[C], rawbet[C];
+    float g[3][C];           // cumulative log2 decay (summed in float64), chunk mod 3
+    float bet[3][C];         // b (0 on padding)
+    float gam[3][C];         // 2^{g_i}
+    float glast[3][C];       // 2^{g_{C-1} - g_i}
+    int nflag;               // chunks whose N^T has been published
+    int pctr;                // arrivals at the preparation waves' syncs
+    int stuck;               // set once any wait ran out; later waits return at once
 };
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
@@ -168,24 +161,78 @@ __device__ __forceinline__ f32x4_t zero4() {
 }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A 32x32x16 accumulator holds row 8q + 4h + m of its column (lane % 32) in
+// register 4q + m of lane half h = lane / 32.  The A and B operands of the same
+// instruction hold, in lane half h, the 8 consecutive k-rows 8h .. 8h + 7 of
+// row/column lane % 32.  So the rows 16 KK .. 16 KK + 15 of an accumulator
+// become one k-step of an operand (rows as k, the accumulator's columns as the
+// operand's rows/columns) by exchanging 4 rows between the lane halves:
+// v_permlane32_swap swaps the upper half of its first operand with the lower
+// half of its second.
+template <int KK>
+__device__ __forceinline__ bf16x8_t acc_to_op(const f32x16_t &a) {
+    const uint32_t x0 = pack_bf16x2(a[8 * KK + 0], a[8 * KK + 1]);  // rows 16KK + 4h + 0..1
+    const uint32_t x1 = pack_bf16x2(a[8 * KK + 2], a[8 * KK + 3]);  // rows 16KK + 4h + 2..3
+    const uint32_t y0 = pack_bf16x2(a[8 * KK + 4], a[8 * KK + 5]);  // rows 16KK + 8 + 4h + 0..1
+    const uint32_t y1 = pack_bf16x2(a[8 * KK + 6], a[8 * KK + 7]);  // rows 16KK + 8 + 4h + 2..3
+    const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+    const uint4 w = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+    bf16x8_t r;
+    __builtin_memcpy(&r, &w, 16);
+    return r;
+}
+
 // Off-diagonal blocks of block column CB of Tm = (I + A)^{-1}, walking down:
 //   T_rc = -T_rr * sum_{k=c}^{r-1} A_rk T_kc   (16x16 blocks, bf16 16x16x16 MFMA).
 // The diagonal blocks are already in Tb; the column's blocks are passed from one
 // product to the next in registers (accumulator layout == B-operand layout).
+// All A and T_rr operands are read before any block is written.
 template <int CB>
 __device__ __forceinline__ void tm_column(uint16_t (*Tb)[LC], const uint16_t (*Ab)[LC], int l16, int g16) {
     s16x4_t tcol[4];
+    s16x4_t aop[4][4];  // aop[rb][kb] = A_rb,kb for CB <= kb < rb
+    s16x4_t top[4];     // top[rb] = T_rb,rb
     tcol[CB] = lds_tr(&Tb[16 * CB + 4 * g16 + (l16 >> 2)][16 * CB + 4 * (l16 & 3)]);
+#pragma unroll
+    for (int rb = CB + 1; rb < 4; ++rb) {
+        top[rb] = lds8(&Tb[16 * rb + l16][16 * rb + 4 * g16]);
+#pragma unroll
+        for (int kb = CB; kb < rb; ++kb) aop[rb][kb] = lds8(&Ab[16 * rb + l16][16 * kb + 4 * g16]);
+    }
+    f32x4_t tout[4];
 #pragma unroll
     for (int rb = CB + 1; rb < 4; ++rb) {
         f32x4_t y = zero4();
 #pragma unroll
-        for (int kb = CB; kb < rb; ++kb) y = mfma16(lds8(&Ab[16 * rb + l16][16 * kb + 4 * g16]), tcol[kb], y);
-        const f32x4_t t = mfma16(lds8(&Tb[16 * rb + l16][16 * rb + 4 * g16]), pack4s(y[0], y[1], y[2], y[3]), zero4());
+        for (int kb = CB; kb < rb; ++kb) y = mfma16(aop[rb][kb], tcol[kb], y);
+        const f32x4_t t = mfma16(top[rb], pack4s(y[0], y[1], y[2], y[3]), zero4());
         tcol[rb] = pack4s(-t[0], -t[1], -t[2], -t[3]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Tb[16 * rb + 4 * g16 + r][16 * CB + l16] = (uint16_t)f32_to_bf16_bits(-t[r]);
+        tout[rb] = t;
     }
+#pragma unroll
+    for (int rb = CB + 1; rb < 4; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Tb[16 * rb + 4 * g16 + r][16 * CB + l16] = (uint16_t)f32_to_bf16_bits(-tout[rb][r]);
+}
+
+// Bounded waits on LDS counters.  In a correct run every wait ends within a
+// chunk period; the bound (and the sticky `stuck` flag, which makes every later
+// wait return at once) only guarantees that the kernel always terminates.
+__device__ __forceinline__ void wait_at_least(int *ctr, int target, int *stuck) {
+    for (int i = 0; i < SPIN_LIMIT; ++i) {
+        if (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
+        if (__hip_atomic_load(stuck, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __hip_atomic_store(stuck, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void publish(int *ctr, int value, int lane) {
+    // release: this wave's earlier LDS writes are complete before the counter moves
+    if (lane == 0) __hip_atomic_store(ctr, value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void arrive(int *ctr, int lane) {
+    if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // Per-block constants: base pointers already offset to (b, token 0, h), token
@@ -199,6 +246,7 @@ struct Ctx {
     int rsv;  // v/out elements between consecutive tokens: H * d_v
     int H;    // gate elements between consecutive tokens
     int reverse;
+    __device__ bool has(int c) const { return c >= 0 && c < nchunks; }
     __device__ int ntok(int c) const {
         const long long r = T - (long long)c * C;
         return r < C ? (int)r : C;
@@ -207,6 +255,19 @@ struct Ctx {
         const long long s = (long long)c * C + j;
         return reverse ? T - 1 - s : s;
     }
+    // token j of chunk c, with rows past the end of a short final chunk clamped
+    // to its last token (loads stay in bounds and read finite data)
+    __device__ long long tok_clamped(int c, int j) const {
+        const int nt = ntok(c);
+        return tok(c, j < nt ? j : nt - 1);
+    }
+};
+
+// One wave's 32-row block of K or Q in MFMA operand layout: lane l holds row
+// l % 32, columns 16 s + 8 (l / 32) .. + 7 in r[s].
+template <int DK>
+struct RowBlock {
+    bf16x8_t r[DK / 16];
 };
 
 // Loads are unconditional: rows past the end of a final short chunk re-read
@@ -214,344 +275,440 @@ struct Ctx {
 // they enter is multiplied by 0 or never stored).  Conditional loads into
 // zeroed registers would make the compiler wait for all earlier loads.
 template <int DK>
-__device__ __forceinline__ void load_block(const Ctx &x, int c, int role, int lane, bf16x8_t *dst) {
-    if (c >= x.nchunks) return;  // uniform
-    const int nt = x.ntok(c);
+__device__ __forceinline__ RowBlock<DK> load_block(const Ctx &x, int c, int role, int lane) {
+    RowBlock<DK> d;
     const int r = 32 * (role & 1) + (lane & 31);
-    const uint16_t *src = ((role < 2) ? x.k : x.q) + (size_t)x.tok(c, r < nt ? r : nt - 1) * x.rs + 8 * (lane >> 5);
+    const uint16_t *src = ((role < 2) ? x.k : x.q) + (size_t)x.tok_clamped(c, r) * x.rs + 8 * (lane >> 5);
 #pragma unroll
-    for (int s = 0; s < DK / 16; ++s) {
-        const uint4 w = *reinterpret_cast<const uint4 *>(src + 16 * s);
-        __builtin_memcpy(&dst[s], &w, 16);
-    }
+    for (int s = 0; s < DK / 16; ++s) d.r[s] = *reinterpret_cast<const bf16x8_t *>(src + 16 * s);
+    return d;
 }
 
-// ---- state chain: waves 0-3 -------------------------------------------------
+// ---- wave 0: the state chain ------------------------------------------------
 template <int DK, bool BF16>
-__device__ __forceinline__ void chain_loop(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int wid,
-                                           int lane, void *out_b, float *part_b, size_t sbase) {
+struct Chain {
+    static constexpr int NKS = DK / 16;  // k-steps over d_k
+    static constexpr int NSB = DK / 32;  // 32-row blocks of S^T
+    f32x16_t sacc[NSB];                  // S^T: d_k rows 32*rb + .., d_v column lane % 32
+    bf16x8_t sop[NKS];                   // bf16 S^T as the B operand of X = K S^T
+
+    __device__ __forceinline__ void publish_state(Smem<DK> &sm, int slot, int lane) {
+        const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+        for (int rb = 0; rb < NSB; ++rb) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<uint2 *>(&sm.Sb[slot][l32][32 * rb + 8 * q + 4 * hi]) =
+                    pack4(sacc[rb][4 * q], sacc[rb][4 * q + 1], sacc[rb][4 * q + 2], sacc[rb][4 * q + 3]);
+            sop[2 * rb] = acc_to_op<0>(sacc[rb]);
+            sop[2 * rb + 1] = acc_to_op<1>(sacc[rb]);
+        }
+    }
+
+    __device__ __forceinline__ void init(const ChunkParams &p, Smem<DK> &sm, size_t sbase, int lane) {
+        const int hi = lane >> 5;
+#pragma unroll
+        for (int rb = 0; rb < NSB; ++rb) {
+            sacc[rb] = zero16();
+            if (p.state_in) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 s4 = *reinterpret_cast<const float4 *>(p.state_in + sbase + 32 * rb + 8 * q + 4 * hi);
+                    sacc[rb][4 * q + 0] = s4.x; sacc[rb][4 * q + 1] = s4.y;
+                    sacc[rb][4 * q + 2] = s4.z; sacc[rb][4 * q + 3] = s4.w;
+                }
+            }
+        }
+        publish_state(sm, 0, lane);
+    }
+
+    __device__ __forceinline__ void step(Smem<DK> &sm, int c, int lane) {
+        const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g16 = lane >> 4;
+        const int s2 = c & 1, s3 = c % 3;
+        // X = K S^T  (tokens x d_v), two 32-token blocks
+        f32x16_t xacc[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            xacc[0] = mfma32(lds16(&sm.Ks[s2][l32][16 * s + 8 * hi]), sop[s], xacc[0]);
+            xacc[1] = mfma32(lds16(&sm.Ks[s2][32 + l32][16 * s + 8 * hi]), sop[s], xacc[1]);
+        }
+        // R = diag(b) (V - diag(gam) X), then as the B operand of N = Tm R
+        bf16x8_t rop[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i0 = 32 * i + 8 * q + 4 * hi;
+                const s16x4_t vv = lds_tr(&sm.Vs[s2][i0 + (l16 >> 2)][16 * (g16 & 1) + 4 * (l16 & 3)]);
+                uint2 vu;
+                __builtin_memcpy(&vu, &vv, 8);
+                const float4 bt = *reinterpret_cast<const float4 *>(&sm.bet[s3][i0]);
+                const float4 gm = *reinterpret_cast<const float4 *>(&sm.gam[s3][i0]);
+                xacc[i][4 * q + 0] = bt.x * (bf16_lo(vu.x) - gm.x * xacc[i][4 * q + 0]);
+                xacc[i][4 * q + 1] = bt.y * (bf16_hi(vu.x) - gm.y * xacc[i][4 * q + 1]);
+                xacc[i][4 * q + 2] = bt.z * (bf16_lo(vu.y) - gm.z * xacc[i][4 * q + 2]);
+                xacc[i][4 * q + 3] = bt.w * (bf16_hi(vu.y) - gm.w * xacc[i][4 * q + 3]);
+            }
+            rop[2 * i] = acc_to_op<0>(xacc[i]);
+            rop[2 * i + 1] = acc_to_op<1>(xacc[i]);
+        }
+        // N = Tm R; Tm is lower triangular: token block i needs keys < 32 (i + 1)
+        f32x16_t nacc[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (t < 2) nacc[0] = mfma32(lds16(&sm.Tb[s2][l32][16 * t + 8 * hi]), rop[t], nacc[0]);
+            nacc[1] = mfma32(lds16(&sm.Tb[s2][32 + l32][16 * t + 8 * hi]), rop[t], nacc[1]);
+        }
+        // publish N^T for the output waves
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<uint2 *>(&sm.Nt[l32][32 * i + 8 * q + 4 * hi]) =
+                    pack4(nacc[i][4 * q], nacc[i][4 * q + 1], nacc[i][4 * q + 2], nacc[i][4 * q + 3]);
+        publish(&sm.nflag, c + 1, lane);
+        // N~ = diag(G_{C-1,.}) N as the B operand of the update
+        bf16x8_t nop[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 gl = *reinterpret_cast<const float4 *>(&sm.glast[s3][32 * i + 8 * q + 4 * hi]);
+                nacc[i][4 * q + 0] *= gl.x; nacc[i][4 * q + 1] *= gl.y;
+                nacc[i][4 * q + 2] *= gl.z; nacc[i][4 * q + 3] *= gl.w;
+            }
+            nop[2 * i] = acc_to_op<0>(nacc[i]);
+            nop[2 * i + 1] = acc_to_op<1>(nacc[i]);
+        }
+        // S^T <- gam_{C-1} S^T + K^T N~  (K^T read transposed from the token-major K)
+        const float gl = sm.gam[s3][C - 1];
+#pragma unroll
+        for (int rb = 0; rb < NSB; ++rb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[rb][r] *= gl;
+            const int dcol = 32 * rb + 16 * (g16 & 1) + 4 * (l16 & 3);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int t0 = 16 * t + 8 * hi + (l16 >> 2);
+                const bf16x8_t a = join(lds_tr(&sm.Ks[s2][t0][dcol]), lds_tr(&sm.Ks[s2][t0 + 4][dcol]));
+                sacc[rb] = mfma32(a, nop[t], sacc[rb]);
+            }
+        }
+        publish_state(sm, (c + 1) & 1, lane);
+    }
+
+    __device__ __forceinline__ void finish(const ChunkParams &p, size_t sbase, int lane) {
+        const int hi = lane >> 5;
+        if (!p.state_out) return;
+#pragma unroll
+        for (int rb = 0; rb < NSB; ++rb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<float4 *>(p.state_out + sbase + 32 * rb + 8 * q + 4 * hi) =
+                    make_float4(sacc[rb][4 * q], sacc[rb][4 * q + 1], sacc[rb][4 * q + 2], sacc[rb][4 * q + 3]);
+    }
+};
+
+// ---- waves 3 and 7: outputs of one 32-token half --------------------------------
+template <int DK, bool BF16>
+__device__ __forceinline__ void output_step(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int c, int tb,
+                                            int lane, void *out_b, float *part_b) {
     constexpr int NKS = DK / 16;
-    constexpr int NSB = DK / 32;
-    const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g16 = lane >> 4;
-
-    f32x16_t sacc = zero16();  // S^T block: d_k rows 32*wid.., d_v cols l32 (waves < NSB)
-    if (wid < NSB) {
-        if (p.state_in) {
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int s2 = c & 1, s3 = c % 3;
+    // (S Q^T) for the half's query columns, scaled by gam of the column
+    f32x16_t acc = zero16();
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const float4 s4 = *reinterpret_cast<const float4 *>(p.state_in + sbase + 32 * wid + 8 * rb + 4 * hi);
-                sacc[4 * rb + 0] = s4.x; sacc[4 * rb + 1] = s4.y; sacc[4 * rb + 2] = s4.z; sacc[4 * rb + 3] = s4.w;
-            }
-        }
+    for (int s = 0; s < NKS; ++s)
+        acc = mfma32(lds16(&sm.Sb[s2][l32][16 * s + 8 * hi]), lds16(&sm.Qs[s2][32 * tb + l32][16 * s + 8 * hi]), acc);
+    const float gq = sm.gam[s3][32 * tb + l32];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-            *reinterpret_cast<uint2 *>(&sm.Sb[l32][32 * wid + 8 * rb + 4 * hi]) =
-                pack4(sacc[4 * rb], sacc[4 * rb + 1], sacc[4 * rb + 2], sacc[4 * rb + 3]);
+    for (int r = 0; r < 16; ++r) acc[r] *= gq;
+    // + N^T P^T, keys < 32 (tb + 1), once the chain has published N^T
+    wait_at_least(&sm.nflag, c + 1, &sm.stuck);
+#pragma unroll
+    for (int k = 0; k < 64; k += 16) {
+        if (k >= 32 * (tb + 1)) break;
+        acc = mfma32(lds16(&sm.Nt[l32][k + 8 * hi]), lds16(&sm.Pb[s2][32 * tb + l32][k + 8 * hi]), acc);
     }
-    __syncthreads();
-
-    for (int c = -1; c < x.nchunks; ++c) {
-        const bool chain = c >= 0;
-        const int cb = (c + 3) & 1;  // gate/P buffer of chunk c
-        // ===== phase 1: X = [K;Q] S^T, R ===================================
-        // this wave's row block of chunk c (K rows for waves 0-1, Q rows for 2-3)
-        const uint16_t *blk = (wid < 2) ? &sm.Ks[c < 0 ? 0 : c % 3][32 * (wid & 1) + l32][8 * hi]
-                                        : &sm.Qs[c & 1][32 * (wid & 1) + l32][8 * hi];
-        f32x16_t xacc = zero16();
-        if (chain) {
-            if (wid < 2) {
-                // K S^T (tokens x d_v), then R = diag(b)(V - diag(gam) K S^T) -> R^T
+    const int i = 32 * tb + l32;
+    if (i < x.ntok(c)) {
+        const size_t e0 = (size_t)x.tok(c, i) * x.rsv;
 #pragma unroll
-                for (int s = 0; s < NKS; ++s) xacc = mfma32(lds16(blk + 16 * s), lds16(&sm.Sb[l32][16 * s + 8 * hi]), xacc);
-#pragma unroll
-                for (int rb = 0; rb < 4; ++rb) {
-                    const int i0 = 32 * wid + 8 * rb + 4 * hi;
-                    const s16x4_t vv = lds_tr(&sm.Vs[i0 + (l16 >> 2)][16 * (g16 & 1) + 4 * (l16 & 3)]);
-                    uint2 vu;
-                    __builtin_memcpy(&vu, &vv, 8);
-                    const float4 bt = *reinterpret_cast<const float4 *>(&sm.bet[cb][i0]);
-                    const float4 gm = *reinterpret_cast<const float4 *>(&sm.gam[cb][i0]);
-                    const float r0 = bt.x * (bf16_lo(vu.x) - gm.x * xacc[4 * rb + 0]);
-                    const float r1 = bt.y * (bf16_hi(vu.x) - gm.y * xacc[4 * rb + 1]);
-                    const float r2 = bt.z * (bf16_lo(vu.y) - gm.z * xacc[4 * rb + 2]);
-                    const float r3 = bt.w * (bf16_hi(vu.y) - gm.w * xacc[4 * rb + 3]);
-                    *reinterpret_cast<uint2 *>(&sm.Rt[l32][i0]) = pack4(r0, r1, r2, r3);
-                }
+        for (int q = 0; q < 4; ++q) {
+            const size_t e = e0 + 8 * q + 4 * hi;
+            const float o0 = acc[4 * q] * p.scale, o1 = acc[4 * q + 1] * p.scale;
+            const float o2 = acc[4 * q + 2] * p.scale, o3 = acc[4 * q + 3] * p.scale;
+            if (p.out_mode == OUT_PARTIAL) {
+                *reinterpret_cast<float4 *>(part_b + e) = make_float4(o0, o1, o2, o3);
             } else {
-                // (Q S^T)^T (d_v x tokens), scaled by gam of the token column
-#pragma unroll
-                for (int s = 0; s < NKS; ++s) xacc = mfma32(lds16(&sm.Sb[l32][16 * s + 8 * hi]), lds16(blk + 16 * s), xacc);
-                const float gq = sm.gam[cb][32 * (wid - 2) + l32];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) xacc[r] *= gq;
+                if constexpr (BF16)
+                    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out_b) + e) = pack4(o0, o1, o2, o3);
+                else
+                    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out_b) + e) = make_float4(o0, o1, o2, o3);
             }
         }
-        __syncthreads();
-        // ===== phase 2: N = Tm R ==============================================
-        if (chain && wid < 2) {
-            f32x16_t nacc = zero16();  // token block wid; Tm lower triangular: keys < 32*(wid+1)
-#pragma unroll
-            for (int k = 0; k < 64; k += 16) {
-                if (k >= 32 * (wid + 1)) break;
-                nacc = mfma32(lds16(&sm.Tb[32 * wid + l32][k + 8 * hi]), lds16(&sm.Rt[l32][k + 8 * hi]), nacc);
-            }
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const int i0 = 32 * wid + 8 * rb + 4 * hi;
-                const float4 gl = *reinterpret_cast<const float4 *>(&sm.glast[cb][i0]);
-                *reinterpret_cast<uint2 *>(&sm.Nt[l32][i0]) =
-                    pack4(nacc[4 * rb], nacc[4 * rb + 1], nacc[4 * rb + 2], nacc[4 * rb + 3]);
-                *reinterpret_cast<uint2 *>(&sm.Nd[l32][i0]) =
-                    pack4(gl.x * nacc[4 * rb], gl.y * nacc[4 * rb + 1], gl.z * nacc[4 * rb + 2], gl.w * nacc[4 * rb + 3]);
-            }
-        }
-        __syncthreads();
-        // ===== phase 3: outputs, state update =================================
-        if (chain) {
-            if (wid >= 2) {
-                // O^T = gam (Q S^T)^T + N^T P^T for query block tb, keys < 32*(tb+1)
-                const int tb = wid - 2;
-#pragma unroll
-                for (int k = 0; k < 64; k += 16) {
-                    if (k >= 32 * (tb + 1)) break;
-                    xacc = mfma32(lds16(&sm.Nt[l32][k + 8 * hi]), lds16(&sm.Pb[cb][32 * tb + l32][k + 8 * hi]), xacc);
-                }
-                const int i = 32 * tb + l32;
-                if (i < x.ntok(c)) {
-                    const size_t e0 = (size_t)x.tok(c, i) * x.rsv;
-#pragma unroll
-                    for (int rb = 0; rb < 4; ++rb) {
-                        const size_t e = e0 + 8 * rb + 4 * hi;
-                        float o0 = xacc[4 * rb] * p.scale, o1 = xacc[4 * rb + 1] * p.scale;
-                        float o2 = xacc[4 * rb + 2] * p.scale, o3 = xacc[4 * rb + 3] * p.scale;
-                        if (p.out_mode == OUT_PARTIAL) {
-                            *reinterpret_cast<float4 *>(part_b + e) = make_float4(o0, o1, o2, o3);
-                        } else {
-                            if constexpr (BF16)
-                                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out_b) + e) = pack4(o0, o1, o2, o3);
-                            else
-                                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out_b) + e) = make_float4(o0, o1, o2, o3);
-                        }
-                    }
-                }
-            }
-            if (wid < NSB) {
-                // S^T <- gam_{C-1} S^T + K^T N~  (K^T read transposed from the token-major K)
-                const float gl = sm.gam[cb][C - 1];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[r] *= gl;
-                const int kb3 = c % 3;
-                const int dcol = 32 * wid + 16 * (g16 & 1) + 4 * (l16 & 3);
-#pragma unroll
-                for (int t = 0; t < 64; t += 16) {
-                    const int t0 = t + 8 * hi + (l16 >> 2);
-                    const bf16x8_t a = join(lds_tr(&sm.Ks[kb3][t0][dcol]), lds_tr(&sm.Ks[kb3][t0 + 4][dcol]));
-                    sacc = mfma32(a, lds16(&sm.Nd[l32][t + 8 * hi]), sacc);
-                }
-#pragma unroll
-                for (int rb = 0; rb < 4; ++rb)
-                    *reinterpret_cast<uint2 *>(&sm.Sb[l32][32 * wid + 8 * rb + 4 * hi]) =
-                        pack4(sacc[4 * rb], sacc[4 * rb + 1], sacc[4 * rb + 2], sacc[4 * rb + 3]);
-            }
-        }
-        __syncthreads();
-    }
-
-    if (p.state_out && wid < NSB) {
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-            *reinterpret_cast<float4 *>(p.state_out + sbase + 32 * wid + 8 * rb + 4 * hi) =
-                make_float4(sacc[4 * rb], sacc[4 * rb + 1], sacc[4 * rb + 2], sacc[4 * rb + 3]);
     }
 }
 
-// ---- preparation: waves 4-7 (role = wid - 4) ---------------------------------
-template <int DK>
-__device__ __forceinline__ void prep_loop(const Ctx &x, Smem<DK> &sm, int role, int lane) {
-    constexpr int NKS = DK / 16;
-    const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g16 = lane >> 4;
-    const int ptid = 64 * role + lane;
-    const int v_tok = ptid >> 2, v_part = ptid & 3;  // V tile: 64 tokens x 4 16-byte vectors
+// ---- wave 4: V tiles and gate vectors ----------------------------------------
+struct GateRegs {
+    float b, a;
+};
 
-    auto store_block = [&](int c, const bf16x8_t *src) {
-        uint16_t *row = (role < 2) ? &sm.Ks[c % 3][32 * (role & 1) + l32][8 * hi] : &sm.Qs[c & 1][32 * (role & 1) + l32][8 * hi];
+struct VRow {
+    u32x4_t w[4];  // one token's 32 d_v values of the tile
+};
+__device__ __forceinline__ VRow load_v(const Ctx &x, int c, int lane) {
+    VRow d;
+    const uint16_t *src = x.v + (size_t)x.tok_clamped(c, lane) * x.rsv;
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) __builtin_memcpy(row + 16 * s, &src[s], 16);
-    };
-    auto load_v = [&](int c, uint4 &w) {
-        if (c >= x.nchunks) return;  // uniform
-        const int nt = x.ntok(c);
-        w = *reinterpret_cast<const uint4 *>(x.v + (size_t)x.tok(c, v_tok < nt ? v_tok : nt - 1) * x.rsv + 8 * v_part);
-    };
-    // gates of chunk c (role 0, lane = token); padding gets b = 0, a = 1 when stored
-    auto load_gates = [&](int c, float &bb, float &aa, bool &ok) {
-        ok = false;
-        if (c >= x.nchunks) return;  // uniform
-        const int nt = x.ntok(c);
-        ok = lane < nt;
-        const size_t g = (size_t)x.tok(c, ok ? lane : nt - 1) * x.H;
-        bb = x.beta[g];
-        aa = x.decay[g];
-    };
+    for (int u = 0; u < 4; ++u) d.w[u] = *reinterpret_cast<const u32x4_t *>(src + 8 * u);
+    return d;
+}
+__device__ __forceinline__ void load_gates(const Ctx &x, int c, int lane, GateRegs &g) {
+    if (!x.has(c)) return;  // uniform
+    const size_t o = (size_t)x.tok_clamped(c, lane) * x.H;
+    g.b = x.beta[o];
+    g.a = x.decay[o];
+}
 
-    bf16x8_t rcur[NKS], rnext[NKS];  // this wave's row block of chunk c+1, and of chunk c+2
-    uint4 vpf = make_uint4(0, 0, 0, 0);
-    float bpf = 0.f, apf = 1.f;
-    bool gpf = false;
-    if (x.nchunks > 0) {
-        load_block<DK>(x, 0, role, lane, rcur);
-        if (role == 0) load_gates(0, bpf, apf, gpf);
-        store_block(0, rcur);
-        if (role == 0) {
-            sm.rawbet[lane] = gpf ? bpf : 0.f;
-            sm.rawdec[lane] = gpf ? apf : 1.f;
+template <int DK>
+__device__ __forceinline__ void gates_compute(const Ctx &x, Smem<DK> &sm, int c, int lane, const GateRegs &gr) {
+    const bool real = lane < x.ntok(c);
+    const float a = real ? gr.a : 1.f;
+    float l2 = __builtin_amdgcn_logf(a);  // log2
+    if (!(l2 > -200.0f)) l2 = -200.0f;    // a = 0: 2^-200 is 0 in fp32
+    double xs = (double)l2;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(xs, off, 64);
+        if (lane >= off) xs += y;
+    }
+    const double xl = __shfl(xs, 63, 64);
+    const int s3 = c % 3;
+    sm.g[s3][lane] = (float)xs;
+    sm.gam[s3][lane] = exp2_fast((float)xs);
+    sm.glast[s3][lane] = exp2_fast((float)(xl - xs));
+    sm.bet[s3][lane] = real ? gr.b : 0.f;
+}
+
+// ---- waves 1, 2, 5, 6: preparation of the next chunk --------------------------
+// role 0: K rows 0-31 (K_a), 1: K rows 32-63 (K_b), 2: Q rows 0-31, 3: Q rows 32-63.
+// Gram products as (keys x queries):
+//   role 0: A(0,0) = K_a K_a^T      role 1: A(1,1) = K_b K_b^T
+//   role 2: A(1,0) = K_a K_b^T, P(0,0) = K_a Q_a^T
+//   role 3: P(1,0) = K_a Q_b^T, P(1,1) = K_b Q_b^T
+// Epilogue of a Gram block (keys x queries): element (key j, query i) times
+// 2^{g_i - g_j}; for A also times b_i and kept for j < i, for P kept for j <= i.
+// Every LDS read is issued before any LDS write, so the reads' latencies overlap
+// (the compiler keeps LDS accesses that may alias in program order).
+template <int DK>
+__device__ __forceinline__ void gram_epilogue(Smem<DK> &sm, int cp, const f32x16_t &acc, int jb, int ib, bool is_k,
+                                              int lane) {
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int s3 = cp % 3, s2 = cp & 1;
+    const float *gg = sm.g[s3];
+    const int i = 32 * ib + l32;
+    const float gi = gg[i];
+    const float bi = sm.bet[s3][i];
+    float4 gj[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) gj[q] = *reinterpret_cast<const float4 *>(&gg[32 * jb + 8 * q + 4 * hi]);
+    uint2 w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int j0 = 32 * jb + 8 * q + 4 * hi;
+        const float gjv[4] = {gj[q].x, gj[q].y, gj[q].z, gj[q].w};
+        float v4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = j0 + e;
+            const float val = acc[4 * q + e] * exp2_fast(gi - gjv[e]);
+            if (ib > jb)  // off-diagonal block: every j < i
+                v4[e] = is_k ? bi * val : val;
+            else
+                v4[e] = is_k ? ((j < i) ? bi * val : 0.f) : ((j <= i) ? val : 0.f);
+        }
+        w[q] = pack4(v4[0], v4[1], v4[2], v4[3]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int j0 = 32 * jb + 8 * q + 4 * hi;
+        if (!is_k)
+            *reinterpret_cast<uint2 *>(&sm.Pb[s2][i][j0]) = w[q];
+        else  // an off-diagonal 32x32 block of A: every 16x16 block in it is off-diagonal
+            *reinterpret_cast<uint2 *>(&sm.Ab[i][j0]) = w[q];
+    }
+}
+
+// y += a_J * b, where a_J is lane J's value of a within each 16-lane row: one
+// v_fmac_f32 with a DPP row_newbcast source (register arithmetic only; no
+// memory access).  The s_nop covers the wait states a DPP source read needs
+// after a VALU write of that register.
+template <int J>
+__device__ __forceinline__ void fmac_row_bcast(float &y, float a, float b) {
+    asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                 : "+v"(y)
+                 : "v"(a), "v"(b), "n"(J));
+}
+
+// A diagonal 32x32 block kk of A, from its Gram accumulator acc = K_kk K_kk^T
+// (keys x queries), and the two diagonal 16x16 blocks of Tm inside it.
+//   * epilogue: A_ij = b_i (k_i . k_j) 2^{g_i - g_j} for j < i, else 0;
+//     the off-diagonal 16x16 block (rows 16-31, cols 0-15) goes to Ab for the
+//     block-column products;
+//   * the lane halves exchange 8 keys (v_permlane32_swap) so that lane i of
+//     half 0 holds A[i][0..15] and lane i of half 1 holds A[i][16..31]: lanes
+//     0-15 then own the rows of diagonal block 0, lanes 48-63 those of block 1,
+//     each 16-lane row one block;
+//   * row r of (I + A_bb)^{-1} solves (I + A_bb)^T y = e_r by backward
+//     substitution, right-looking (once y_j is known, y_m -= A[j][m] y_j for
+//     m < j), with row j of A taken from lane j of the 16-lane row by a DPP
+//     broadcast folded into the FMA: no LDS traffic and no waits on it.
+template <int DK>
+__device__ __forceinline__ void a_diag_block(Smem<DK> &sm, int cp, const f32x16_t &acc, int kk, int lane) {
+    const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15;
+    const int s3 = cp % 3, s2 = cp & 1;
+    const float *gg = sm.g[s3];
+    const int i = 32 * kk + l32;
+    const float gi = gg[i];
+    const float bi = sm.bet[s3][i];
+    float4 gj[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) gj[q] = *reinterpret_cast<const float4 *>(&gg[32 * kk + 8 * q + 4 * hi]);
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int j0 = 32 * kk + 8 * q + 4 * hi;
+        const float gjv[4] = {gj[q].x, gj[q].y, gj[q].z, gj[q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float val = acc[4 * q + e] * exp2_fast(gi - gjv[e]);
+            v[4 * q + e] = (j0 + e < i) ? bi * val : 0.f;
         }
     }
-    __syncthreads();
+    if (l32 >= 16) {  // rows 16-31, keys 0-15: the off-diagonal 16x16 block
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            *reinterpret_cast<uint2 *>(&sm.Ab[i][32 * kk + 8 * q + 4 * hi]) =
+                pack4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    }
+    // half 0: keys 0-3 (q0), 8-11 (q1), 16-19 (q2), 24-27 (q3); half 1: +4.
+    // Swap q2 of half 0 with q0 of half 1, q3 of half 0 with q1 of half 1.
+    float a[16];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[e]), __float_as_uint(v[8 + e]), false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[4 + e]), __float_as_uint(v[12 + e]), false, false);
+        a[e] = __uint_as_float(s02[0]);       // keys 0-3 (half 0) / 16-19 (half 1)
+        a[4 + e] = __uint_as_float(s02[1]);   // keys 4-7 / 20-23
+        a[8 + e] = __uint_as_float(s13[0]);   // keys 8-11 / 24-27
+        a[12 + e] = __uint_as_float(s13[1]);  // keys 12-15 / 28-31
+    }
+    float y[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) y[m] = (m == l16) ? 1.f : 0.f;
+#define GDN_SUBST_STEP(J)                                                         \
+    {                                                                             \
+        const float nyj = -y[J];                                                  \
+        _Pragma("unroll") for (int m = 0; m < J; ++m) fmac_row_bcast<J>(y[m], a[m], nyj); \
+    }
+    GDN_SUBST_STEP(15) GDN_SUBST_STEP(14) GDN_SUBST_STEP(13) GDN_SUBST_STEP(12)
+    GDN_SUBST_STEP(11) GDN_SUBST_STEP(10) GDN_SUBST_STEP(9) GDN_SUBST_STEP(8)
+    GDN_SUBST_STEP(7) GDN_SUBST_STEP(6) GDN_SUBST_STEP(5) GDN_SUBST_STEP(4)
+    GDN_SUBST_STEP(3) GDN_SUBST_STEP(2) GDN_SUBST_STEP(1)
+#undef GDN_SUBST_STEP
+    const bool blk0 = lane < 16, blk1 = lane >= 48;
+    if (blk0 || blk1) {
+        const int kb = 2 * kk + (blk1 ? 1 : 0);
+        uint16_t *row = &sm.Tb[s2][16 * kb + l16][16 * kb];
+        *reinterpret_cast<uint4 *>(row) = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                                                     pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+        *reinterpret_cast<uint4 *>(row + 8) = make_uint4(pack_bf16x2(y[8], y[9]), pack_bf16x2(y[10], y[11]),
+                                                         pack_bf16x2(y[12], y[13]), pack_bf16x2(y[14], y[15]));
+        if (blk0) {  // zero block right of the diagonal inside the 32-row block
+            *reinterpret_cast<uint4 *>(row + 16) = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(row + 24) = make_uint4(0, 0, 0, 0);
+        }
+    }
+}
 
-    for (int c = -1; c < x.nchunks; ++c) {
-        const bool prep = c + 1 < x.nchunks;
-        const int nb = c & 1;  // gate/P buffer of chunk c+1 (== (c + 4) & 1)
-        f32x16_t g0 = zero16(), g1 = zero16();
-        // ===== phase 1: later chunks' loads; Tm of chunk c; Gram products of c+1
-        load_block<DK>(x, c + 2, role, lane, rnext);
-        load_v(c + 1, vpf);
-        if (role == 0) load_gates(c + 2, bpf, apf, gpf);
-        if (c >= 0) {  // off-diagonal 16x16 blocks of Tm for chunk c: block column `role`
-            if (role == 0) tm_column<0>(sm.Tb, sm.Ab, l16, g16);
-            else if (role == 1) tm_column<1>(sm.Tb, sm.Ab, l16, g16);
-            else if (role == 2) tm_column<2>(sm.Tb, sm.Ab, l16, g16);
-        }
-        if (prep) {
-            if (role == 3) {
-                // decay factors of chunk c+1: g = cumulative log2 a (summed in float64)
-                const float a = sm.rawdec[lane];
-                float l2 = __builtin_amdgcn_logf(a);  // log2
-                if (!(l2 > -200.0f)) l2 = -200.0f;    // a = 0: 2^-200 is 0 in fp32
-                double xs = (double)l2;
+template <int DK>
+__device__ __forceinline__ void prep_step(const Ctx &x, Smem<DK> &sm, int it, int role, int lane, int &psyncs,
+                                          RowBlock<DK> &blk) {
+    constexpr int NKS = DK / 16;
+    const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g16 = lane >> 4;
+    const int cp = it + 1;  // the chunk prepared in this period
+    const bool valid = x.has(cp);
+    const int s2 = cp & 1;
+    // 1. this wave's row block of chunk cp -> LDS; the registers then take the
+    //    loads of chunk it + 3 at once (two periods to land), and every product
+    //    below reads its operands from LDS, so nothing here waits on them
+    if (valid) {
+        uint16_t *row = (role < 2) ? &sm.Ks[s2][32 * (role & 1) + l32][8 * hi] : &sm.Qs[s2][32 * (role & 1) + l32][8 * hi];
 #pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const double y = __shfl_up(xs, off, 64);
-                    if (lane >= off) xs += y;
-                }
-                const double xl = __shfl(xs, 63, 64);
-                sm.g[nb][lane] = (float)xs;
-                sm.gam[nb][lane] = exp2_fast((float)xs);
-                sm.glast[nb][lane] = exp2_fast((float)(xl - xs));
-                sm.bet[nb][lane] = sm.rawbet[lane];
+        for (int s = 0; s < NKS; ++s) *reinterpret_cast<bf16x8_t *>(row + 16 * s) = blk.r[s];
+    }
+    if (x.has(it + 3)) blk = load_block<DK>(x, it + 3, role, lane);
+    psyncs += 4;
+    arrive(&sm.pctr, lane);
+    const uint16_t *ka = &sm.Ks[s2][l32][8 * hi];       // K rows 0-31
+    const uint16_t *kb = &sm.Ks[s2][32 + l32][8 * hi];  // K rows 32-63
+    if (role < 2) {
+        // 2a. K_kk K_kk^T (this wave's own rows, just stored) -> A's diagonal 32x32
+        //     block and the diagonal 16x16 blocks of Tm; needs no other wave's data
+        if (valid) {
+            const uint16_t *kk = role == 0 ? ka : kb;
+            f32x16_t g0 = zero16();
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) {
+                const bf16x8_t r = lds16(kk + 16 * s);
+                g0 = mfma32(r, r, g0);
             }
-            // Gram products of chunk c+1, computed as (keys x queries):
-            //   role 0: K_a K_a^T          role 1: K_b K_b^T
-            //   role 2: K_a Q_a^T, K_a K_b^T   role 3: K_a Q_b^T, K_b Q_b^T
-            const int kb3 = (c + 1) % 3;
-            if (role < 2) {
-#pragma unroll
-                for (int s = 0; s < NKS; ++s) g0 = mfma32(rcur[s], rcur[s], g0);
-            } else if (role == 2) {
-#pragma unroll
-                for (int s = 0; s < NKS; ++s) {
-                    const int ko = 16 * s + 8 * hi;
-                    const bf16x8_t ka = lds16(&sm.Ks[kb3][l32][ko]);
-                    g0 = mfma32(ka, rcur[s], g0);
-                    g1 = mfma32(ka, lds16(&sm.Ks[kb3][32 + l32][ko]), g1);
-                }
-            } else {
-#pragma unroll
-                for (int s = 0; s < NKS; ++s) {
-                    const int ko = 16 * s + 8 * hi;
-                    g0 = mfma32(lds16(&sm.Ks[kb3][l32][ko]), rcur[s], g0);
-                    g1 = mfma32(lds16(&sm.Ks[kb3][32 + l32][ko]), rcur[s], g1);
-                }
-            }
+            a_diag_block(sm, cp, g0, role, lane);
         }
-        __syncthreads();
-        // ===== phase 2: Gram epilogues of chunk c+1 -> A, P ===================
-        if (prep) {
-            // element (key j, query i); factor 2^{g_i - g_j} for j <= i
-            const float *gg = sm.g[nb];
-            auto epi = [&](const f32x16_t &acc, int jb, int ib, bool is_k) {
-                const int i = 32 * ib + l32;
-                const float gi = gg[i];
-                const float bi = sm.bet[nb][i];
+        wait_at_least(&sm.pctr, psyncs, &sm.stuck);
+    } else if (role == 2) {
+        // 2b. A(1,0) = K_a K_b^T and P(0,0) = K_a Q_a^T
+        wait_at_least(&sm.pctr, psyncs, &sm.stuck);
+        if (valid) {
+            const uint16_t *qa = &sm.Qs[s2][l32][8 * hi];
+            f32x16_t g0 = zero16(), g1 = zero16();
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb) {
-                    const int j0 = 32 * jb + 8 * rb + 4 * hi;
-                    const float4 gj = *reinterpret_cast<const float4 *>(&gg[j0]);
-                    const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
-                    float v4[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int j = j0 + e;
-                        const float val = acc[4 * rb + e] * exp2_fast(gi - gjv[e]);
-                        v4[e] = is_k ? ((j < i) ? bi * val : 0.f) : ((j <= i) ? val : 0.f);
-                    }
-                    if (!is_k) {
-                        *reinterpret_cast<uint2 *>(&sm.Pb[nb][i][j0]) = pack4(v4[0], v4[1], v4[2], v4[3]);
-                    } else if ((i >> 4) == (j0 >> 4)) {
-                        *reinterpret_cast<float4 *>(&sm.Ad[i >> 4][i & 15][j0 & 15]) = make_float4(v4[0], v4[1], v4[2], v4[3]);
-                    } else if ((i >> 4) > (j0 >> 4)) {
-                        *reinterpret_cast<uint2 *>(&sm.Ab[i][j0]) = pack4(v4[0], v4[1], v4[2], v4[3]);
-                    }
-                }
-            };
-            if (role == 0) {
-                epi(g0, 0, 0, true);
-            } else if (role == 1) {
-                epi(g0, 1, 1, true);
-            } else if (role == 2) {
-                epi(g0, 0, 0, false);
-                epi(g1, 0, 1, true);
-            } else {
-                epi(g0, 0, 1, false);
-                epi(g1, 1, 1, false);
+            for (int s = 0; s < NKS; ++s) {
+                const bf16x8_t a = lds16(ka + 16 * s);
+                g0 = mfma32(a, lds16(kb + 16 * s), g0);
+                g1 = mfma32(a, lds16(qa + 16 * s), g1);
             }
+            gram_epilogue(sm, cp, g0, 0, 1, true, lane);
+            gram_epilogue(sm, cp, g1, 0, 0, false, lane);
         }
-        __syncthreads();
-        // ===== phase 3: diagonal blocks of Tm for chunk c+1; staging ==========
-        if (prep && role < 2 && g16 < 2) {
-            // lane l16 of half g16 owns row l16 of block 2*role + g16.  Row i of
-            // (I + A_kk)^{-1} solves (I + A_kk)^T y = e_i; backward substitution,
-            // right-looking: once y_j is known, y_m -= A[j][m] y_j for every m < j.
-            const int kb = 2 * role + g16;
-            const int i = l16;
-            float y[16];
+    } else {
+        // 2c. P(1,0) = K_a Q_b^T and P(1,1) = K_b Q_b^T
+        wait_at_least(&sm.pctr, psyncs, &sm.stuck);
+        if (valid) {
+            const uint16_t *qb = &sm.Qs[s2][32 + l32][8 * hi];
+            f32x16_t g0 = zero16(), g1 = zero16();
 #pragma unroll
-            for (int m = 0; m < 16; ++m) y[m] = (m == i) ? 1.f : 0.f;
-#pragma unroll
-            for (int j = 15; j >= 1; --j) {
-                const float *arow = &sm.Ad[kb][j][0];  // A[j][m], m < j
-                float av[16];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    if (4 * q4 >= j) break;
-                    const float4 f = *reinterpret_cast<const float4 *>(arow + 4 * q4);
-                    av[4 * q4] = f.x; av[4 * q4 + 1] = f.y; av[4 * q4 + 2] = f.z; av[4 * q4 + 3] = f.w;
-                }
-#pragma unroll
-                for (int m = 0; m < j; ++m) y[m] -= av[m] * y[j];
+            for (int s = 0; s < NKS; ++s) {
+                const bf16x8_t q = lds16(qb + 16 * s);
+                g0 = mfma32(lds16(ka + 16 * s), q, g0);
+                g1 = mfma32(lds16(kb + 16 * s), q, g1);
             }
-            uint16_t *row = &sm.Tb[16 * kb + i][16 * kb];
-            const uint4 w0 = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
-                                        pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
-            const uint4 w1 = make_uint4(pack_bf16x2(y[8], y[9]), pack_bf16x2(y[10], y[11]),
-                                        pack_bf16x2(y[12], y[13]), pack_bf16x2(y[14], y[15]));
-            *reinterpret_cast<uint4 *>(row) = w0;
-            *reinterpret_cast<uint4 *>(row + 8) = w1;
-            if ((kb & 1) == 0) {  // zero block right of the diagonal inside the 32-row block
-                *reinterpret_cast<uint4 *>(row + 16) = make_uint4(0, 0, 0, 0);
-                *reinterpret_cast<uint4 *>(row + 24) = make_uint4(0, 0, 0, 0);
-            }
+            gram_epilogue(sm, cp, g0, 0, 1, false, lane);
+            gram_epilogue(sm, cp, g1, 1, 1, false, lane);
         }
-        // stage chunk c+2 (row blocks), chunk c+1's V tile and chunk c+2's gates
-        if (c + 2 < x.nchunks) store_block(c + 2, rnext);
-        if (prep) *reinterpret_cast<uint4 *>(&sm.Vs[v_tok][8 * v_part]) = vpf;
-        if (role == 0 && c + 2 < x.nchunks) {
-            sm.rawbet[lane] = gpf ? bpf : 0.f;
-            sm.rawdec[lane] = gpf ? apf : 1.f;
-        }
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) rcur[s] = rnext[s];
-        __syncthreads();
+    }
+    // 3. off-diagonal blocks of Tm, one block column per wave, once every wave's
+    //    diagonal blocks and A blocks are in LDS
+    psyncs += 4;
+    arrive(&sm.pctr, lane);
+    wait_at_least(&sm.pctr, psyncs, &sm.stuck);
+    if (valid) {
+        if (role == 0) tm_column<0>(sm.Tb[s2], sm.Ab, l16, g16);
+        else if (role == 1) tm_column<1>(sm.Tb[s2], sm.Ab, l16, g16);
+        else if (role == 2) tm_column<2>(sm.Tb[s2], sm.Ab, l16, g16);
     }
 }
 
@@ -592,16 +749,83 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     x.v = p.v + tok0 * p.dv + dv0;
     x.beta = p.beta + tok0;
     x.decay = p.decay + tok0;
+    const int n = x.nchunks;
 
-    if (wid < 4) {
+    if (tid == 0) {
+        sm.nflag = 0;
+        sm.pctr = 0;
+        sm.stuck = 0;
+    }
+
+    // Every role walks the same periods it = -2 .. n-1 (two per loop trip, so
+    // that register sets alternate at compile time) with one barrier each.
+    if (wid == 0) {
+        const size_t sbase = ((size_t)(b * p.H + h) * p.dv + dv0 + (lane & 31)) * DK;
+        Chain<DK, BF16> ch;
+        ch.init(p, sm, sbase, lane);
+        __syncthreads();
+        for (int it = -2; it < n; it += 2) {
+            if (it >= 0) ch.step(sm, it, lane);
+            __syncthreads();
+            if (it + 1 >= 0 && it + 1 < n) ch.step(sm, it + 1, lane);
+            __syncthreads();
+        }
+        ch.finish(p, sbase, lane);
+    } else if (wid == 3 || wid == 7) {
+        const int tb = wid == 7 ? 1 : 0;
         void *out_b = BF16 ? (void *)(reinterpret_cast<uint16_t *>(p.out) + tok0 * p.dv + dv0)
                            : (void *)(reinterpret_cast<float *>(p.out) + tok0 * p.dv + dv0);
         float *part = dir ? p.partial_rev : p.partial;
         float *part_b = part ? part + tok0 * p.dv + dv0 : nullptr;
-        const size_t sbase = ((size_t)(b * p.H + h) * p.dv + dv0 + (lane & 31)) * DK;
-        chain_loop<DK, BF16>(x, sm, p, wid, lane, out_b, part_b, sbase);
+        __syncthreads();
+        for (int it = -2; it < n; it += 2) {
+            if (it >= 0) output_step<DK, BF16>(x, sm, p, it, tb, lane, out_b, part_b);
+            __syncthreads();
+            if (it + 1 >= 0 && it + 1 < n) output_step<DK, BF16>(x, sm, p, it + 1, tb, lane, out_b, part_b);
+            __syncthreads();
+        }
+    } else if (wid == 4) {
+        // V of chunk c is stored in period c-1 from register set c&1 (loaded in
+        // period c-3); gates of chunk c are computed in period c-2 from set c&1
+        // (loaded in period c-4).
+        VRow vA, vB;
+        GateRegs gA{0.f, 1.f}, gB{0.f, 1.f};
+        if (x.has(0)) vA = load_v(x, 0, lane);
+        load_gates(x, 0, lane, gA);
+        load_gates(x, 1, lane, gB);
+        __syncthreads();
+        for (int it = -2; it < n; it += 2) {
+            // period it (even): V of chunk it+1 (odd, set B); gates of chunk it+2 (even, set A)
+            if (x.has(it + 1)) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4_t *>(&sm.Vs[1][lane][8 * u]) = vB.w[u];
+            }
+            if (x.has(it + 3)) vB = load_v(x, it + 3, lane);
+            if (x.has(it + 2)) gates_compute(x, sm, it + 2, lane, gA);
+            load_gates(x, it + 4, lane, gA);
+            __syncthreads();
+            // period it+1 (odd): V of chunk it+2 (even, set A); gates of chunk it+3 (odd, set B)
+            if (x.has(it + 2)) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4_t *>(&sm.Vs[0][lane][8 * u]) = vA.w[u];
+            }
+            if (x.has(it + 4)) vA = load_v(x, it + 4, lane);
+            if (x.has(it + 3)) gates_compute(x, sm, it + 3, lane, gB);
+            load_gates(x, it + 5, lane, gB);
+            __syncthreads();
+        }
     } else {
-        prep_loop<DK>(x, sm, wid - 4, lane);
+        const int role = (wid == 1) ? 0 : (wid == 2) ? 1 : (wid == 5) ? 2 : 3;
+        RowBlock<DK> rA, rB;  // row blocks of even / odd chunks
+        int psyncs = 0;
+        if (x.has(0)) rA = load_block<DK>(x, 0, role, lane);
+        __syncthreads();
+        for (int it = -2; it < n; it += 2) {
+            prep_step<DK>(x, sm, it, role, lane, psyncs, rB);      // prepares chunk it+1 (odd)
+            __syncthreads();
+            prep_step<DK>(x, sm, it + 1, role, lane, psyncs, rA);  // prepares chunk it+2 (even)
+            __syncthreads();
+        }
     }
 }
 
