@@ -22,28 +22,32 @@
 // HBM traffic, because the tiles of a head are placed on one XCD and share q/k
 // through its L2, and it buys the CU count the sequential chunk chain needs.
 //
-// Roles.  Eight waves; waves w and w + 4 share a SIMD.  One workgroup barrier
-// per chunk period.  In period c:
-//   wave 0     the state chain of chunk c.  S^T (d_k x 32) lives in fp32 MFMA
-//              accumulators for the whole call; X = K S^T, R, N = Tm R and the
-//              update S^T = gam_{C-1} S^T + K^T N~ hand their results from one
-//              product to the next in registers: a 32x32 accumulator becomes the
-//              next product's bf16 operand with one v_permlane32_swap per two
-//              rows (the 32x32x16 A and B operands share one lane layout), so
-//              the chain has no barrier and no LDS round trip of its own.  It
-//              publishes bf16 copies of S (for the next period's outputs) and of
-//              N (behind an LDS flag, for this period's outputs).
-//   wave 4     (light work beside the chain) V tile of chunk c+1 into LDS; gate
-//              vectors of chunk c+2 (float64 prefix sum of log2 a, 2^g,
-//              2^{g_last - g}, b).
-//   waves 3, 7 outputs of chunk c, one 32-token half each:
+// Roles.  Eight waves; waves w and w + 4 share a SIMD, and the pairs are chosen
+// to even out the SIMDs' work.  One workgroup barrier per chunk period.  In
+// period c:
+//   wave 0     the state chain of chunk c, alone on its SIMD.  S^T (d_k x 32)
+//              lives in fp32 MFMA accumulators for the whole call; X = K S^T,
+//              R, N = Tm R and the update S^T = gam_{C-1} S^T + K^T N~ hand their
+//              results from one product to the next in registers: a 32x32
+//              accumulator becomes the next product's bf16 operand with one
+//              v_permlane32_swap per two rows (the 32x32x16 A and B operands
+//              share one lane layout), so the chain has no barrier and no LDS
+//              round trip of its own.  It publishes bf16 copies of S (for the
+//              next period's outputs) and of N (behind an LDS flag, for this
+//              period's outputs).
+//   waves 6, 3 outputs of chunk c, one 32-token half each: P of the half's query
+//              rows in registers (formed while the chain works on N), then
 //              O^T = gam .* (S Q^T) + N^T P^T, written as 8-byte row segments.
-//   waves 1, 2, 5, 6  chunk c+1 (preparation roles 0-3; a K-row wave shares its
-//              SIMD with a Q-row wave): their K or Q row block (HBM -> registers -> LDS),
-//              the Gram products K K^T and K Q^T, the A and P epilogues, and
-//              Tm -- 16x16 diagonal blocks by fp32 substitution, the other
-//              blocks by 16x16x16 MFMA -- with two LDS-counter syncs among
-//              themselves.
+//   waves 1, 2, 5  chunk c+1: K rows 0-31, K rows 32-63 and Q rows 0-31
+//              (HBM -> registers -> LDS); the diagonal 32x32 blocks of A and their
+//              16x16 diagonal Tm blocks (fp32 substitution in registers) from the
+//              K waves' own rows, the off-diagonal block A(1,0), and the other Tm
+//              blocks by 16x16x16 MFMA, with LDS counters as their only syncs.
+//   wave 4     V tile and Q rows 32-63 of chunk c+1 into LDS (memory operations
+//              only, beside the chain).
+//   wave 7     gate vectors of chunk c+2: float64 prefix sum of log2 a (DPP
+//              within 16-lane rows, then the row carries), 2^g, 2^{g_last - g},
+//              b, and the factors of the off-diagonal 32x32 block.
 // Global loads run two periods ahead (K/Q/V of chunk c+3, gates of c+4, in
 // alternating register sets), so their latency hides behind two periods; a
 // register set is refilled right after it has been stored to LDS, and no
@@ -97,15 +101,16 @@ struct __align__(16) Smem {
     uint16_t Vs[2][C][LV];   // V tile, token-major
     uint16_t Sb[2][DVT][LK]; // bf16 state tile at the start of a chunk, [d_v][d_k]
     uint16_t Nt[DVT][LC];    // N^T of the current chunk
-    uint16_t Pb[2][C][LC];   // P, row-major, zero above the diagonal
     uint16_t Tb[2][C][LC];   // Tm, row-major, zero above the diagonal
     uint16_t Ab[C][LC];      // A (its off-diagonal 16x16 blocks are read)
     float g[3][C];           // cumulative log2 decay (summed in float64), chunk mod 3
     float bet[3][C];         // b (0 on padding)
     float gam[3][C];         // 2^{g_i}
     float glast[3][C];       // 2^{g_{C-1} - g_i}
+    float xf[3][C];          // 2^{g_31 - g_j} (j < 32), 2^{g_i - g_31} (i >= 32): both <= 1
     int nflag;               // chunks whose N^T has been published
-    int pctr;                // arrivals at the preparation waves' syncs
+    int kctr;                // K row blocks stored (one arrival per K wave and period)
+    int tctr;                // A blocks and diagonal Tm blocks ready (three arrivals per period)
     int stuck;               // set once any wait ran out; later waits return at once
 };
 
@@ -409,29 +414,93 @@ struct Chain {
     }
 };
 
-// ---- waves 3 and 7: outputs of one 32-token half --------------------------------
-template <int DK, bool BF16>
-__device__ __forceinline__ void output_step(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int c, int tb,
-                                            int lane, void *out_b, float *part_b) {
+// ---- outputs of one 32-token half (query block TB) -----------------------------
+// P of the half's query rows is formed here, in registers, from K and Q in LDS
+// while the chain is still working on N:
+//   TB = 0: P(0,0) = K_a Q_a^T                    (keys 0-31)
+//   TB = 1: P(1,0) = K_a Q_b^T, P(1,1) = K_b Q_b^T  (keys 0-63)
+// as (keys x queries) accumulators, whose rows become the k-steps of the
+// B operand of O^T += N^T P^T.  The same Q operand feeds (S Q^T)^T.
+template <int DK>
+__device__ __forceinline__ void p_diag_epilogue(const Smem<DK> &sm, int s3, f32x16_t &acc, int b, int lane) {
+    // diagonal block b: element (key j, query i) times 2^{g_i - g_j}, kept for j <= i
+    const int l32 = lane & 31, hi = lane >> 5;
+    const float *gg = sm.g[s3];
+    const int i = 32 * b + l32;
+    const float gi = gg[i];
+    float4 gj[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) gj[q] = *reinterpret_cast<const float4 *>(&gg[32 * b + 8 * q + 4 * hi]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int j0 = 32 * b + 8 * q + 4 * hi;
+        const float gjv[4] = {gj[q].x, gj[q].y, gj[q].z, gj[q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float val = acc[4 * q + e] * exp2_fast(gi - gjv[e]);
+            acc[4 * q + e] = (j0 + e <= i) ? val : 0.f;
+        }
+    }
+}
+
+template <int DK>
+__device__ __forceinline__ void cross_scale(const Smem<DK> &sm, int s3, f32x16_t &acc, float si, int lane) {
+    // keys 0-31 x queries 32-63: G_ij = 2^{g_i - g_31} 2^{g_31 - g_j}; si carries
+    // the query factor (and b_i for A)
+    const int hi = lane >> 5;
+    float4 fj[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) fj[q] = *reinterpret_cast<const float4 *>(&sm.xf[s3][8 * q + 4 * hi]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        acc[4 * q + 0] *= fj[q].x * si;
+        acc[4 * q + 1] *= fj[q].y * si;
+        acc[4 * q + 2] *= fj[q].z * si;
+        acc[4 * q + 3] *= fj[q].w * si;
+    }
+}
+
+template <int DK, bool BF16, int TB>
+__device__ __forceinline__ void output_step(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int c, int lane,
+                                            void *out_b, float *part_b) {
     constexpr int NKS = DK / 16;
     const int l32 = lane & 31, hi = lane >> 5;
     const int s2 = c & 1, s3 = c % 3;
-    // (S Q^T) for the half's query columns, scaled by gam of the column
-    f32x16_t acc = zero16();
+    const uint16_t *qrow = &sm.Qs[s2][32 * TB + l32][8 * hi];
+    const uint16_t *ka = &sm.Ks[s2][l32][8 * hi];
+    const uint16_t *kb = &sm.Ks[s2][32 + l32][8 * hi];
+    const uint16_t *srow = &sm.Sb[s2][l32][8 * hi];
+    f32x16_t acc = zero16(), p0 = zero16(), p1 = zero16();
 #pragma unroll
-    for (int s = 0; s < NKS; ++s)
-        acc = mfma32(lds16(&sm.Sb[s2][l32][16 * s + 8 * hi]), lds16(&sm.Qs[s2][32 * tb + l32][16 * s + 8 * hi]), acc);
-    const float gq = sm.gam[s3][32 * tb + l32];
+    for (int s = 0; s < NKS; ++s) {
+        const bf16x8_t q = lds16(qrow + 16 * s);
+        acc = mfma32(lds16(srow + 16 * s), q, acc);
+        p0 = mfma32(lds16(ka + 16 * s), q, p0);
+        if constexpr (TB == 1) p1 = mfma32(lds16(kb + 16 * s), q, p1);
+    }
+    // (S Q^T)^T scaled by gam of the query column
+    const int i = 32 * TB + l32;
+    const float gq = sm.gam[s3][i];
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] *= gq;
-    // + N^T P^T, keys < 32 (tb + 1), once the chain has published N^T
+    // P^T as B operands, k-step t = keys 16 t .. 16 t + 15
+    bf16x8_t pop[4];
+    if constexpr (TB == 0) {
+        p_diag_epilogue(sm, s3, p0, 0, lane);
+        pop[0] = acc_to_op<0>(p0);
+        pop[1] = acc_to_op<1>(p0);
+    } else {
+        cross_scale(sm, s3, p0, sm.xf[s3][i], lane);
+        p_diag_epilogue(sm, s3, p1, 1, lane);
+        pop[0] = acc_to_op<0>(p0);
+        pop[1] = acc_to_op<1>(p0);
+        pop[2] = acc_to_op<0>(p1);
+        pop[3] = acc_to_op<1>(p1);
+    }
+    // + N^T P^T once the chain has published N^T
     wait_at_least(&sm.nflag, c + 1, &sm.stuck);
 #pragma unroll
-    for (int k = 0; k < 64; k += 16) {
-        if (k >= 32 * (tb + 1)) break;
-        acc = mfma32(lds16(&sm.Nt[l32][k + 8 * hi]), lds16(&sm.Pb[s2][32 * tb + l32][k + 8 * hi]), acc);
-    }
-    const int i = 32 * tb + l32;
+    for (int t = 0; t < 2 * (TB + 1); ++t) acc = mfma32(lds16(&sm.Nt[l32][16 * t + 8 * hi]), pop[t], acc);
     if (i < x.ntok(c)) {
         const size_t e0 = (size_t)x.tok(c, i) * x.rsv;
 #pragma unroll
@@ -473,20 +542,45 @@ __device__ __forceinline__ void load_gates(const Ctx &x, int c, int lane, GateRe
     g.a = x.decay[o];
 }
 
+// Float64 helpers for the gate prefix sum (64 lanes, lane = token).
+template <int CTRL>
+__device__ __forceinline__ double dpp_shr_f64(double x) {  // row_shr:k, 0 shifted in
+    const uint64_t u = __double_as_longlong(x);
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)u, CTRL, 0xF, 0xF, true);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(u >> 32), CTRL, 0xF, 0xF, true);
+    return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double lane_value(double x, int l) {
+    const uint64_t u = __double_as_longlong(x);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), l);
+    return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele inside each 16-lane row
+// (DPP row_shr 1, 2, 4, 8), then the row totals carried across rows.
+__device__ __forceinline__ double prefix_sum64(int lane, double x) {
+    x += dpp_shr_f64<0x111>(x);
+    x += dpp_shr_f64<0x112>(x);
+    x += dpp_shr_f64<0x114>(x);
+    x += dpp_shr_f64<0x118>(x);
+    const double t0 = lane_value(x, 15), t2 = lane_value(x, 47);
+    if ((lane & 16) != 0) x += (lane < 32) ? t0 : t2;  // rows 1 and 3
+    const double t01 = lane_value(x, 31);
+    if (lane >= 32) x += t01;  // rows 2 and 3
+    return x;
+}
+
 template <int DK>
 __device__ __forceinline__ void gates_compute(const Ctx &x, Smem<DK> &sm, int c, int lane, const GateRegs &gr) {
     const bool real = lane < x.ntok(c);
     const float a = real ? gr.a : 1.f;
     float l2 = __builtin_amdgcn_logf(a);  // log2
     if (!(l2 > -200.0f)) l2 = -200.0f;    // a = 0: 2^-200 is 0 in fp32
-    double xs = (double)l2;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const double y = __shfl_up(xs, off, 64);
-        if (lane >= off) xs += y;
-    }
-    const double xl = __shfl(xs, 63, 64);
+    const double xs = prefix_sum64(lane, (double)l2);
+    const double xl = lane_value(xs, 63);
+    const double x31 = lane_value(xs, 31);
     const int s3 = c % 3;
+    sm.xf[s3][lane] = exp2_fast((float)(lane < 32 ? x31 - xs : xs - x31));
     sm.g[s3][lane] = (float)xs;
     sm.gam[s3][lane] = exp2_fast((float)xs);
     sm.glast[s3][lane] = exp2_fast((float)(xl - xs));
@@ -499,58 +593,36 @@ __device__ __forceinline__ void gates_compute(const Ctx &x, Smem<DK> &sm, int c,
 //   role 0: A(0,0) = K_a K_a^T      role 1: A(1,1) = K_b K_b^T
 //   role 2: A(1,0) = K_a K_b^T, P(0,0) = K_a Q_a^T
 //   role 3: P(1,0) = K_a Q_b^T, P(1,1) = K_b Q_b^T
-// Epilogue of a Gram block (keys x queries): element (key j, query i) times
-// 2^{g_i - g_j}; for A also times b_i and kept for j < i, for P kept for j <= i.
-// Every LDS read is issued before any LDS write, so the reads' latencies overlap
-// (the compiler keeps LDS accesses that may alias in program order).
+// A(1,0) = b_i (k_i . k_j) G_ij for keys j in 0-31 and queries i in 32-63 (every
+// j < i), from its Gram accumulator, with the separable cross-block factors;
+// written as bf16 to Ab (all of its 16x16 blocks are off-diagonal blocks of A).
 template <int DK>
-__device__ __forceinline__ void gram_epilogue(Smem<DK> &sm, int cp, const f32x16_t &acc, int jb, int ib, bool is_k,
-                                              int lane) {
+__device__ __forceinline__ void a_cross_block(Smem<DK> &sm, int cp, f32x16_t acc, int lane) {
     const int l32 = lane & 31, hi = lane >> 5;
-    const int s3 = cp % 3, s2 = cp & 1;
-    const float *gg = sm.g[s3];
-    const int i = 32 * ib + l32;
-    const float gi = gg[i];
-    const float bi = sm.bet[s3][i];
-    float4 gj[4];
+    const int s3 = cp % 3;
+    const int i = 32 + l32;
+    cross_scale(sm, s3, acc, sm.xf[s3][i] * sm.bet[s3][i], lane);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) gj[q] = *reinterpret_cast<const float4 *>(&gg[32 * jb + 8 * q + 4 * hi]);
-    uint2 w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int j0 = 32 * jb + 8 * q + 4 * hi;
-        const float gjv[4] = {gj[q].x, gj[q].y, gj[q].z, gj[q].w};
-        float v4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int j = j0 + e;
-            const float val = acc[4 * q + e] * exp2_fast(gi - gjv[e]);
-            if (ib > jb)  // off-diagonal block: every j < i
-                v4[e] = is_k ? bi * val : val;
-            else
-                v4[e] = is_k ? ((j < i) ? bi * val : 0.f) : ((j <= i) ? val : 0.f);
-        }
-        w[q] = pack4(v4[0], v4[1], v4[2], v4[3]);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int j0 = 32 * jb + 8 * q + 4 * hi;
-        if (!is_k)
-            *reinterpret_cast<uint2 *>(&sm.Pb[s2][i][j0]) = w[q];
-        else  // an off-diagonal 32x32 block of A: every 16x16 block in it is off-diagonal
-            *reinterpret_cast<uint2 *>(&sm.Ab[i][j0]) = w[q];
-    }
+    for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<uint2 *>(&sm.Ab[i][8 * q + 4 * hi]) =
+            pack4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
 }
 
 // y += a_J * b, where a_J is lane J's value of a within each 16-lane row: one
 // v_fmac_f32 with a DPP row_newbcast source (register arithmetic only; no
-// memory access).  The s_nop covers the wait states a DPP source read needs
-// after a VALU write of that register.
+// memory access).  A DPP source read needs two wait states after a VALU write
+// of that register; the caller issues them once, after the last write of every
+// register it will broadcast from (fmac_dpp_fence).
 template <int J>
 __device__ __forceinline__ void fmac_row_bcast(float &y, float a, float b) {
-    asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+    asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
                  : "+v"(y)
                  : "v"(a), "v"(b), "n"(J));
+}
+// Two wait states that every register in a[0..14] has been written before.
+__device__ __forceinline__ void fmac_dpp_fence(const float (&a)[16]) {
+    asm volatile("s_nop 1" ::"v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+                 "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]));
 }
 
 // A diagonal 32x32 block kk of A, from its Gram accumulator acc = K_kk K_kk^T
@@ -609,11 +681,13 @@ __device__ __forceinline__ void a_diag_block(Smem<DK> &sm, int cp, const f32x16_
     float y[16];
 #pragma unroll
     for (int m = 0; m < 16; ++m) y[m] = (m == l16) ? 1.f : 0.f;
+    // level J updates y[J-1] first: the next level starts from it
 #define GDN_SUBST_STEP(J)                                                         \
     {                                                                             \
         const float nyj = -y[J];                                                  \
-        _Pragma("unroll") for (int m = 0; m < J; ++m) fmac_row_bcast<J>(y[m], a[m], nyj); \
+        _Pragma("unroll") for (int m = J - 1; m >= 0; --m) fmac_row_bcast<J>(y[m], a[m], nyj); \
     }
+    fmac_dpp_fence(a);
     GDN_SUBST_STEP(15) GDN_SUBST_STEP(14) GDN_SUBST_STEP(13) GDN_SUBST_STEP(12)
     GDN_SUBST_STEP(11) GDN_SUBST_STEP(10) GDN_SUBST_STEP(9) GDN_SUBST_STEP(8)
     GDN_SUBST_STEP(7) GDN_SUBST_STEP(6) GDN_SUBST_STEP(5) GDN_SUBST_STEP(4)
@@ -634,28 +708,31 @@ __device__ __forceinline__ void a_diag_block(Smem<DK> &sm, int cp, const f32x16_
     }
 }
 
+// Preparation of chunk cp = it + 1 in period it.
+//   role 0: K rows 0-31 (K_a): A(0,0), its diagonal Tm blocks, Tm block column 0
+//   role 1: K rows 32-63 (K_b): A(1,1), its diagonal Tm blocks, Tm block column 1
+//   role 2: Q rows 0-31 (Q_a): A(1,0) = K_a K_b^T, Tm block column 2
 template <int DK>
-__device__ __forceinline__ void prep_step(const Ctx &x, Smem<DK> &sm, int it, int role, int lane, int &psyncs,
+__device__ __forceinline__ void prep_step(const Ctx &x, Smem<DK> &sm, int it, int role, int lane, int np,
                                           RowBlock<DK> &blk) {
     constexpr int NKS = DK / 16;
     const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g16 = lane >> 4;
-    const int cp = it + 1;  // the chunk prepared in this period
+    const int cp = it + 1;
     const bool valid = x.has(cp);
     const int s2 = cp & 1;
     // 1. this wave's row block of chunk cp -> LDS; the registers then take the
     //    loads of chunk it + 3 at once (two periods to land), and every product
     //    below reads its operands from LDS, so nothing here waits on them
     if (valid) {
-        uint16_t *row = (role < 2) ? &sm.Ks[s2][32 * (role & 1) + l32][8 * hi] : &sm.Qs[s2][32 * (role & 1) + l32][8 * hi];
+        uint16_t *row = (role < 2) ? &sm.Ks[s2][32 * role + l32][8 * hi] : &sm.Qs[s2][l32][8 * hi];
 #pragma unroll
         for (int s = 0; s < NKS; ++s) *reinterpret_cast<bf16x8_t *>(row + 16 * s) = blk.r[s];
     }
     if (x.has(it + 3)) blk = load_block<DK>(x, it + 3, role, lane);
-    psyncs += 4;
-    arrive(&sm.pctr, lane);
     const uint16_t *ka = &sm.Ks[s2][l32][8 * hi];       // K rows 0-31
     const uint16_t *kb = &sm.Ks[s2][32 + l32][8 * hi];  // K rows 32-63
     if (role < 2) {
+        arrive(&sm.kctr, lane);
         // 2a. K_kk K_kk^T (this wave's own rows, just stored) -> A's diagonal 32x32
         //     block and the diagonal 16x16 blocks of Tm; needs no other wave's data
         if (valid) {
@@ -668,47 +745,24 @@ __device__ __forceinline__ void prep_step(const Ctx &x, Smem<DK> &sm, int it, in
             }
             a_diag_block(sm, cp, g0, role, lane);
         }
-        wait_at_least(&sm.pctr, psyncs, &sm.stuck);
-    } else if (role == 2) {
-        // 2b. A(1,0) = K_a K_b^T and P(0,0) = K_a Q_a^T
-        wait_at_least(&sm.pctr, psyncs, &sm.stuck);
-        if (valid) {
-            const uint16_t *qa = &sm.Qs[s2][l32][8 * hi];
-            f32x16_t g0 = zero16(), g1 = zero16();
-#pragma unroll
-            for (int s = 0; s < NKS; ++s) {
-                const bf16x8_t a = lds16(ka + 16 * s);
-                g0 = mfma32(a, lds16(kb + 16 * s), g0);
-                g1 = mfma32(a, lds16(qa + 16 * s), g1);
-            }
-            gram_epilogue(sm, cp, g0, 0, 1, true, lane);
-            gram_epilogue(sm, cp, g1, 0, 0, false, lane);
-        }
     } else {
-        // 2c. P(1,0) = K_a Q_b^T and P(1,1) = K_b Q_b^T
-        wait_at_least(&sm.pctr, psyncs, &sm.stuck);
+        // 2b. A(1,0) = K_a K_b^T, once both K blocks are in LDS
+        wait_at_least(&sm.kctr, 2 * np, &sm.stuck);
         if (valid) {
-            const uint16_t *qb = &sm.Qs[s2][32 + l32][8 * hi];
-            f32x16_t g0 = zero16(), g1 = zero16();
+            f32x16_t g0 = zero16();
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) {
-                const bf16x8_t q = lds16(qb + 16 * s);
-                g0 = mfma32(lds16(ka + 16 * s), q, g0);
-                g1 = mfma32(lds16(kb + 16 * s), q, g1);
-            }
-            gram_epilogue(sm, cp, g0, 0, 1, false, lane);
-            gram_epilogue(sm, cp, g1, 1, 1, false, lane);
+            for (int s = 0; s < NKS; ++s) g0 = mfma32(lds16(ka + 16 * s), lds16(kb + 16 * s), g0);
+            a_cross_block(sm, cp, g0, lane);
         }
     }
     // 3. off-diagonal blocks of Tm, one block column per wave, once every wave's
     //    diagonal blocks and A blocks are in LDS
-    psyncs += 4;
-    arrive(&sm.pctr, lane);
-    wait_at_least(&sm.pctr, psyncs, &sm.stuck);
+    arrive(&sm.tctr, lane);
+    wait_at_least(&sm.tctr, 3 * np, &sm.stuck);
     if (valid) {
         if (role == 0) tm_column<0>(sm.Tb[s2], sm.Ab, l16, g16);
         else if (role == 1) tm_column<1>(sm.Tb[s2], sm.Ab, l16, g16);
-        else if (role == 2) tm_column<2>(sm.Tb[s2], sm.Ab, l16, g16);
+        else tm_column<2>(sm.Tb[s2], sm.Ab, l16, g16);
     }
 }
 
@@ -753,12 +807,21 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
 
     if (tid == 0) {
         sm.nflag = 0;
-        sm.pctr = 0;
+        sm.kctr = 0;
+        sm.tctr = 0;
         sm.stuck = 0;
     }
 
-    // Every role walks the same periods it = -2 .. n-1 (two per loop trip, so
-    // that register sets alternate at compile time) with one barrier each.
+    // Roles by wave (waves w and w + 4 share a SIMD): 0 chain and 4 the V / Q_b
+    // loader beside it (memory operations only); 1 and 5: preparation roles 0
+    // and 2; 2 and 6: preparation role 1 and the outputs of tokens 0-31; 3 and
+    // 7: the outputs of tokens 32-63 and the gate vectors.  Every role walks the same periods it = -2 .. n-1
+    // (two per loop trip, so that register sets alternate at compile time) with
+    // one barrier each.
+    void *out_b = BF16 ? (void *)(reinterpret_cast<uint16_t *>(p.out) + tok0 * p.dv + dv0)
+                       : (void *)(reinterpret_cast<float *>(p.out) + tok0 * p.dv + dv0);
+    float *part = dir ? p.partial_rev : p.partial;
+    float *part_b = part ? part + tok0 * p.dv + dv0 : nullptr;
     if (wid == 0) {
         const size_t sbase = ((size_t)(b * p.H + h) * p.dv + dv0 + (lane & 31)) * DK;
         Chain<DK, BF16> ch;
@@ -771,59 +834,79 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
             __syncthreads();
         }
         ch.finish(p, sbase, lane);
-    } else if (wid == 3 || wid == 7) {
-        const int tb = wid == 7 ? 1 : 0;
-        void *out_b = BF16 ? (void *)(reinterpret_cast<uint16_t *>(p.out) + tok0 * p.dv + dv0)
-                           : (void *)(reinterpret_cast<float *>(p.out) + tok0 * p.dv + dv0);
-        float *part = dir ? p.partial_rev : p.partial;
-        float *part_b = part ? part + tok0 * p.dv + dv0 : nullptr;
+    } else if (wid == 6) {
         __syncthreads();
         for (int it = -2; it < n; it += 2) {
-            if (it >= 0) output_step<DK, BF16>(x, sm, p, it, tb, lane, out_b, part_b);
+            if (it >= 0) output_step<DK, BF16, 0>(x, sm, p, it, lane, out_b, part_b);
             __syncthreads();
-            if (it + 1 >= 0 && it + 1 < n) output_step<DK, BF16>(x, sm, p, it + 1, tb, lane, out_b, part_b);
+            if (it + 1 >= 0 && it + 1 < n) output_step<DK, BF16, 0>(x, sm, p, it + 1, lane, out_b, part_b);
+            __syncthreads();
+        }
+    } else if (wid == 3) {
+        __syncthreads();
+        for (int it = -2; it < n; it += 2) {
+            if (it >= 0) output_step<DK, BF16, 1>(x, sm, p, it, lane, out_b, part_b);
+            __syncthreads();
+            if (it + 1 >= 0 && it + 1 < n) output_step<DK, BF16, 1>(x, sm, p, it + 1, lane, out_b, part_b);
             __syncthreads();
         }
     } else if (wid == 4) {
-        // V of chunk c is stored in period c-1 from register set c&1 (loaded in
-        // period c-3); gates of chunk c are computed in period c-2 from set c&1
-        // (loaded in period c-4).
+        // V and Q rows 32-63 of chunk c are stored in period c-1 from register set
+        // c&1 (loaded in period c-3).  Memory operations only, beside the chain.
         VRow vA, vB;
+        RowBlock<DK> qA, qB;
+        if (x.has(0)) {
+            vA = load_v(x, 0, lane);
+            qA = load_block<DK>(x, 0, 3, lane);
+        }
+        auto store_vq = [&](int c, const VRow &v, const RowBlock<DK> &q) {
+            const int s2 = c & 1;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4_t *>(&sm.Vs[s2][lane][8 * u]) = v.w[u];
+            uint16_t *row = &sm.Qs[s2][32 + (lane & 31)][8 * (lane >> 5)];
+#pragma unroll
+            for (int s_ = 0; s_ < DK / 16; ++s_) *reinterpret_cast<bf16x8_t *>(row + 16 * s_) = q.r[s_];
+        };
+        __syncthreads();
+        for (int it = -2; it < n; it += 2) {
+            if (x.has(it + 1)) store_vq(it + 1, vB, qB);
+            if (x.has(it + 3)) {
+                vB = load_v(x, it + 3, lane);
+                qB = load_block<DK>(x, it + 3, 3, lane);
+            }
+            __syncthreads();
+            if (x.has(it + 2)) store_vq(it + 2, vA, qA);
+            if (x.has(it + 4)) {
+                vA = load_v(x, it + 4, lane);
+                qA = load_block<DK>(x, it + 4, 3, lane);
+            }
+            __syncthreads();
+        }
+    } else if (wid == 7) {
+        // gates of chunk c are computed in period c-2 from register set c&1
+        // (loaded in period c-4)
         GateRegs gA{0.f, 1.f}, gB{0.f, 1.f};
-        if (x.has(0)) vA = load_v(x, 0, lane);
         load_gates(x, 0, lane, gA);
         load_gates(x, 1, lane, gB);
         __syncthreads();
         for (int it = -2; it < n; it += 2) {
-            // period it (even): V of chunk it+1 (odd, set B); gates of chunk it+2 (even, set A)
-            if (x.has(it + 1)) {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4_t *>(&sm.Vs[1][lane][8 * u]) = vB.w[u];
-            }
-            if (x.has(it + 3)) vB = load_v(x, it + 3, lane);
             if (x.has(it + 2)) gates_compute(x, sm, it + 2, lane, gA);
             load_gates(x, it + 4, lane, gA);
             __syncthreads();
-            // period it+1 (odd): V of chunk it+2 (even, set A); gates of chunk it+3 (odd, set B)
-            if (x.has(it + 2)) {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4_t *>(&sm.Vs[0][lane][8 * u]) = vA.w[u];
-            }
-            if (x.has(it + 4)) vA = load_v(x, it + 4, lane);
             if (x.has(it + 3)) gates_compute(x, sm, it + 3, lane, gB);
             load_gates(x, it + 5, lane, gB);
             __syncthreads();
         }
     } else {
-        const int role = (wid == 1) ? 0 : (wid == 2) ? 1 : (wid == 5) ? 2 : 3;
+        const int role = (wid == 1) ? 0 : (wid == 2) ? 1 : 2;
         RowBlock<DK> rA, rB;  // row blocks of even / odd chunks
-        int psyncs = 0;
         if (x.has(0)) rA = load_block<DK>(x, 0, role, lane);
         __syncthreads();
+        int np = 0;  // periods walked so far (sync targets)
         for (int it = -2; it < n; it += 2) {
-            prep_step<DK>(x, sm, it, role, lane, psyncs, rB);      // prepares chunk it+1 (odd)
+            prep_step<DK>(x, sm, it, role, lane, ++np, rB);      // prepares chunk it+1 (odd)
             __syncthreads();
-            prep_step<DK>(x, sm, it + 1, role, lane, psyncs, rA);  // prepares chunk it+2 (even)
+            prep_step<DK>(x, sm, it + 1, role, lane, ++np, rA);  // prepares chunk it+2 (even)
             __syncthreads();
         }
     }
