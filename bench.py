@@ -76,7 +76,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens per head of the oracle's CPU sample (prefix of the same inputs); "
                          "0 = every token of the workload")

@@ -43,11 +43,12 @@
 //              16x16 diagonal Tm blocks (fp32 substitution in registers) from the
 //              K waves' own rows, the off-diagonal block A(1,0), and the other Tm
 //              blocks by 16x16x16 MFMA, with LDS counters as their only syncs.
-//   wave 4     V tile and Q rows 32-63 of chunk c+1 into LDS (memory operations
-//              only, beside the chain).
+//   wave 4     Q rows 32-63 of chunk c+1 into LDS (memory operations only,
+//              beside the chain).
 //   wave 7     gate vectors of chunk c+2: float64 prefix sum of log2 a (DPP
-//              within 16-lane rows, then the row carries), 2^g, 2^{g_last - g},
-//              b, and the factors of the off-diagonal 32x32 block.
+//              within 16-lane rows, then the row carries), 2^g, b 2^g,
+//              2^{g_last - g}, b, and the factors of the off-diagonal 32x32
+//              block; b_t v_t of chunk c+1 (fp32, d_v-major) for R.
 // Global loads run two periods ahead (K/Q/V of chunk c+3, gates of c+4, in
 // alternating register sets), so their latency hides behind two periods; a
 // register set is refilled right after it has been stored to LDS, and no
@@ -77,7 +78,6 @@ constexpr int C = 64;     // chunk length
 constexpr int NT = 512;   // threads per block: 8 waves
 constexpr int DVT = 32;   // d_v columns per block
 constexpr int LC = C + 8; // padded bf16 row pitch of C-long rows
-constexpr int LV = DVT + 8;
 constexpr int SPIN_LIMIT = 1 << 20;  // bound on any LDS-flag wait (never reached in a correct run)
 
 struct ChunkParams {
@@ -98,7 +98,7 @@ struct __align__(16) Smem {
     static constexpr int LK = DK + 8;  // padded bf16 row pitch of d_k-long rows
     uint16_t Ks[2][C][LK];   // K, token-major (chunk parity)
     uint16_t Qs[2][C][LK];   // Q, token-major
-    uint16_t Vs[2][C][LV];   // V tile, token-major
+    float bVt[2][DVT][C + 4];  // b_t v_t of the d_v tile, fp32, [d_v][token]
     uint16_t Sb[2][DVT][LK]; // bf16 state tile at the start of a chunk, [d_v][d_k]
     uint16_t Nt[DVT][LC];    // N^T of the current chunk
     uint16_t Tb[2][C][LC];   // Tm, row-major, zero above the diagonal
@@ -106,6 +106,7 @@ struct __align__(16) Smem {
     float g[3][C];           // cumulative log2 decay (summed in float64), chunk mod 3
     float bet[3][C];         // b (0 on padding)
     float gam[3][C];         // 2^{g_i}
+    float bg[3][C];          // b_i 2^{g_i}
     float glast[3][C];       // 2^{g_{C-1} - g_i}
     float xf[3][C];          // 2^{g_31 - g_j} (j < 32), 2^{g_i - g_31} (i >= 32): both <= 1
     int nflag;               // chunks whose N^T has been published
@@ -174,18 +175,19 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // operand's rows/columns) by exchanging 4 rows between the lane halves:
 // v_permlane32_swap swaps the upper half of its first operand with the lower
 // half of its second.
-template <int KK>
-__device__ __forceinline__ bf16x8_t acc_to_op(const f32x16_t &a) {
-    const uint32_t x0 = pack_bf16x2(a[8 * KK + 0], a[8 * KK + 1]);  // rows 16KK + 4h + 0..1
-    const uint32_t x1 = pack_bf16x2(a[8 * KK + 2], a[8 * KK + 3]);  // rows 16KK + 4h + 2..3
-    const uint32_t y0 = pack_bf16x2(a[8 * KK + 4], a[8 * KK + 5]);  // rows 16KK + 8 + 4h + 0..1
-    const uint32_t y1 = pack_bf16x2(a[8 * KK + 6], a[8 * KK + 7]);  // rows 16KK + 8 + 4h + 2..3
-    const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
-    const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+// x = rows 16KK + 4h + 0..3 and y = rows 16KK + 8 + 4h + 0..3, already packed to bf16.
+__device__ __forceinline__ bf16x8_t packed_to_op(uint2 x, uint2 y) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(x.x, y.x, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(x.y, y.y, false, false);
     const uint4 w = make_uint4(s0[0], s1[0], s0[1], s1[1]);
     bf16x8_t r;
     __builtin_memcpy(&r, &w, 16);
     return r;
+}
+template <int KK>
+__device__ __forceinline__ bf16x8_t acc_to_op(const f32x16_t &a) {
+    return packed_to_op(make_uint2(pack_bf16x2(a[8 * KK + 0], a[8 * KK + 1]), pack_bf16x2(a[8 * KK + 2], a[8 * KK + 3])),
+                        make_uint2(pack_bf16x2(a[8 * KK + 4], a[8 * KK + 5]), pack_bf16x2(a[8 * KK + 6], a[8 * KK + 7])));
 }
 
 // Off-diagonal blocks of block column CB of Tm = (I + A)^{-1}, walking down:
@@ -268,11 +270,16 @@ struct Ctx {
     }
 };
 
-// One wave's 32-row block of K or Q in MFMA operand layout: lane l holds row
-// l % 32, columns 16 s + 8 (l / 32) .. + 7 in r[s].
+// One wave's 32-row block of K or Q (rows 32 (role & 1) .. + 31 of K for roles
+// 0-1, of Q for roles 2-3), loaded row-coalesced: DK / 8 lanes per row, each
+// with 8 consecutive columns, 512 / DK rows per load instruction, so every load
+// reads whole rows and touches only the cache lines those rows span.
 template <int DK>
 struct RowBlock {
-    bf16x8_t r[DK / 16];
+    static constexpr int LPR = DK / 8;         // lanes per row
+    static constexpr int RPL = 64 / LPR;       // rows per load
+    static constexpr int NLD = 32 / RPL;       // loads per 32 rows
+    bf16x8_t r[NLD];
 };
 
 // Loads are unconditional: rows past the end of a final short chunk re-read
@@ -281,12 +288,25 @@ struct RowBlock {
 // zeroed registers would make the compiler wait for all earlier loads.
 template <int DK>
 __device__ __forceinline__ RowBlock<DK> load_block(const Ctx &x, int c, int role, int lane) {
-    RowBlock<DK> d;
-    const int r = 32 * (role & 1) + (lane & 31);
-    const uint16_t *src = ((role < 2) ? x.k : x.q) + (size_t)x.tok_clamped(c, r) * x.rs + 8 * (lane >> 5);
+    using RB = RowBlock<DK>;
+    RB d;
+    const uint16_t *base = (role < 2) ? x.k : x.q;
+    const int r0 = 32 * (role & 1) + lane / RB::LPR;
+    const int col = 8 * (lane % RB::LPR);
 #pragma unroll
-    for (int s = 0; s < DK / 16; ++s) d.r[s] = *reinterpret_cast<const bf16x8_t *>(src + 16 * s);
+    for (int s = 0; s < RB::NLD; ++s)
+        d.r[s] = *reinterpret_cast<const bf16x8_t *>(base + (size_t)x.tok_clamped(c, r0 + RB::RPL * s) * x.rs + col);
     return d;
+}
+
+// The same block into a token-major [C][LK] LDS buffer.
+template <int DK>
+__device__ __forceinline__ void store_block(uint16_t (*dst)[DK + 8], const RowBlock<DK> &blk, int role, int lane) {
+    using RB = RowBlock<DK>;
+    const int r0 = 32 * (role & 1) + lane / RB::LPR;
+    const int col = 8 * (lane % RB::LPR);
+#pragma unroll
+    for (int s = 0; s < RB::NLD; ++s) *reinterpret_cast<bf16x8_t *>(&dst[r0 + RB::RPL * s][col]) = blk.r[s];
 }
 
 // ---- wave 0: the state chain ------------------------------------------------
@@ -301,12 +321,14 @@ struct Chain {
         const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
         for (int rb = 0; rb < NSB; ++rb) {
+            uint2 w[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<uint2 *>(&sm.Sb[slot][l32][32 * rb + 8 * q + 4 * hi]) =
-                    pack4(sacc[rb][4 * q], sacc[rb][4 * q + 1], sacc[rb][4 * q + 2], sacc[rb][4 * q + 3]);
-            sop[2 * rb] = acc_to_op<0>(sacc[rb]);
-            sop[2 * rb + 1] = acc_to_op<1>(sacc[rb]);
+            for (int q = 0; q < 4; ++q) {
+                w[q] = pack4(sacc[rb][4 * q], sacc[rb][4 * q + 1], sacc[rb][4 * q + 2], sacc[rb][4 * q + 3]);
+                *reinterpret_cast<uint2 *>(&sm.Sb[slot][l32][32 * rb + 8 * q + 4 * hi]) = w[q];
+            }
+            sop[2 * rb] = packed_to_op(w[0], w[1]);
+            sop[2 * rb + 1] = packed_to_op(w[2], w[3]);
         }
     }
 
@@ -337,22 +359,19 @@ struct Chain {
             xacc[0] = mfma32(lds16(&sm.Ks[s2][l32][16 * s + 8 * hi]), sop[s], xacc[0]);
             xacc[1] = mfma32(lds16(&sm.Ks[s2][32 + l32][16 * s + 8 * hi]), sop[s], xacc[1]);
         }
-        // R = diag(b) (V - diag(gam) X), then as the B operand of N = Tm R
+        // R = diag(b) V - diag(b gam) X, then as the B operand of N = Tm R
         bf16x8_t rop[4];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int i0 = 32 * i + 8 * q + 4 * hi;
-                const s16x4_t vv = lds_tr(&sm.Vs[s2][i0 + (l16 >> 2)][16 * (g16 & 1) + 4 * (l16 & 3)]);
-                uint2 vu;
-                __builtin_memcpy(&vu, &vv, 8);
-                const float4 bt = *reinterpret_cast<const float4 *>(&sm.bet[s3][i0]);
-                const float4 gm = *reinterpret_cast<const float4 *>(&sm.gam[s3][i0]);
-                xacc[i][4 * q + 0] = bt.x * (bf16_lo(vu.x) - gm.x * xacc[i][4 * q + 0]);
-                xacc[i][4 * q + 1] = bt.y * (bf16_hi(vu.x) - gm.y * xacc[i][4 * q + 1]);
-                xacc[i][4 * q + 2] = bt.z * (bf16_lo(vu.y) - gm.z * xacc[i][4 * q + 2]);
-                xacc[i][4 * q + 3] = bt.w * (bf16_hi(vu.y) - gm.w * xacc[i][4 * q + 3]);
+                const float4 bv = *reinterpret_cast<const float4 *>(&sm.bVt[s2][l32][i0]);
+                const float4 bgm = *reinterpret_cast<const float4 *>(&sm.bg[s3][i0]);
+                xacc[i][4 * q + 0] = fmaf(-bgm.x, xacc[i][4 * q + 0], bv.x);
+                xacc[i][4 * q + 1] = fmaf(-bgm.y, xacc[i][4 * q + 1], bv.y);
+                xacc[i][4 * q + 2] = fmaf(-bgm.z, xacc[i][4 * q + 2], bv.z);
+                xacc[i][4 * q + 3] = fmaf(-bgm.w, xacc[i][4 * q + 3], bv.w);
             }
             rop[2 * i] = acc_to_op<0>(xacc[i]);
             rop[2 * i + 1] = acc_to_op<1>(xacc[i]);
@@ -525,14 +544,17 @@ struct GateRegs {
     float b, a;
 };
 
+// The chunk's V tile (64 tokens x 32 d_v), row-coalesced: in w[s], lane l holds
+// token 16 s + l / 4, d_v columns 8 (l % 4) .. + 7.
 struct VRow {
-    u32x4_t w[4];  // one token's 32 d_v values of the tile
+    u32x4_t w[4];
 };
 __device__ __forceinline__ VRow load_v(const Ctx &x, int c, int lane) {
     VRow d;
-    const uint16_t *src = x.v + (size_t)x.tok_clamped(c, lane) * x.rsv;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) d.w[u] = *reinterpret_cast<const u32x4_t *>(src + 8 * u);
+    for (int s = 0; s < 4; ++s)
+        d.w[s] = *reinterpret_cast<const u32x4_t *>(x.v + (size_t)x.tok_clamped(c, 16 * s + (lane >> 2)) * x.rsv +
+                                                    8 * (lane & 3));
     return d;
 }
 __device__ __forceinline__ void load_gates(const Ctx &x, int c, int lane, GateRegs &g) {
@@ -582,7 +604,9 @@ __device__ __forceinline__ void gates_compute(const Ctx &x, Smem<DK> &sm, int c,
     const int s3 = c % 3;
     sm.xf[s3][lane] = exp2_fast((float)(lane < 32 ? x31 - xs : xs - x31));
     sm.g[s3][lane] = (float)xs;
-    sm.gam[s3][lane] = exp2_fast((float)xs);
+    const float gm = exp2_fast((float)xs);
+    sm.gam[s3][lane] = gm;
+    sm.bg[s3][lane] = real ? gr.b * gm : 0.f;
     sm.glast[s3][lane] = exp2_fast((float)(xl - xs));
     sm.bet[s3][lane] = real ? gr.b : 0.f;
 }
@@ -723,11 +747,7 @@ __device__ __forceinline__ void prep_step(const Ctx &x, Smem<DK> &sm, int it, in
     // 1. this wave's row block of chunk cp -> LDS; the registers then take the
     //    loads of chunk it + 3 at once (two periods to land), and every product
     //    below reads its operands from LDS, so nothing here waits on them
-    if (valid) {
-        uint16_t *row = (role < 2) ? &sm.Ks[s2][32 * role + l32][8 * hi] : &sm.Qs[s2][l32][8 * hi];
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) *reinterpret_cast<bf16x8_t *>(row + 16 * s) = blk.r[s];
-    }
+    if (valid) store_block<DK>(role < 2 ? sm.Ks[s2] : sm.Qs[s2], blk, role, lane);
     if (x.has(it + 3)) blk = load_block<DK>(x, it + 3, role, lane);
     const uint16_t *ka = &sm.Ks[s2][l32][8 * hi];       // K rows 0-31
     const uint16_t *kb = &sm.Ks[s2][32 + l32][8 * hi];  // K rows 32-63
@@ -812,10 +832,10 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         sm.stuck = 0;
     }
 
-    // Roles by wave (waves w and w + 4 share a SIMD): 0 chain and 4 the V / Q_b
+    // Roles by wave (waves w and w + 4 share a SIMD): 0 chain and 4 the Q_b
     // loader beside it (memory operations only); 1 and 5: preparation roles 0
     // and 2; 2 and 6: preparation role 1 and the outputs of tokens 0-31; 3 and
-    // 7: the outputs of tokens 32-63 and the gate vectors.  Every role walks the same periods it = -2 .. n-1
+    // 7: the outputs of tokens 32-63 and the gate vectors with b v.  Every role walks the same periods it = -2 .. n-1
     // (two per loop trip, so that register sets alternate at compile time) with
     // one barrier each.
     void *out_b = BF16 ? (void *)(reinterpret_cast<uint16_t *>(p.out) + tok0 * p.dv + dv0)
@@ -851,48 +871,53 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
             __syncthreads();
         }
     } else if (wid == 4) {
-        // V and Q rows 32-63 of chunk c are stored in period c-1 from register set
-        // c&1 (loaded in period c-3).  Memory operations only, beside the chain.
-        VRow vA, vB;
+        // Q rows 32-63 of chunk c are stored in period c-1 from register set c&1
+        // (loaded in period c-3).  Memory operations only, beside the chain.
         RowBlock<DK> qA, qB;
-        if (x.has(0)) {
-            vA = load_v(x, 0, lane);
-            qA = load_block<DK>(x, 0, 3, lane);
-        }
-        auto store_vq = [&](int c, const VRow &v, const RowBlock<DK> &q) {
-            const int s2 = c & 1;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4_t *>(&sm.Vs[s2][lane][8 * u]) = v.w[u];
-            uint16_t *row = &sm.Qs[s2][32 + (lane & 31)][8 * (lane >> 5)];
-#pragma unroll
-            for (int s_ = 0; s_ < DK / 16; ++s_) *reinterpret_cast<bf16x8_t *>(row + 16 * s_) = q.r[s_];
-        };
+        if (x.has(0)) qA = load_block<DK>(x, 0, 3, lane);
+        auto store_q = [&](int c, const RowBlock<DK> &q) { store_block<DK>(sm.Qs[c & 1], q, 3, lane); };
         __syncthreads();
         for (int it = -2; it < n; it += 2) {
-            if (x.has(it + 1)) store_vq(it + 1, vB, qB);
-            if (x.has(it + 3)) {
-                vB = load_v(x, it + 3, lane);
-                qB = load_block<DK>(x, it + 3, 3, lane);
-            }
+            if (x.has(it + 1)) store_q(it + 1, qB);
+            if (x.has(it + 3)) qB = load_block<DK>(x, it + 3, 3, lane);
             __syncthreads();
-            if (x.has(it + 2)) store_vq(it + 2, vA, qA);
-            if (x.has(it + 4)) {
-                vA = load_v(x, it + 4, lane);
-                qA = load_block<DK>(x, it + 4, 3, lane);
-            }
+            if (x.has(it + 2)) store_q(it + 2, qA);
+            if (x.has(it + 4)) qA = load_block<DK>(x, it + 4, 3, lane);
             __syncthreads();
         }
     } else if (wid == 7) {
-        // gates of chunk c are computed in period c-2 from register set c&1
-        // (loaded in period c-4)
+        // Gates of chunk c are computed in period c-2 from register set c&1
+        // (loaded in period c-4); b_t v_t of chunk c is stored in period c-1 from
+        // V register set c&1 (loaded in period c-3), with b_t from the gate slot.
         GateRegs gA{0.f, 1.f}, gB{0.f, 1.f};
+        VRow vA, vB;
+        if (x.has(0)) vA = load_v(x, 0, lane);
         load_gates(x, 0, lane, gA);
         load_gates(x, 1, lane, gB);
+        auto store_bv = [&](int c, const VRow &v) {
+            const int d0 = 8 * (lane & 3);
+#pragma unroll
+            for (int s_ = 0; s_ < 4; ++s_) {
+                const int t = 16 * s_ + (lane >> 2);
+                const float bt = sm.bet[c % 3][t];
+                float *col = &sm.bVt[c & 1][d0][t];
+                const uint32_t w4[4] = {v.w[s_].x, v.w[s_].y, v.w[s_].z, v.w[s_].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    col[(2 * e) * (C + 4)] = bt * bf16_lo(w4[e]);
+                    col[(2 * e + 1) * (C + 4)] = bt * bf16_hi(w4[e]);
+                }
+            }
+        };
         __syncthreads();
         for (int it = -2; it < n; it += 2) {
+            if (x.has(it + 1)) store_bv(it + 1, vB);
+            if (x.has(it + 3)) vB = load_v(x, it + 3, lane);
             if (x.has(it + 2)) gates_compute(x, sm, it + 2, lane, gA);
             load_gates(x, it + 4, lane, gA);
             __syncthreads();
+            if (x.has(it + 2)) store_bv(it + 2, vA);
+            if (x.has(it + 4)) vA = load_v(x, it + 4, lane);
             if (x.has(it + 3)) gates_compute(x, sm, it + 3, lane, gB);
             load_gates(x, it + 5, lane, gB);
             __syncthreads();
