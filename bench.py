@@ -75,8 +75,9 @@ def load_traffic(workload):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=40,
+                    help="untimed steps; the clock settles over the first ~30 launches of this kernel")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens per head of the oracle's CPU sample (prefix of the same inputs); "
                          "0 = every token of the workload")

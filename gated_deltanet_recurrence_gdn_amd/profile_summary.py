@@ -4,7 +4,7 @@ Three rocprofv3 runs of bench.py feed it (each its own process; see the command 
 written into the summaries):
 
   kernel trace:  rocprofv3 --kernel-trace --stats --output-format csv -d DIR/kt -o kt -- \\
-                     python bench.py --steps 5 --warmup 1 --no-cpu --no-forms
+                     python bench.py --no-cpu --no-forms
   fetch bytes:   rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o fetch -- \\
                      python bench.py --steps 2 --warmup 1 --no-cpu --no-forms --calib-copy
   write bytes:   rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o write -- \\
@@ -37,7 +37,8 @@ COPY = "copyBuffer"
 COPY_BYTES = 512 * 1024 * 1024
 
 KT_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d {d}/kt -o kt -- "
-          "python bench.py --steps 5 --warmup 1 --no-cpu --no-forms")
+          "python bench.py --no-cpu --no-forms")
+TIMED_STEPS = 40  # bench.py's default --steps: the last dispatches of the trace are its timed region
 PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d {d}/{n} -o {n} -- "
            "python bench.py --steps 2 --warmup 1 --no-cpu --no-forms --calib-copy")
 
@@ -62,6 +63,13 @@ def kernel_stats(d):
         out.append((r["Name"], int(r["Calls"]), float(r["TotalDurationNs"]), float(r["AverageNs"]),
                     float(r["Percentage"])))
     return out
+
+
+def trace_durations(d):
+    rows = _csv(os.path.join(d, "kt", "**", "*kernel_trace.csv"))
+    rows = [r for r in rows if CHUNK in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    return [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
 
 
 def counter_per_dispatch(d, sub, counter):
@@ -105,8 +113,14 @@ def main():
         lines.append(f"  {n[:60]:60s} {c:6d} {t:14.0f} {av:12.0f} {pc:7.2f}")
     if chunk_avg:
         av = chunk_avg[0][3]
-        lines += ["", f"chunk kernel average: {av / 1e6:.4f} ms -> algorithmic {abytes / (av * 1e-9) / 1e9:.1f} GB/s "
-                  f"({abytes:.0f} B per launch)"]
+        dur = trace_durations(a.dir)
+        timed = dur[-TIMED_STEPS:]
+        tav = statistics.mean(timed)
+        lines += ["", f"chunk kernel average over all {len(dur)} dispatches: {av / 1e6:.4f} ms",
+                  f"chunk kernel average over the last {len(timed)} dispatches (bench.py's timed steps): "
+                  f"{tav / 1e6:.4f} ms -> algorithmic {abytes / (tav * 1e-9) / 1e9:.1f} GB/s "
+                  f"({abytes:.0f} B per launch)",
+                  "per-dispatch durations (ms): " + " ".join(f"{x / 1e6:.3f}" for x in dur)]
     with open(os.path.join(PROFILES, f"chunk_kernel_{w.name}.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
