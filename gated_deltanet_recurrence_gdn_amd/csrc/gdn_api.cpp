@@ -24,6 +24,8 @@ struct gdn_ctx {
     std::string err;
     float *scratch = nullptr;  // two fp32 [B, max_T, H, d_v] partials for the bidirectional form
     size_t scratch_bytes = 0;
+    uint16_t *tm = nullptr;    // per-chunk triangular inverses of the MFMA chunked kernel
+    long long tm_chunks = 0;   // their capacity: directions x B x H x ceil(max_T / 64)
 };
 
 namespace {
@@ -195,8 +197,15 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
 
     size_t scratch_bytes = 0;
     if (c.flags & GDN_FLAG_BIDI) scratch_bytes = 2 * (size_t)c.B * (size_t)c.max_T * c.H * c.d_v * sizeof(float);
+    // The MFMA chunked kernel (bf16 I/O, chunk 64, d_k and d_v >= 32) forms each
+    // chunk's triangular inverse in a pass of its own and reads it back.
+    long long tm_chunks = 0;
+    if (gdn::chunk_mfma_supported(64, c.d_k, c.d_v, c.io_dtype == GDN_BF16))
+        tm_chunks = ((c.flags & GDN_FLAG_BIDI) ? 2LL : 1LL) * c.B * c.H * ((c.max_T + 63) / 64);
+    const size_t tm_bytes = gdn::chunk_mfma_tm_bytes(tm_chunks);
 
     float *scratch = nullptr;
+    uint16_t *tm = nullptr;
     if (c.device >= 0) {
         int n = 0;
         hipError_t e = hipGetDeviceCount(&n);
@@ -221,15 +230,28 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
                                    scratch_bytes, hipGetErrorString(e));
             }
         }
+        if (tm_bytes) {
+            DeviceGuard g(c.device);
+            e = hipMalloc(reinterpret_cast<void **>(&tm), tm_bytes);
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                if (scratch) (void)hipFree(scratch);
+                return fail_create(GDN_ERR_OOM, "hipMalloc(%zu bytes) for the per-chunk inverses: %s", tm_bytes,
+                                   hipGetErrorString(e));
+            }
+        }
     }
     gdn_ctx *h = new (std::nothrow) gdn_ctx;
     if (!h) {
         if (scratch) (void)hipFree(scratch);
+        if (tm) (void)hipFree(tm);
         return fail_create(GDN_ERR_OOM, "out of host memory");
     }
     h->cfg = c;
     h->scratch = scratch;
     h->scratch_bytes = scratch_bytes;
+    h->tm = tm;
+    h->tm_chunks = tm ? tm_chunks : 0;
     *out_h = h;
     g_create_err.clear();
     return GDN_OK;
@@ -237,9 +259,10 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
 
 void gdn_free(gdn_handle h) {
     if (!h) return;
-    if (h->scratch) {
+    if (h->scratch || h->tm) {
         DeviceGuard g(h->cfg.device);
-        (void)hipFree(h->scratch);
+        if (h->scratch) (void)hipFree(h->scratch);
+        if (h->tm) (void)hipFree(h->tm);
     }
     delete h;
 }
@@ -296,6 +319,7 @@ int gdn_forward(gdn_handle h, const void *q, const void *k, const void *v, const
     a.state_in = state_in; a.state_out = state_out; a.out = out; a.partial = nullptr;
     a.B = c.B; a.H = c.H; a.dk = c.d_k; a.dv = c.d_v; a.T = T;
     a.io_bf16 = c.io_dtype == GDN_BF16; a.reverse = 0; a.out_mode = gdn::OUT_STORE;
+    a.tm = h->tm; a.tm_chunks = h->tm_chunks;
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
     hipError_t e = (C == 1) ? gdn::launch_scan(a, s) : gdn::launch_chunk(a, C, s);
     return launch_status(h, e, C == 1 ? "scan" : "chunked");
@@ -336,6 +360,7 @@ int gdn_forward_bidi(gdn_handle h, const void *q, const void *k, const void *v, 
     a.partial_rev = h->scratch + n_out;
     a.B = c.B; a.H = c.H; a.dk = c.d_k; a.dv = c.d_v; a.T = T;
     a.io_bf16 = c.io_dtype == GDN_BF16;
+    a.tm = h->tm; a.tm_chunks = h->tm_chunks;
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
     // Both directions in one launch, each into its own fp32 partial (the reverse
     // direction walks the tokens from T-1 down, chunk grid anchored there), then

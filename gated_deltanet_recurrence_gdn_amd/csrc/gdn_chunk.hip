@@ -15,44 +15,42 @@
 // sglang SANA-WM record names its Triton kernel cam_scan_bidi_chunkwise).  Every
 // C x C and C x d product runs on MFMA (bf16 operands, fp32 accumulation).
 //
-// Parallel decomposition.  Rows of S are independent, so a block owns one
-// (b, h) and a 32-wide tile of d_v and walks the head's chunks in order.  The
-// S-independent per-chunk work (decay factors, Gram products, the triangular
-// inverse) is recomputed by each d_v tile of a head: that costs MFMA time, not
-// HBM traffic, because the tiles of a head are placed on one XCD and share q/k
-// through its L2, and it buys the CU count the sequential chunk chain needs.
+// Two kernels per call.
 //
-// Roles.  Eight waves; waves w and w + 4 share a SIMD, and the pairs are chosen
-// to even out the SIMDs' work.  One workgroup barrier per chunk period.  In
-// period c:
-//   wave 0     the state chain of chunk c, alone on its SIMD.  S^T (d_k x 32)
-//              lives in fp32 MFMA accumulators for the whole call; X = K S^T,
-//              R, N = Tm R and the update S^T = gam_{C-1} S^T + K^T N~ hand their
-//              results from one product to the next in registers: a 32x32
-//              accumulator becomes the next product's bf16 operand with one
-//              v_permlane32_swap per two rows (the 32x32x16 A and B operands
-//              share one lane layout), so the chain has no barrier and no LDS
-//              round trip of its own.  It publishes bf16 copies of S (for the
-//              next period's outputs) and of N (behind an LDS flag, for this
-//              period's outputs).
-//   waves 6, 3 outputs of chunk c, one 32-token half each: P of the half's query
-//              rows in registers (formed while the chain works on N), then
-//              O^T = gam .* (S Q^T) + N^T P^T, written as 8-byte row segments.
-//   waves 1, 2, 5  chunk c+1: K rows 0-31, K rows 32-63 and Q rows 0-31
-//              (HBM -> registers -> LDS); the diagonal 32x32 blocks of A and their
-//              16x16 diagonal Tm blocks (fp32 substitution in registers) from the
-//              K waves' own rows, the off-diagonal block A(1,0), and the other Tm
-//              blocks by 16x16x16 MFMA, with LDS counters as their only syncs.
-//   wave 4     Q rows 32-63 of chunk c+1 into LDS (memory operations only,
-//              beside the chain).
-//   wave 7     gate vectors of chunk c+2: float64 prefix sum of log2 a (DPP
-//              within 16-lane rows, then the row carries), 2^g, b 2^g,
-//              2^{g_last - g}, b, and the factors of the off-diagonal 32x32
-//              block; b_t v_t of chunk c+1 (fp32, d_v-major) for R.
-// Global loads run two periods ahead (K/Q/V of chunk c+3, gates of c+4, in
-// alternating register sets), so their latency hides behind two periods; a
-// register set is refilled right after it has been stored to LDS, and no
-// product reads it, so no wait on an in-flight load lands inside a period.
+// tm_kernel (throughput): Tm depends only on K and the gates, so it is formed
+// once per (direction, b, h, chunk) -- one block each, all chunks in parallel --
+// and written as bf16 in exactly the register order in which the state chain
+// uses it as an MFMA operand (6 KiB per chunk).  That costs extra HBM traffic
+// (K read again, Tm written and read back) and takes the Gram products, the
+// decay epilogues and the triangular inverse off the sequential path, where
+// every d_v tile of a head would otherwise redo them.
+//
+// chunk_kernel (sequential over chunks): rows of S are independent, so a block
+// owns one (b, h) and a 32-wide tile of d_v and walks the head's chunks in
+// order.  The tiles of a head are placed on one XCD and share q/k/Tm through its
+// L2.  Eight waves with fixed roles; waves w and w + 4 share a SIMD; one
+// workgroup barrier per chunk period.  In period c:
+//   waves 0, 1  the state chain of chunk c, 16 d_v columns each.  S^T (d_k x 16)
+//               lives in fp32 accumulators of 16x16x32 MFMAs for the whole call.
+//               X = K S^T, R, N = Tm R and S^T = gam_{C-1} S^T + K^T N~ hand their
+//               results from one product to the next in registers with no lane
+//               exchange: a 16x16 accumulator holds rows 4(l/16) .. +3 of column
+//               l % 16, and two of them side by side are one k-step of a B
+//               operand if the k index is permuted (slots 0-3 = rows 4g .. 4g+3 of
+//               the first block, slots 4-7 = the same rows of the second); the A
+//               operand is read from LDS (or Tm from HBM) under the same
+//               permutation.  Each publishes its columns of N (behind an LDS
+//               counter) and a bf16 copy of its S columns for the outputs.
+//   waves 2, 3  outputs of chunk c, one 32-token half each: P of the half's query
+//               rows in registers (formed while the chain works on N), then
+//               O^T = gam .* (S Q^T) + N^T P^T, written as 8-byte row segments.
+//   waves 4, 5  K and Q of chunk c+1 (HBM -> registers -> LDS), loaded in
+//               period c-2 (two register sets alternate).
+//   wave 6      gate vectors of chunk c+2: float64 prefix sum of log2 a (DPP
+//               within 16-lane rows, then the row carries), 2^g, b 2^g,
+//               2^{g_last - g}, b, and the factors of the off-diagonal 32x32
+//               block.
+//   wave 7      b_t v_t of chunk c+1 (fp32, d_v-major) for R.
 //
 // Decay numerics: log2 a is accumulated in float64 (log2 a is clamped at
 // -200, and 2^-200 is 0 in fp32, so a = 0 makes every factor across that token
@@ -75,48 +73,24 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;     // chunk length
-constexpr int NT = 512;   // threads per block: 8 waves
+constexpr int NT = 512;   // threads per block of the chunk kernel: 8 waves
 constexpr int DVT = 32;   // d_v columns per block
 constexpr int LC = C + 8; // padded bf16 row pitch of C-long rows
 constexpr int SPIN_LIMIT = 1 << 20;  // bound on any LDS-flag wait (never reached in a correct run)
 
-struct ChunkParams {
-    const uint16_t *q, *k, *v;
-    const float *beta, *decay;
-    const float *state_in;
-    float *state_out;
-    void *out;
-    float *partial, *partial_rev;
-    long long T;
-    int H, dv, ntile, nblk_dir;
-    int reverse, out_mode, xcd_remap, both_dirs;
-    float scale;
-};
-
-template <int DK>
-struct __align__(16) Smem {
-    static constexpr int LK = DK + 8;  // padded bf16 row pitch of d_k-long rows
-    uint16_t Ks[2][C][LK];   // K, token-major (chunk parity)
-    uint16_t Qs[2][C][LK];   // Q, token-major
-    float bVt[2][DVT][C + 4];  // b_t v_t of the d_v tile, fp32, [d_v][token]
-    uint16_t Sb[2][DVT][LK]; // bf16 state tile at the start of a chunk, [d_v][d_k]
-    uint16_t Nt[DVT][LC];    // N^T of the current chunk
-    uint16_t Tb[2][C][LC];   // Tm, row-major, zero above the diagonal
-    uint16_t Ab[C][LC];      // A (its off-diagonal 16x16 blocks are read)
-    float g[3][C];           // cumulative log2 decay (summed in float64), chunk mod 3
-    float bet[3][C];         // b (0 on padding)
-    float gam[3][C];         // 2^{g_i}
-    float bg[3][C];          // b_i 2^{g_i}
-    float glast[3][C];       // 2^{g_{C-1} - g_i}
-    float xf[3][C];          // 2^{g_31 - g_j} (j < 32), 2^{g_i - g_31} (i >= 32): both <= 1
-    int nflag;               // chunks whose N^T has been published
-    int kctr;                // K row blocks stored (one arrival per K wave and period)
-    int tctr;                // A blocks and diagonal Tm blocks ready (three arrivals per period)
-    int stuck;               // set once any wait ran out; later waits return at once
-};
+// Tm in chain operand order: operand o = (token block nb, k-step ks) of N = Tm R
+// for (nb, ks) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1) -- the blocks above the
+// diagonal are zero and never stored.  Lane l of operand o holds
+// Tm[16 nb + l%16][32 ks + 4 (l/16) + 0..3] and Tm[16 nb + l%16][32 ks + 16 + 4 (l/16) + 0..3].
+constexpr int TM_OPS = 6;
+constexpr int TM_ELEMS = TM_OPS * 64 * 8;  // bf16 per chunk
+__host__ __device__ constexpr int tm_op(int nb, int ks) { return nb < 2 ? nb : 2 + 2 * (nb - 2) + ks; }
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16k32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4_t mfma16(s16x4_t a, s16x4_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -153,6 +127,13 @@ __device__ __forceinline__ s16x4_t pack4s(float a, float b, float c, float d) {
     __builtin_memcpy(&r, &u, 8);
     return r;
 }
+__device__ __forceinline__ s16x4_t pack4s(const f32x4_t &v) { return pack4s(v[0], v[1], v[2], v[3]); }
+__device__ __forceinline__ bf16x8_t join_u2(uint2 a, uint2 b) {
+    const uint4 w = make_uint4(a.x, a.y, b.x, b.y);
+    bf16x8_t r;
+    __builtin_memcpy(&r, &w, 16);
+    return r;
+}
 __device__ __forceinline__ f32x16_t zero16() {
     f32x16_t z;
 #pragma unroll
@@ -167,62 +148,6 @@ __device__ __forceinline__ f32x4_t zero4() {
 }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// A 32x32x16 accumulator holds row 8q + 4h + m of its column (lane % 32) in
-// register 4q + m of lane half h = lane / 32.  The A and B operands of the same
-// instruction hold, in lane half h, the 8 consecutive k-rows 8h .. 8h + 7 of
-// row/column lane % 32.  So the rows 16 KK .. 16 KK + 15 of an accumulator
-// become one k-step of an operand (rows as k, the accumulator's columns as the
-// operand's rows/columns) by exchanging 4 rows between the lane halves:
-// v_permlane32_swap swaps the upper half of its first operand with the lower
-// half of its second.
-// x = rows 16KK + 4h + 0..3 and y = rows 16KK + 8 + 4h + 0..3, already packed to bf16.
-__device__ __forceinline__ bf16x8_t packed_to_op(uint2 x, uint2 y) {
-    const auto s0 = __builtin_amdgcn_permlane32_swap(x.x, y.x, false, false);
-    const auto s1 = __builtin_amdgcn_permlane32_swap(x.y, y.y, false, false);
-    const uint4 w = make_uint4(s0[0], s1[0], s0[1], s1[1]);
-    bf16x8_t r;
-    __builtin_memcpy(&r, &w, 16);
-    return r;
-}
-template <int KK>
-__device__ __forceinline__ bf16x8_t acc_to_op(const f32x16_t &a) {
-    return packed_to_op(make_uint2(pack_bf16x2(a[8 * KK + 0], a[8 * KK + 1]), pack_bf16x2(a[8 * KK + 2], a[8 * KK + 3])),
-                        make_uint2(pack_bf16x2(a[8 * KK + 4], a[8 * KK + 5]), pack_bf16x2(a[8 * KK + 6], a[8 * KK + 7])));
-}
-
-// Off-diagonal blocks of block column CB of Tm = (I + A)^{-1}, walking down:
-//   T_rc = -T_rr * sum_{k=c}^{r-1} A_rk T_kc   (16x16 blocks, bf16 16x16x16 MFMA).
-// The diagonal blocks are already in Tb; the column's blocks are passed from one
-// product to the next in registers (accumulator layout == B-operand layout).
-// All A and T_rr operands are read before any block is written.
-template <int CB>
-__device__ __forceinline__ void tm_column(uint16_t (*Tb)[LC], const uint16_t (*Ab)[LC], int l16, int g16) {
-    s16x4_t tcol[4];
-    s16x4_t aop[4][4];  // aop[rb][kb] = A_rb,kb for CB <= kb < rb
-    s16x4_t top[4];     // top[rb] = T_rb,rb
-    tcol[CB] = lds_tr(&Tb[16 * CB + 4 * g16 + (l16 >> 2)][16 * CB + 4 * (l16 & 3)]);
-#pragma unroll
-    for (int rb = CB + 1; rb < 4; ++rb) {
-        top[rb] = lds8(&Tb[16 * rb + l16][16 * rb + 4 * g16]);
-#pragma unroll
-        for (int kb = CB; kb < rb; ++kb) aop[rb][kb] = lds8(&Ab[16 * rb + l16][16 * kb + 4 * g16]);
-    }
-    f32x4_t tout[4];
-#pragma unroll
-    for (int rb = CB + 1; rb < 4; ++rb) {
-        f32x4_t y = zero4();
-#pragma unroll
-        for (int kb = CB; kb < rb; ++kb) y = mfma16(aop[rb][kb], tcol[kb], y);
-        const f32x4_t t = mfma16(top[rb], pack4s(y[0], y[1], y[2], y[3]), zero4());
-        tcol[rb] = pack4s(-t[0], -t[1], -t[2], -t[3]);
-        tout[rb] = t;
-    }
-#pragma unroll
-    for (int rb = CB + 1; rb < 4; ++rb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Tb[16 * rb + 4 * g16 + r][16 * CB + l16] = (uint16_t)f32_to_bf16_bits(-tout[rb][r]);
-}
-
 // Bounded waits on LDS counters.  In a correct run every wait ends within a
 // chunk period; the bound (and the sticky `stuck` flag, which makes every later
 // wait return at once) only guarantees that the kernel always terminates.
@@ -234,11 +159,8 @@ __device__ __forceinline__ void wait_at_least(int *ctr, int target, int *stuck) 
     }
     __hip_atomic_store(stuck, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void publish(int *ctr, int value, int lane) {
-    // release: this wave's earlier LDS writes are complete before the counter moves
-    if (lane == 0) __hip_atomic_store(ctr, value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
 __device__ __forceinline__ void arrive(int *ctr, int lane) {
+    // release: this wave's earlier LDS writes are complete before the counter moves
     if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
@@ -270,301 +192,24 @@ struct Ctx {
     }
 };
 
-// One wave's 32-row block of K or Q (rows 32 (role & 1) .. + 31 of K for roles
-// 0-1, of Q for roles 2-3), loaded row-coalesced: DK / 8 lanes per row, each
-// with 8 consecutive columns, 512 / DK rows per load instruction, so every load
-// reads whole rows and touches only the cache lines those rows span.
-template <int DK>
-struct RowBlock {
-    static constexpr int LPR = DK / 8;         // lanes per row
-    static constexpr int RPL = 64 / LPR;       // rows per load
-    static constexpr int NLD = 32 / RPL;       // loads per 32 rows
-    bf16x8_t r[NLD];
+// Row j of chunk c of a token-major tensor with `stride` elements per token:
+// one 64-bit base per chunk, then a 32-bit signed offset per row (clamped to the
+// chunk's last token as in Ctx::tok_clamped).
+struct ChunkRows {
+    const uint16_t *base;  // token 0 of the chunk
+    int step;              // +stride, or -stride when walking backwards
+    int last;              // ntok - 1
+    __device__ const uint16_t *row(int j) const { return base + (long long)((j < last ? j : last) * step); }
 };
-
-// Loads are unconditional: rows past the end of a final short chunk re-read
-// token n-1 (finite data; those tokens carry b = 0 and a = 1, so every product
-// they enter is multiplied by 0 or never stored).  Conditional loads into
-// zeroed registers would make the compiler wait for all earlier loads.
-template <int DK>
-__device__ __forceinline__ RowBlock<DK> load_block(const Ctx &x, int c, int role, int lane) {
-    using RB = RowBlock<DK>;
-    RB d;
-    const uint16_t *base = (role < 2) ? x.k : x.q;
-    const int r0 = 32 * (role & 1) + lane / RB::LPR;
-    const int col = 8 * (lane % RB::LPR);
-#pragma unroll
-    for (int s = 0; s < RB::NLD; ++s)
-        d.r[s] = *reinterpret_cast<const bf16x8_t *>(base + (size_t)x.tok_clamped(c, r0 + RB::RPL * s) * x.rs + col);
-    return d;
+__device__ __forceinline__ ChunkRows chunk_rows(const Ctx &x, const uint16_t *p, int c, int stride) {
+    ChunkRows r;
+    r.base = p + x.tok(c, 0) * stride;
+    r.step = x.reverse ? -stride : stride;
+    r.last = x.ntok(c) - 1;
+    return r;
 }
 
-// The same block into a token-major [C][LK] LDS buffer.
-template <int DK>
-__device__ __forceinline__ void store_block(uint16_t (*dst)[DK + 8], const RowBlock<DK> &blk, int role, int lane) {
-    using RB = RowBlock<DK>;
-    const int r0 = 32 * (role & 1) + lane / RB::LPR;
-    const int col = 8 * (lane % RB::LPR);
-#pragma unroll
-    for (int s = 0; s < RB::NLD; ++s) *reinterpret_cast<bf16x8_t *>(&dst[r0 + RB::RPL * s][col]) = blk.r[s];
-}
-
-// ---- wave 0: the state chain ------------------------------------------------
-template <int DK, bool BF16>
-struct Chain {
-    static constexpr int NKS = DK / 16;  // k-steps over d_k
-    static constexpr int NSB = DK / 32;  // 32-row blocks of S^T
-    f32x16_t sacc[NSB];                  // S^T: d_k rows 32*rb + .., d_v column lane % 32
-    bf16x8_t sop[NKS];                   // bf16 S^T as the B operand of X = K S^T
-
-    __device__ __forceinline__ void publish_state(Smem<DK> &sm, int slot, int lane) {
-        const int l32 = lane & 31, hi = lane >> 5;
-#pragma unroll
-        for (int rb = 0; rb < NSB; ++rb) {
-            uint2 w[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                w[q] = pack4(sacc[rb][4 * q], sacc[rb][4 * q + 1], sacc[rb][4 * q + 2], sacc[rb][4 * q + 3]);
-                *reinterpret_cast<uint2 *>(&sm.Sb[slot][l32][32 * rb + 8 * q + 4 * hi]) = w[q];
-            }
-            sop[2 * rb] = packed_to_op(w[0], w[1]);
-            sop[2 * rb + 1] = packed_to_op(w[2], w[3]);
-        }
-    }
-
-    __device__ __forceinline__ void init(const ChunkParams &p, Smem<DK> &sm, size_t sbase, int lane) {
-        const int hi = lane >> 5;
-#pragma unroll
-        for (int rb = 0; rb < NSB; ++rb) {
-            sacc[rb] = zero16();
-            if (p.state_in) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 s4 = *reinterpret_cast<const float4 *>(p.state_in + sbase + 32 * rb + 8 * q + 4 * hi);
-                    sacc[rb][4 * q + 0] = s4.x; sacc[rb][4 * q + 1] = s4.y;
-                    sacc[rb][4 * q + 2] = s4.z; sacc[rb][4 * q + 3] = s4.w;
-                }
-            }
-        }
-        publish_state(sm, 0, lane);
-    }
-
-    __device__ __forceinline__ void step(Smem<DK> &sm, int c, int lane) {
-        const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g16 = lane >> 4;
-        const int s2 = c & 1, s3 = c % 3;
-        // X = K S^T  (tokens x d_v), two 32-token blocks
-        f32x16_t xacc[2] = {zero16(), zero16()};
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-            xacc[0] = mfma32(lds16(&sm.Ks[s2][l32][16 * s + 8 * hi]), sop[s], xacc[0]);
-            xacc[1] = mfma32(lds16(&sm.Ks[s2][32 + l32][16 * s + 8 * hi]), sop[s], xacc[1]);
-        }
-        // R = diag(b) V - diag(b gam) X, then as the B operand of N = Tm R
-        bf16x8_t rop[4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int i0 = 32 * i + 8 * q + 4 * hi;
-                const float4 bv = *reinterpret_cast<const float4 *>(&sm.bVt[s2][l32][i0]);
-                const float4 bgm = *reinterpret_cast<const float4 *>(&sm.bg[s3][i0]);
-                xacc[i][4 * q + 0] = fmaf(-bgm.x, xacc[i][4 * q + 0], bv.x);
-                xacc[i][4 * q + 1] = fmaf(-bgm.y, xacc[i][4 * q + 1], bv.y);
-                xacc[i][4 * q + 2] = fmaf(-bgm.z, xacc[i][4 * q + 2], bv.z);
-                xacc[i][4 * q + 3] = fmaf(-bgm.w, xacc[i][4 * q + 3], bv.w);
-            }
-            rop[2 * i] = acc_to_op<0>(xacc[i]);
-            rop[2 * i + 1] = acc_to_op<1>(xacc[i]);
-        }
-        // N = Tm R; Tm is lower triangular: token block i needs keys < 32 (i + 1)
-        f32x16_t nacc[2] = {zero16(), zero16()};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            if (t < 2) nacc[0] = mfma32(lds16(&sm.Tb[s2][l32][16 * t + 8 * hi]), rop[t], nacc[0]);
-            nacc[1] = mfma32(lds16(&sm.Tb[s2][32 + l32][16 * t + 8 * hi]), rop[t], nacc[1]);
-        }
-        // publish N^T for the output waves
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<uint2 *>(&sm.Nt[l32][32 * i + 8 * q + 4 * hi]) =
-                    pack4(nacc[i][4 * q], nacc[i][4 * q + 1], nacc[i][4 * q + 2], nacc[i][4 * q + 3]);
-        publish(&sm.nflag, c + 1, lane);
-        // N~ = diag(G_{C-1,.}) N as the B operand of the update
-        bf16x8_t nop[4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 gl = *reinterpret_cast<const float4 *>(&sm.glast[s3][32 * i + 8 * q + 4 * hi]);
-                nacc[i][4 * q + 0] *= gl.x; nacc[i][4 * q + 1] *= gl.y;
-                nacc[i][4 * q + 2] *= gl.z; nacc[i][4 * q + 3] *= gl.w;
-            }
-            nop[2 * i] = acc_to_op<0>(nacc[i]);
-            nop[2 * i + 1] = acc_to_op<1>(nacc[i]);
-        }
-        // S^T <- gam_{C-1} S^T + K^T N~  (K^T read transposed from the token-major K)
-        const float gl = sm.gam[s3][C - 1];
-#pragma unroll
-        for (int rb = 0; rb < NSB; ++rb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[rb][r] *= gl;
-            const int dcol = 32 * rb + 16 * (g16 & 1) + 4 * (l16 & 3);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int t0 = 16 * t + 8 * hi + (l16 >> 2);
-                const bf16x8_t a = join(lds_tr(&sm.Ks[s2][t0][dcol]), lds_tr(&sm.Ks[s2][t0 + 4][dcol]));
-                sacc[rb] = mfma32(a, nop[t], sacc[rb]);
-            }
-        }
-        publish_state(sm, (c + 1) & 1, lane);
-    }
-
-    __device__ __forceinline__ void finish(const ChunkParams &p, size_t sbase, int lane) {
-        const int hi = lane >> 5;
-        if (!p.state_out) return;
-#pragma unroll
-        for (int rb = 0; rb < NSB; ++rb)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<float4 *>(p.state_out + sbase + 32 * rb + 8 * q + 4 * hi) =
-                    make_float4(sacc[rb][4 * q], sacc[rb][4 * q + 1], sacc[rb][4 * q + 2], sacc[rb][4 * q + 3]);
-    }
-};
-
-// ---- outputs of one 32-token half (query block TB) -----------------------------
-// P of the half's query rows is formed here, in registers, from K and Q in LDS
-// while the chain is still working on N:
-//   TB = 0: P(0,0) = K_a Q_a^T                    (keys 0-31)
-//   TB = 1: P(1,0) = K_a Q_b^T, P(1,1) = K_b Q_b^T  (keys 0-63)
-// as (keys x queries) accumulators, whose rows become the k-steps of the
-// B operand of O^T += N^T P^T.  The same Q operand feeds (S Q^T)^T.
-template <int DK>
-__device__ __forceinline__ void p_diag_epilogue(const Smem<DK> &sm, int s3, f32x16_t &acc, int b, int lane) {
-    // diagonal block b: element (key j, query i) times 2^{g_i - g_j}, kept for j <= i
-    const int l32 = lane & 31, hi = lane >> 5;
-    const float *gg = sm.g[s3];
-    const int i = 32 * b + l32;
-    const float gi = gg[i];
-    float4 gj[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) gj[q] = *reinterpret_cast<const float4 *>(&gg[32 * b + 8 * q + 4 * hi]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int j0 = 32 * b + 8 * q + 4 * hi;
-        const float gjv[4] = {gj[q].x, gj[q].y, gj[q].z, gj[q].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float val = acc[4 * q + e] * exp2_fast(gi - gjv[e]);
-            acc[4 * q + e] = (j0 + e <= i) ? val : 0.f;
-        }
-    }
-}
-
-template <int DK>
-__device__ __forceinline__ void cross_scale(const Smem<DK> &sm, int s3, f32x16_t &acc, float si, int lane) {
-    // keys 0-31 x queries 32-63: G_ij = 2^{g_i - g_31} 2^{g_31 - g_j}; si carries
-    // the query factor (and b_i for A)
-    const int hi = lane >> 5;
-    float4 fj[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) fj[q] = *reinterpret_cast<const float4 *>(&sm.xf[s3][8 * q + 4 * hi]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        acc[4 * q + 0] *= fj[q].x * si;
-        acc[4 * q + 1] *= fj[q].y * si;
-        acc[4 * q + 2] *= fj[q].z * si;
-        acc[4 * q + 3] *= fj[q].w * si;
-    }
-}
-
-template <int DK, bool BF16, int TB>
-__device__ __forceinline__ void output_step(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int c, int lane,
-                                            void *out_b, float *part_b) {
-    constexpr int NKS = DK / 16;
-    const int l32 = lane & 31, hi = lane >> 5;
-    const int s2 = c & 1, s3 = c % 3;
-    const uint16_t *qrow = &sm.Qs[s2][32 * TB + l32][8 * hi];
-    const uint16_t *ka = &sm.Ks[s2][l32][8 * hi];
-    const uint16_t *kb = &sm.Ks[s2][32 + l32][8 * hi];
-    const uint16_t *srow = &sm.Sb[s2][l32][8 * hi];
-    f32x16_t acc = zero16(), p0 = zero16(), p1 = zero16();
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-        const bf16x8_t q = lds16(qrow + 16 * s);
-        acc = mfma32(lds16(srow + 16 * s), q, acc);
-        p0 = mfma32(lds16(ka + 16 * s), q, p0);
-        if constexpr (TB == 1) p1 = mfma32(lds16(kb + 16 * s), q, p1);
-    }
-    // (S Q^T)^T scaled by gam of the query column
-    const int i = 32 * TB + l32;
-    const float gq = sm.gam[s3][i];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] *= gq;
-    // P^T as B operands, k-step t = keys 16 t .. 16 t + 15
-    bf16x8_t pop[4];
-    if constexpr (TB == 0) {
-        p_diag_epilogue(sm, s3, p0, 0, lane);
-        pop[0] = acc_to_op<0>(p0);
-        pop[1] = acc_to_op<1>(p0);
-    } else {
-        cross_scale(sm, s3, p0, sm.xf[s3][i], lane);
-        p_diag_epilogue(sm, s3, p1, 1, lane);
-        pop[0] = acc_to_op<0>(p0);
-        pop[1] = acc_to_op<1>(p0);
-        pop[2] = acc_to_op<0>(p1);
-        pop[3] = acc_to_op<1>(p1);
-    }
-    // + N^T P^T once the chain has published N^T
-    wait_at_least(&sm.nflag, c + 1, &sm.stuck);
-#pragma unroll
-    for (int t = 0; t < 2 * (TB + 1); ++t) acc = mfma32(lds16(&sm.Nt[l32][16 * t + 8 * hi]), pop[t], acc);
-    if (i < x.ntok(c)) {
-        const size_t e0 = (size_t)x.tok(c, i) * x.rsv;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const size_t e = e0 + 8 * q + 4 * hi;
-            const float o0 = acc[4 * q] * p.scale, o1 = acc[4 * q + 1] * p.scale;
-            const float o2 = acc[4 * q + 2] * p.scale, o3 = acc[4 * q + 3] * p.scale;
-            if (p.out_mode == OUT_PARTIAL) {
-                *reinterpret_cast<float4 *>(part_b + e) = make_float4(o0, o1, o2, o3);
-            } else {
-                if constexpr (BF16)
-                    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out_b) + e) = pack4(o0, o1, o2, o3);
-                else
-                    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out_b) + e) = make_float4(o0, o1, o2, o3);
-            }
-        }
-    }
-}
-
-// ---- wave 4: V tiles and gate vectors ----------------------------------------
-struct GateRegs {
-    float b, a;
-};
-
-// The chunk's V tile (64 tokens x 32 d_v), row-coalesced: in w[s], lane l holds
-// token 16 s + l / 4, d_v columns 8 (l % 4) .. + 7.
-struct VRow {
-    u32x4_t w[4];
-};
-__device__ __forceinline__ VRow load_v(const Ctx &x, int c, int lane) {
-    VRow d;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-        d.w[s] = *reinterpret_cast<const u32x4_t *>(x.v + (size_t)x.tok_clamped(c, 16 * s + (lane >> 2)) * x.rsv +
-                                                    8 * (lane & 3));
-    return d;
-}
-__device__ __forceinline__ void load_gates(const Ctx &x, int c, int lane, GateRegs &g) {
-    if (!x.has(c)) return;  // uniform
-    const size_t o = (size_t)x.tok_clamped(c, lane) * x.H;
-    g.b = x.beta[o];
-    g.a = x.decay[o];
-}
-
-// Float64 helpers for the gate prefix sum (64 lanes, lane = token).
+// ---- gate vectors (one lane per token of the chunk) ----------------------------
 template <int CTRL>
 __device__ __forceinline__ double dpp_shr_f64(double x) {  // row_shr:k, 0 shifted in
     const uint64_t u = __double_as_longlong(x);
@@ -592,45 +237,52 @@ __device__ __forceinline__ double prefix_sum64(int lane, double x) {
     return x;
 }
 
-template <int DK>
-__device__ __forceinline__ void gates_compute(const Ctx &x, Smem<DK> &sm, int c, int lane, const GateRegs &gr) {
-    const bool real = lane < x.ntok(c);
-    const float a = real ? gr.a : 1.f;
-    float l2 = __builtin_amdgcn_logf(a);  // log2
-    if (!(l2 > -200.0f)) l2 = -200.0f;    // a = 0: 2^-200 is 0 in fp32
+// The chunk's gate vectors, lane = token.  Both kernels compute them with this
+// one function, so they agree bit for bit.
+struct GateVals {
+    float g;      // cumulative log2 decay (summed in float64)
+    float bet;    // b (0 on padding)
+    float gam;    // 2^{g_i}
+    float bg;     // b_i 2^{g_i}
+    float glast;  // 2^{g_{C-1} - g_i}
+    float xf;     // 2^{g_31 - g_j} (j < 32), 2^{g_i - g_31} (i >= 32): both <= 1
+};
+__device__ __forceinline__ GateVals gate_values(int lane, int ntok, float b, float a) {
+    const bool real = lane < ntok;
+    const float av = real ? a : 1.f;
+    float l2 = __builtin_amdgcn_logf(av);  // log2
+    if (!(l2 > -200.0f)) l2 = -200.0f;     // a = 0: 2^-200 is 0 in fp32
     const double xs = prefix_sum64(lane, (double)l2);
     const double xl = lane_value(xs, 63);
     const double x31 = lane_value(xs, 31);
-    const int s3 = c % 3;
-    sm.xf[s3][lane] = exp2_fast((float)(lane < 32 ? x31 - xs : xs - x31));
-    sm.g[s3][lane] = (float)xs;
-    const float gm = exp2_fast((float)xs);
-    sm.gam[s3][lane] = gm;
-    sm.bg[s3][lane] = real ? gr.b * gm : 0.f;
-    sm.glast[s3][lane] = exp2_fast((float)(xl - xs));
-    sm.bet[s3][lane] = real ? gr.b : 0.f;
+    GateVals r;
+    r.xf = exp2_fast((float)(lane < 32 ? x31 - xs : xs - x31));
+    r.g = (float)xs;
+    r.gam = exp2_fast((float)xs);
+    r.bg = real ? b * r.gam : 0.f;
+    r.glast = exp2_fast((float)(xl - xs));
+    r.bet = real ? b : 0.f;
+    return r;
 }
 
-// ---- waves 1, 2, 5, 6: preparation of the next chunk --------------------------
-// role 0: K rows 0-31 (K_a), 1: K rows 32-63 (K_b), 2: Q rows 0-31, 3: Q rows 32-63.
-// Gram products as (keys x queries):
-//   role 0: A(0,0) = K_a K_a^T      role 1: A(1,1) = K_b K_b^T
-//   role 2: A(1,0) = K_a K_b^T, P(0,0) = K_a Q_a^T
-//   role 3: P(1,0) = K_a Q_b^T, P(1,1) = K_b Q_b^T
-// A(1,0) = b_i (k_i . k_j) G_ij for keys j in 0-31 and queries i in 32-63 (every
-// j < i), from its Gram accumulator, with the separable cross-block factors;
-// written as bf16 to Ab (all of its 16x16 blocks are off-diagonal blocks of A).
+// =============================================================================
+// tm_kernel: Tm = (I + A)^{-1} of every chunk, in chain operand order.
+// =============================================================================
+struct TmParams {
+    const uint16_t *k;
+    const float *beta, *decay;
+    uint16_t *tm;  // [dirs][B][H][nchunks][TM_ELEMS]
+    long long T;
+    int B, H, nchunks, reverse;
+};
+
 template <int DK>
-__device__ __forceinline__ void a_cross_block(Smem<DK> &sm, int cp, f32x16_t acc, int lane) {
-    const int l32 = lane & 31, hi = lane >> 5;
-    const int s3 = cp % 3;
-    const int i = 32 + l32;
-    cross_scale(sm, s3, acc, sm.xf[s3][i] * sm.bet[s3][i], lane);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<uint2 *>(&sm.Ab[i][8 * q + 4 * hi]) =
-            pack4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
-}
+struct __align__(16) TmSmem {
+    uint16_t Ks[C][DK + 8];  // K, token-major
+    uint16_t Tb[C][LC];      // Tm, row-major, zero above the diagonal
+    uint16_t Ab[C][LC];      // A (its off-diagonal 16x16 blocks are read)
+    float g[C], bet[C], xf[C];
+};
 
 // y += a_J * b, where a_J is lane J's value of a within each 16-lane row: one
 // v_fmac_f32 with a DPP row_newbcast source (register arithmetic only; no
@@ -663,13 +315,12 @@ __device__ __forceinline__ void fmac_dpp_fence(const float (&a)[16]) {
 //     m < j), with row j of A taken from lane j of the 16-lane row by a DPP
 //     broadcast folded into the FMA: no LDS traffic and no waits on it.
 template <int DK>
-__device__ __forceinline__ void a_diag_block(Smem<DK> &sm, int cp, const f32x16_t &acc, int kk, int lane) {
+__device__ __forceinline__ void a_diag_block(TmSmem<DK> &sm, const f32x16_t &acc, int kk, int lane) {
     const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15;
-    const int s3 = cp % 3, s2 = cp & 1;
-    const float *gg = sm.g[s3];
+    const float *gg = sm.g;
     const int i = 32 * kk + l32;
     const float gi = gg[i];
-    const float bi = sm.bet[s3][i];
+    const float bi = sm.bet[i];
     float4 gj[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) gj[q] = *reinterpret_cast<const float4 *>(&gg[32 * kk + 8 * q + 4 * hi]);
@@ -720,7 +371,7 @@ __device__ __forceinline__ void a_diag_block(Smem<DK> &sm, int cp, const f32x16_
     const bool blk0 = lane < 16, blk1 = lane >= 48;
     if (blk0 || blk1) {
         const int kb = 2 * kk + (blk1 ? 1 : 0);
-        uint16_t *row = &sm.Tb[s2][16 * kb + l16][16 * kb];
+        uint16_t *row = &sm.Tb[16 * kb + l16][16 * kb];
         *reinterpret_cast<uint4 *>(row) = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
                                                      pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
         *reinterpret_cast<uint4 *>(row + 8) = make_uint4(pack_bf16x2(y[8], y[9]), pack_bf16x2(y[10], y[11]),
@@ -732,57 +383,525 @@ __device__ __forceinline__ void a_diag_block(Smem<DK> &sm, int cp, const f32x16_
     }
 }
 
-// Preparation of chunk cp = it + 1 in period it.
-//   role 0: K rows 0-31 (K_a): A(0,0), its diagonal Tm blocks, Tm block column 0
-//   role 1: K rows 32-63 (K_b): A(1,1), its diagonal Tm blocks, Tm block column 1
-//   role 2: Q rows 0-31 (Q_a): A(1,0) = K_a K_b^T, Tm block column 2
+// A(1,0) = b_i (k_i . k_j) G_ij for keys j in 0-31 and queries i in 32-63 (every
+// j < i), from its Gram accumulator K_a K_b^T (keys x queries), with the
+// separable factors G_ij = 2^{g_i - g_31} 2^{g_31 - g_j} (both <= 1); written as
+// bf16 to Ab (all of its 16x16 blocks are off-diagonal blocks of A).
 template <int DK>
-__device__ __forceinline__ void prep_step(const Ctx &x, Smem<DK> &sm, int it, int role, int lane, int np,
-                                          RowBlock<DK> &blk) {
+__device__ __forceinline__ void a_cross_block(TmSmem<DK> &sm, const f32x16_t &acc, int lane) {
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int i = 32 + l32;
+    const float si = sm.xf[i] * sm.bet[i];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float4 fj = *reinterpret_cast<const float4 *>(&sm.xf[8 * q + 4 * hi]);
+        *reinterpret_cast<uint2 *>(&sm.Ab[i][8 * q + 4 * hi]) =
+            pack4(acc[4 * q] * (fj.x * si), acc[4 * q + 1] * (fj.y * si), acc[4 * q + 2] * (fj.z * si),
+                  acc[4 * q + 3] * (fj.w * si));
+    }
+}
+
+// Off-diagonal blocks of block column CB of Tm = (I + A)^{-1}, walking down:
+//   T_rc = -T_rr * sum_{k=c}^{r-1} A_rk T_kc   (16x16 blocks, bf16 16x16x16 MFMA).
+// The diagonal blocks are already in Tb; the column's blocks are passed from one
+// product to the next in registers (accumulator layout == B-operand layout).
+// All A and T_rr operands are read before any block is written.
+template <int CB>
+__device__ __forceinline__ void tm_column(uint16_t (*Tb)[LC], const uint16_t (*Ab)[LC], int l16, int g16) {
+    s16x4_t tcol[4];
+    s16x4_t aop[4][4];  // aop[rb][kb] = A_rb,kb for CB <= kb < rb
+    s16x4_t top[4];     // top[rb] = T_rb,rb
+    tcol[CB] = lds_tr(&Tb[16 * CB + 4 * g16 + (l16 >> 2)][16 * CB + 4 * (l16 & 3)]);
+#pragma unroll
+    for (int rb = CB + 1; rb < 4; ++rb) {
+        top[rb] = lds8(&Tb[16 * rb + l16][16 * rb + 4 * g16]);
+#pragma unroll
+        for (int kb = CB; kb < rb; ++kb) aop[rb][kb] = lds8(&Ab[16 * rb + l16][16 * kb + 4 * g16]);
+    }
+    f32x4_t tout[4];
+#pragma unroll
+    for (int rb = CB + 1; rb < 4; ++rb) {
+        f32x4_t y = zero4();
+#pragma unroll
+        for (int kb = CB; kb < rb; ++kb) y = mfma16(aop[rb][kb], tcol[kb], y);
+        const f32x4_t t = mfma16(top[rb], pack4s(y[0], y[1], y[2], y[3]), zero4());
+        tcol[rb] = pack4s(-t[0], -t[1], -t[2], -t[3]);
+        tout[rb] = t;
+    }
+#pragma unroll
+    for (int rb = CB + 1; rb < 4; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Tb[16 * rb + 4 * g16 + r][16 * CB + l16] = (uint16_t)f32_to_bf16_bits(-tout[rb][r]);
+}
+
+// One block (4 waves) per (direction, b, h, chunk).
+template <int DK>
+__global__ __launch_bounds__(256) void tm_kernel(TmParams p) {
+    __shared__ TmSmem<DK> sm;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    long long L = blockIdx.x;
+    const int c = (int)(L % p.nchunks);
+    L /= p.nchunks;
+    const int h = (int)(L % p.H);
+    L /= p.H;
+    const int b = (int)(L % p.B);
+    const int dir = (int)(L / p.B);
+
+    Ctx x;
+    x.T = p.T;
+    x.nchunks = p.nchunks;
+    x.rs = p.H * DK;
+    x.rsv = 0;
+    x.H = p.H;
+    x.reverse = p.reverse ^ dir;
+    const size_t tok0 = (size_t)b * p.T * p.H + h;
+    x.q = nullptr;
+    x.v = nullptr;
+    x.k = p.k + tok0 * DK;
+    x.beta = p.beta + tok0;
+    x.decay = p.decay + tok0;
+
+    // 1. K rows 16 wid .. 16 wid + 15 into LDS (row-coalesced: DK / 8 lanes per
+    //    row); wave 3 also forms the gate vectors.
+    {
+        constexpr int LPR = DK / 8, RPL = 64 / LPR, NLD = 16 / RPL;
+        const int r0 = 16 * wid + lane / LPR, col = 8 * (lane % LPR);
+        bf16x8_t r[NLD];
+#pragma unroll
+        for (int s = 0; s < NLD; ++s)
+            r[s] = *reinterpret_cast<const bf16x8_t *>(x.k + (size_t)x.tok_clamped(c, r0 + RPL * s) * x.rs + col);
+#pragma unroll
+        for (int s = 0; s < NLD; ++s) *reinterpret_cast<bf16x8_t *>(&sm.Ks[r0 + RPL * s][col]) = r[s];
+    }
+    if (wid == 3) {
+        const size_t o = (size_t)x.tok_clamped(c, lane) * x.H;
+        const GateVals gv = gate_values(lane, x.ntok(c), x.beta[o], x.decay[o]);
+        sm.g[lane] = gv.g;
+        sm.bet[lane] = gv.bet;
+        sm.xf[lane] = gv.xf;
+    }
+    __syncthreads();
+
+    // 2. the diagonal 32x32 blocks of A with their diagonal 16x16 Tm blocks
+    //    (waves 0, 1) and the off-diagonal block A(1,0) (wave 2)
     constexpr int NKS = DK / 16;
     const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g16 = lane >> 4;
-    const int cp = it + 1;
-    const bool valid = x.has(cp);
-    const int s2 = cp & 1;
-    // 1. this wave's row block of chunk cp -> LDS; the registers then take the
-    //    loads of chunk it + 3 at once (two periods to land), and every product
-    //    below reads its operands from LDS, so nothing here waits on them
-    if (valid) store_block<DK>(role < 2 ? sm.Ks[s2] : sm.Qs[s2], blk, role, lane);
-    if (x.has(it + 3)) blk = load_block<DK>(x, it + 3, role, lane);
-    const uint16_t *ka = &sm.Ks[s2][l32][8 * hi];       // K rows 0-31
-    const uint16_t *kb = &sm.Ks[s2][32 + l32][8 * hi];  // K rows 32-63
-    if (role < 2) {
-        arrive(&sm.kctr, lane);
-        // 2a. K_kk K_kk^T (this wave's own rows, just stored) -> A's diagonal 32x32
-        //     block and the diagonal 16x16 blocks of Tm; needs no other wave's data
-        if (valid) {
-            const uint16_t *kk = role == 0 ? ka : kb;
-            f32x16_t g0 = zero16();
+    const uint16_t *ka = &sm.Ks[l32][8 * hi];
+    const uint16_t *kb = &sm.Ks[32 + l32][8 * hi];
+    if (wid < 2) {
+        const uint16_t *kk = wid == 0 ? ka : kb;
+        f32x16_t g0 = zero16();
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) {
-                const bf16x8_t r = lds16(kk + 16 * s);
-                g0 = mfma32(r, r, g0);
-            }
-            a_diag_block(sm, cp, g0, role, lane);
+        for (int s = 0; s < NKS; ++s) {
+            const bf16x8_t r = lds16(kk + 16 * s);
+            g0 = mfma32(r, r, g0);
         }
-    } else {
-        // 2b. A(1,0) = K_a K_b^T, once both K blocks are in LDS
-        wait_at_least(&sm.kctr, 2 * np, &sm.stuck);
-        if (valid) {
-            f32x16_t g0 = zero16();
+        a_diag_block(sm, g0, wid, lane);
+    } else if (wid == 2) {
+        f32x16_t g0 = zero16();
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) g0 = mfma32(lds16(ka + 16 * s), lds16(kb + 16 * s), g0);
-            a_cross_block(sm, cp, g0, lane);
+        for (int s = 0; s < NKS; ++s) g0 = mfma32(lds16(ka + 16 * s), lds16(kb + 16 * s), g0);
+        a_cross_block(sm, g0, lane);
+    }
+    __syncthreads();
+
+    // 3. the off-diagonal 16x16 blocks of Tm, one block column per wave
+    if (wid == 0) tm_column<0>(sm.Tb, sm.Ab, l16, g16);
+    else if (wid == 1) tm_column<1>(sm.Tb, sm.Ab, l16, g16);
+    else if (wid == 2) tm_column<2>(sm.Tb, sm.Ab, l16, g16);
+    __syncthreads();
+
+    // 4. the six operand blocks, 1 KiB each, one 16-byte store per lane
+    uint16_t *dst = p.tm + ((size_t)((dir * p.B + b) * p.H + h) * p.nchunks + c) * TM_ELEMS;
+    for (int o = wid; o < TM_OPS; o += 4) {
+        const int nb = o < 2 ? o : 2 + (o - 2) / 2;
+        const int ks = o < 2 ? 0 : (o - 2) & 1;
+        const uint16_t *row = &sm.Tb[16 * nb + l16][32 * ks + 4 * g16];
+        const uint2 lo = *reinterpret_cast<const uint2 *>(row);
+        const uint2 up = *reinterpret_cast<const uint2 *>(row + 16);
+        *reinterpret_cast<uint4 *>(dst + (size_t)(o * 64 + lane) * 8) = make_uint4(lo.x, lo.y, up.x, up.y);
+    }
+}
+
+// =============================================================================
+// chunk_kernel: the chunks of a head in order.
+// =============================================================================
+struct ChunkParams {
+    const uint16_t *q, *k, *v;
+    const float *beta, *decay;
+    const float *state_in;
+    float *state_out;
+    void *out;
+    float *partial, *partial_rev;
+    const uint16_t *tm;
+    long long T;
+    int B, H, dv, ntile, nblk_dir;
+    int reverse, out_mode, xcd_remap, both_dirs;
+    float scale;
+};
+
+template <int DK>
+struct __align__(16) Smem {
+    // Row pitch of K, Q and S: reads of one 16-byte segment per lane from 16
+    // consecutive rows (and the chain's transposed reads of K) spread over the banks.
+    static constexpr int LKK = DK + 16;
+    uint16_t Ks[2][C][LKK];  // K, token-major (chunk parity)
+    uint16_t Qs[2][C][LKK];  // Q, token-major
+    float bVt[2][DVT][C + 4];  // b_t v_t of the d_v tile, fp32, [d_v][bv_slot(d_v, token)]
+    uint16_t Sb[2][DVT][LKK];  // bf16 state tile at the start of a chunk, [d_v][d_k]
+    uint16_t Nt[DVT][LC];    // N^T of the current chunk, keys in sdk order
+    float g[3][C];           // gate vectors, chunk mod 3 (GateVals)
+    float bet[3][C];
+    float gam[3][C];
+    float bg[3][C];
+    float glast[3][C];
+    float xf[3][C];
+    int nflag;               // chain-wave arrivals: two per chunk whose N^T is in Nt
+    int stuck;               // set once any wait ran out; later waits return at once
+};
+
+// Column d of bVt holds token t at position t + 16 (d / 8), mod 64: the four
+// 8-column groups that one store instruction writes then start on different
+// banks, and runs of 4 aligned tokens stay aligned.
+__device__ __forceinline__ int bv_slot(int d, int t) { return (t + 16 * (d >> 3)) & 63; }
+
+// ---- waves 0, 1: the state chain, 16 d_v columns each ------------------------
+// Lane l = 16 g + r.  A 16x16 accumulator block holds rows 4g .. 4g + 3 of column
+// r.  Two blocks side by side form one k-step of a B operand with the k index
+// permuted: slot s < 4 is row 4g + s of the first block, slot s >= 4 row
+// 4g + s - 4 of the second.  The matching A operand row r holds, in lane group
+// g, columns 4g .. 4g + 3 of the first 16 and of the second 16 of its 32.
+//
+// The d_k axis of S is stored permuted the same way in reverse: row 4g + m of
+// S^T block db (32-wide group kd = db / 2, h = db % 2) is d_k index
+// 32 kd + 8 g + 4 h + m, so that the eight d_k of one k-step of X = K S^T are
+// consecutive and the A operand is a single 16-byte read of a K row.
+__device__ __forceinline__ int sdk(int db, int g4) { return 32 * (db >> 1) + 8 * g4 + 4 * (db & 1); }
+struct TmOps {
+    bf16x8_t o[TM_OPS];
+};
+
+template <int DK>
+struct Chain16 {
+    static constexpr int NKS = DK / 32;  // k-steps of X over d_k
+    static constexpr int NDB = DK / 16;  // 16-row blocks of S^T
+    f32x4_t sacc[NDB];                   // S^T rows 16 db + 4g + 0..3, column r
+    bf16x8_t sop[NKS];                   // bf16 S^T as the B operand of X = K S^T
+
+    __device__ __forceinline__ void publish_state(Smem<DK> &sm, int slot, int col, int g4) {
+        uint2 w[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            w[db] = pack4(sacc[db][0], sacc[db][1], sacc[db][2], sacc[db][3]);
+            *reinterpret_cast<uint2 *>(&sm.Sb[slot][col][sdk(db, g4)]) = w[db];
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) sop[ks] = join_u2(w[2 * ks], w[2 * ks + 1]);
+    }
+
+    __device__ __forceinline__ void init(const ChunkParams &p, Smem<DK> &sm, size_t sbase, int col, int g4) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            sacc[db] = zero4();
+            if (p.state_in) {
+                const float4 s4 = *reinterpret_cast<const float4 *>(p.state_in + sbase + sdk(db, g4));
+                sacc[db][0] = s4.x; sacc[db][1] = s4.y; sacc[db][2] = s4.z; sacc[db][3] = s4.w;
+            }
+        }
+        publish_state(sm, 0, col, g4);
+    }
+
+    // First half of chunk c: X, R, N; this wave's columns of N^T published.
+    __device__ __forceinline__ void step_n(Smem<DK> &sm, int c, int lane, int col, const TmOps &tm,
+                                           f32x4_t (&nacc)[4]) {
+        const int g4 = lane >> 4, r16 = lane & 15;
+        const int s2 = c & 1, s3 = c % 3;
+        // X = K S^T, four 16-token blocks; k-step ks = d_k 32 ks + 8 g .. + 7
+        f32x4_t xacc[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                xacc[tb] = mfma16k32(lds16(&sm.Ks[s2][16 * tb + r16][32 * ks + 8 * g4]), sop[ks], xacc[tb]);
+        }
+        // R = diag(b) V - diag(b gam) X
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const float4 bv = *reinterpret_cast<const float4 *>(&sm.bVt[s2][col][bv_slot(col, 16 * tb + 4 * g4)]);
+            const float4 bgm = *reinterpret_cast<const float4 *>(&sm.bg[s3][16 * tb + 4 * g4]);
+            xacc[tb][0] = fmaf(-bgm.x, xacc[tb][0], bv.x);
+            xacc[tb][1] = fmaf(-bgm.y, xacc[tb][1], bv.y);
+            xacc[tb][2] = fmaf(-bgm.z, xacc[tb][2], bv.z);
+            xacc[tb][3] = fmaf(-bgm.w, xacc[tb][3], bv.w);
+        }
+        const bf16x8_t rop0 = join(pack4s(xacc[0]), pack4s(xacc[1]));
+        const bf16x8_t rop1 = join(pack4s(xacc[2]), pack4s(xacc[3]));
+        // N = Tm R (Tm lower triangular: token blocks 0, 1 need keys 0-31 only)
+        nacc[0] = mfma16k32(tm.o[tm_op(0, 0)], rop0, zero4());
+        nacc[1] = mfma16k32(tm.o[tm_op(1, 0)], rop0, zero4());
+        nacc[2] = mfma16k32(tm.o[tm_op(2, 0)], rop0, zero4());
+        nacc[3] = mfma16k32(tm.o[tm_op(3, 0)], rop0, zero4());
+        nacc[2] = mfma16k32(tm.o[tm_op(2, 1)], rop1, nacc[2]);
+        nacc[3] = mfma16k32(tm.o[tm_op(3, 1)], rop1, nacc[3]);
+        // publish this wave's columns of N^T for the output waves, keys in the
+        // permuted order of the state's d_k (sdk)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+            *reinterpret_cast<uint2 *>(&sm.Nt[col][sdk(nb, g4)]) =
+                pack4(nacc[nb][0], nacc[nb][1], nacc[nb][2], nacc[nb][3]);
+        arrive(&sm.nflag, lane);
+    }
+
+    // Second half: S^T <- gam_{C-1} S^T + K^T N~, N~ = diag(G_{C-1,.}) N.
+    __device__ __forceinline__ void step_s(Smem<DK> &sm, int c, int lane, int col, f32x4_t (&nacc)[4]) {
+        constexpr int LK = Smem<DK>::LKK;
+        const int g4 = lane >> 4, r16 = lane & 15;
+        const int s2 = c & 1, s3 = c % 3;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const float4 gl = *reinterpret_cast<const float4 *>(&sm.glast[s3][16 * nb + 4 * g4]);
+            nacc[nb][0] *= gl.x; nacc[nb][1] *= gl.y; nacc[nb][2] *= gl.z; nacc[nb][3] *= gl.w;
+        }
+        const bf16x8_t nop0 = join(pack4s(nacc[0]), pack4s(nacc[1]));
+        const bf16x8_t nop1 = join(pack4s(nacc[2]), pack4s(nacc[3]));
+        const float gl = sm.gam[s3][C - 1];
+        // K^T as the A operand: row r of block db is d_k sdk(db, r / 4) + r % 4,
+        // tokens 32 ks + 4g + (0..3, 16..19), read transposed from the token-major K
+        // (lane 4s + j of a 16-lane group addresses token 4g + s, columns
+        // sdk(db, j) .. + 3)
+        const uint16_t *kt = &sm.Ks[s2][4 * g4 + (r16 >> 2)][8 * (r16 & 3)];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) sacc[db][m] *= gl;
+            const uint16_t *p0 = kt + 32 * (db >> 1) + 4 * (db & 1);
+            sacc[db] = mfma16k32(join(lds_tr(p0), lds_tr(p0 + 16 * LK)), nop0, sacc[db]);
+            sacc[db] = mfma16k32(join(lds_tr(p0 + 32 * LK), lds_tr(p0 + 48 * LK)), nop1, sacc[db]);
+        }
+        publish_state(sm, (c + 1) & 1, col, g4);
+    }
+
+    __device__ __forceinline__ void finish(const ChunkParams &p, size_t sbase, int g4) {
+        if (!p.state_out) return;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            *reinterpret_cast<float4 *>(p.state_out + sbase + sdk(db, g4)) =
+                make_float4(sacc[db][0], sacc[db][1], sacc[db][2], sacc[db][3]);
+    }
+};
+
+// Tm operands of chunk c (clamped into range: the load is unconditional and
+// its result unused past the last chunk).
+__device__ __forceinline__ TmOps load_tm(const uint16_t *tm_head, int c, int n, int lane) {
+    const int cc = c < n ? c : n - 1;
+    const uint16_t *src = tm_head + (size_t)cc * TM_ELEMS + (size_t)lane * 8;
+    TmOps t;
+#pragma unroll
+    for (int o = 0; o < TM_OPS; ++o) t.o[o] = *reinterpret_cast<const bf16x8_t *>(src + (size_t)o * 512);
+    return t;
+}
+
+// ---- waves 2, 3: outputs of chunk c ------------------------------------------
+// For a block of 16 queries q: O^T (d_v x queries) = gam .* (S Q_q^T) + N^T P_q^T,
+// with P_q^T (keys x queries) = K Q_q^T .* G for keys j <= query i, as 16x16x32
+// products: S Q^T and K Q^T read rows of S, K and Q with 8 consecutive d_k per
+// lane (one 16-byte read); N^T P^T takes two P accumulator blocks side by side as
+// its B operand (the permuted k order of the chain) and N^T, whose keys the
+// chain stores in the matching order, as its A operand.  Query blocks {0, 3} and
+// {1, 2} need five key blocks each, so the two waves do the same work.
+template <int DK>
+__device__ __forceinline__ void out_products(const Smem<DK> &sm, int s2, int s3, int q, int lane,
+                                             const bf16x8_t (&sa)[2][DK / 32], f32x4_t (&o)[2], f32x4_t (&pk)[4]) {
+    constexpr int NKS = DK / 32;
+    const int g4 = lane >> 4, r16 = lane & 15;
+    bf16x8_t qo[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qo[ks] = lds16(&sm.Qs[s2][16 * q + r16][32 * ks + 8 * g4]);
+    o[0] = zero4();
+    o[1] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) pk[kb] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        o[0] = mfma16k32(sa[0][ks], qo[ks], o[0]);
+        o[1] = mfma16k32(sa[1][ks], qo[ks], o[1]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        if (kb > q) break;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            pk[kb] = mfma16k32(lds16(&sm.Ks[s2][16 * kb + r16][32 * ks + 8 * g4]), qo[ks], pk[kb]);
+    }
+    // gam of the query column on S Q^T; 2^{g_i - g_j} and the causal mask on P^T
+    const int qi = 16 * q + r16;
+    const float gq = sm.gam[s3][qi];
+    const float gi = sm.g[s3][qi];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        o[0][m] *= gq;
+        o[1][m] *= gq;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        if (kb > q) break;
+        const float4 gj = *reinterpret_cast<const float4 *>(&sm.g[s3][16 * kb + 4 * g4]);
+        const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float v = pk[kb][m] * exp2_fast(gi - gjv[m]);
+            pk[kb][m] = (kb < q || 4 * g4 + m <= r16) ? v : 0.f;
         }
     }
-    // 3. off-diagonal blocks of Tm, one block column per wave, once every wave's
-    //    diagonal blocks and A blocks are in LDS
-    arrive(&sm.tctr, lane);
-    wait_at_least(&sm.tctr, 3 * np, &sm.stuck);
-    if (valid) {
-        if (role == 0) tm_column<0>(sm.Tb[s2], sm.Ab, l16, g16);
-        else if (role == 1) tm_column<1>(sm.Tb[s2], sm.Ab, l16, g16);
-        else tm_column<2>(sm.Tb[s2], sm.Ab, l16, g16);
+}
+
+template <int DK>
+__device__ __forceinline__ void out_pn(const Smem<DK> &sm, int q, int lane, f32x4_t (&o)[2], const f32x4_t (&pk)[4]) {
+    const int g4 = lane >> 4, r16 = lane & 15;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        if (2 * t > q) break;
+        const bf16x8_t b = join(pack4s(pk[2 * t]), 2 * t + 1 <= q ? pack4s(pk[2 * t + 1]) : pack4s(zero4()));
+        o[0] = mfma16k32(lds16(&sm.Nt[r16][32 * t + 8 * g4]), b, o[0]);
+        o[1] = mfma16k32(lds16(&sm.Nt[16 + r16][32 * t + 8 * g4]), b, o[1]);
+    }
+}
+
+template <int DK, bool BF16>
+__device__ __forceinline__ void out_store(const Ctx &x, const ChunkParams &p, int c, int q, int lane,
+                                          const f32x4_t (&o)[2], void *out_b, float *part_b) {
+    const int g4 = lane >> 4, qi = 16 * q + (lane & 15);
+    if (qi >= x.ntok(c)) return;
+    const size_t e0 = (size_t)x.tok(c, qi) * x.rsv + 4 * g4;
+#pragma unroll
+    for (int dvb = 0; dvb < 2; ++dvb) {
+        const size_t e = e0 + 16 * dvb;
+        const float o0 = o[dvb][0] * p.scale, o1 = o[dvb][1] * p.scale;
+        const float o2 = o[dvb][2] * p.scale, o3 = o[dvb][3] * p.scale;
+        if (p.out_mode == OUT_PARTIAL) {
+            *reinterpret_cast<float4 *>(part_b + e) = make_float4(o0, o1, o2, o3);
+        } else {
+            if constexpr (BF16)
+                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out_b) + e) = pack4(o0, o1, o2, o3);
+            else
+                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out_b) + e) = make_float4(o0, o1, o2, o3);
+        }
+    }
+}
+
+// Wave W of the two output waves: query blocks {0, 3} (W = 0) or {1, 2} (W = 1).
+template <int DK, bool BF16, int W>
+__device__ __forceinline__ void output_step(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int c, int lane,
+                                            void *out_b, float *part_b) {
+    constexpr int NKS = DK / 32;
+    constexpr int QA = W ? 1 : 0, QB = W ? 2 : 3;
+    const int g4 = lane >> 4, r16 = lane & 15;
+    const int s2 = c & 1, s3 = c % 3;
+    bf16x8_t sa[2][NKS];  // rows of S (two 16-column blocks of d_v) as A operands
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        sa[0][ks] = lds16(&sm.Sb[s2][r16][32 * ks + 8 * g4]);
+        sa[1][ks] = lds16(&sm.Sb[s2][16 + r16][32 * ks + 8 * g4]);
+    }
+    f32x4_t oa[2], ob[2], pa[4], pb[4];
+    out_products(sm, s2, s3, QA, lane, sa, oa, pa);
+    out_products(sm, s2, s3, QB, lane, sa, ob, pb);
+    // + N^T P^T once both chain waves have published their columns of N^T
+    wait_at_least(&sm.nflag, 2 * (c + 1), &sm.stuck);
+    out_pn(sm, QA, lane, oa, pa);
+    out_pn(sm, QB, lane, ob, pb);
+    out_store<DK, BF16>(x, p, c, QA, lane, oa, out_b, part_b);
+    out_store<DK, BF16>(x, p, c, QB, lane, ob, out_b, part_b);
+}
+
+// ---- waves 4, 5: K and Q of a chunk, row-coalesced -----------------------------
+// DK / 8 lanes per row, each with 8 consecutive columns, 512 / DK rows per load
+// instruction, so every load reads whole rows.
+template <int DK>
+struct Rows64 {
+    static constexpr int LPR = DK / 8;    // lanes per row
+    static constexpr int RPL = 64 / LPR;  // rows per load
+    static constexpr int NLD = C / RPL;   // loads per chunk
+    bf16x8_t r[NLD];
+};
+
+// Loads are unconditional per lane: rows past the end of a final short chunk
+// re-read token n-1 (finite data; those tokens carry b = 0 and a = 1, so every
+// product they enter is multiplied by 0 or never stored).
+template <int DK>
+__device__ __forceinline__ Rows64<DK> load_rows(const uint16_t *base, const Ctx &x, int c, int lane) {
+    using RB = Rows64<DK>;
+    RB d;
+    const ChunkRows cr = chunk_rows(x, base, c, x.rs);
+    const int r0 = lane / RB::LPR;
+    const int col = 8 * (lane % RB::LPR);
+#pragma unroll
+    for (int s = 0; s < RB::NLD; ++s)
+        d.r[s] = *reinterpret_cast<const bf16x8_t *>(cr.row(r0 + RB::RPL * s) + col);
+    return d;
+}
+template <int DK, int PITCH>
+__device__ __forceinline__ void store_rows(uint16_t (*dst)[PITCH], const Rows64<DK> &blk, int lane) {
+    using RB = Rows64<DK>;
+    const int r0 = lane / RB::LPR;
+    const int col = 8 * (lane % RB::LPR);
+#pragma unroll
+    for (int s = 0; s < RB::NLD; ++s) *reinterpret_cast<bf16x8_t *>(&dst[r0 + RB::RPL * s][col]) = blk.r[s];
+}
+
+// ---- waves 6, 7: gate vectors; V tiles -----------------------------------------
+struct GateRegs {
+    float b, a;
+};
+
+// The chunk's V tile (64 tokens x 32 d_v), row-coalesced: in w[s], lane l holds
+// token 16 s + l / 4, d_v columns 8 (l % 4) .. + 7.
+struct VRow {
+    u32x4_t w[4];
+};
+__device__ __forceinline__ VRow load_v(const Ctx &x, int c, int lane) {
+    VRow d;
+    const ChunkRows cr = chunk_rows(x, x.v, c, x.rsv);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        d.w[s] = *reinterpret_cast<const u32x4_t *>(cr.row(16 * s + (lane >> 2)) + 8 * (lane & 3));
+    return d;
+}
+// Unconditional (c is clamped into range by the caller), so that the count of
+// loads in flight is the same on every path.
+__device__ __forceinline__ void load_gates(const Ctx &x, int c, int lane, GateRegs &g) {
+    const size_t o = (size_t)x.tok_clamped(c, lane) * x.H;
+    g.b = x.beta[o];
+    g.a = x.decay[o];
+}
+
+template <int DK>
+__device__ __forceinline__ void gates_store(const Ctx &x, Smem<DK> &sm, int c, int lane, const GateRegs &gr) {
+    const GateVals v = gate_values(lane, x.ntok(c), gr.b, gr.a);
+    const int s3 = c % 3;
+    sm.g[s3][lane] = v.g;
+    sm.bet[s3][lane] = v.bet;
+    sm.gam[s3][lane] = v.gam;
+    sm.bg[s3][lane] = v.bg;
+    sm.glast[s3][lane] = v.glast;
+    sm.xf[s3][lane] = v.xf;
+}
+
+template <int DK>
+__device__ __forceinline__ void store_bv(Smem<DK> &sm, int c, const VRow &v, int lane) {
+    const int d0 = 8 * (lane & 3);
+#pragma unroll
+    for (int s_ = 0; s_ < 4; ++s_) {
+        const int t = 16 * s_ + (lane >> 2);
+        const float bt = sm.bet[c % 3][t];
+        float *col = &sm.bVt[c & 1][d0][bv_slot(d0, t)];
+        const uint32_t w4[4] = {v.w[s_].x, v.w[s_].y, v.w[s_].z, v.w[s_].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            col[(2 * e) * (C + 4)] = bt * bf16_lo(w4[e]);
+            col[(2 * e + 1) * (C + 4)] = bt * bf16_hi(w4[e]);
+        }
     }
 }
 
@@ -827,34 +946,41 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
 
     if (tid == 0) {
         sm.nflag = 0;
-        sm.kctr = 0;
-        sm.tctr = 0;
         sm.stuck = 0;
     }
 
-    // Roles by wave (waves w and w + 4 share a SIMD): 0 chain and 4 the Q_b
-    // loader beside it (memory operations only); 1 and 5: preparation roles 0
-    // and 2; 2 and 6: preparation role 1 and the outputs of tokens 0-31; 3 and
-    // 7: the outputs of tokens 32-63 and the gate vectors with b v.  Every role walks the same periods it = -2 .. n-1
-    // (two per loop trip, so that register sets alternate at compile time) with
-    // one barrier each.
+    // Every role walks the same periods it = -2 .. n-1, two per loop trip so that
+    // register sets alternate at compile time, with one barrier each.
     void *out_b = BF16 ? (void *)(reinterpret_cast<uint16_t *>(p.out) + tok0 * p.dv + dv0)
                        : (void *)(reinterpret_cast<float *>(p.out) + tok0 * p.dv + dv0);
     float *part = dir ? p.partial_rev : p.partial;
     float *part_b = part ? part + tok0 * p.dv + dv0 : nullptr;
-    if (wid == 0) {
-        const size_t sbase = ((size_t)(b * p.H + h) * p.dv + dv0 + (lane & 31)) * DK;
-        Chain<DK, BF16> ch;
-        ch.init(p, sm, sbase, lane);
+    if (wid < 2) {
+        // Tm operands of chunk c are loaded in period c-2, right after chunk c-2
+        // has used that register set.
+        const int g4 = lane >> 4;
+        const int col = 16 * wid + (lane & 15);
+        const size_t sbase = ((size_t)(b * p.H + h) * p.dv + dv0 + col) * DK;
+        const uint16_t *tm_head = p.tm + (size_t)((dir * p.B + b) * p.H + h) * n * TM_ELEMS;
+        Chain16<DK> ch;
+        ch.init(p, sm, sbase, col, g4);
+        TmOps tA = load_tm(tm_head, 0, n, lane);
+        TmOps tB = load_tm(tm_head, 1, n, lane);
         __syncthreads();
+        f32x4_t nacc[4];
         for (int it = -2; it < n; it += 2) {
-            if (it >= 0) ch.step(sm, it, lane);
+            if (it >= 0) ch.step_n(sm, it, lane, col, tA, nacc);
+            tA = load_tm(tm_head, it + 2, n, lane);
+            if (it >= 0) ch.step_s(sm, it, lane, col, nacc);
             __syncthreads();
-            if (it + 1 >= 0 && it + 1 < n) ch.step(sm, it + 1, lane);
+            const bool run = it + 1 >= 0 && it + 1 < n;
+            if (run) ch.step_n(sm, it + 1, lane, col, tB, nacc);
+            tB = load_tm(tm_head, it + 3, n, lane);
+            if (run) ch.step_s(sm, it + 1, lane, col, nacc);
             __syncthreads();
         }
-        ch.finish(p, sbase, lane);
-    } else if (wid == 6) {
+        ch.finish(p, sbase, g4);
+    } else if (wid == 2) {
         __syncthreads();
         for (int it = -2; it < n; it += 2) {
             if (it >= 0) output_step<DK, BF16, 0>(x, sm, p, it, lane, out_b, part_b);
@@ -870,68 +996,57 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
             if (it + 1 >= 0 && it + 1 < n) output_step<DK, BF16, 1>(x, sm, p, it + 1, lane, out_b, part_b);
             __syncthreads();
         }
-    } else if (wid == 4) {
-        // Q rows 32-63 of chunk c are stored in period c-1 from register set c&1
-        // (loaded in period c-3).  Memory operations only, beside the chain.
-        RowBlock<DK> qA, qB;
-        if (x.has(0)) qA = load_block<DK>(x, 0, 3, lane);
-        auto store_q = [&](int c, const RowBlock<DK> &q) { store_block<DK>(sm.Qs[c & 1], q, 3, lane); };
+    } else if (wid < 6) {
+        // K (wave 4) or Q (wave 5) of chunk c is stored in period c-1 from register
+        // set c&1, loaded in period c-3.  Memory operations only.  The loads are
+        // unconditional (past the last chunk they re-read it), so that the count
+        // of loads in flight is the same on every path and the wait before a store
+        // covers only the loads of the chunk being stored.
+        const bool is_k = wid == 4;
+        const uint16_t *base = is_k ? x.k : x.q;
+        auto store = [&](int c, const Rows64<DK> &r) {
+            if (is_k) store_rows<DK, Smem<DK>::LKK>(sm.Ks[c & 1], r, lane);
+            else store_rows<DK, Smem<DK>::LKK>(sm.Qs[c & 1], r, lane);
+        };
+        Rows64<DK> rA, rB;
+        rA = load_rows<DK>(base, x, 0, lane);
         __syncthreads();
         for (int it = -2; it < n; it += 2) {
-            if (x.has(it + 1)) store_q(it + 1, qB);
-            if (x.has(it + 3)) qB = load_block<DK>(x, it + 3, 3, lane);
+            if (x.has(it + 1)) store(it + 1, rB);
+            rB = load_rows<DK>(base, x, it + 3 < n ? it + 3 : n - 1, lane);
             __syncthreads();
-            if (x.has(it + 2)) store_q(it + 2, qA);
-            if (x.has(it + 4)) qA = load_block<DK>(x, it + 4, 3, lane);
+            if (x.has(it + 2)) store(it + 2, rA);
+            rA = load_rows<DK>(base, x, it + 4 < n ? it + 4 : n - 1, lane);
             __syncthreads();
         }
-    } else if (wid == 7) {
+    } else if (wid == 6) {
         // Gates of chunk c are computed in period c-2 from register set c&1
-        // (loaded in period c-4); b_t v_t of chunk c is stored in period c-1 from
-        // V register set c&1 (loaded in period c-3), with b_t from the gate slot.
-        GateRegs gA{0.f, 1.f}, gB{0.f, 1.f};
-        VRow vA, vB;
-        if (x.has(0)) vA = load_v(x, 0, lane);
+        // (loaded in period c-4).
+        GateRegs gA, gB;
         load_gates(x, 0, lane, gA);
-        load_gates(x, 1, lane, gB);
-        auto store_bv = [&](int c, const VRow &v) {
-            const int d0 = 8 * (lane & 3);
-#pragma unroll
-            for (int s_ = 0; s_ < 4; ++s_) {
-                const int t = 16 * s_ + (lane >> 2);
-                const float bt = sm.bet[c % 3][t];
-                float *col = &sm.bVt[c & 1][d0][t];
-                const uint32_t w4[4] = {v.w[s_].x, v.w[s_].y, v.w[s_].z, v.w[s_].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    col[(2 * e) * (C + 4)] = bt * bf16_lo(w4[e]);
-                    col[(2 * e + 1) * (C + 4)] = bt * bf16_hi(w4[e]);
-                }
-            }
-        };
+        load_gates(x, 1 < n ? 1 : n - 1, lane, gB);
         __syncthreads();
         for (int it = -2; it < n; it += 2) {
-            if (x.has(it + 1)) store_bv(it + 1, vB);
-            if (x.has(it + 3)) vB = load_v(x, it + 3, lane);
-            if (x.has(it + 2)) gates_compute(x, sm, it + 2, lane, gA);
-            load_gates(x, it + 4, lane, gA);
+            if (x.has(it + 2)) gates_store(x, sm, it + 2, lane, gA);
+            load_gates(x, it + 4 < n ? it + 4 : n - 1, lane, gA);
             __syncthreads();
-            if (x.has(it + 2)) store_bv(it + 2, vA);
-            if (x.has(it + 4)) vA = load_v(x, it + 4, lane);
-            if (x.has(it + 3)) gates_compute(x, sm, it + 3, lane, gB);
-            load_gates(x, it + 5, lane, gB);
+            if (x.has(it + 3)) gates_store(x, sm, it + 3, lane, gB);
+            load_gates(x, it + 5 < n ? it + 5 : n - 1, lane, gB);
             __syncthreads();
         }
     } else {
-        const int role = (wid == 1) ? 0 : (wid == 2) ? 1 : 2;
-        RowBlock<DK> rA, rB;  // row blocks of even / odd chunks
-        if (x.has(0)) rA = load_block<DK>(x, 0, role, lane);
+        // b_t v_t of chunk c is stored in period c-1 from V register set c&1
+        // (loaded in period c-3, unconditionally as for K and Q), with b_t from
+        // the gate slot of chunk c.
+        VRow vA, vB;
+        vA = load_v(x, 0, lane);
         __syncthreads();
-        int np = 0;  // periods walked so far (sync targets)
         for (int it = -2; it < n; it += 2) {
-            prep_step<DK>(x, sm, it, role, lane, ++np, rB);      // prepares chunk it+1 (odd)
+            if (x.has(it + 1)) store_bv(sm, it + 1, vB, lane);
+            vB = load_v(x, it + 3 < n ? it + 3 : n - 1, lane);
             __syncthreads();
-            prep_step<DK>(x, sm, it + 1, role, lane, ++np, rA);  // prepares chunk it+2 (even)
+            if (x.has(it + 2)) store_bv(sm, it + 2, vA, lane);
+            vA = load_v(x, it + 4 < n ? it + 4 : n - 1, lane);
             __syncthreads();
         }
     }
@@ -939,6 +1054,20 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
 
 template <int DK>
 hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
+    const int nchunks = (int)((a.T + C - 1) / C);
+    const int dirs = a.both_dirs ? 2 : 1;
+    const long long ntm = (long long)dirs * a.B * a.H * nchunks;
+    if (!a.tm || ntm > a.tm_chunks || ntm > 0x7fffffffLL) return hipErrorInvalidValue;
+
+    TmParams t;
+    t.k = static_cast<const uint16_t *>(a.k);
+    t.beta = a.beta; t.decay = a.decay;
+    t.tm = a.tm;
+    t.T = a.T; t.B = a.B; t.H = a.H; t.nchunks = nchunks; t.reverse = a.reverse;
+    hipLaunchKernelGGL((tm_kernel<DK>), dim3((unsigned)ntm), dim3(256), 0, stream, t);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
     ChunkParams p;
     p.q = static_cast<const uint16_t *>(a.q);
     p.k = static_cast<const uint16_t *>(a.k);
@@ -946,13 +1075,14 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.beta = a.beta; p.decay = a.decay;
     p.state_in = a.state_in; p.state_out = a.state_out; p.out = a.out;
     p.partial = a.partial; p.partial_rev = a.partial_rev;
-    p.T = a.T; p.H = a.H; p.dv = a.dv;
+    p.tm = a.tm;
+    p.T = a.T; p.B = a.B; p.H = a.H; p.dv = a.dv;
     p.ntile = a.dv / DVT;
     p.nblk_dir = a.B * a.H * p.ntile;
     p.xcd_remap = (p.nblk_dir % 8) == 0;
     p.reverse = a.reverse; p.out_mode = a.out_mode; p.both_dirs = a.both_dirs;
     p.scale = (float)(1.0 / __builtin_sqrt((double)DK));
-    const int nblk = p.nblk_dir * (a.both_dirs ? 2 : 1);
+    const int nblk = p.nblk_dir * dirs;
     hipLaunchKernelGGL((chunk_kernel<DK, true>), dim3(nblk), dim3(NT), 0, stream, p);
     return hipGetLastError();
 }
@@ -963,6 +1093,8 @@ bool chunk_mfma_supported(int C_, int dk, int dv, int io_bf16) {
     const bool dims = (dk == 32 || dk == 64 || dk == 128) && (dv == 32 || dv == 64 || dv == 128);
     return C_ == C && dims && io_bf16;
 }
+
+size_t chunk_mfma_tm_bytes(long long chunks) { return (size_t)chunks * TM_ELEMS * sizeof(uint16_t); }
 
 hipError_t launch_chunk_mfma(const PassArgs &a, int C_, hipStream_t stream) {
     if (!chunk_mfma_supported(C_, a.dk, a.dv, a.io_bf16)) return hipErrorInvalidValue;

@@ -4,6 +4,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
+#include <cstdint>
+
 namespace gdn {
 
 // What a pass does with the per-token outputs o_t.
@@ -31,6 +34,8 @@ struct PassArgs {
     int out_mode;           // OutMode
     int both_dirs;          // 1: one launch runs both directions (OUT_PARTIAL into
                             //    partial and partial_rev), from zero state
+    uint16_t *tm;           // MFMA kernel only: the per-chunk Tm scratch of the handle
+    long long tm_chunks;    // chunk capacity of tm (directions x B x H x chunks)
 };
 
 // Sequential per-token scan (the chunk_len = 1 form).
@@ -38,7 +43,10 @@ hipError_t launch_scan(const PassArgs &a, hipStream_t stream);
 
 // Chunked (UT-transform) form, bf16 MFMA kernel: C = 64, bf16 I/O,
 // d_k, d_v in {32, 64, 128}.
+// It needs PassArgs::tm: chunk_mfma_tm_bytes(n) bytes hold the triangular
+// inverses of n chunks (one per direction, b, h and chunk).
 bool chunk_mfma_supported(int C, int dk, int dv, int io_bf16);
+size_t chunk_mfma_tm_bytes(long long chunks);
 hipError_t launch_chunk_mfma(const PassArgs &a, int C, hipStream_t stream);
 
 // Chunked form, general fp32 kernel: C, d_k, d_v in {16, 32, 64, 128}, fp32 or
