@@ -76,7 +76,6 @@ constexpr int C = 64;     // chunk length
 constexpr int NT = 512;   // threads per block of the chunk kernel: 8 waves
 constexpr int DVT = 32;   // d_v columns per block
 constexpr int LC = C + 8; // padded bf16 row pitch of C-long rows
-constexpr int SPIN_LIMIT = 1 << 20;  // bound on any LDS-flag wait (never reached in a correct run)
 
 // Tm in chain operand order: operand o = (token block nb, k-step ks) of N = Tm R
 // for (nb, ks) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1) -- the blocks above the
@@ -147,22 +146,6 @@ __device__ __forceinline__ f32x4_t zero4() {
     return z;
 }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Bounded waits on LDS counters.  In a correct run every wait ends within a
-// chunk period; the bound (and the sticky `stuck` flag, which makes every later
-// wait return at once) only guarantees that the kernel always terminates.
-__device__ __forceinline__ void wait_at_least(int *ctr, int target, int *stuck) {
-    for (int i = 0; i < SPIN_LIMIT; ++i) {
-        if (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
-        if (__hip_atomic_load(stuck, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return;
-        __builtin_amdgcn_s_sleep(1);
-    }
-    __hip_atomic_store(stuck, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ __forceinline__ void arrive(int *ctr, int lane) {
-    // release: this wave's earlier LDS writes are complete before the counter moves
-    if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
 
 // Per-block constants: base pointers already offset to (b, token 0, h), token
 // strides in elements, and the chunk walk.
@@ -276,11 +259,17 @@ struct TmParams {
     int B, H, nchunks, reverse;
 };
 
+// K is dead once the Gram products are in registers, so Tm and A reuse its
+// space (a barrier separates the last read of K from the first write of Tm / A).
 template <int DK>
 struct __align__(16) TmSmem {
-    uint16_t Ks[C][DK + 8];  // K, token-major
-    uint16_t Tb[C][LC];      // Tm, row-major, zero above the diagonal
-    uint16_t Ab[C][LC];      // A (its off-diagonal 16x16 blocks are read)
+    union {
+        uint16_t Ks[C][DK + 8];  // K, token-major
+        struct {
+            uint16_t Tb[C][LC];  // Tm, row-major, zero above the diagonal
+            uint16_t Ab[C][LC];  // A (its off-diagonal 16x16 blocks are read)
+        };
+    };
     float g[C], bet[C], xf[C];
 };
 
@@ -434,17 +423,19 @@ __device__ __forceinline__ void tm_column(uint16_t (*Tb)[LC], const uint16_t (*A
         for (int r = 0; r < 4; ++r) Tb[16 * rb + 4 * g16 + r][16 * CB + l16] = (uint16_t)f32_to_bf16_bits(-tout[rb][r]);
 }
 
-// One block (4 waves) per (direction, b, h, chunk).
+// One block (4 waves) per (direction, b, h, chunk); up to 8 blocks per CU.
 template <int DK>
-__global__ __launch_bounds__(256) void tm_kernel(TmParams p) {
+__global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
     __shared__ TmSmem<DK> sm;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Head fastest: blocks that run together read the same tokens of all heads,
+    // which lie next to each other in the token-major K.
     long long L = blockIdx.x;
-    const int c = (int)(L % p.nchunks);
-    L /= p.nchunks;
     const int h = (int)(L % p.H);
     L /= p.H;
+    const int c = (int)(L % p.nchunks);
+    L /= p.nchunks;
     const int b = (int)(L % p.B);
     const int dir = (int)(L / p.B);
 
@@ -489,21 +480,21 @@ __global__ __launch_bounds__(256) void tm_kernel(TmParams p) {
     const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g16 = lane >> 4;
     const uint16_t *ka = &sm.Ks[l32][8 * hi];
     const uint16_t *kb = &sm.Ks[32 + l32][8 * hi];
+    f32x16_t g0 = zero16();
     if (wid < 2) {
         const uint16_t *kk = wid == 0 ? ka : kb;
-        f32x16_t g0 = zero16();
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
             const bf16x8_t r = lds16(kk + 16 * s);
             g0 = mfma32(r, r, g0);
         }
-        a_diag_block(sm, g0, wid, lane);
     } else if (wid == 2) {
-        f32x16_t g0 = zero16();
 #pragma unroll
         for (int s = 0; s < NKS; ++s) g0 = mfma32(lds16(ka + 16 * s), lds16(kb + 16 * s), g0);
-        a_cross_block(sm, g0, lane);
     }
+    __syncthreads();  // K is read; Tm and A overwrite it
+    if (wid < 2) a_diag_block(sm, g0, wid, lane);
+    else if (wid == 2) a_cross_block(sm, g0, lane);
     __syncthreads();
 
     // 3. the off-diagonal 16x16 blocks of Tm, one block column per wave
@@ -550,15 +541,13 @@ struct __align__(16) Smem {
     uint16_t Qs[2][C][LKK];  // Q, token-major
     float bVt[2][DVT][C + 4];  // b_t v_t of the d_v tile, fp32, [d_v][bv_slot(d_v, token)]
     uint16_t Sb[2][DVT][LKK];  // bf16 state tile at the start of a chunk, [d_v][d_k]
-    uint16_t Nt[DVT][LC];    // N^T of the current chunk, keys in sdk order
+    uint16_t Nt[2][DVT][LC];  // N^T (chunk parity), keys in sdk order
     float g[3][C];           // gate vectors, chunk mod 3 (GateVals)
     float bet[3][C];
     float gam[3][C];
     float bg[3][C];
     float glast[3][C];
     float xf[3][C];
-    int nflag;               // chain-wave arrivals: two per chunk whose N^T is in Nt
-    int stuck;               // set once any wait ran out; later waits return at once
 };
 
 // Column d of bVt holds token t at position t + 16 (d / 8), mod 64: the four
@@ -612,9 +601,32 @@ struct Chain16 {
         publish_state(sm, 0, col, g4);
     }
 
-    // First half of chunk c: X, R, N; this wave's columns of N^T published.
+    // K^T as the A operands of the update: row r of block db is d_k
+    // sdk(db, r / 4) + r % 4, tokens 32 ks + 4g + (0..3, 16..19), read transposed
+    // from the token-major K (lane 4s + j of a 16-lane group addresses token
+    // 4g + s, columns sdk(db, j) .. + 3).  They do not depend on N, so they are
+    // read before N is formed.
+    struct KtOps {
+        bf16x8_t o[2 * NDB];
+    };
+    __device__ __forceinline__ KtOps load_kt(const Smem<DK> &sm, int s2, int lane) const {
+        constexpr int LK = Smem<DK>::LKK;
+        const int g4 = lane >> 4, r16 = lane & 15;
+        const uint16_t *kt = &sm.Ks[s2][4 * g4 + (r16 >> 2)][8 * (r16 & 3)];
+        KtOps k;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const uint16_t *p0 = kt + 32 * (db >> 1) + 4 * (db & 1);
+            k.o[2 * db] = join(lds_tr(p0), lds_tr(p0 + 16 * LK));
+            k.o[2 * db + 1] = join(lds_tr(p0 + 32 * LK), lds_tr(p0 + 48 * LK));
+        }
+        return k;
+    }
+
+    // First half of chunk c: X, R, N, and S scaled by the chunk's decay; this
+    // wave's columns of N^T published; the K^T operands read.
     __device__ __forceinline__ void step_n(Smem<DK> &sm, int c, int lane, int col, const TmOps &tm,
-                                           f32x4_t (&nacc)[4]) {
+                                           f32x4_t (&nacc)[4], KtOps &kt) {
         const int g4 = lane >> 4, r16 = lane & 15;
         const int s2 = c & 1, s3 = c % 3;
         // X = K S^T, four 16-token blocks; k-step ks = d_k 32 ks + 8 g .. + 7
@@ -625,6 +637,12 @@ struct Chain16 {
             for (int tb = 0; tb < 4; ++tb)
                 xacc[tb] = mfma16k32(lds16(&sm.Ks[s2][16 * tb + r16][32 * ks + 8 * g4]), sop[ks], xacc[tb]);
         }
+        // the decay of S over the chunk, off the X -> N -> S path
+        const float gl = sm.gam[s3][C - 1];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) sacc[db][m] *= gl;
         // R = diag(b) V - diag(b gam) X
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
@@ -637,6 +655,7 @@ struct Chain16 {
         }
         const bf16x8_t rop0 = join(pack4s(xacc[0]), pack4s(xacc[1]));
         const bf16x8_t rop1 = join(pack4s(xacc[2]), pack4s(xacc[3]));
+        kt = load_kt(sm, s2, lane);
         // N = Tm R (Tm lower triangular: token blocks 0, 1 need keys 0-31 only)
         nacc[0] = mfma16k32(tm.o[tm_op(0, 0)], rop0, zero4());
         nacc[1] = mfma16k32(tm.o[tm_op(1, 0)], rop0, zero4());
@@ -648,15 +667,14 @@ struct Chain16 {
         // permuted order of the state's d_k (sdk)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-            *reinterpret_cast<uint2 *>(&sm.Nt[col][sdk(nb, g4)]) =
+            *reinterpret_cast<uint2 *>(&sm.Nt[s2][col][sdk(nb, g4)]) =
                 pack4(nacc[nb][0], nacc[nb][1], nacc[nb][2], nacc[nb][3]);
-        arrive(&sm.nflag, lane);
     }
 
-    // Second half: S^T <- gam_{C-1} S^T + K^T N~, N~ = diag(G_{C-1,.}) N.
-    __device__ __forceinline__ void step_s(Smem<DK> &sm, int c, int lane, int col, f32x4_t (&nacc)[4]) {
-        constexpr int LK = Smem<DK>::LKK;
-        const int g4 = lane >> 4, r16 = lane & 15;
+    // Second half: S^T <- (gam_{C-1} S^T) + K^T N~, N~ = diag(G_{C-1,.}) N.
+    __device__ __forceinline__ void step_s(Smem<DK> &sm, int c, int lane, int col, f32x4_t (&nacc)[4],
+                                           const KtOps &kt) {
+        const int g4 = lane >> 4;
         const int s2 = c & 1, s3 = c % 3;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
@@ -665,19 +683,10 @@ struct Chain16 {
         }
         const bf16x8_t nop0 = join(pack4s(nacc[0]), pack4s(nacc[1]));
         const bf16x8_t nop1 = join(pack4s(nacc[2]), pack4s(nacc[3]));
-        const float gl = sm.gam[s3][C - 1];
-        // K^T as the A operand: row r of block db is d_k sdk(db, r / 4) + r % 4,
-        // tokens 32 ks + 4g + (0..3, 16..19), read transposed from the token-major K
-        // (lane 4s + j of a 16-lane group addresses token 4g + s, columns
-        // sdk(db, j) .. + 3)
-        const uint16_t *kt = &sm.Ks[s2][4 * g4 + (r16 >> 2)][8 * (r16 & 3)];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) sacc[db][m] *= gl;
-            const uint16_t *p0 = kt + 32 * (db >> 1) + 4 * (db & 1);
-            sacc[db] = mfma16k32(join(lds_tr(p0), lds_tr(p0 + 16 * LK)), nop0, sacc[db]);
-            sacc[db] = mfma16k32(join(lds_tr(p0 + 32 * LK), lds_tr(p0 + 48 * LK)), nop1, sacc[db]);
+            sacc[db] = mfma16k32(kt.o[2 * db], nop0, sacc[db]);
+            sacc[db] = mfma16k32(kt.o[2 * db + 1], nop1, sacc[db]);
         }
         publish_state(sm, (c + 1) & 1, col, g4);
     }
@@ -757,14 +766,15 @@ __device__ __forceinline__ void out_products(const Smem<DK> &sm, int s2, int s3,
 }
 
 template <int DK>
-__device__ __forceinline__ void out_pn(const Smem<DK> &sm, int q, int lane, f32x4_t (&o)[2], const f32x4_t (&pk)[4]) {
+__device__ __forceinline__ void out_pn(const Smem<DK> &sm, int slot, int q, int lane, f32x4_t (&o)[2],
+                                       const f32x4_t (&pk)[4]) {
     const int g4 = lane >> 4, r16 = lane & 15;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         if (2 * t > q) break;
         const bf16x8_t b = join(pack4s(pk[2 * t]), 2 * t + 1 <= q ? pack4s(pk[2 * t + 1]) : pack4s(zero4()));
-        o[0] = mfma16k32(lds16(&sm.Nt[r16][32 * t + 8 * g4]), b, o[0]);
-        o[1] = mfma16k32(lds16(&sm.Nt[16 + r16][32 * t + 8 * g4]), b, o[1]);
+        o[0] = mfma16k32(lds16(&sm.Nt[slot][r16][32 * t + 8 * g4]), b, o[0]);
+        o[1] = mfma16k32(lds16(&sm.Nt[slot][16 + r16][32 * t + 8 * g4]), b, o[1]);
     }
 }
 
@@ -791,9 +801,15 @@ __device__ __forceinline__ void out_store(const Ctx &x, const ChunkParams &p, in
 }
 
 // Wave W of the two output waves: query blocks {0, 3} (W = 0) or {1, 2} (W = 1).
-template <int DK, bool BF16, int W>
-__device__ __forceinline__ void output_step(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int c, int lane,
-                                            void *out_b, float *part_b) {
+// The products of chunk c are formed in period c and held in registers; N^T P^T
+// and the stores follow at the start of period c + 1, when N^T of chunk c is in
+// its LDS slot (written by the chain in period c, visible after the barrier).
+struct OutRegs {
+    f32x4_t oa[2], ob[2], pa[4], pb[4];
+};
+
+template <int DK, int W>
+__device__ __forceinline__ void out_products_step(Smem<DK> &sm, int c, int lane, OutRegs &r) {
     constexpr int NKS = DK / 32;
     constexpr int QA = W ? 1 : 0, QB = W ? 2 : 3;
     const int g4 = lane >> 4, r16 = lane & 15;
@@ -804,15 +820,33 @@ __device__ __forceinline__ void output_step(const Ctx &x, Smem<DK> &sm, const Ch
         sa[0][ks] = lds16(&sm.Sb[s2][r16][32 * ks + 8 * g4]);
         sa[1][ks] = lds16(&sm.Sb[s2][16 + r16][32 * ks + 8 * g4]);
     }
-    f32x4_t oa[2], ob[2], pa[4], pb[4];
-    out_products(sm, s2, s3, QA, lane, sa, oa, pa);
-    out_products(sm, s2, s3, QB, lane, sa, ob, pb);
-    // + N^T P^T once both chain waves have published their columns of N^T
-    wait_at_least(&sm.nflag, 2 * (c + 1), &sm.stuck);
-    out_pn(sm, QA, lane, oa, pa);
-    out_pn(sm, QB, lane, ob, pb);
-    out_store<DK, BF16>(x, p, c, QA, lane, oa, out_b, part_b);
-    out_store<DK, BF16>(x, p, c, QB, lane, ob, out_b, part_b);
+    out_products(sm, s2, s3, QA, lane, sa, r.oa, r.pa);
+    out_products(sm, s2, s3, QB, lane, sa, r.ob, r.pb);
+}
+
+template <int DK, bool BF16, int W>
+__device__ __forceinline__ void out_finish_step(const Ctx &x, const Smem<DK> &sm, const ChunkParams &p, int c,
+                                                int lane, OutRegs &r, void *out_b, float *part_b) {
+    constexpr int QA = W ? 1 : 0, QB = W ? 2 : 3;
+    out_pn(sm, c & 1, QA, lane, r.oa, r.pa);
+    out_pn(sm, c & 1, QB, lane, r.ob, r.pb);
+    out_store<DK, BF16>(x, p, c, QA, lane, r.oa, out_b, part_b);
+    out_store<DK, BF16>(x, p, c, QB, lane, r.ob, out_b, part_b);
+}
+
+// Period c of an output wave: finish chunk c - 1, then the products of chunk c.
+template <int DK, bool BF16, int W>
+__device__ __forceinline__ void output_period(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int c, int lane,
+                                              OutRegs &r, void *out_b, float *part_b) {
+    const bool fin = x.has(c - 1), run = x.has(c);
+    if (fin && run) {
+        out_finish_step<DK, BF16, W>(x, sm, p, c - 1, lane, r, out_b, part_b);
+        out_products_step<DK, W>(sm, c, lane, r);
+    } else if (run) {
+        out_products_step<DK, W>(sm, c, lane, r);
+    } else if (fin) {
+        out_finish_step<DK, BF16, W>(x, sm, p, c - 1, lane, r, out_b, part_b);
+    }
 }
 
 // ---- waves 4, 5: K and Q of a chunk, row-coalesced -----------------------------
@@ -944,13 +978,9 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     x.decay = p.decay + tok0;
     const int n = x.nchunks;
 
-    if (tid == 0) {
-        sm.nflag = 0;
-        sm.stuck = 0;
-    }
-
-    // Every role walks the same periods it = -2 .. n-1, two per loop trip so that
-    // register sets alternate at compile time, with one barrier each.
+    // Every role walks the same periods it = -2 .. n (the last one finishes the
+    // outputs of chunk n-1), two per loop trip so that register sets alternate at
+    // compile time, with one barrier each.
     void *out_b = BF16 ? (void *)(reinterpret_cast<uint16_t *>(p.out) + tok0 * p.dv + dv0)
                        : (void *)(reinterpret_cast<float *>(p.out) + tok0 * p.dv + dv0);
     float *part = dir ? p.partial_rev : p.partial;
@@ -968,32 +998,35 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         TmOps tB = load_tm(tm_head, 1, n, lane);
         __syncthreads();
         f32x4_t nacc[4];
-        for (int it = -2; it < n; it += 2) {
-            if (it >= 0) ch.step_n(sm, it, lane, col, tA, nacc);
+        typename Chain16<DK>::KtOps kt;
+        for (int it = -2; it < n + 1; it += 2) {
+            const bool run0 = x.has(it), run1 = x.has(it + 1);
+            if (run0) ch.step_n(sm, it, lane, col, tA, nacc, kt);
             tA = load_tm(tm_head, it + 2, n, lane);
-            if (it >= 0) ch.step_s(sm, it, lane, col, nacc);
+            if (run0) ch.step_s(sm, it, lane, col, nacc, kt);
             __syncthreads();
-            const bool run = it + 1 >= 0 && it + 1 < n;
-            if (run) ch.step_n(sm, it + 1, lane, col, tB, nacc);
+            if (run1) ch.step_n(sm, it + 1, lane, col, tB, nacc, kt);
             tB = load_tm(tm_head, it + 3, n, lane);
-            if (run) ch.step_s(sm, it + 1, lane, col, nacc);
+            if (run1) ch.step_s(sm, it + 1, lane, col, nacc, kt);
             __syncthreads();
         }
         ch.finish(p, sbase, g4);
     } else if (wid == 2) {
+        OutRegs r;
         __syncthreads();
-        for (int it = -2; it < n; it += 2) {
-            if (it >= 0) output_step<DK, BF16, 0>(x, sm, p, it, lane, out_b, part_b);
+        for (int it = -2; it < n + 1; it += 2) {
+            output_period<DK, BF16, 0>(x, sm, p, it, lane, r, out_b, part_b);
             __syncthreads();
-            if (it + 1 >= 0 && it + 1 < n) output_step<DK, BF16, 0>(x, sm, p, it + 1, lane, out_b, part_b);
+            output_period<DK, BF16, 0>(x, sm, p, it + 1, lane, r, out_b, part_b);
             __syncthreads();
         }
     } else if (wid == 3) {
+        OutRegs r;
         __syncthreads();
-        for (int it = -2; it < n; it += 2) {
-            if (it >= 0) output_step<DK, BF16, 1>(x, sm, p, it, lane, out_b, part_b);
+        for (int it = -2; it < n + 1; it += 2) {
+            output_period<DK, BF16, 1>(x, sm, p, it, lane, r, out_b, part_b);
             __syncthreads();
-            if (it + 1 >= 0 && it + 1 < n) output_step<DK, BF16, 1>(x, sm, p, it + 1, lane, out_b, part_b);
+            output_period<DK, BF16, 1>(x, sm, p, it + 1, lane, r, out_b, part_b);
             __syncthreads();
         }
     } else if (wid < 6) {
@@ -1011,7 +1044,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         Rows64<DK> rA, rB;
         rA = load_rows<DK>(base, x, 0, lane);
         __syncthreads();
-        for (int it = -2; it < n; it += 2) {
+        for (int it = -2; it < n + 1; it += 2) {
             if (x.has(it + 1)) store(it + 1, rB);
             rB = load_rows<DK>(base, x, it + 3 < n ? it + 3 : n - 1, lane);
             __syncthreads();
@@ -1026,7 +1059,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         load_gates(x, 0, lane, gA);
         load_gates(x, 1 < n ? 1 : n - 1, lane, gB);
         __syncthreads();
-        for (int it = -2; it < n; it += 2) {
+        for (int it = -2; it < n + 1; it += 2) {
             if (x.has(it + 2)) gates_store(x, sm, it + 2, lane, gA);
             load_gates(x, it + 4 < n ? it + 4 : n - 1, lane, gA);
             __syncthreads();
@@ -1041,7 +1074,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         VRow vA, vB;
         vA = load_v(x, 0, lane);
         __syncthreads();
-        for (int it = -2; it < n; it += 2) {
+        for (int it = -2; it < n + 1; it += 2) {
             if (x.has(it + 1)) store_bv(sm, it + 1, vB, lane);
             vB = load_v(x, it + 3 < n ? it + 3 : n - 1, lane);
             __syncthreads();
