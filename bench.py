@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 FP32_VALU_PEAK_TFS = 157.3   # MI355X fp32 vector (published, packed)
-CHUNK_KERNEL = "chunk_kernel"
+CHUNK_KERNEL = "tm_kernel + chunk_kernel"  # the two launches of one chunked gdn_forward
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -126,7 +126,7 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = ev0.elapsed_time(ev1) / args.steps  # one kernel launch per step
+    kern_ms = ev0.elapsed_time(ev1) / args.steps  # one gdn_forward (its two kernel launches) per step
     ms_per_step = wall * 1000.0 / args.steps
     th = B * H * T
     value = th / (ms_per_step / 1000.0)

@@ -12,10 +12,12 @@ written into the summaries):
 
     python -m gated_deltanet_recurrence_gdn_amd.profile_summary DIR [--workload NAME]
 
+One chunked gdn_forward is two launches, tm_kernel (the per-chunk triangular
+inverses) and chunk_kernel (the sequential pass); both are summarised and summed.
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same counters
 read for the plain 512 MiB device copy that --calib-copy adds to the run: the copy
 reads and writes exactly 512 MiB, so scale = 512 MiB / counter.  The scaled bytes
-per launch of the chunked kernel are written to
+per gdn_forward (both kernels) are written to
 profiles/chunk_kernel_<workload>_traffic.json together with a hash of the kernel
 source, which bench.py checks before reporting them.
 """
@@ -33,6 +35,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 PROFILES = os.path.join(ROOT, "profiles")
 CHUNK = "chunk_kernel"
+TM = "tm_kernel"
+KERNELS = (TM, CHUNK)
 COPY = "copyBuffer"
 COPY_BYTES = 512 * 1024 * 1024
 
@@ -65,9 +69,9 @@ def kernel_stats(d):
     return out
 
 
-def trace_durations(d):
+def trace_durations(d, kernel):
     rows = _csv(os.path.join(d, "kt", "**", "*kernel_trace.csv"))
-    rows = [r for r in rows if CHUNK in r["Kernel_Name"]]
+    rows = [r for r in rows if kernel in r["Kernel_Name"]]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     return [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
 
@@ -79,11 +83,16 @@ def counter_per_dispatch(d, sub, counter):
         if r["Counter_Name"] != counter:
             continue
         vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-    chunk = [v for k, vs in vals.items() if CHUNK in k for v in vs]
     copy = [v for k, vs in vals.items() if COPY in k for v in vs]
-    if not chunk or not copy:
-        raise RuntimeError(f"{counter}: chunk kernel or copy dispatch missing in {d}/{sub}")
-    return statistics.mean(chunk), statistics.mean(copy), len(chunk)
+    if not copy:
+        raise RuntimeError(f"{counter}: copy dispatch missing in {d}/{sub}")
+    per = {}
+    for kn in KERNELS:
+        ks = [v for k, vs in vals.items() if kn in k for v in vs]
+        if not ks:
+            raise RuntimeError(f"{counter}: {kn} dispatch missing in {d}/{sub}")
+        per[kn] = (statistics.mean(ks), len(ks))
+    return per, statistics.mean(copy)
 
 
 def main():
@@ -102,8 +111,7 @@ def main():
     abytes = a.algorithmic_bytes or bench.algorithmic_bytes(w.B, w.T, w.H, w.dk, w.dv)
 
     stats = kernel_stats(a.dir)
-    chunk_avg = [s for s in stats if CHUNK in s[0]]
-    lines = [f"rocprofv3 kernel trace: chunked GDN kernel, workload {w.name}",
+    lines = [f"rocprofv3 kernel trace: chunked GDN forward (tm_kernel + chunk_kernel), workload {w.name}",
              f"(B={w.B}, H={w.H}, T={w.T}, d_k={w.dk}, d_v={w.dv}, bf16 I/O, chunk_len=64, fp32 state in/out)",
              "", "command (MI355X, repo root, TMPDIR=/tmp):", "  " + KT_CMD.format(d="gpurun_out/prof"),
              f"kernel source sha256[:16]: {src_hash()}", "",
@@ -111,46 +119,51 @@ def main():
              f"  {'name':60s} {'calls':>6s} {'total_ns':>14s} {'avg_ns':>12s} {'pct':>7s}"]
     for n, c, t, av, pc in stats:
         lines.append(f"  {n[:60]:60s} {c:6d} {t:14.0f} {av:12.0f} {pc:7.2f}")
-    if chunk_avg:
-        av = chunk_avg[0][3]
-        dur = trace_durations(a.dir)
+    path = 0.0
+    lines.append("")
+    for kn in KERNELS:
+        dur = trace_durations(a.dir, kn)
         timed = dur[-TIMED_STEPS:]
         tav = statistics.mean(timed)
-        lines += ["", f"chunk kernel average over all {len(dur)} dispatches: {av / 1e6:.4f} ms",
-                  f"chunk kernel average over the last {len(timed)} dispatches (bench.py's timed steps): "
-                  f"{tav / 1e6:.4f} ms -> algorithmic {abytes / (tav * 1e-9) / 1e9:.1f} GB/s "
-                  f"({abytes:.0f} B per launch)",
-                  "per-dispatch durations (ms): " + " ".join(f"{x / 1e6:.3f}" for x in dur)]
+        path += tav
+        lines += [f"{kn}: average over the last {len(timed)} of {len(dur)} dispatches (bench.py's timed steps): "
+                  f"{tav / 1e6:.4f} ms",
+                  f"  per-dispatch durations (ms): " + " ".join(f"{x / 1e6:.3f}" for x in dur)]
+    lines += ["", f"one gdn_forward (both kernels): {path / 1e6:.4f} ms -> algorithmic "
+              f"{abytes / (path * 1e-9) / 1e9:.1f} GB/s ({abytes:.0f} B per call)"]
     with open(os.path.join(PROFILES, f"chunk_kernel_{w.name}.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
-    fetch_k, fetch_c, nf = counter_per_dispatch(a.dir, "fetch", "FETCH_SIZE")
-    write_k, write_c, nw = counter_per_dispatch(a.dir, "write", "WRITE_SIZE")
+    fetch, fetch_c = counter_per_dispatch(a.dir, "fetch", "FETCH_SIZE")
+    write, write_c = counter_per_dispatch(a.dir, "write", "WRITE_SIZE")
     f_scale = COPY_BYTES / (fetch_c * 1024.0)
     w_scale = COPY_BYTES / (write_c * 1024.0)
-    fetch_b = fetch_k * 1024.0 * f_scale
-    write_b = write_k * 1024.0 * w_scale
+    fetch_b = sum(fetch[kn][0] for kn in KERNELS) * 1024.0 * f_scale
+    write_b = sum(write[kn][0] for kn in KERNELS) * 1024.0 * w_scale
     rec = {"workload": w.name, "kernel_src_sha256_16": src_hash(),
            "bytes_per_launch": fetch_b + write_b, "fetch_bytes": fetch_b, "write_bytes": write_b,
-           "fetch_size_kib_raw": fetch_k, "write_size_kib_raw": write_k,
+           "per_kernel_kib_raw": {kn: {"fetch": fetch[kn][0], "write": write[kn][0]} for kn in KERNELS},
            "copy_fetch_kib": fetch_c, "copy_write_kib": write_c,
            "fetch_scale": f_scale, "write_scale": w_scale,
-           "algorithmic_bytes_per_launch": abytes, "dispatches": [nf, nw]}
+           "algorithmic_bytes_per_launch": abytes,
+           "dispatches": {kn: [fetch[kn][1], write[kn][1]] for kn in KERNELS}}
     with open(os.path.join(PROFILES, f"chunk_kernel_{w.name}_traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
-    tl = [f"rocprofv3 HBM traffic counters: chunked GDN kernel, workload {w.name}", "",
+    tl = [f"rocprofv3 HBM traffic counters: chunked GDN forward (tm_kernel + chunk_kernel), workload {w.name}", "",
           "commands (MI355X, repo root, TMPDIR=/tmp), one counter per run:",
           "  " + PMC_CMD.format(c="FETCH_SIZE", d="gpurun_out/prof", n="fetch"),
           "  " + PMC_CMD.format(c="WRITE_SIZE", d="gpurun_out/prof", n="write"),
           f"kernel source sha256[:16]: {src_hash()}", "",
           "scale: the run's plain 512 MiB device copy (--calib-copy) reads and writes 512 MiB;",
           f"  FETCH_SIZE reads {fetch_c:.0f} KiB for it -> scale {f_scale:.3f}",
-          f"  WRITE_SIZE reads {write_c:.0f} KiB for it -> scale {w_scale:.3f}", "",
-          f"chunk kernel per launch (mean of {nf} / {nw} dispatches):",
-          f"  FETCH_SIZE {fetch_k:.0f} KiB raw -> {fetch_b / 1e9:.4f} GB",
-          f"  WRITE_SIZE {write_k:.0f} KiB raw -> {write_b / 1e9:.4f} GB",
-          f"  total {(fetch_b + write_b) / 1e9:.4f} GB vs algorithmic {abytes / 1e9:.4f} GB "
-          f"({(fetch_b + write_b) / abytes:.3f}x)"]
+          f"  WRITE_SIZE reads {write_c:.0f} KiB for it -> scale {w_scale:.3f}", ""]
+    for kn in KERNELS:
+        tl.append(f"{kn} per dispatch (mean of {fetch[kn][1]} / {write[kn][1]} dispatches): "
+                  f"FETCH_SIZE {fetch[kn][0]:.0f} KiB raw -> {fetch[kn][0] * 1024 * f_scale / 1e9:.4f} GB, "
+                  f"WRITE_SIZE {write[kn][0]:.0f} KiB raw -> {write[kn][0] * 1024 * w_scale / 1e9:.4f} GB")
+    tl += [f"one gdn_forward: fetch {fetch_b / 1e9:.4f} GB + write {write_b / 1e9:.4f} GB = "
+           f"{(fetch_b + write_b) / 1e9:.4f} GB vs algorithmic {abytes / 1e9:.4f} GB "
+           f"({(fetch_b + write_b) / abytes:.3f}x)"]
     with open(os.path.join(PROFILES, f"chunk_kernel_{w.name}_traffic.txt"), "w") as f:
         f.write("\n".join(tl) + "\n")
     print("\n".join(lines + [""] + tl))
