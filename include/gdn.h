@@ -32,7 +32,10 @@
  *
  * Ownership.  The caller owns every tensor and the stream.  The library owns
  * the handle and its device scratch, allocated once in gdn_create and freed in
- * gdn_free.  gdn_forward and gdn_forward_bidi allocate nothing, never
+ * gdn_free: the two fp32 partials of gdn_forward_bidi (GDN_FLAG_BIDI), and, on
+ * handles the bf16 chunked kernel can serve (bf16 I/O, d_k and d_v >= 32), the
+ * per-chunk triangular inverses of that kernel (6 KiB per direction, b, h and
+ * 64-token chunk up to max_T).  gdn_forward and gdn_forward_bidi allocate nothing, never
  * synchronise and never copy between host and device: they validate, enqueue
  * kernels on the given stream and return.  Device faults surface at the
  * caller's next synchronisation, as with any HIP launch.  A handle must be
