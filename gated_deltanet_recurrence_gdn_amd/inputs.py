@@ -88,6 +88,32 @@ def make_inputs(B: int, T: int, H: int, dk: int, dv: int, io: str = "bf16", seed
             "beta": beta.contiguous(), "decay": decay.contiguous()}
 
 
+def make_packed_inputs(B: int, T: int, H: int, dk: int, dv: int, io: str = "bf16", seed: int = 0,
+                       a_mean: float = 0.0, b_mean: float = 0.0, pad: int = 0, gap: int = 0) -> dict:
+    """Raw inputs of the fused prologue, drawn on the CPU: the projection output
+    before any normalisation and the gate logits.
+
+    ``qkv_buf`` is a [B, T + gap, W + pad] tensor in the I/O dtype with W = 2 H d_k + H d_v;
+    ``qkv`` is its [B, T, W] view (token stride W + pad, batch stride (T + gap)(W + pad)
+    elements), holding q (H d_k columns), k (H d_k) and v (H d_v), standard normal.  The
+    pad columns and gap tokens hold NaN: they are never part of the input.
+    ``beta_logit`` = x_b + b_mean and ``decay_logit`` = x_a + a_mean, float32 [B, T, H],
+    with x_b, x_a standard normal.  Draw order: q, k, v, x_b, x_a as in make_inputs."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    q = torch.randn((B, T, H * dk), generator=g, dtype=torch.float32)
+    k = torch.randn((B, T, H * dk), generator=g, dtype=torch.float32)
+    v = torch.randn((B, T, H * dv), generator=g, dtype=torch.float32)
+    xb = torch.randn((B, T, H), generator=g, dtype=torch.float32)
+    xa = torch.randn((B, T, H), generator=g, dtype=torch.float32)
+    dt = {"fp32": torch.float32, "bf16": torch.bfloat16}[io]
+    W = 2 * H * dk + H * dv
+    buf = torch.full((B, T + gap, W + pad), float("nan"), dtype=dt)
+    buf[:, :T, :W] = torch.cat([q, k, v], dim=-1).to(dt)
+    return {"qkv_buf": buf, "qkv": buf[:, :T, :W], "beta_logit": (xb + b_mean).contiguous(),
+            "decay_logit": (xa + a_mean).contiguous()}
+
+
 def make_workload(w: Workload | str, seed: int = 0, T: int | None = None) -> dict:
     """Inputs for a named workload; ``T`` overrides the sequence length (a prefix-sized
     sample of the same distribution, drawn from the same seed)."""

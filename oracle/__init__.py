@@ -11,6 +11,15 @@ Arrays use the device library's layouts: q, k [B,T,H,d_k]; v, out [B,T,H,d_v];
 beta, decay [B,T,H]; state [B,H,d_v,d_k].  Inputs of any real dtype are widened
 exactly to float64 (bf16 -> fp32 -> f64 is exact), so the oracle sees the very
 values the GPU receives.
+
+The fused input prologue (``unpack_qkv``, ``l2_normalize``, ``sigmoid``,
+``decay_from_logit``, ``prologue``, ``forward_packed``, ``bidi_packed``) is plain
+numpy float64: split the packed [B, T, 2 H d_k + H d_v] projection into q, k, v
+(the column order of the [N, 3C] qkv that the librediffusion PR #21 page's review
+splits on the GPU, suggestion "k_split_qkv"), divide q and k by max(||.||_2, 1e-12)
+and map the gate logits through b = sigmoid(x_b), a = exp(-softplus(x_a)), then
+run the float64 recurrence above.  The pages print neither the normalisation nor
+the activations; they are the reading the library documents for the prologue.
 """
 from __future__ import annotations
 
@@ -156,6 +165,58 @@ def dense(q, k, v, beta, decay, state_in=None, lib=None):
     lib.oracle_dense_f64(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay),
                          _ptr(s0), _ptr(out), _ptr(st))
     return out, st
+
+
+# ---- fused input prologue ------------------------------------------------------
+
+def unpack_qkv(qkv, H: int, dk: int, dv: int):
+    """Split a packed [B, T, W] projection (W >= 2 H d_k + H d_v) into float64
+    q, k [B,T,H,d_k] and v [B,T,H,d_v]: q of head h at columns h d_k .. h d_k + d_k - 1,
+    k after all of q, v after all of k.  Columns past 2 H d_k + H d_v are ignored."""
+    x = _as(qkv, np.float64)
+    B, T, W = x.shape
+    assert W >= 2 * H * dk + H * dv, (W, H, dk, dv)
+    q = x[:, :, :H * dk].reshape(B, T, H, dk)
+    k = x[:, :, H * dk:2 * H * dk].reshape(B, T, H, dk)
+    v = x[:, :, 2 * H * dk:2 * H * dk + H * dv].reshape(B, T, H, dv)
+    return np.ascontiguousarray(q), np.ascontiguousarray(k), np.ascontiguousarray(v)
+
+
+def l2_normalize(x, eps: float = 1e-12):
+    """x / max(||x||_2, eps) over the last axis, float64 (a zero row stays zero)."""
+    x = _as(x, np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, eps)
+
+
+def sigmoid(x):
+    """1 / (1 + e^-x) in float64, evaluated without overflow for either sign."""
+    x = _as(x, np.float64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def decay_from_logit(x):
+    """exp(-softplus(x)) = exp(-log(1 + e^x)) in float64."""
+    x = _as(x, np.float64)
+    return np.exp(-np.logaddexp(0.0, x))
+
+
+def prologue(qkv, beta_logit, decay_logit, H: int, dk: int, dv: int) -> dict:
+    """The recurrence inputs the prologue defines: dict(q, k, v, beta, decay), float64."""
+    q, k, v = unpack_qkv(qkv, H, dk, dv)
+    return dict(q=l2_normalize(q), k=l2_normalize(k), v=v, beta=sigmoid(beta_logit),
+                decay=decay_from_logit(decay_logit))
+
+
+def forward_packed(qkv, beta_logit, decay_logit, H: int, dk: int, dv: int, state_in=None, lib=None):
+    """Causal recurrence on the prologue's inputs.  Returns (out, state_out)."""
+    return forward(**prologue(qkv, beta_logit, decay_logit, H, dk, dv), state_in=state_in, lib=lib)
+
+
+def bidi_packed(qkv, beta_logit, decay_logit, H: int, dk: int, dv: int, lib=None):
+    """Bidirectional form on the prologue's inputs.  Returns out."""
+    return bidi(**prologue(qkv, beta_logit, decay_logit, H, dk, dv), lib=lib)
 
 
 def num_threads(lib=None) -> int:
