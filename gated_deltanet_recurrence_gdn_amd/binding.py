@@ -4,9 +4,10 @@ Argument marshalling only: every step of the recurrence runs in the library's HI
 kernels.  PyTorch is used for device memory and streams.  If libgdn.so is missing
 the import of this module raises: there is no fallback implementation.
 
-Raw functions (``gdn_create``, ``gdn_forward``, ``gdn_forward_bidi``, ``gdn_free``,
-``gdn_last_error``, ``gdn_version``) take device pointers as ints or torch tensors
-and return the C status.  ``GDN`` wraps a handle for torch callers.
+Raw functions (``gdn_create``, ``gdn_forward``, ``gdn_forward_bidi``,
+``gdn_forward_packed``, ``gdn_forward_bidi_packed``, ``gdn_free``, ``gdn_last_error``,
+``gdn_version``) take device pointers as ints or torch tensors and return the C
+status.  ``GDN`` wraps a handle for torch callers.
 """
 from __future__ import annotations
 
@@ -60,6 +61,10 @@ def _load():
     lib.gdn_forward.restype = I
     lib.gdn_forward_bidi.argtypes = [P, P, P, P, P, P, P, LL, I, P]
     lib.gdn_forward_bidi.restype = I
+    lib.gdn_forward_packed.argtypes = [P, P, LL, LL, P, P, P, P, P, LL, I, P]
+    lib.gdn_forward_packed.restype = I
+    lib.gdn_forward_bidi_packed.argtypes = [P, P, LL, LL, P, P, P, LL, I, P]
+    lib.gdn_forward_bidi_packed.restype = I
     lib.gdn_free.argtypes = [P]
     lib.gdn_free.restype = None
     lib.gdn_last_error.argtypes = [P]
@@ -116,6 +121,19 @@ def gdn_forward_bidi(h, q, k, v, beta, decay, out, T: int, chunk_len: int, strea
                                  int(chunk_len), stream)
 
 
+def gdn_forward_packed(h, qkv, token_stride: int, batch_stride: int, beta_logit, decay_logit, state_in,
+                       state_out, out, T: int, chunk_len: int, stream=None) -> int:
+    return _lib.gdn_forward_packed(h, _p(qkv), int(token_stride), int(batch_stride), _p(beta_logit),
+                                   _p(decay_logit), _p(state_in), _p(state_out), _p(out), int(T),
+                                   int(chunk_len), stream)
+
+
+def gdn_forward_bidi_packed(h, qkv, token_stride: int, batch_stride: int, beta_logit, decay_logit, out,
+                            T: int, chunk_len: int, stream=None) -> int:
+    return _lib.gdn_forward_bidi_packed(h, _p(qkv), int(token_stride), int(batch_stride), _p(beta_logit),
+                                        _p(decay_logit), _p(out), int(T), int(chunk_len), stream)
+
+
 def current_stream():
     """The raw hipStream_t of torch's current stream on the current device."""
     import torch
@@ -136,14 +154,16 @@ class GDN:
         self.io = {"bf16": GDN_BF16, "fp32": GDN_F32}[dtype]
         self.max_T = max_T
         self.device = device
+        self.h = None
+        self._free = _lib.gdn_free  # kept on the object: usable while the interpreter shuts down
         st, h = gdn_create(device, B, H, d_k, d_v, self.io, max_T, GDN_FLAG_BIDI if bidi else 0)
         if st != GDN_OK:
             raise GDNError(st, gdn_last_error(None))
         self.h = h
 
     def close(self):
-        if self.h is not None:
-            gdn_free(self.h)
+        if getattr(self, "h", None) is not None:
+            self._free(self.h)
             self.h = None
 
     __del__ = close
@@ -196,4 +216,45 @@ class GDN:
         if out is None:
             out = torch.empty((self.B, T, self.H, self.d_v), dtype=self._torch_dtype(), device=q.device)
         self._check(gdn_forward_bidi(self.h, q, k, v, beta, decay, out, T, chunk_len, current_stream()))
+        return out
+
+    def _check_packed(self, qkv, beta_logit, decay_logit):
+        """qkv: a [B, T, W] tensor (any strides whose last one is 1, W >= 2 H d_k + H d_v)."""
+        import torch
+        B, H = self.B, self.H
+        if qkv.dim() != 3 or qkv.shape[0] != B or qkv.dtype != self._torch_dtype() or qkv.stride(2) != 1:
+            raise ValueError(f"qkv: expected a [B={B}, T, W] {self._torch_dtype()} view with unit last stride, "
+                             f"got {qkv.dtype} {tuple(qkv.shape)} strides {qkv.stride()}")
+        if qkv.shape[2] < 2 * H * self.d_k + H * self.d_v:
+            raise ValueError(f"qkv: last dim {qkv.shape[2]} < 2 H d_k + H d_v")
+        T = qkv.shape[1]
+        for name, x in (("beta_logit", beta_logit), ("decay_logit", decay_logit)):
+            if tuple(x.shape) != (B, T, H) or x.dtype != torch.float32 or not x.is_contiguous():
+                raise ValueError(f"{name}: expected contiguous float32 {(B, T, H)}, got {x.dtype} {tuple(x.shape)}")
+        return T, qkv.stride(1), qkv.stride(0)
+
+    def forward_packed(self, qkv, beta_logit, decay_logit, state_in=None, state_out=None, out=None,
+                       chunk_len=64, return_state=True):
+        """Causal recurrence with the fused prologue from a packed [B, T, W] qkv view
+        (q, k, v of every head side by side in W; L2-normalised q, k and
+        sigmoid / exp(-softplus) gates applied in the kernels).  Returns (out, state_out)."""
+        import torch
+        T, ts, bs = self._check_packed(qkv, beta_logit, decay_logit)
+        if out is None:
+            out = torch.empty((self.B, T, self.H, self.d_v), dtype=self._torch_dtype(), device=qkv.device)
+        if state_out is None and return_state:
+            state_out = torch.empty((self.B, self.H, self.d_v, self.d_k), dtype=torch.float32,
+                                    device=qkv.device)
+        self._check(gdn_forward_packed(self.h, qkv, ts, bs, beta_logit, decay_logit, state_in, state_out, out, T,
+                                       chunk_len, current_stream()))
+        return out, state_out
+
+    def forward_bidi_packed(self, qkv, beta_logit, decay_logit, out=None, chunk_len=64):
+        """Bidirectional form with the fused prologue.  Returns out."""
+        import torch
+        T, ts, bs = self._check_packed(qkv, beta_logit, decay_logit)
+        if out is None:
+            out = torch.empty((self.B, T, self.H, self.d_v), dtype=self._torch_dtype(), device=qkv.device)
+        self._check(gdn_forward_bidi_packed(self.h, qkv, ts, bs, beta_logit, decay_logit, out, T, chunk_len,
+                                            current_stream()))
         return out

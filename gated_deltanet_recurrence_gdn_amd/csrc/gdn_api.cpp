@@ -103,29 +103,123 @@ struct DeviceGuard {
     }
 };
 
-// Shared validation of the token tensors.  Fills sizes.
-int validate_tokens(gdn_ctx *h, const void *q, const void *k, const void *v, const float *beta,
-                    const float *decay, const void *out, long long T, size_t *qk_bytes,
-                    size_t *v_bytes, size_t *g_bytes) {
+// Largest token stride (elements) of q, k, v: the kernels address up to 64
+// tokens of a chunk with 32-bit offsets from the chunk's first token.
+constexpr long long MAX_TOKEN_STRIDE = 1LL << 24;
+
+// The token inputs of one call: contiguous [B,T,H,d] tensors, or views into a
+// packed qkv projection with the prologue applied in the kernels.
+struct Inputs {
+    const void *q, *k, *v;
+    long long qk_ts, qk_bs, v_ts, v_bs;  // elements between tokens / batch elements
+    const float *beta, *decay;           // values, or logits (prologue)
+    int prologue;
+    Range in[5];                         // the byte ranges read, for the aliasing check
+    int n_in;
+    const void *dev_ptrs[5];             // distinct device pointers to check
+    const char *dev_names[5];
+    int n_dev;
+};
+
+int check_gate_ptrs(gdn_ctx *h, const float *beta, const float *decay, const char *nb, const char *nd) {
+    if (reinterpret_cast<uintptr_t>(beta) % 4 || reinterpret_cast<uintptr_t>(decay) % 4)
+        return fail(h, GDN_ERR_ALIGN, "%s/%s are not 4-byte aligned", nb, nd);
+    return GDN_OK;
+}
+
+// Plain inputs: q, k [B,T,H,d_k], v [B,T,H,d_v], beta and decay [B,T,H] values.
+int prepare_plain(gdn_ctx *h, const void *q, const void *k, const void *v, const float *beta,
+                  const float *decay, const void *out, long long T, Inputs *in, size_t *out_bytes) {
     const gdn_config &c = h->cfg;
     if (T < 0) return fail(h, GDN_ERR_ARG, "T = %lld is negative", T);
     if (T > c.max_T) return fail(h, GDN_ERR_ARG, "T = %lld exceeds max_T = %lld", T, c.max_T);
     const size_t es = c.io_dtype == GDN_BF16 ? 2 : 4;
     const size_t tok = (size_t)c.B * (size_t)T * (size_t)c.H;
-    *qk_bytes = tok * c.d_k * es;
-    *v_bytes = tok * c.d_v * es;
-    *g_bytes = tok * sizeof(float);
-    if (T > 0) {
-        if (!q || !k || !v || !beta || !decay || !out)
-            return fail(h, GDN_ERR_ARG, "q, k, v, beta, decay and out must be non-NULL when T > 0");
-        const void *a16[] = {q, k, v, out};
-        const char *n16[] = {"q", "k", "v", "out"};
-        for (int i = 0; i < 4; ++i)
-            if (reinterpret_cast<uintptr_t>(a16[i]) % 16)
-                return fail(h, GDN_ERR_ALIGN, "%s is not 16-byte aligned", n16[i]);
-        if (reinterpret_cast<uintptr_t>(beta) % 4 || reinterpret_cast<uintptr_t>(decay) % 4)
-            return fail(h, GDN_ERR_ALIGN, "beta/decay are not 4-byte aligned");
+    const size_t qk_bytes = tok * c.d_k * es, v_bytes = tok * c.d_v * es, g_bytes = tok * sizeof(float);
+    *out_bytes = v_bytes;
+    *in = Inputs{};
+    in->q = q; in->k = k; in->v = v; in->beta = beta; in->decay = decay; in->prologue = 0;
+    in->qk_ts = (long long)c.H * c.d_k; in->qk_bs = T * in->qk_ts;
+    in->v_ts = (long long)c.H * c.d_v; in->v_bs = T * in->v_ts;
+    if (T == 0) return GDN_OK;
+    if (!q || !k || !v || !beta || !decay || !out)
+        return fail(h, GDN_ERR_ARG, "q, k, v, beta, decay and out must be non-NULL when T > 0");
+    const void *a16[] = {q, k, v, out};
+    const char *n16[] = {"q", "k", "v", "out"};
+    for (int i = 0; i < 4; ++i)
+        if (reinterpret_cast<uintptr_t>(a16[i]) % 16)
+            return fail(h, GDN_ERR_ALIGN, "%s is not 16-byte aligned", n16[i]);
+    int st = check_gate_ptrs(h, beta, decay, "beta", "decay");
+    if (st) return st;
+    in->in[0] = rng("q", q, qk_bytes);
+    in->in[1] = rng("k", k, qk_bytes);
+    in->in[2] = rng("v", v, v_bytes);
+    in->in[3] = rng("beta", beta, g_bytes);
+    in->in[4] = rng("decay", decay, g_bytes);
+    in->n_in = 5;
+    const void *dp[] = {q, k, v, beta, decay};
+    const char *dn[] = {"q", "k", "v", "beta", "decay"};
+    for (int i = 0; i < 5; ++i) {
+        in->dev_ptrs[i] = dp[i];
+        in->dev_names[i] = dn[i];
     }
+    in->n_dev = 5;
+    return GDN_OK;
+}
+
+// Packed inputs: element j of token t of batch element b at
+// qkv[b * batch_stride + t * token_stride + j], q at j in [0, H d_k), k at
+// [H d_k, 2 H d_k), v at [2 H d_k, 2 H d_k + H d_v); beta and decay are logits.
+int prepare_packed(gdn_ctx *h, const void *qkv, long long token_stride, long long batch_stride,
+                   const float *beta_logit, const float *decay_logit, const void *out, long long T,
+                   Inputs *in, size_t *out_bytes) {
+    const gdn_config &c = h->cfg;
+    if (T < 0) return fail(h, GDN_ERR_ARG, "T = %lld is negative", T);
+    if (T > c.max_T) return fail(h, GDN_ERR_ARG, "T = %lld exceeds max_T = %lld", T, c.max_T);
+    const long long row = 2LL * c.H * c.d_k + (long long)c.H * c.d_v;
+    if (token_stride < row)
+        return fail(h, GDN_ERR_ARG, "token_stride = %lld is below the packed row of %lld elements (2 H d_k + H d_v)",
+                    token_stride, row);
+    if (batch_stride < 0) return fail(h, GDN_ERR_ARG, "batch_stride = %lld is negative", batch_stride);
+    if (token_stride > MAX_TOKEN_STRIDE)
+        return fail(h, GDN_ERR_UNSUPPORTED, "token_stride = %lld exceeds %lld elements", token_stride,
+                    MAX_TOKEN_STRIDE);
+    const size_t es = c.io_dtype == GDN_BF16 ? 2 : 4;
+    if ((token_stride * (long long)es) % 16 || (batch_stride * (long long)es) % 16)
+        return fail(h, GDN_ERR_ALIGN, "token_stride and batch_stride must be multiples of 16 bytes (%zu elements)",
+                    16 / es);
+    const size_t tok = (size_t)c.B * (size_t)T * (size_t)c.H;
+    const size_t g_bytes = tok * sizeof(float);
+    *out_bytes = tok * c.d_v * es;
+    *in = Inputs{};
+    const char *base = static_cast<const char *>(qkv);
+    in->q = qkv;
+    in->k = base ? base + (size_t)c.H * c.d_k * es : nullptr;
+    in->v = base ? base + 2 * (size_t)c.H * c.d_k * es : nullptr;
+    in->qk_ts = in->v_ts = token_stride;
+    in->qk_bs = in->v_bs = batch_stride;
+    in->beta = beta_logit; in->decay = decay_logit; in->prologue = 1;
+    if (T == 0) return GDN_OK;
+    if (!qkv || !beta_logit || !decay_logit || !out)
+        return fail(h, GDN_ERR_ARG, "qkv, beta_logit, decay_logit and out must be non-NULL when T > 0");
+    if (reinterpret_cast<uintptr_t>(qkv) % 16) return fail(h, GDN_ERR_ALIGN, "qkv is not 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(out) % 16) return fail(h, GDN_ERR_ALIGN, "out is not 16-byte aligned");
+    int st = check_gate_ptrs(h, beta_logit, decay_logit, "beta_logit", "decay_logit");
+    if (st) return st;
+    const double ext = ((double)(c.B - 1) * batch_stride + (double)(T - 1) * token_stride + row) * es;
+    if (ext > 9.0e18) return fail(h, GDN_ERR_ARG, "the qkv extent is too large");
+    const size_t qkv_bytes = (size_t)((c.B - 1) * batch_stride + (T - 1) * token_stride + row) * es;
+    in->in[0] = rng("qkv", qkv, qkv_bytes);
+    in->in[1] = rng("beta_logit", beta_logit, g_bytes);
+    in->in[2] = rng("decay_logit", decay_logit, g_bytes);
+    in->n_in = 3;
+    const void *dp[] = {qkv, beta_logit, decay_logit};
+    const char *dn[] = {"qkv", "beta_logit", "decay_logit"};
+    for (int i = 0; i < 3; ++i) {
+        in->dev_ptrs[i] = dp[i];
+        in->dev_names[i] = dn[i];
+    }
+    in->n_dev = 3;
     return GDN_OK;
 }
 
@@ -191,6 +285,9 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
     if (c.max_T < 0) return fail_create(GDN_ERR_ARG, "max_T = %lld is negative", c.max_T);
     if (c.device < -1) return fail_create(GDN_ERR_ARG, "device = %d", c.device);
     if (c.flags & ~GDN_FLAG_BIDI) return fail_create(GDN_ERR_ARG, "unknown flags 0x%x", c.flags);
+    if ((long long)c.H * (c.d_k > c.d_v ? c.d_k : c.d_v) > MAX_TOKEN_STRIDE / 3)
+        return fail_create(GDN_ERR_UNSUPPORTED, "H = %d is too large (H * max(d_k, d_v) * 3 must be <= %lld)", c.H,
+                           MAX_TOKEN_STRIDE);
     // Element count guard: B*T*H*d must fit comfortably in 64-bit byte offsets.
     const double elems = (double)c.B * (double)c.max_T * (double)c.H * 128.0 * 4.0;
     if (elems > 9.0e18) return fail_create(GDN_ERR_ARG, "B*max_T*H is too large");
@@ -269,19 +366,26 @@ void gdn_free(gdn_handle h) {
 
 const char *gdn_last_error(gdn_handle h) { return h ? h->err.c_str() : g_create_err.c_str(); }
 
-int gdn_forward(gdn_handle h, const void *q, const void *k, const void *v, const float *beta,
-                const float *decay, const float *state_in, float *state_out, void *out, long long T,
-                int chunk_len, void *hip_stream) {
-    if (!h) {
-        g_create_err = "gdn_forward: NULL handle";
-        return GDN_ERR_ARG;
-    }
-    h->err.clear();
+}  // extern "C"
+
+namespace {
+
+gdn::PassArgs pass_args(const gdn_ctx *h, const Inputs &in, long long T) {
     const gdn_config &c = h->cfg;
-    size_t qk_bytes, v_bytes, g_bytes;
-    int st = validate_tokens(h, q, k, v, beta, decay, out, T, &qk_bytes, &v_bytes, &g_bytes);
-    if (st) return st;
-    int C = 0;
+    gdn::PassArgs a{};
+    a.q = in.q; a.k = in.k; a.v = in.v;
+    a.qk_ts = in.qk_ts; a.qk_bs = in.qk_bs; a.v_ts = in.v_ts; a.v_bs = in.v_bs;
+    a.beta = in.beta; a.decay = in.decay; a.prologue = in.prologue;
+    a.B = c.B; a.H = c.H; a.dk = c.d_k; a.dv = c.d_v; a.T = T;
+    a.io_bf16 = c.io_dtype == GDN_BF16;
+    a.tm = h->tm; a.tm_chunks = h->tm_chunks;
+    return a;
+}
+
+int run_forward(gdn_ctx *h, const Inputs &in, const float *state_in, float *state_out, void *out,
+                size_t out_bytes, long long T, int chunk_len, void *hip_stream) {
+    const gdn_config &c = h->cfg;
+    int st, C = 0;
     if ((st = resolve_chunk(h, chunk_len, &C))) return st;
     const size_t s_bytes = (size_t)c.B * c.H * c.d_v * c.d_k * sizeof(float);
     if ((state_in && reinterpret_cast<uintptr_t>(state_in) % 16) ||
@@ -290,77 +394,53 @@ int gdn_forward(gdn_handle h, const void *q, const void *k, const void *v, const
     const bool tok = T > 0;
     Range outs[2];
     int n_out = 0;
-    if (tok) outs[n_out++] = rng("out", out, v_bytes);
+    if (tok) outs[n_out++] = rng("out", out, out_bytes);
     if (state_out) outs[n_out++] = rng("state_out", state_out, s_bytes);
     Range ins[6];
     int n_in = 0;
-    if (tok) {
-        ins[n_in++] = rng("q", q, qk_bytes);
-        ins[n_in++] = rng("k", k, qk_bytes);
-        ins[n_in++] = rng("v", v, v_bytes);
-        ins[n_in++] = rng("beta", beta, g_bytes);
-        ins[n_in++] = rng("decay", decay, g_bytes);
-    }
+    if (tok)
+        for (int i = 0; i < in.n_in; ++i) ins[n_in++] = in.in[i];
     if (state_in) ins[n_in++] = rng("state_in", state_in, s_bytes);
     if ((st = check_aliasing(h, outs, n_out, ins, n_in, state_in, state_out))) return st;
     if (c.device < 0) return GDN_OK;  // dry run: validated, nothing launched
 
-    const void *ptrs[] = {q, k, v, beta, decay, state_in, state_out, out};
-    const char *names[] = {"q", "k", "v", "beta", "decay", "state_in", "state_out", "out"};
-    for (int i = 0; i < 8; ++i) {
-        if (!tok && i != 5 && i != 6) continue;
-        if ((st = check_device_ptr(h, names[i], ptrs[i]))) return st;
+    if (tok) {
+        for (int i = 0; i < in.n_dev; ++i)
+            if ((st = check_device_ptr(h, in.dev_names[i], in.dev_ptrs[i]))) return st;
+        if ((st = check_device_ptr(h, "out", out))) return st;
     }
+    if ((st = check_device_ptr(h, "state_in", state_in))) return st;
+    if ((st = check_device_ptr(h, "state_out", state_out))) return st;
     if (!tok && !state_out) return GDN_OK;  // nothing to compute or write
 
     DeviceGuard g(c.device);
-    gdn::PassArgs a{};
-    a.q = q; a.k = k; a.v = v; a.beta = beta; a.decay = decay;
+    gdn::PassArgs a = pass_args(h, in, T);
     a.state_in = state_in; a.state_out = state_out; a.out = out; a.partial = nullptr;
-    a.B = c.B; a.H = c.H; a.dk = c.d_k; a.dv = c.d_v; a.T = T;
-    a.io_bf16 = c.io_dtype == GDN_BF16; a.reverse = 0; a.out_mode = gdn::OUT_STORE;
-    a.tm = h->tm; a.tm_chunks = h->tm_chunks;
+    a.reverse = 0; a.out_mode = gdn::OUT_STORE;
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
     hipError_t e = (C == 1) ? gdn::launch_scan(a, s) : gdn::launch_chunk(a, C, s);
     return launch_status(h, e, C == 1 ? "scan" : "chunked");
 }
 
-int gdn_forward_bidi(gdn_handle h, const void *q, const void *k, const void *v, const float *beta,
-                     const float *decay, void *out, long long T, int chunk_len, void *hip_stream) {
-    if (!h) {
-        g_create_err = "gdn_forward_bidi: NULL handle";
-        return GDN_ERR_ARG;
-    }
-    h->err.clear();
+int run_bidi(gdn_ctx *h, const Inputs &in, void *out, size_t out_bytes, long long T, int chunk_len,
+             void *hip_stream) {
     const gdn_config &c = h->cfg;
-    if (!(c.flags & GDN_FLAG_BIDI))
-        return fail(h, GDN_ERR_ARG, "gdn_forward_bidi needs a handle created with GDN_FLAG_BIDI");
-    size_t qk_bytes, v_bytes, g_bytes;
-    int st = validate_tokens(h, q, k, v, beta, decay, out, T, &qk_bytes, &v_bytes, &g_bytes);
-    if (st) return st;
-    int C = 0;
+    int st, C = 0;
     if ((st = resolve_chunk(h, chunk_len, &C))) return st;
     if (T == 0) return GDN_OK;
-    Range outs[1] = {rng("out", out, v_bytes)};
-    Range ins[5] = {rng("q", q, qk_bytes), rng("k", k, qk_bytes), rng("v", v, v_bytes),
-                    rng("beta", beta, g_bytes), rng("decay", decay, g_bytes)};
-    if ((st = check_aliasing(h, outs, 1, ins, 5, nullptr, nullptr))) return st;
+    Range outs[1] = {rng("out", out, out_bytes)};
+    if ((st = check_aliasing(h, outs, 1, in.in, in.n_in, nullptr, nullptr))) return st;
     if (c.device < 0) return GDN_OK;
-    const void *ptrs[] = {q, k, v, beta, decay, out};
-    const char *names[] = {"q", "k", "v", "beta", "decay", "out"};
-    for (int i = 0; i < 6; ++i)
-        if ((st = check_device_ptr(h, names[i], ptrs[i]))) return st;
+    for (int i = 0; i < in.n_dev; ++i)
+        if ((st = check_device_ptr(h, in.dev_names[i], in.dev_ptrs[i]))) return st;
+    if ((st = check_device_ptr(h, "out", out))) return st;
 
     DeviceGuard g(c.device);
-    gdn::PassArgs a{};
-    a.q = q; a.k = k; a.v = v; a.beta = beta; a.decay = decay;
+    gdn::PassArgs a = pass_args(h, in, T);
     const size_t n_out = (size_t)c.B * (size_t)T * c.H * c.d_v;
     a.state_in = nullptr; a.state_out = nullptr; a.out = out;
     a.partial = h->scratch;
     a.partial_rev = h->scratch + n_out;
-    a.B = c.B; a.H = c.H; a.dk = c.d_k; a.dv = c.d_v; a.T = T;
-    a.io_bf16 = c.io_dtype == GDN_BF16;
-    a.tm = h->tm; a.tm_chunks = h->tm_chunks;
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
     // Both directions in one launch, each into its own fp32 partial (the reverse
     // direction walks the tokens from T-1 down, chunk grid anchored there), then
@@ -373,6 +453,79 @@ int gdn_forward_bidi(gdn_handle h, const void *q, const void *k, const void *v, 
     if ((st = launch_status(h, e, "bidirectional pass"))) return st;
     e = gdn::launch_combine(out, a.partial, a.partial_rev, (long long)n_out, a.io_bf16, s);
     return launch_status(h, e, "bidirectional combine");
+}
+
+int need_bidi(gdn_ctx *h, const char *fn) {
+    if (!(h->cfg.flags & GDN_FLAG_BIDI))
+        return fail(h, GDN_ERR_ARG, "%s needs a handle created with GDN_FLAG_BIDI", fn);
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_forward(gdn_handle h, const void *q, const void *k, const void *v, const float *beta,
+                const float *decay, const float *state_in, float *state_out, void *out, long long T,
+                int chunk_len, void *hip_stream) {
+    if (!h) {
+        g_create_err = "gdn_forward: NULL handle";
+        return GDN_ERR_ARG;
+    }
+    h->err.clear();
+    Inputs in;
+    size_t out_bytes;
+    int st = prepare_plain(h, q, k, v, beta, decay, out, T, &in, &out_bytes);
+    if (st) return st;
+    return run_forward(h, in, state_in, state_out, out, out_bytes, T, chunk_len, hip_stream);
+}
+
+int gdn_forward_packed(gdn_handle h, const void *qkv, long long token_stride, long long batch_stride,
+                       const float *beta_logit, const float *decay_logit, const float *state_in,
+                       float *state_out, void *out, long long T, int chunk_len, void *hip_stream) {
+    if (!h) {
+        g_create_err = "gdn_forward_packed: NULL handle";
+        return GDN_ERR_ARG;
+    }
+    h->err.clear();
+    Inputs in;
+    size_t out_bytes;
+    int st = prepare_packed(h, qkv, token_stride, batch_stride, beta_logit, decay_logit, out, T, &in, &out_bytes);
+    if (st) return st;
+    return run_forward(h, in, state_in, state_out, out, out_bytes, T, chunk_len, hip_stream);
+}
+
+int gdn_forward_bidi(gdn_handle h, const void *q, const void *k, const void *v, const float *beta,
+                     const float *decay, void *out, long long T, int chunk_len, void *hip_stream) {
+    if (!h) {
+        g_create_err = "gdn_forward_bidi: NULL handle";
+        return GDN_ERR_ARG;
+    }
+    h->err.clear();
+    int st = need_bidi(h, "gdn_forward_bidi");
+    if (st) return st;
+    Inputs in;
+    size_t out_bytes;
+    if ((st = prepare_plain(h, q, k, v, beta, decay, out, T, &in, &out_bytes))) return st;
+    return run_bidi(h, in, out, out_bytes, T, chunk_len, hip_stream);
+}
+
+int gdn_forward_bidi_packed(gdn_handle h, const void *qkv, long long token_stride, long long batch_stride,
+                            const float *beta_logit, const float *decay_logit, void *out, long long T,
+                            int chunk_len, void *hip_stream) {
+    if (!h) {
+        g_create_err = "gdn_forward_bidi_packed: NULL handle";
+        return GDN_ERR_ARG;
+    }
+    h->err.clear();
+    int st = need_bidi(h, "gdn_forward_bidi_packed");
+    if (st) return st;
+    Inputs in;
+    size_t out_bytes;
+    if ((st = prepare_packed(h, qkv, token_stride, batch_stride, beta_logit, decay_logit, out, T, &in,
+                             &out_bytes)))
+        return st;
+    return run_bidi(h, in, out, out_bytes, T, chunk_len, hip_stream);
 }
 
 }  // extern "C"

@@ -52,6 +52,17 @@
 //               block.
 //   wave 7      b_t v_t of chunk c+1 (fp32, d_v-major) for R.
 //
+// Fused input prologue (template flag PRO): q, k, v are read in place from a
+// packed token-major projection (token and batch strides), the gate inputs are
+// logits (b = sigmoid(x_b), log2 a = -softplus(x_a) / ln 2, in the gate
+// function), and q, k are L2-normalised without touching the bf16 operands:
+// tm_kernel forms each token's 1 / ||k|| from the K rows it loads and folds it
+// into A's row and column factors (and writes it for chunk_kernel, which folds
+// it into the per-token factors of R, the state update and P); the output waves
+// form 1 / ||q|| from diag(Q Q^T) on MFMA and apply it with the 1/sqrt(d_k)
+// scale.  Only per-token factors change, so without the prologue every factor is
+// bit for bit the plain one.
+//
 // Decay numerics: log2 a is accumulated in float64 (log2 a is clamped at
 // -200, and 2^-200 is 0 in fp32, so a = 0 makes every factor across that token
 // exactly 0), and only 2^{g_i - g_j} for j <= i is ever formed, so nothing
@@ -152,10 +163,12 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 struct Ctx {
     const uint16_t *q, *k, *v;  // v offset to the block's d_v tile
     const float *beta, *decay;
+    const float *norms;         // prologue: the head's inverse k norms, C floats per chunk
     long long T;
     int nchunks;
-    int rs;   // q/k elements between consecutive tokens: H * d_k
-    int rsv;  // v/out elements between consecutive tokens: H * d_v
+    int rs;   // q/k elements between consecutive tokens (H * d_k when contiguous)
+    int rsv;  // v elements between consecutive tokens (H * d_v when contiguous)
+    int rso;  // out elements between consecutive tokens: H * d_v
     int H;    // gate elements between consecutive tokens
     int reverse;
     __device__ bool has(int c) const { return c >= 0 && c < nchunks; }
@@ -222,29 +235,59 @@ __device__ __forceinline__ double prefix_sum64(int lane, double x) {
 
 // The chunk's gate vectors, lane = token.  Both kernels compute them with this
 // one function, so they agree bit for bit.
+//
+// With the fused prologue, q and k enter only through per-token factors:
+// q^_i = rq_i q_i and k^_j = rk_j k_j (rq, rk the inverse L2 norms), so
+//   A_ij = (b_i rk_i) 2^{g_i - gk_j} (k_i . k_j),   gk_j = g_j - log2 rk_j,
+//   R    = diag(b) V - diag(b gam rk) K S0^T,
+//   S    = gam_{C-1} S0 + N^T diag(2^{g_{C-1} - gk}) K,
+//   O_i  = rq_i (gam_i (Q S0^T)_i + sum_j 2^{g_i - gk_j} (q_i . k_j) N_j)  (times 1/sqrt(d_k)),
+// and the bf16 operands stay the inputs as given.  rk comes from the inverse
+// pass (which reads K anyway); rq is formed by the output waves (diag(Q Q^T) of
+// the Q operands they hold).  Without the prologue rk = 1 and gk = g.
 struct GateVals {
-    float g;      // cumulative log2 decay (summed in float64)
+    float g;      // cumulative log2 decay g_i (summed in float64)
+    float gk;     // g_j - log2 rk_j: key-side exponent of A and P
     float bet;    // b (0 on padding)
+    float bk;     // b_i rk_i: row factor of A (0 on padding)
     float gam;    // 2^{g_i}
-    float bg;     // b_i 2^{g_i}
-    float glast;  // 2^{g_{C-1} - g_i}
-    float xf;     // 2^{g_31 - g_j} (j < 32), 2^{g_i - g_31} (i >= 32): both <= 1
+    float bg;     // b_i 2^{g_i} rk_i
+    float glast;  // 2^{g_{C-1} - gk_i}
+    float xf;     // 2^{g_31 - gk_j} (j < 32), 2^{g_i - g_31} (i >= 32): both <= 1 for unit rk
 };
-__device__ __forceinline__ GateVals gate_values(int lane, int ntok, float b, float a) {
+// b_t and log2 a_t of one token from the gate inputs (values, or logits with
+// the prologue); log2 a is clamped at -200 (a = 0: 2^-200 is 0 in fp32).
+template <bool PRO>
+__device__ __forceinline__ void gate_in(float xb, float xa, float &b, float &l2a) {
+    if constexpr (PRO) {
+        b = sigmoid_f32(xb);
+        l2a = log2_decay_from_logit(xa);
+    } else {
+        b = xb;
+        l2a = __builtin_amdgcn_logf(xa);  // log2
+    }
+    if (!(l2a > -200.0f)) l2a = -200.0f;
+}
+template <bool PRO>
+__device__ __forceinline__ GateVals gate_values(int lane, int ntok, float xb, float xa, float rk) {
     const bool real = lane < ntok;
-    const float av = real ? a : 1.f;
-    float l2 = __builtin_amdgcn_logf(av);  // log2
-    if (!(l2 > -200.0f)) l2 = -200.0f;     // a = 0: 2^-200 is 0 in fp32
+    float b, l2;
+    gate_in<PRO>(xb, xa, b, l2);
+    if (!real) l2 = 0.0f;  // padding: a = 1
     const double xs = prefix_sum64(lane, (double)l2);
     const double xl = lane_value(xs, 63);
     const double x31 = lane_value(xs, 31);
+    double xk = xs;
+    if constexpr (PRO) xk = xs - (double)__builtin_amdgcn_logf(rk);
     GateVals r;
-    r.xf = exp2_fast((float)(lane < 32 ? x31 - xs : xs - x31));
+    r.xf = exp2_fast((float)(lane < 32 ? x31 - xk : xs - x31));
     r.g = (float)xs;
+    r.gk = (float)xk;
     r.gam = exp2_fast((float)xs);
-    r.bg = real ? b * r.gam : 0.f;
-    r.glast = exp2_fast((float)(xl - xs));
+    r.bg = real ? b * r.gam * rk : 0.f;
+    r.glast = exp2_fast((float)(xl - xk));
     r.bet = real ? b : 0.f;
+    r.bk = real ? b * rk : 0.f;
     return r;
 }
 
@@ -252,10 +295,12 @@ __device__ __forceinline__ GateVals gate_values(int lane, int ntok, float b, flo
 // tm_kernel: Tm = (I + A)^{-1} of every chunk, in chain operand order.
 // =============================================================================
 struct TmParams {
-    const uint16_t *k;
+    const uint16_t *q, *k;
     const float *beta, *decay;
-    uint16_t *tm;  // [dirs][B][H][nchunks][TM_ELEMS]
+    uint16_t *tm;     // [dirs][B][H][nchunks][TM_ELEMS]
+    float *norms;     // prologue: [dirs][B][H][nchunks][C] inverse norms of k
     long long T;
+    long long qk_ts, qk_bs;
     int B, H, nchunks, reverse;
 };
 
@@ -270,7 +315,8 @@ struct __align__(16) TmSmem {
             uint16_t Ab[C][LC];  // A (its off-diagonal 16x16 blocks are read)
         };
     };
-    float g[C], bet[C], xf[C];
+    float g[C], gk[C], bk[C], xf[C];  // GateVals
+    float rk[C];                     // prologue: inverse L2 norms of k_t
 };
 
 // y += a_J * b, where a_J is lane J's value of a within each 16-lane row: one
@@ -292,7 +338,8 @@ __device__ __forceinline__ void fmac_dpp_fence(const float (&a)[16]) {
 
 // A diagonal 32x32 block kk of A, from its Gram accumulator acc = K_kk K_kk^T
 // (keys x queries), and the two diagonal 16x16 blocks of Tm inside it.
-//   * epilogue: A_ij = b_i (k_i . k_j) 2^{g_i - g_j} for j < i, else 0;
+//   * epilogue: A_ij = b_i rk_i (k_i . k_j) 2^{g_i - gk_j} for j < i, else 0
+//     (rk = 1 and gk = g without the prologue);
 //     the off-diagonal 16x16 block (rows 16-31, cols 0-15) goes to Ab for the
 //     block-column products;
 //   * the lane halves exchange 8 keys (v_permlane32_swap) so that lane i of
@@ -306,13 +353,12 @@ __device__ __forceinline__ void fmac_dpp_fence(const float (&a)[16]) {
 template <int DK>
 __device__ __forceinline__ void a_diag_block(TmSmem<DK> &sm, const f32x16_t &acc, int kk, int lane) {
     const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15;
-    const float *gg = sm.g;
     const int i = 32 * kk + l32;
-    const float gi = gg[i];
-    const float bi = sm.bet[i];
+    const float gi = sm.g[i];
+    const float bi = sm.bk[i];
     float4 gj[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) gj[q] = *reinterpret_cast<const float4 *>(&gg[32 * kk + 8 * q + 4 * hi]);
+    for (int q = 0; q < 4; ++q) gj[q] = *reinterpret_cast<const float4 *>(&sm.gk[32 * kk + 8 * q + 4 * hi]);
     float v[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -372,15 +418,15 @@ __device__ __forceinline__ void a_diag_block(TmSmem<DK> &sm, const f32x16_t &acc
     }
 }
 
-// A(1,0) = b_i (k_i . k_j) G_ij for keys j in 0-31 and queries i in 32-63 (every
-// j < i), from its Gram accumulator K_a K_b^T (keys x queries), with the
-// separable factors G_ij = 2^{g_i - g_31} 2^{g_31 - g_j} (both <= 1); written as
-// bf16 to Ab (all of its 16x16 blocks are off-diagonal blocks of A).
+// A(1,0) = b_i rk_i (k_i . k_j) 2^{g_i - gk_j} for keys j in 0-31 and queries i
+// in 32-63 (every j < i), from its Gram accumulator K_a K_b^T (keys x queries),
+// with the separable factors 2^{g_i - g_31} 2^{g_31 - gk_j}; written as bf16 to
+// Ab (all of its 16x16 blocks are off-diagonal blocks of A).
 template <int DK>
 __device__ __forceinline__ void a_cross_block(TmSmem<DK> &sm, const f32x16_t &acc, int lane) {
     const int l32 = lane & 31, hi = lane >> 5;
     const int i = 32 + l32;
-    const float si = sm.xf[i] * sm.bet[i];
+    const float si = sm.xf[i] * sm.bk[i];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const float4 fj = *reinterpret_cast<const float4 *>(&sm.xf[8 * q + 4 * hi]);
@@ -423,8 +469,23 @@ __device__ __forceinline__ void tm_column(uint16_t (*Tb)[LC], const uint16_t (*A
         for (int r = 0; r < 4; ++r) Tb[16 * rb + 4 * g16 + r][16 * CB + l16] = (uint16_t)f32_to_bf16_bits(-tout[rb][r]);
 }
 
+// Sum of squares of 8 bf16 values.
+__device__ __forceinline__ float sumsq8(const bf16x8_t &r) {
+    uint4 w;
+    __builtin_memcpy(&w, &r, 16);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_lo(u[e]), hi = bf16_hi(u[e]);
+        s = fmaf(lo, lo, s);
+        s = fmaf(hi, hi, s);
+    }
+    return s;
+}
+
 // One block (4 waves) per (direction, b, h, chunk); up to 8 blocks per CU.
-template <int DK>
+template <int DK, bool PRO>
 __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
     __shared__ TmSmem<DK> sm;
     const int lane = threadIdx.x & 63;
@@ -442,19 +503,29 @@ __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
     Ctx x;
     x.T = p.T;
     x.nchunks = p.nchunks;
-    x.rs = p.H * DK;
+    x.rs = (int)p.qk_ts;
     x.rsv = 0;
+    x.rso = 0;
     x.H = p.H;
     x.reverse = p.reverse ^ dir;
-    const size_t tok0 = (size_t)b * p.T * p.H + h;
+    const size_t gtok0 = (size_t)b * p.T * p.H + h;  // (b, token 0, h) of the [B, T, H] gates
+    const size_t qk0 = (size_t)b * p.qk_bs + (size_t)h * DK;
     x.q = nullptr;
     x.v = nullptr;
-    x.k = p.k + tok0 * DK;
-    x.beta = p.beta + tok0;
-    x.decay = p.decay + tok0;
+    x.k = p.k + qk0;
+    x.beta = p.beta + gtok0;
+    x.decay = p.decay + gtok0;
+    x.norms = nullptr;
 
     // 1. K rows 16 wid .. 16 wid + 15 into LDS (row-coalesced: DK / 8 lanes per
-    //    row); wave 3 also forms the gate vectors.
+    //    row).  With the prologue the same lanes form every row's inverse L2 norm
+    //    (a sum over the row's lanes).  Wave 3 reads the gate inputs.
+    float xb = 0.f, xa = 1.f;
+    if (wid == 3) {
+        const size_t o = (size_t)x.tok_clamped(c, lane) * x.H;
+        xb = x.beta[o];
+        xa = x.decay[o];
+    }
     {
         constexpr int LPR = DK / 8, RPL = 64 / LPR, NLD = 16 / RPL;
         const int r0 = 16 * wid + lane / LPR, col = 8 * (lane % LPR);
@@ -464,18 +535,19 @@ __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
             r[s] = *reinterpret_cast<const bf16x8_t *>(x.k + (size_t)x.tok_clamped(c, r0 + RPL * s) * x.rs + col);
 #pragma unroll
         for (int s = 0; s < NLD; ++s) *reinterpret_cast<bf16x8_t *>(&sm.Ks[r0 + RPL * s][col]) = r[s];
-    }
-    if (wid == 3) {
-        const size_t o = (size_t)x.tok_clamped(c, lane) * x.H;
-        const GateVals gv = gate_values(lane, x.ntok(c), x.beta[o], x.decay[o]);
-        sm.g[lane] = gv.g;
-        sm.bet[lane] = gv.bet;
-        sm.xf[lane] = gv.xf;
+        if constexpr (PRO) {
+#pragma unroll
+            for (int s = 0; s < NLD; ++s) {
+                const float sk = group_sum<LPR>(sumsq8(r[s]));
+                if (lane % LPR == 0) sm.rk[r0 + RPL * s] = inv_norm(sk);
+            }
+        }
     }
     __syncthreads();
 
-    // 2. the diagonal 32x32 blocks of A with their diagonal 16x16 Tm blocks
-    //    (waves 0, 1) and the off-diagonal block A(1,0) (wave 2)
+    // 2. the Gram products of the diagonal 32x32 blocks of A (waves 0, 1) and of
+    //    the off-diagonal block A(1,0) (wave 2), then the epilogues with their
+    //    diagonal 16x16 Tm blocks
     constexpr int NKS = DK / 16;
     const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g16 = lane >> 4;
     const uint16_t *ka = &sm.Ks[l32][8 * hi];
@@ -491,6 +563,15 @@ __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
     } else if (wid == 2) {
 #pragma unroll
         for (int s = 0; s < NKS; ++s) g0 = mfma32(lds16(ka + 16 * s), lds16(kb + 16 * s), g0);
+    } else {
+        // wave 3: the gate vectors (the prologue's factors need every row's norm)
+        const float rk = PRO ? sm.rk[lane] : 1.f;
+        const GateVals gv = gate_values<PRO>(lane, x.ntok(c), xb, xa, rk);
+        sm.g[lane] = gv.g;
+        sm.gk[lane] = gv.gk;
+        sm.bk[lane] = gv.bk;
+        sm.xf[lane] = gv.xf;
+        if constexpr (PRO) p.norms[((size_t)((dir * p.B + b) * p.H + h) * p.nchunks + c) * C + lane] = rk;
     }
     __syncthreads();  // K is read; Tm and A overwrite it
     if (wid < 2) a_diag_block(sm, g0, wid, lane);
@@ -520,7 +601,9 @@ __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
 // =============================================================================
 struct ChunkParams {
     const uint16_t *q, *k, *v;
+    long long qk_ts, qk_bs, v_ts, v_bs;  // element strides between tokens / batch elements
     const float *beta, *decay;
+    const float *norms;                  // prologue: written by tm_kernel
     const float *state_in;
     float *state_out;
     void *out;
@@ -543,11 +626,11 @@ struct __align__(16) Smem {
     uint16_t Sb[2][DVT][LKK];  // bf16 state tile at the start of a chunk, [d_v][d_k]
     uint16_t Nt[2][DVT][LC];  // N^T (chunk parity), keys in sdk order
     float g[3][C];           // gate vectors, chunk mod 3 (GateVals)
+    float gk[3][C];
     float bet[3][C];
     float gam[3][C];
     float bg[3][C];
     float glast[3][C];
-    float xf[3][C];
 };
 
 // Column d of bVt holds token t at position t + 16 (d / 8), mod 64: the four
@@ -675,7 +758,7 @@ struct Chain16 {
     __device__ __forceinline__ void step_s(Smem<DK> &sm, int c, int lane, int col, f32x4_t (&nacc)[4],
                                            const KtOps &kt) {
         const int g4 = lane >> 4;
-        const int s2 = c & 1, s3 = c % 3;
+        const int s3 = c % 3;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
             const float4 gl = *reinterpret_cast<const float4 *>(&sm.glast[s3][16 * nb + 4 * g4]);
@@ -719,14 +802,28 @@ __device__ __forceinline__ TmOps load_tm(const uint16_t *tm_head, int c, int n, 
 // its B operand (the permuted k order of the chain) and N^T, whose keys the
 // chain stores in the matching order, as its A operand.  Query blocks {0, 3} and
 // {1, 2} need five key blocks each, so the two waves do the same work.
-template <int DK>
+// With the prologue, rq is set to this lane's query's inverse L2 norm: diag(Q Q^T)
+// of the block on MFMA from the Q operands already held (bf16 products are exact in
+// fp32), the diagonal entry of query r taken from the lane that holds it (lane
+// 16 (r / 4) + r, slot r % 4).
+template <int DK, bool PRO>
 __device__ __forceinline__ void out_products(const Smem<DK> &sm, int s2, int s3, int q, int lane,
-                                             const bf16x8_t (&sa)[2][DK / 32], f32x4_t (&o)[2], f32x4_t (&pk)[4]) {
+                                             const bf16x8_t (&sa)[2][DK / 32], f32x4_t (&o)[2], f32x4_t (&pk)[4],
+                                             float &rq) {
     constexpr int NKS = DK / 32;
     const int g4 = lane >> 4, r16 = lane & 15;
     bf16x8_t qo[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qo[ks] = lds16(&sm.Qs[s2][16 * q + r16][32 * ks + 8 * g4]);
+    if constexpr (PRO) {
+        f32x4_t nn = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) nn = mfma16k32(qo[ks], qo[ks], nn);
+        const int m = r16 - 4 * g4;  // nn[m] = (Q Q^T)[4 g4 + m][r16]
+        const float d = m == 0 ? nn[0] : m == 1 ? nn[1] : m == 2 ? nn[2] : m == 3 ? nn[3] : 0.f;
+        const int src = 16 * (r16 >> 2) + r16;
+        rq = inv_norm(__int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(d))));
+    }
     o[0] = zero4();
     o[1] = zero4();
 #pragma unroll
@@ -743,7 +840,8 @@ __device__ __forceinline__ void out_products(const Smem<DK> &sm, int s2, int s3,
         for (int ks = 0; ks < NKS; ++ks)
             pk[kb] = mfma16k32(lds16(&sm.Ks[s2][16 * kb + r16][32 * ks + 8 * g4]), qo[ks], pk[kb]);
     }
-    // gam of the query column on S Q^T; 2^{g_i - g_j} and the causal mask on P^T
+    // gam of the query column on S Q^T; 2^{g_i - gk_j} and the causal mask on
+    // P^T (gk = g without the prologue)
     const int qi = 16 * q + r16;
     const float gq = sm.gam[s3][qi];
     const float gi = sm.g[s3][qi];
@@ -755,7 +853,7 @@ __device__ __forceinline__ void out_products(const Smem<DK> &sm, int s2, int s3,
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         if (kb > q) break;
-        const float4 gj = *reinterpret_cast<const float4 *>(&sm.g[s3][16 * kb + 4 * g4]);
+        const float4 gj = *reinterpret_cast<const float4 *>(&sm.gk[s3][16 * kb + 4 * g4]);
         const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -778,17 +876,18 @@ __device__ __forceinline__ void out_pn(const Smem<DK> &sm, int slot, int q, int 
     }
 }
 
-template <int DK, bool BF16>
+template <int DK, bool BF16, bool PRO>
 __device__ __forceinline__ void out_store(const Ctx &x, const ChunkParams &p, int c, int q, int lane,
-                                          const f32x4_t (&o)[2], void *out_b, float *part_b) {
+                                          const f32x4_t (&o)[2], float rq, void *out_b, float *part_b) {
     const int g4 = lane >> 4, qi = 16 * q + (lane & 15);
     if (qi >= x.ntok(c)) return;
-    const size_t e0 = (size_t)x.tok(c, qi) * x.rsv + 4 * g4;
+    const size_t e0 = (size_t)x.tok(c, qi) * x.rso + 4 * g4;
+    const float sc = PRO ? p.scale * rq : p.scale;
 #pragma unroll
     for (int dvb = 0; dvb < 2; ++dvb) {
         const size_t e = e0 + 16 * dvb;
-        const float o0 = o[dvb][0] * p.scale, o1 = o[dvb][1] * p.scale;
-        const float o2 = o[dvb][2] * p.scale, o3 = o[dvb][3] * p.scale;
+        const float o0 = o[dvb][0] * sc, o1 = o[dvb][1] * sc;
+        const float o2 = o[dvb][2] * sc, o3 = o[dvb][3] * sc;
         if (p.out_mode == OUT_PARTIAL) {
             *reinterpret_cast<float4 *>(part_b + e) = make_float4(o0, o1, o2, o3);
         } else {
@@ -806,9 +905,10 @@ __device__ __forceinline__ void out_store(const Ctx &x, const ChunkParams &p, in
 // its LDS slot (written by the chain in period c, visible after the barrier).
 struct OutRegs {
     f32x4_t oa[2], ob[2], pa[4], pb[4];
+    float ra = 1.f, rb = 1.f;  // prologue: inverse q norms of the lane's query in blocks QA, QB
 };
 
-template <int DK, int W>
+template <int DK, int W, bool PRO>
 __device__ __forceinline__ void out_products_step(Smem<DK> &sm, int c, int lane, OutRegs &r) {
     constexpr int NKS = DK / 32;
     constexpr int QA = W ? 1 : 0, QB = W ? 2 : 3;
@@ -820,32 +920,32 @@ __device__ __forceinline__ void out_products_step(Smem<DK> &sm, int c, int lane,
         sa[0][ks] = lds16(&sm.Sb[s2][r16][32 * ks + 8 * g4]);
         sa[1][ks] = lds16(&sm.Sb[s2][16 + r16][32 * ks + 8 * g4]);
     }
-    out_products(sm, s2, s3, QA, lane, sa, r.oa, r.pa);
-    out_products(sm, s2, s3, QB, lane, sa, r.ob, r.pb);
+    out_products<DK, PRO>(sm, s2, s3, QA, lane, sa, r.oa, r.pa, r.ra);
+    out_products<DK, PRO>(sm, s2, s3, QB, lane, sa, r.ob, r.pb, r.rb);
 }
 
-template <int DK, bool BF16, int W>
+template <int DK, bool BF16, int W, bool PRO>
 __device__ __forceinline__ void out_finish_step(const Ctx &x, const Smem<DK> &sm, const ChunkParams &p, int c,
                                                 int lane, OutRegs &r, void *out_b, float *part_b) {
     constexpr int QA = W ? 1 : 0, QB = W ? 2 : 3;
     out_pn(sm, c & 1, QA, lane, r.oa, r.pa);
     out_pn(sm, c & 1, QB, lane, r.ob, r.pb);
-    out_store<DK, BF16>(x, p, c, QA, lane, r.oa, out_b, part_b);
-    out_store<DK, BF16>(x, p, c, QB, lane, r.ob, out_b, part_b);
+    out_store<DK, BF16, PRO>(x, p, c, QA, lane, r.oa, r.ra, out_b, part_b);
+    out_store<DK, BF16, PRO>(x, p, c, QB, lane, r.ob, r.rb, out_b, part_b);
 }
 
 // Period c of an output wave: finish chunk c - 1, then the products of chunk c.
-template <int DK, bool BF16, int W>
+template <int DK, bool BF16, int W, bool PRO>
 __device__ __forceinline__ void output_period(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int c, int lane,
                                               OutRegs &r, void *out_b, float *part_b) {
     const bool fin = x.has(c - 1), run = x.has(c);
     if (fin && run) {
-        out_finish_step<DK, BF16, W>(x, sm, p, c - 1, lane, r, out_b, part_b);
-        out_products_step<DK, W>(sm, c, lane, r);
+        out_finish_step<DK, BF16, W, PRO>(x, sm, p, c - 1, lane, r, out_b, part_b);
+        out_products_step<DK, W, PRO>(sm, c, lane, r);
     } else if (run) {
-        out_products_step<DK, W>(sm, c, lane, r);
+        out_products_step<DK, W, PRO>(sm, c, lane, r);
     } else if (fin) {
-        out_finish_step<DK, BF16, W>(x, sm, p, c - 1, lane, r, out_b, part_b);
+        out_finish_step<DK, BF16, W, PRO>(x, sm, p, c - 1, lane, r, out_b, part_b);
     }
 }
 
@@ -886,7 +986,8 @@ __device__ __forceinline__ void store_rows(uint16_t (*dst)[PITCH], const Rows64<
 
 // ---- waves 6, 7: gate vectors; V tiles -----------------------------------------
 struct GateRegs {
-    float b, a;
+    float b, a;  // gate inputs (values, or logits with the prologue)
+    float rk;    // prologue: inverse norm of k_t (from tm_kernel)
 };
 
 // The chunk's V tile (64 tokens x 32 d_v), row-coalesced: in w[s], lane l holds
@@ -904,22 +1005,27 @@ __device__ __forceinline__ VRow load_v(const Ctx &x, int c, int lane) {
 }
 // Unconditional (c is clamped into range by the caller), so that the count of
 // loads in flight is the same on every path.
+template <bool PRO>
 __device__ __forceinline__ void load_gates(const Ctx &x, int c, int lane, GateRegs &g) {
     const size_t o = (size_t)x.tok_clamped(c, lane) * x.H;
     g.b = x.beta[o];
     g.a = x.decay[o];
+    if constexpr (PRO)
+        g.rk = x.norms[(size_t)c * C + lane];
+    else
+        g.rk = 1.f;
 }
 
-template <int DK>
+template <int DK, bool PRO>
 __device__ __forceinline__ void gates_store(const Ctx &x, Smem<DK> &sm, int c, int lane, const GateRegs &gr) {
-    const GateVals v = gate_values(lane, x.ntok(c), gr.b, gr.a);
+    const GateVals v = gate_values<PRO>(lane, x.ntok(c), gr.b, gr.a, gr.rk);
     const int s3 = c % 3;
     sm.g[s3][lane] = v.g;
+    sm.gk[s3][lane] = v.gk;
     sm.bet[s3][lane] = v.bet;
     sm.gam[s3][lane] = v.gam;
     sm.bg[s3][lane] = v.bg;
     sm.glast[s3][lane] = v.glast;
-    sm.xf[s3][lane] = v.xf;
 }
 
 template <int DK>
@@ -939,7 +1045,7 @@ __device__ __forceinline__ void store_bv(Smem<DK> &sm, int c, const VRow &v, int
     }
 }
 
-template <int DK, bool BF16>
+template <int DK, bool BF16, bool PRO>
 __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     static_assert(DK % 32 == 0 && DK <= 128, "d_k must be 32, 64 or 128");
     __shared__ Smem<DK> sm;
@@ -966,17 +1072,20 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     Ctx x;
     x.T = p.T;
     x.nchunks = (int)((p.T + C - 1) / C);
-    x.rs = p.H * DK;
-    x.rsv = p.H * p.dv;
+    x.rs = (int)p.qk_ts;
+    x.rsv = (int)p.v_ts;
+    x.rso = p.H * p.dv;
     x.H = p.H;
     x.reverse = p.reverse ^ dir;
-    const size_t tok0 = (size_t)b * p.T * p.H + h;  // (b, token 0, h) in [B, T, H]
-    x.q = p.q + tok0 * DK;
-    x.k = p.k + tok0 * DK;
-    x.v = p.v + tok0 * p.dv + dv0;
+    const size_t tok0 = (size_t)b * p.T * p.H + h;  // (b, token 0, h) of the [B, T, H] gates and out rows
+    const size_t qk0 = (size_t)b * p.qk_bs + (size_t)h * DK;
+    x.q = p.q + qk0;
+    x.k = p.k + qk0;
+    x.v = p.v + (size_t)b * p.v_bs + (size_t)h * p.dv + dv0;
     x.beta = p.beta + tok0;
     x.decay = p.decay + tok0;
     const int n = x.nchunks;
+    x.norms = PRO ? p.norms + (size_t)((dir * p.B + b) * p.H + h) * n * C : nullptr;
 
     // Every role walks the same periods it = -2 .. n (the last one finishes the
     // outputs of chunk n-1), two per loop trip so that register sets alternate at
@@ -1015,18 +1124,18 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         OutRegs r;
         __syncthreads();
         for (int it = -2; it < n + 1; it += 2) {
-            output_period<DK, BF16, 0>(x, sm, p, it, lane, r, out_b, part_b);
+            output_period<DK, BF16, 0, PRO>(x, sm, p, it, lane, r, out_b, part_b);
             __syncthreads();
-            output_period<DK, BF16, 0>(x, sm, p, it + 1, lane, r, out_b, part_b);
+            output_period<DK, BF16, 0, PRO>(x, sm, p, it + 1, lane, r, out_b, part_b);
             __syncthreads();
         }
     } else if (wid == 3) {
         OutRegs r;
         __syncthreads();
         for (int it = -2; it < n + 1; it += 2) {
-            output_period<DK, BF16, 1>(x, sm, p, it, lane, r, out_b, part_b);
+            output_period<DK, BF16, 1, PRO>(x, sm, p, it, lane, r, out_b, part_b);
             __syncthreads();
-            output_period<DK, BF16, 1>(x, sm, p, it + 1, lane, r, out_b, part_b);
+            output_period<DK, BF16, 1, PRO>(x, sm, p, it + 1, lane, r, out_b, part_b);
             __syncthreads();
         }
     } else if (wid < 6) {
@@ -1056,15 +1165,15 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         // Gates of chunk c are computed in period c-2 from register set c&1
         // (loaded in period c-4).
         GateRegs gA, gB;
-        load_gates(x, 0, lane, gA);
-        load_gates(x, 1 < n ? 1 : n - 1, lane, gB);
+        load_gates<PRO>(x, 0, lane, gA);
+        load_gates<PRO>(x, 1 < n ? 1 : n - 1, lane, gB);
         __syncthreads();
         for (int it = -2; it < n + 1; it += 2) {
-            if (x.has(it + 2)) gates_store(x, sm, it + 2, lane, gA);
-            load_gates(x, it + 4 < n ? it + 4 : n - 1, lane, gA);
+            if (x.has(it + 2)) gates_store<DK, PRO>(x, sm, it + 2, lane, gA);
+            load_gates<PRO>(x, it + 4 < n ? it + 4 : n - 1, lane, gA);
             __syncthreads();
-            if (x.has(it + 3)) gates_store(x, sm, it + 3, lane, gB);
-            load_gates(x, it + 5 < n ? it + 5 : n - 1, lane, gB);
+            if (x.has(it + 3)) gates_store<DK, PRO>(x, sm, it + 3, lane, gB);
+            load_gates<PRO>(x, it + 5 < n ? it + 5 : n - 1, lane, gB);
             __syncthreads();
         }
     } else {
@@ -1085,19 +1194,24 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     }
 }
 
-template <int DK>
+template <int DK, bool PRO>
 hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     const int nchunks = (int)((a.T + C - 1) / C);
     const int dirs = a.both_dirs ? 2 : 1;
     const long long ntm = (long long)dirs * a.B * a.H * nchunks;
     if (!a.tm || ntm > a.tm_chunks || ntm > 0x7fffffffLL) return hipErrorInvalidValue;
+    // The inverse norms follow the Tm blocks of the handle's whole capacity.
+    float *norms = PRO ? reinterpret_cast<float *>(a.tm + (size_t)a.tm_chunks * TM_ELEMS) : nullptr;
 
     TmParams t;
+    t.q = static_cast<const uint16_t *>(a.q);
     t.k = static_cast<const uint16_t *>(a.k);
     t.beta = a.beta; t.decay = a.decay;
     t.tm = a.tm;
-    t.T = a.T; t.B = a.B; t.H = a.H; t.nchunks = nchunks; t.reverse = a.reverse;
-    hipLaunchKernelGGL((tm_kernel<DK>), dim3((unsigned)ntm), dim3(256), 0, stream, t);
+    t.norms = norms;
+    t.T = a.T; t.qk_ts = a.qk_ts; t.qk_bs = a.qk_bs;
+    t.B = a.B; t.H = a.H; t.nchunks = nchunks; t.reverse = a.reverse;
+    hipLaunchKernelGGL((tm_kernel<DK, PRO>), dim3((unsigned)ntm), dim3(256), 0, stream, t);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -1105,7 +1219,9 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.q = static_cast<const uint16_t *>(a.q);
     p.k = static_cast<const uint16_t *>(a.k);
     p.v = static_cast<const uint16_t *>(a.v);
+    p.qk_ts = a.qk_ts; p.qk_bs = a.qk_bs; p.v_ts = a.v_ts; p.v_bs = a.v_bs;
     p.beta = a.beta; p.decay = a.decay;
+    p.norms = norms;
     p.state_in = a.state_in; p.state_out = a.state_out; p.out = a.out;
     p.partial = a.partial; p.partial_rev = a.partial_rev;
     p.tm = a.tm;
@@ -1116,8 +1232,13 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.reverse = a.reverse; p.out_mode = a.out_mode; p.both_dirs = a.both_dirs;
     p.scale = (float)(1.0 / __builtin_sqrt((double)DK));
     const int nblk = p.nblk_dir * dirs;
-    hipLaunchKernelGGL((chunk_kernel<DK, true>), dim3(nblk), dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL((chunk_kernel<DK, true, PRO>), dim3(nblk), dim3(NT), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
+    return a.prologue ? launch_dk<DK, true>(a, stream) : launch_dk<DK, false>(a, stream);
 }
 
 }  // namespace
@@ -1127,7 +1248,9 @@ bool chunk_mfma_supported(int C_, int dk, int dv, int io_bf16) {
     return C_ == C && dims && io_bf16;
 }
 
-size_t chunk_mfma_tm_bytes(long long chunks) { return (size_t)chunks * TM_ELEMS * sizeof(uint16_t); }
+size_t chunk_mfma_tm_bytes(long long chunks) {
+    return (size_t)chunks * (TM_ELEMS * sizeof(uint16_t) + C * sizeof(float));
+}
 
 hipError_t launch_chunk_mfma(const PassArgs &a, int C_, hipStream_t stream) {
     if (!chunk_mfma_supported(C_, a.dk, a.dv, a.io_bf16)) return hipErrorInvalidValue;

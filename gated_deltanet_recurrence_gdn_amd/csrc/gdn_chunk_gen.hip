@@ -27,6 +27,11 @@
 // n real rows of a final partial chunk are ever touched, so no padding enters
 // any product.
 //
+// q, k and v are addressed by token and batch strides.  With the fused prologue
+// (template flag PRO) the staged K rows are divided by max(||k||_2, 1e-12), the
+// products with q are scaled by 1 / max(||q||_2, 1e-12), and the gate logits
+// become b = sigmoid(x_b) and log2 a = -softplus(x_a) / ln 2 (float64).
+//
 // Decay numerics: log2 a is taken and accumulated in float64, clamped at -200
 // (2^-200 is 0 in fp32, so a = 0 zeroes every factor across that token), and
 // only 2^{g_i - g_j} with j <= i is formed, from the float64 difference.
@@ -42,6 +47,7 @@ constexpr int GMAXE = 128 * GDVT / GT;  // (token, column) elements per thread, 
 
 struct GenParams {
     const void *q, *k, *v;
+    long long qk_ts, qk_bs, v_ts, v_bs;  // element strides between tokens / batch elements
     const float *beta, *decay;
     const float *state_in;
     float *state_out;
@@ -72,14 +78,14 @@ __device__ __forceinline__ void st_io(void *p, size_t i, float x) {
 // Shared-memory footprint in bytes for one block.
 __host__ __device__ inline size_t gen_lds_bytes(int C, int dk, int dvt) {
     return (size_t)C * sizeof(double)                       // g
-           + (size_t)3 * C * sizeof(float)                  // b, gam, G_{n-1,i}
+           + (size_t)5 * C * sizeof(float)                  // b, gam, G_{n-1,i}, rk, rq
            + (size_t)C * (dk + 1) * sizeof(float)           // K
            + (size_t)C * (C + 1) * sizeof(float)            // A / Tm / P
            + (size_t)dvt * (dk + 1) * sizeof(float)         // S tile
            + (size_t)C * dvt * sizeof(float);               // R, then N
 }
 
-template <bool BF16>
+template <bool BF16, bool PRO>
 __global__ __launch_bounds__(GT) void chunk_gen_kernel(GenParams p) {
     extern __shared__ double smem_d[];
     const int C = p.C, dk = p.dk, dvt = p.dvt;
@@ -88,7 +94,9 @@ __global__ __launch_bounds__(GT) void chunk_gen_kernel(GenParams p) {
     float *bet = reinterpret_cast<float *>(g + C);
     float *gam = bet + C;
     float *wl = gam + C;
-    float *Ks = wl + C;
+    float *rk = wl + C;  // prologue: inverse L2 norms of k_i and q_i
+    float *rq = rk + C;
+    float *Ks = rq + C;
     float *Bf = Ks + (size_t)C * PK;
     float *Ss = Bf + (size_t)C * PC;
     float *Rs = Ss + (size_t)dvt * PK;
@@ -101,8 +109,11 @@ __global__ __launch_bounds__(GT) void chunk_gen_kernel(GenParams p) {
     const bool rev = (p.reverse ^ dir) != 0;
     const long long T = p.T;
     const int H = p.H, dv = p.dv;
-    // Row (b, t, h) of the token-major [B, T, H, *] tensors.
+    // Row (b, t, h) of the token-major [B, T, H, *] gates and out; q, k and v
+    // rows by their strides.
     auto row = [&](long long t) -> size_t { return ((size_t)b * T + t) * H + h; };
+    auto qk_row = [&](long long t) -> size_t { return (size_t)b * p.qk_bs + (size_t)t * p.qk_ts + (size_t)h * dk; };
+    auto v_row = [&](long long t) -> size_t { return (size_t)b * p.v_bs + (size_t)t * p.v_ts + (size_t)h * dv; };
 
     const size_t sbase = ((size_t)(b * H + h) * dv + dv0) * dk;
     for (int idx = tid; idx < dvt * dk; idx += GT) {
@@ -120,12 +131,19 @@ __global__ __launch_bounds__(GT) void chunk_gen_kernel(GenParams p) {
 
         for (int idx = tid; idx < n * dk; idx += GT) {
             const int i = idx / dk, f = idx - i * dk;
-            Ks[i * PK + f] = ld_io<BF16>(p.k, row(tok(i)) * dk + f);
+            Ks[i * PK + f] = ld_io<BF16>(p.k, qk_row(tok(i)) + f);
         }
         if (tid < n) {
             const size_t r = row(tok(tid));
-            bet[tid] = p.beta[r];
-            double la = log2((double)p.decay[r]);
+            double la;
+            if constexpr (PRO) {  // b = sigmoid(x), log2 a = -softplus(x) / ln 2
+                const double xb = p.beta[r], xa = p.decay[r];
+                bet[tid] = (float)(1.0 / (1.0 + exp(-xb)));
+                la = -(fmax(xa, 0.0) + log1p(exp(-fabs(xa)))) * 1.4426950408889634;
+            } else {
+                bet[tid] = p.beta[r];
+                la = log2((double)p.decay[r]);
+            }
             if (!(la > -200.0)) la = -200.0;
             g[tid] = la;
         }
@@ -137,10 +155,28 @@ __global__ __launch_bounds__(GT) void chunk_gen_kernel(GenParams p) {
                 g[i] = s;
             }
         }
+        if (PRO && tid < n) {  // q and k of token tid divided by max(||.||_2, 1e-12)
+            const size_t qr = qk_row(tok(tid));
+            float sk = 0.0f, sq = 0.0f;
+            for (int f = 0; f < dk; ++f) {
+                const float kf = Ks[tid * PK + f], qf = ld_io<BF16>(p.q, qr + f);
+                sk = fmaf(kf, kf, sk);
+                sq = fmaf(qf, qf, sq);
+            }
+            rk[tid] = inv_norm(sk);
+            rq[tid] = inv_norm(sq);
+        }
         __syncthreads();
         if (tid < n) {
             gam[tid] = exp2f((float)g[tid]);
             wl[tid] = exp2f((float)(g[n - 1] - g[tid]));
+        }
+        if constexpr (PRO) {
+            for (int idx = tid; idx < n * dk; idx += GT) {
+                const int i = idx / dk, f = idx - i * dk;
+                Ks[i * PK + f] *= rk[i];
+            }
+            __syncthreads();
         }
         // A_ij = b_i (k_i . k_j) G_ij, j < i, into the strict lower triangle.
         for (int idx = tid; idx < n * n; idx += GT) {
@@ -178,7 +214,7 @@ __global__ __launch_bounds__(GT) void chunk_gen_kernel(GenParams p) {
             const int i = idx / dvt, e = idx - i * dvt;
             float x = 0.0f;
             for (int f = 0; f < dk; ++f) x = fmaf(Ks[i * PK + f], Ss[e * PK + f], x);
-            const float vv = ld_io<BF16>(p.v, row(tok(i)) * dv + dv0 + e);
+            const float vv = ld_io<BF16>(p.v, v_row(tok(i)) + dv0 + e);
             Rs[i * dvt + e] = bet[i] * (vv - gam[i] * x);
         }
         __syncthreads();
@@ -205,9 +241,10 @@ __global__ __launch_bounds__(GT) void chunk_gen_kernel(GenParams p) {
         for (int idx = tid; idx < n * n; idx += GT) {
             const int i = idx / n, j = idx - i * n;
             if (j <= i) {
-                const size_t qr = row(tok(i)) * dk;
+                const size_t qr = qk_row(tok(i));
                 float s = 0.0f;
                 for (int f = 0; f < dk; ++f) s = fmaf(ld_io<BF16>(p.q, qr + f), Ks[j * PK + f], s);
+                if constexpr (PRO) s *= rq[i];
                 Bf[i * PC + j] = s * exp2f((float)(g[i] - g[j]));
             }
         }
@@ -216,9 +253,10 @@ __global__ __launch_bounds__(GT) void chunk_gen_kernel(GenParams p) {
         for (int idx = tid; idx < n * dvt; idx += GT) {
             const int i = idx / dvt, e = idx - i * dvt;
             const size_t r = row(tok(i));
-            const size_t qr = r * dk;
+            const size_t qr = qk_row(tok(i));
             float y = 0.0f;
             for (int f = 0; f < dk; ++f) y = fmaf(ld_io<BF16>(p.q, qr + f), Ss[e * PK + f], y);
+            if constexpr (PRO) y *= rq[i];
             float s = gam[i] * y;
             for (int j = 0; j <= i; ++j) s = fmaf(Bf[i * PC + j], Rs[j * dvt + e], s);
             s *= p.scale;
@@ -247,14 +285,14 @@ __global__ __launch_bounds__(GT) void chunk_gen_kernel(GenParams p) {
     }
 }
 
-template <bool BF16>
+template <bool BF16, bool PRO>
 hipError_t launch_gen(const GenParams &p, hipStream_t stream) {
     const size_t lds = gen_lds_bytes(p.C, p.dk, p.dvt);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_gen_kernel<BF16>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_gen_kernel<BF16, PRO>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const dim3 grid(p.dv / p.dvt, p.H, p.B * (p.both_dirs ? 2 : 1));
-    hipLaunchKernelGGL((chunk_gen_kernel<BF16>), grid, dim3(GT), lds, stream, p);
+    hipLaunchKernelGGL((chunk_gen_kernel<BF16, PRO>), grid, dim3(GT), lds, stream, p);
     return hipGetLastError();
 }
 
@@ -271,6 +309,7 @@ hipError_t launch_chunk_general(const PassArgs &a, int C, hipStream_t stream) {
     if (!chunk_general_supported(C, a.dk, a.dv)) return hipErrorInvalidValue;
     GenParams p;
     p.q = a.q; p.k = a.k; p.v = a.v;
+    p.qk_ts = a.qk_ts; p.qk_bs = a.qk_bs; p.v_ts = a.v_ts; p.v_bs = a.v_bs;
     p.beta = a.beta; p.decay = a.decay;
     p.state_in = a.state_in; p.state_out = a.state_out; p.out = a.out;
     p.partial = a.partial; p.partial_rev = a.partial_rev;
@@ -278,7 +317,8 @@ hipError_t launch_chunk_general(const PassArgs &a, int C, hipStream_t stream) {
     p.dvt = a.dv < GDVT ? a.dv : GDVT;
     p.reverse = a.reverse; p.out_mode = a.out_mode; p.both_dirs = a.both_dirs;
     p.scale = (float)(1.0 / __builtin_sqrt((double)a.dk));
-    return a.io_bf16 ? launch_gen<true>(p, stream) : launch_gen<false>(p, stream);
+    if (a.prologue) return a.io_bf16 ? launch_gen<true, true>(p, stream) : launch_gen<false, true>(p, stream);
+    return a.io_bf16 ? launch_gen<true, false>(p, stream) : launch_gen<false, false>(p, stream);
 }
 
 }  // namespace gdn

@@ -48,4 +48,18 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// ---- the fused prologue's activations (fp32) --------------------------------
+// b = sigmoid(x); a = exp(-softplus(x)) = 1 / (1 + e^x); log2 a = -softplus(x) / ln 2,
+// written as -(max(y, 0) + log2(1 + 2^-|y|)) with y = x log2 e so that nothing
+// overflows for large |x|.
+constexpr float LOG2E_F = 1.4426950408889634f;
+__device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + exp2f(-x * LOG2E_F)); }
+__device__ __forceinline__ float decay_from_logit(float x) { return 1.0f / (1.0f + exp2f(x * LOG2E_F)); }
+__device__ __forceinline__ float log2_decay_from_logit(float x) {
+    const float y = x * LOG2E_F;
+    return -(fmaxf(y, 0.0f) + log2f(1.0f + exp2f(-fabsf(y))));
+}
+// 1 / max(||x||_2, 1e-12) from the sum of squares: a zero row stays zero.
+__device__ __forceinline__ float inv_norm(float sumsq) { return 1.0f / fmaxf(sqrtf(sumsq), 1e-12f); }
+
 }  // namespace gdn

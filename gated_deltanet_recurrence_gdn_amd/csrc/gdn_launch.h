@@ -17,11 +17,18 @@ enum OutMode : int {
 
 // One pass of the recurrence over a whole call, all (b, h) pairs.
 struct PassArgs {
-    const void *q;          // [B,T,H,dk] io dtype
-    const void *k;          // [B,T,H,dk]
-    const void *v;          // [B,T,H,dv]
-    const float *beta;      // [B,T,H]
-    const float *decay;     // [B,T,H]
+    // q, k, v: head h of token t of batch element b starts at element
+    // b * qk_bs + t * qk_ts + h * dk of q and k (b * v_bs + t * v_ts + h * dv of
+    // v): contiguous [B,T,H,d] tensors, or views into a packed projection.
+    const void *q;          // io dtype
+    const void *k;
+    const void *v;
+    long long qk_ts, qk_bs; // q and k: elements between tokens / batch elements
+    long long v_ts, v_bs;   // v: the same
+    const float *beta;      // [B,T,H]: b_t (prologue: its logit)
+    const float *decay;     // [B,T,H]: a_t (prologue: its logit)
+    int prologue;           // 1: q, k are L2-normalised per token and head, and
+                            //    b = sigmoid(beta), a = exp(-softplus(decay))
     const float *state_in;  // [B,H,dv,dk] or nullptr (zeros)
     float *state_out;       // [B,H,dv,dk] or nullptr; may equal state_in
     void *out;              // [B,T,H,dv] io dtype (OUT_STORE)
@@ -34,9 +41,17 @@ struct PassArgs {
     int out_mode;           // OutMode
     int both_dirs;          // 1: one launch runs both directions (OUT_PARTIAL into
                             //    partial and partial_rev), from zero state
-    uint16_t *tm;           // MFMA kernel only: the per-chunk Tm scratch of the handle
+    uint16_t *tm;           // MFMA kernel only: the per-chunk scratch of the handle
     long long tm_chunks;    // chunk capacity of tm (directions x B x H x chunks)
 };
+
+// Token-major contiguous strides for q, k [B,T,H,dk] and v [B,T,H,dv].
+inline void contiguous_strides(PassArgs &a) {
+    a.qk_ts = (long long)a.H * a.dk;
+    a.qk_bs = a.T * a.qk_ts;
+    a.v_ts = (long long)a.H * a.dv;
+    a.v_bs = a.T * a.v_ts;
+}
 
 // Sequential per-token scan (the chunk_len = 1 form).
 hipError_t launch_scan(const PassArgs &a, hipStream_t stream);
@@ -44,7 +59,8 @@ hipError_t launch_scan(const PassArgs &a, hipStream_t stream);
 // Chunked (UT-transform) form, bf16 MFMA kernel: C = 64, bf16 I/O,
 // d_k, d_v in {32, 64, 128}.
 // It needs PassArgs::tm: chunk_mfma_tm_bytes(n) bytes hold the triangular
-// inverses of n chunks (one per direction, b, h and chunk).
+// inverses of n chunks (one per direction, b, h and chunk) and, for the
+// prologue, their tokens' inverse q and k norms.
 bool chunk_mfma_supported(int C, int dk, int dv, int io_bf16);
 size_t chunk_mfma_tm_bytes(long long chunks);
 hipError_t launch_chunk_mfma(const PassArgs &a, int C, hipStream_t stream);

@@ -18,6 +18,12 @@
 //     in registers while the current stage is computed;
 //   * outputs are staged in LDS and written as contiguous row segments.
 //
+// q, k and v are addressed by token and batch strides, so the same kernel reads
+// contiguous [B,T,H,d] tensors or views into a packed projection.  With the fused
+// prologue (template flag PRO) the staging step also divides each q and k row by
+// max(||.||_2, 1e-12) (a sum over the row's L lanes) and turns the gate logits
+// into b = sigmoid(x_b), a = exp(-softplus(x_a)), all in fp32.
+//
 // State traffic: one read of state_in and one write of state_out per call
 // (the review on the same page flags per-step global-memory state traffic in
 // its gdn_bidi kernel; here the state never leaves the VGPRs mid-call).
@@ -32,6 +38,7 @@ constexpr int NT = 256;      // max threads per block
 
 struct ScanParams {
     const void *q, *k, *v;
+    long long qk_ts, qk_bs, v_ts, v_bs;  // element strides between tokens / batch elements
     const float *beta, *decay;
     const float *state_in;
     float *state_out;
@@ -82,7 +89,7 @@ __device__ __forceinline__ void store_out(void *out, size_t elem, float x) {
         reinterpret_cast<float *>(out)[elem] = x;
 }
 
-template <int DK, bool BF16>
+template <int DK, bool BF16, bool PRO>
 __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
     constexpr int E = 8;               // state values per lane
     constexpr int L = DK / E;          // lanes per row
@@ -149,7 +156,8 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
             if (c < KCH) {
                 const int j = c / L;
                 if (st * TB + j < T) {
-                    const size_t e = ((size_t)(b * T + tok_of(st, j)) * H + h) * DK + (c % L) * E;
+                    const size_t e = (size_t)b * p.qk_bs + (size_t)tok_of(st, j) * p.qk_ts + (size_t)h * DK +
+                                     (c % L) * E;
                     kr[i].load(p.k, e);
                     qr[i].load(p.q, e);
                 } else {
@@ -165,7 +173,8 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
                 const int j = c / vpt_tok;
                 const int part = c % vpt_tok;
                 if (st * TB + j < T)
-                    vr[i].load(p.v, ((size_t)(b * T + tok_of(st, j)) * H + h) * dv + row0 + part * E);
+                    vr[i].load(p.v, (size_t)b * p.v_bs + (size_t)tok_of(st, j) * p.v_ts + (size_t)h * dv + row0 +
+                                        part * E);
                 else
                     vr[i].zero();
             }
@@ -190,6 +199,20 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
                 float kk[E], qq[E];
                 kr[i].to_f32(kk);
                 qr[i].to_f32(qq);
+                if constexpr (PRO) {  // q / max(||q||, 1e-12), the same for k
+                    float sk = 0.f, sq = 0.f;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        sk = fmaf(kk[e], kk[e], sk);
+                        sq = fmaf(qq[e], qq[e], sq);
+                    }
+                    const float rk = inv_norm(group_sum<L>(sk)), rq = inv_norm(group_sum<L>(sq));
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        kk[e] *= rk;
+                        qq[e] *= rq;
+                    }
+                }
                 float d = 0.f;
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
@@ -214,8 +237,13 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
             }
         }
         if (tid < TB) {
-            gb[tid] = br;
-            ga[tid] = ar;
+            if constexpr (PRO) {
+                gb[tid] = sigmoid_f32(br);
+                ga[tid] = decay_from_logit(ar);
+            } else {
+                gb[tid] = br;
+                ga[tid] = ar;
+            }
         }
     };
 
@@ -277,6 +305,7 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     const int rows = (NT / L) < a.dv ? (NT / L) : a.dv;
     ScanParams p;
     p.q = a.q; p.k = a.k; p.v = a.v; p.beta = a.beta; p.decay = a.decay;
+    p.qk_ts = a.qk_ts; p.qk_bs = a.qk_bs; p.v_ts = a.v_ts; p.v_bs = a.v_bs;
     p.state_in = a.state_in; p.state_out = a.state_out; p.out = a.out;
     p.partial = a.partial; p.partial_rev = a.partial_rev;
     p.T = a.T; p.B = a.B; p.H = a.H; p.dv = a.dv; p.reverse = a.reverse; p.out_mode = a.out_mode;
@@ -284,10 +313,14 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.scale = (float)(1.0 / __builtin_sqrt((double)DK));
     dim3 grid(a.dv / rows, a.H, a.B * (a.both_dirs ? 2 : 1));
     dim3 block(rows * L);
-    if (a.io_bf16)
-        hipLaunchKernelGGL((scan_kernel<DK, true>), grid, block, 0, stream, p);
+    if (a.io_bf16 && a.prologue)
+        hipLaunchKernelGGL((scan_kernel<DK, true, true>), grid, block, 0, stream, p);
+    else if (a.io_bf16)
+        hipLaunchKernelGGL((scan_kernel<DK, true, false>), grid, block, 0, stream, p);
+    else if (a.prologue)
+        hipLaunchKernelGGL((scan_kernel<DK, false, true>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((scan_kernel<DK, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((scan_kernel<DK, false, false>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

@@ -18,9 +18,11 @@
  * of the FlashDreams "SANA-WM" page (section "Bidirectional variant").  The
  * pages do not print the update; the formula above is the gated delta rule.
  *
- * beta (b_t) and decay (a_t) are plain values in [0, 1], one per token and
- * head -- not logits, not log-decays.  The library does not normalise q or k
- * and applies no gate activation; callers do that beforehand.
+ * gdn_forward and gdn_forward_bidi take q and k as given, and beta (b_t) and
+ * decay (a_t) as plain values in [0, 1], one per token and head -- not logits,
+ * not log-decays.  gdn_forward_packed and gdn_forward_bidi_packed instead read
+ * q, k and v straight from a packed projection and apply the input prologue
+ * inside the kernels (see there).
  *
  * Layouts.  Every tensor pointer is a DEVICE pointer to a contiguous,
  * row-major array on the handle's device:
@@ -34,8 +36,9 @@
  * the handle and its device scratch, allocated once in gdn_create and freed in
  * gdn_free: the two fp32 partials of gdn_forward_bidi (GDN_FLAG_BIDI), and, on
  * handles the bf16 chunked kernel can serve (bf16 I/O, d_k and d_v >= 32), the
- * per-chunk triangular inverses of that kernel (6 KiB per direction, b, h and
- * 64-token chunk up to max_T).  gdn_forward and gdn_forward_bidi allocate nothing, never
+ * per-chunk triangular inverses of that kernel and, for the packed entry
+ * points, each token's inverse k norm (6.25 KiB per direction, b, h and 64-token
+ * chunk up to max_T).  The forward calls allocate nothing, never
  * synchronise and never copy between host and device: they validate, enqueue
  * kernels on the given stream and return.  Device faults surface at the
  * caller's next synchronisation, as with any HIP launch.  A handle must be
@@ -125,6 +128,47 @@ int gdn_forward(gdn_handle h, const void *q, const void *k, const void *v,
 int gdn_forward_bidi(gdn_handle h, const void *q, const void *k, const void *v,
                      const float *beta, const float *decay, void *out,
                      long long T, int chunk_len, void *hip_stream);
+
+/*
+ * Fused input prologue.  The same forms as gdn_forward / gdn_forward_bidi
+ * (same handle, state, out, T, chunk_len and stream rules), with the inputs
+ * taken from a packed token-major projection and prepared in the kernels:
+ *
+ *   qkv    io_dtype; element j of token t of batch element b is
+ *          qkv[b * batch_stride + t * token_stride + j], with
+ *            q of head h at j = h d_k + (0 .. d_k-1),
+ *            k of head h at j = H d_k + h d_k + (0 .. d_k-1),
+ *            v of head h at j = 2 H d_k + h d_v + (0 .. d_v-1)
+ *          -- the [N, 3C] layout (C = H d) whose split into q, k, v the
+ *          librediffusion PR #21 page's review moves onto the GPU (suggestion
+ *          "k_split_qkv"), here read in place by the recurrence kernels.
+ *   token_stride, batch_stride   in elements; token_stride >= 2 H d_k + H d_v,
+ *          batch_stride >= 0, both multiples of 16 bytes; qkv 16-byte aligned.
+ *   beta_logit, decay_logit      [B, T, H] float32 logits x_b, x_a.
+ *
+ * Per token and head the kernels use
+ *     q <- q / max(||q||_2, 1e-12),  k <- k / max(||k||_2, 1e-12),
+ *     b_t = sigmoid(x_b) = 1 / (1 + e^{-x_b}),
+ *     a_t = exp(-softplus(x_a)) = 1 / (1 + e^{x_a}),
+ * computed in fp32 from the inputs as given (the sglang SANA-WM record widens
+ * q, k, v with .float().contiguous() in a separate pass before its scan; here
+ * nothing is materialised).  out (contiguous [B, T, H, d_v]) and state_out
+ * must not overlap the byte range qkv spans.  Errors as for gdn_forward, plus
+ * GDN_ERR_ARG for a token_stride below the packed row, GDN_ERR_ALIGN for a
+ * stride that is not a multiple of 16 bytes and GDN_ERR_UNSUPPORTED for a
+ * token_stride above 2^24 elements.
+ */
+int gdn_forward_packed(gdn_handle h, const void *qkv, long long token_stride,
+                       long long batch_stride, const float *beta_logit,
+                       const float *decay_logit, const float *state_in,
+                       float *state_out, void *out, long long T, int chunk_len,
+                       void *hip_stream);
+
+/* Bidirectional form with the fused prologue (needs GDN_FLAG_BIDI). */
+int gdn_forward_bidi_packed(gdn_handle h, const void *qkv, long long token_stride,
+                            long long batch_stride, const float *beta_logit,
+                            const float *decay_logit, void *out, long long T,
+                            int chunk_len, void *hip_stream);
 
 /* Release the handle and its scratch.  NULL is a no-op. */
 void gdn_free(gdn_handle h);

@@ -22,8 +22,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert set(names) >= {"gdn_create", "gdn_forward", "gdn_forward_bidi", "gdn_free",
-                          "gdn_last_error", "gdn_version"}
+    assert set(names) >= {"gdn_create", "gdn_forward", "gdn_forward_bidi", "gdn_forward_packed",
+                          "gdn_forward_bidi_packed", "gdn_free", "gdn_last_error", "gdn_version"}
     lib = ctypes.CDLL(gb.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in gdn.h but not exported"
@@ -111,6 +111,85 @@ def test_bidi_dry_run(dry):
     assert gb.gdn_forward_bidi(h, a["q"], a["k"], a["v"], a["beta"], a["decay"], a["out"], 5, 1) == gb.GDN_ERR_ARG
     assert "GDN_FLAG_BIDI" in gb.gdn_last_error(h)
     gb.gdn_free(h)
+
+
+# Packed prologue calls on the dry-run handle (B=2, H=3, d_k=64, d_v=32, bf16): the
+# packed row is 2 H d_k + H d_v = 480 elements (960 bytes).
+ROW = 2 * 3 * 64 + 3 * 32
+
+
+def pfwd(h, T=100, chunk=1, ts=ROW, bs=None, **over):
+    a = dict(ADDR)
+    a.update(over)
+    bs = T * ts if bs is None else bs
+    return gb.gdn_forward_packed(h, a["q"], ts, bs, a["beta"], a["decay"], a["s_in"], a["s_out"], a["out"], T,
+                                 chunk)
+
+
+def test_packed_dry_run_valid_calls(dry):
+    assert pfwd(dry) == gb.GDN_OK
+    for chunk in (0, 1, 16, 32, 64, 128):
+        assert pfwd(dry, chunk=chunk) == gb.GDN_OK
+    assert pfwd(dry, ts=ROW + 8) == gb.GDN_OK           # padded rows (976 bytes)
+    assert pfwd(dry, bs=0) == gb.GDN_OK                 # both batch elements read the same tokens
+    assert pfwd(dry, s_in=None, s_out=None) == gb.GDN_OK
+    assert pfwd(dry, s_out=ADDR["s_in"]) == gb.GDN_OK   # in-place carry
+    assert pfwd(dry, T=0, q=None, beta=None, decay=None, out=None) == gb.GDN_OK
+    assert gb.gdn_last_error(dry) == ""
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(ts=ROW - 8), gb.GDN_ERR_ARG),
+    (dict(ts=ROW + 2), gb.GDN_ERR_ALIGN),
+    (dict(bs=-ROW), gb.GDN_ERR_ARG),
+    (dict(bs=4), gb.GDN_ERR_ALIGN),
+    (dict(ts=(1 << 24) + 8), gb.GDN_ERR_UNSUPPORTED),
+    (dict(q=ADDR["q"] + 8), gb.GDN_ERR_ALIGN),
+    (dict(out=ADDR["out"] + 8), gb.GDN_ERR_ALIGN),
+    (dict(beta=ADDR["beta"] + 2), gb.GDN_ERR_ALIGN),
+    (dict(q=None), gb.GDN_ERR_ARG),
+    (dict(decay=None), gb.GDN_ERR_ARG),
+    (dict(T=1001), gb.GDN_ERR_ARG),
+    (dict(chunk=48), gb.GDN_ERR_UNSUPPORTED),
+    (dict(out=ADDR["q"] + 4096), gb.GDN_ERR_ALIAS),
+    (dict(s_out=ADDR["q"]), gb.GDN_ERR_ALIAS),
+    (dict(out=ADDR["beta"]), gb.GDN_ERR_ALIAS),
+])
+def test_packed_dry_run_rejections(dry, over, code):
+    assert pfwd(dry, **over) == code
+    assert gb.gdn_last_error(dry) != ""
+
+
+def test_packed_alias_extent(dry):
+    # the extent of qkv is ((B-1) bs + (T-1) ts + row) elements; out may start right after it
+    T = 100
+    ext = ((2 - 1) * T * ROW + (T - 1) * ROW + ROW) * 2
+    assert pfwd(dry, T=T, out=ADDR["q"] + ext) == gb.GDN_OK
+    assert pfwd(dry, T=T, out=ADDR["q"] + ext - 16) == gb.GDN_ERR_ALIAS
+    # an output in the padding between packed rows still counts as overlapping
+    assert pfwd(dry, T=T, ts=ROW + 64, out=ADDR["q"] + 2 * ROW) == gb.GDN_ERR_ALIAS
+
+
+def test_packed_bidi_dry_run(dry):
+    a = ADDR
+    ok = gb.gdn_forward_bidi_packed(dry, a["q"], ROW, 100 * ROW, a["beta"], a["decay"], a["out"], 100, 64)
+    assert ok == gb.GDN_OK
+    bad = gb.gdn_forward_bidi_packed(dry, a["q"], ROW, 100 * ROW, a["beta"], a["decay"], a["q"] + 64, 100, 64)
+    assert bad == gb.GDN_ERR_ALIAS
+    st, h = gb.gdn_create(-1, 1, 1, 16, 16, gb.GDN_F32, 10, 0)
+    assert gb.gdn_forward_bidi_packed(h, a["q"], 48, 480, a["beta"], a["decay"], a["out"], 5, 1) == gb.GDN_ERR_ARG
+    assert "GDN_FLAG_BIDI" in gb.gdn_last_error(h)
+    gb.gdn_free(h)
+
+
+def test_torch_wrapper_checks_packed_shapes():
+    import torch
+    g = gb.GDN(1, 2, 16, 16, "fp32", max_T=10, device=-1)
+    with pytest.raises(ValueError):  # W below 2 H d_k + H d_v = 96
+        g.forward_packed(torch.zeros(1, 4, 80), torch.zeros(1, 4, 2), torch.zeros(1, 4, 2))
+    with pytest.raises(ValueError):  # last stride not 1
+        g.forward_packed(torch.zeros(1, 96, 4).transpose(1, 2), torch.zeros(1, 4, 2), torch.zeros(1, 4, 2))
+    g.close()
 
 
 @pytest.mark.parametrize("args,code", [
