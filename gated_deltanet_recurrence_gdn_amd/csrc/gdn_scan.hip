@@ -81,6 +81,21 @@ struct Chunk8<false> {
     }
 };
 
+// u and p each summed over the 16 lanes of a DPP row in one shared chain: after
+// the first exchange the even lanes hold partial sums of u and the odd lanes
+// partial sums of p, and rotations of the row by 2, 4 and 8 finish each parity
+// class in every lane.  Returns u in every lane; p is left in the odd lanes.
+__device__ __forceinline__ float row16_sum2(float u, float &p, bool odd) {
+    float t = odd ? p : u;
+    const float o = odd ? u : p;
+    t += dpp_mov<0xB1>(o);   // quad_perm [1,0,3,2]: the pair's other lane
+    t += dpp_mov<0x122>(t);  // row_ror:2
+    t += dpp_mov<0x124>(t);  // row_ror:4
+    t += dpp_mov<0x128>(t);  // row_ror:8
+    p = t;
+    return dpp_mov<0xA0>(t);  // quad_perm [0,0,2,2]: the even lane's sum
+}
+
 template <bool BF16>
 __device__ __forceinline__ void store_out(void *out, size_t elem, float x) {
     if constexpr (BF16)
@@ -89,23 +104,31 @@ __device__ __forceinline__ void store_out(void *out, size_t elem, float x) {
         reinterpret_cast<float *>(out)[elem] = x;
 }
 
-template <int DK, bool BF16, bool PRO>
+// A block holds `rows` consecutive state rows of one (b, h).  A row's d_k values
+// live in the VGPRs of L = DK / E lanes: lane `seg` of the row holds d_k indices
+// 4 (seg + L i) + m (i < E / 4, m < 4), so the row's lanes read one contiguous
+// run of LDS per float4 and every row reads the same addresses (a broadcast).
+template <int DK, int E, bool BF16, bool PRO>
 __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
-    constexpr int E = 8;               // state values per lane
-    constexpr int L = DK / E;          // lanes per row
+    constexpr int L = DK / E;            // lanes per state row
+    constexpr int V4 = E / 4;            // float4 of k (and of q) per lane and token
     constexpr int ROWS_MAX = NT / L;
-    constexpr int KCH = TB * DK / E;   // 8-element q/k chunks per stage
+    constexpr int SL = DK / 8;           // staging: lanes per q/k row, 8 elements each
+    constexpr int KCH = TB * SL;         // 8-element q/k chunks per stage
+    // a block has rows * L >= 16 L threads (d_v >= 16)
+    constexpr int KPT = (KCH + 16 * L - 1) / (16 * L);
+    constexpr int VPT = (TB / 8 + L - 1) / L;
 
     __shared__ __align__(16) float kf[TB][DK];
     __shared__ __align__(16) float qf[TB][DK];
     __shared__ float vf[TB][ROWS_MAX];
     __shared__ float of[TB][ROWS_MAX];
-    __shared__ float gb[TB], ga[TB], gkq[TB];
+    __shared__ __align__(16) float gt[TB][4];  // a, b, (k . q) / sqrt(d_k) per token
 
     const int nthr = blockDim.x;
     const int rows = nthr / L;
     const int tid = threadIdx.x;
-    const int seg = tid % L;           // which 8 of the row's d_k values
+    const int seg = tid % L;           // which E of the row's d_k values
     const int rloc = tid / L;          // row within the block
     const int row0 = blockIdx.x * rows;
     const int h = blockIdx.y;
@@ -118,169 +141,217 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
     const int H = p.H;
     const long long T = p.T;
     const int dv = p.dv;
+    const int vch = TB * rows / 8;     // 8-element v chunks per stage
+    const int vpt_tok = rows / 8;      // v chunks per token
 
-    // q/k chunks this thread stages: chunk c -> token c / L, segment c % L.
-    // A block has rows * L >= 16 L = 2 DK threads (d_v >= 16), so at most
-    // KCH / (2 DK) = TB / 16 = 2 chunks per thread.
-    constexpr int KPT = TB / 16;
-    // v chunks: TB * rows / 8 per stage, i.e. TB / (8 L) per thread.
-    constexpr int VPT = (TB / E + L - 1) / L;
-    const int vch = TB * rows / E;
-    const int vpt_tok = rows / E;         // v chunks per token
-
-    // Initial state: this lane's 8 values of row (row0 + rloc).
+    // Initial state: this lane's E values of row (row0 + rloc).
     float s[E];
-    const size_t srow = ((size_t)(b * H + h) * dv + row0 + rloc) * DK + seg * E;
-    if (p.state_in) {
-        const float4 *sp = reinterpret_cast<const float4 *>(p.state_in + srow);
-        const float4 a0 = sp[0], a1 = sp[1];
-        s[0] = a0.x; s[1] = a0.y; s[2] = a0.z; s[3] = a0.w;
-        s[4] = a1.x; s[5] = a1.y; s[6] = a1.z; s[7] = a1.w;
-    } else {
+    const size_t srow = ((size_t)(b * H + h) * dv + row0 + rloc) * DK;
 #pragma unroll
-        for (int e = 0; e < E; ++e) s[e] = 0.f;
+    for (int i = 0; i < V4; ++i) {
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (p.state_in) x = *reinterpret_cast<const float4 *>(p.state_in + srow + 4 * (seg + L * i));
+        s[4 * i] = x.x; s[4 * i + 1] = x.y; s[4 * i + 2] = x.z; s[4 * i + 3] = x.w;
     }
+    // Wait for the state here, once: the compiler cannot tell through the loops
+    // below that this conditional load has landed, and would otherwise wait for
+    // every load in flight (the next stage's prefetch) before each stage's tokens.
+    __builtin_amdgcn_s_waitcnt(0);
 
     const long long nst = (T + TB - 1) / TB;
     Chunk8<BF16> kr[KPT], qr[KPT], vr[VPT];
-    float br = 0.f, ar = 0.f;
+    float br = 0.f, ar = 1.f;
 
-    auto tok_of = [&](long long st, int j) -> long long {
-        const long long sidx = st * TB + j;
-        return reverse ? T - 1 - sidx : sidx;
+    // Token at walk position sidx, clamped to the last one: the loads are
+    // unconditional (past the end they re-read a real token), and commit()
+    // turns padding into exact no-ops.
+    auto tok_of = [&](long long sidx) -> long long {
+        const long long c = sidx < T ? sidx : T - 1;
+        return reverse ? T - 1 - c : c;
     };
     auto issue = [&](long long st) {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int c = tid + i * nthr;
             if (c < KCH) {
-                const int j = c / L;
-                if (st * TB + j < T) {
-                    const size_t e = (size_t)b * p.qk_bs + (size_t)tok_of(st, j) * p.qk_ts + (size_t)h * DK +
-                                     (c % L) * E;
-                    kr[i].load(p.k, e);
-                    qr[i].load(p.q, e);
-                } else {
-                    kr[i].zero();
-                    qr[i].zero();
-                }
+                const size_t e = (size_t)b * p.qk_bs + (size_t)tok_of(st * TB + c / SL) * p.qk_ts +
+                                 (size_t)h * DK + (c % SL) * 8;
+                kr[i].load(p.k, e);
+                qr[i].load(p.q, e);
             }
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int c = tid + i * nthr;
-            if (c < vch) {
-                const int j = c / vpt_tok;
-                const int part = c % vpt_tok;
-                if (st * TB + j < T)
-                    vr[i].load(p.v, (size_t)b * p.v_bs + (size_t)tok_of(st, j) * p.v_ts + (size_t)h * dv + row0 +
-                                        part * E);
-                else
-                    vr[i].zero();
-            }
+            if (c < vch)
+                vr[i].load(p.v, (size_t)b * p.v_bs + (size_t)tok_of(st * TB + c / vpt_tok) * p.v_ts +
+                                    (size_t)h * dv + row0 + (c % vpt_tok) * 8);
         }
         if (tid < TB) {
-            if (st * TB + tid < T) {
-                const size_t g = (size_t)(b * T + tok_of(st, tid)) * H + h;
-                br = p.beta[g];
-                ar = p.decay[g];
-            } else {
-                br = 0.f;
-                ar = 1.f;
-            }
+            const size_t g = (size_t)(b * T + tok_of(st * TB + tid)) * H + h;
+            br = p.beta[g];
+            ar = p.decay[g];
         }
     };
-    auto commit = [&]() {
+    // Registers -> LDS in fp32.  Tokens past T become b = 0, a = 1, q = k = v = 0:
+    // then u = 0, nu = 0 and S is left exactly as it was.
+    auto commit = [&](long long st) {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int c = tid + i * nthr;
             if (c < KCH) {
-                const int j = c / L, sg = c % L;
-                float kk[E], qq[E];
+                const int j = c / SL, sg = c % SL;
+                const bool real = st * TB + j < T;
+                float kk[8], qq[8];
                 kr[i].to_f32(kk);
                 qr[i].to_f32(qq);
+                if (!real) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) kk[e] = qq[e] = 0.f;
+                }
                 if constexpr (PRO) {  // q / max(||q||, 1e-12), the same for k
                     float sk = 0.f, sq = 0.f;
 #pragma unroll
-                    for (int e = 0; e < E; ++e) {
+                    for (int e = 0; e < 8; ++e) {
                         sk = fmaf(kk[e], kk[e], sk);
                         sq = fmaf(qq[e], qq[e], sq);
                     }
-                    const float rk = inv_norm(group_sum<L>(sk)), rq = inv_norm(group_sum<L>(sq));
+                    const float rk = inv_norm(group_sum<SL>(sk)), rq = inv_norm(group_sum<SL>(sq));
 #pragma unroll
-                    for (int e = 0; e < E; ++e) {
+                    for (int e = 0; e < 8; ++e) {
                         kk[e] *= rk;
                         qq[e] *= rq;
                     }
                 }
                 float d = 0.f;
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    kf[j][sg * E + e] = kk[e];
-                    qf[j][sg * E + e] = qq[e];
-                    d = fmaf(kk[e], qq[e], d);
-                }
-                d = group_sum<L>(d);
-                if (sg == 0) gkq[j] = d;
+                for (int e = 0; e < 8; ++e) d = fmaf(kk[e], qq[e], d);
+                d = group_sum<SL>(d) * p.scale;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qq[e] *= p.scale;  // o = S q / sqrt(d_k): the scale rides on q
+                *reinterpret_cast<float4 *>(&kf[j][sg * 8]) = make_float4(kk[0], kk[1], kk[2], kk[3]);
+                *reinterpret_cast<float4 *>(&kf[j][sg * 8 + 4]) = make_float4(kk[4], kk[5], kk[6], kk[7]);
+                *reinterpret_cast<float4 *>(&qf[j][sg * 8]) = make_float4(qq[0], qq[1], qq[2], qq[3]);
+                *reinterpret_cast<float4 *>(&qf[j][sg * 8 + 4]) = make_float4(qq[4], qq[5], qq[6], qq[7]);
+                if (sg == 0) gt[j][2] = d;
             }
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int c = tid + i * nthr;
             if (c < vch) {
-                const int j = c / vpt_tok;
-                const int part = c % vpt_tok;
-                float vv[E];
+                const int j = c / vpt_tok, part = c % vpt_tok;
+                const bool real = st * TB + j < T;
+                float vv[8];
                 vr[i].to_f32(vv);
 #pragma unroll
-                for (int e = 0; e < E; ++e) vf[j][part * E + e] = vv[e];
+                for (int e = 0; e < 8; ++e) vf[j][part * 8 + e] = real ? vv[e] : 0.f;
             }
         }
         if (tid < TB) {
+            const bool real = st * TB + tid < T;
+            float bb = br, aa = ar;
             if constexpr (PRO) {
-                gb[tid] = sigmoid_f32(br);
-                ga[tid] = decay_from_logit(ar);
-            } else {
-                gb[tid] = br;
-                ga[tid] = ar;
+                bb = sigmoid_f32(br);
+                aa = decay_from_logit(ar);
             }
+            gt[tid][0] = real ? aa : 1.f;
+            gt[tid][1] = real ? bb : 0.f;
         }
+    };
+
+    // One token, with its operands already in registers.
+    struct Tok {
+        float4 k[V4], q[V4];
+        float4 g;  // a, b, (k . q) / sqrt(d_k)
+        float v;
+    };
+    auto ld_tok = [&](int j, Tok &t) {
+#pragma unroll
+        for (int i = 0; i < V4; ++i) {
+            t.k[i] = *reinterpret_cast<const float4 *>(&kf[j][4 * (seg + L * i)]);
+            t.q[i] = *reinterpret_cast<const float4 *>(&qf[j][4 * (seg + L * i)]);
+        }
+        t.g = *reinterpret_cast<const float4 *>(&gt[j][0]);
+        t.v = vf[j][rloc];
+    };
+    const bool odd = (tid & 1) != 0;
+    auto step = [&](int j, const Tok &t) {
+        // u = S_i . k and p = S_i . q (q carries 1/sqrt(d_k))
+        float u, pq;
+        if constexpr (L == 16) {
+            u = 0.f;
+            pq = 0.f;
+#pragma unroll
+            for (int i = 0; i < V4; ++i) {
+                const float kk[4] = {t.k[i].x, t.k[i].y, t.k[i].z, t.k[i].w};
+                const float qq[4] = {t.q[i].x, t.q[i].y, t.q[i].z, t.q[i].w};
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    u = fmaf(s[4 * i + m], kk[m], u);
+                    pq = fmaf(s[4 * i + m], qq[m], pq);
+                }
+            }
+            u = row16_sum2(u, pq, odd);  // pq now on the odd lanes
+        } else {
+            // two partial sums each (four independent chains)
+            float u0 = 0.f, u1 = 0.f, p0 = 0.f, p1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < V4; ++i) {
+                const float kk[4] = {t.k[i].x, t.k[i].y, t.k[i].z, t.k[i].w};
+                const float qq[4] = {t.q[i].x, t.q[i].y, t.q[i].z, t.q[i].w};
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    if (m & 1) {
+                        u1 = fmaf(s[4 * i + m], kk[m], u1);
+                        p1 = fmaf(s[4 * i + m], qq[m], p1);
+                    } else {
+                        u0 = fmaf(s[4 * i + m], kk[m], u0);
+                        p0 = fmaf(s[4 * i + m], qq[m], p0);
+                    }
+                }
+            }
+            u = group_sum<L>(u0 + u1);
+            pq = group_sum<L>(p0 + p1);
+        }
+        const float a = t.g.x, bt = t.g.y, kq = t.g.z;
+        const float nu = bt * (t.v - a * u);
+#pragma unroll
+        for (int i = 0; i < V4; ++i) {
+            s[4 * i] = fmaf(nu, t.k[i].x, a * s[4 * i]);
+            s[4 * i + 1] = fmaf(nu, t.k[i].y, a * s[4 * i + 1]);
+            s[4 * i + 2] = fmaf(nu, t.k[i].z, a * s[4 * i + 2]);
+            s[4 * i + 3] = fmaf(nu, t.k[i].w, a * s[4 * i + 3]);
+        }
+        // one lane of the row writes o (q and k . q carry 1/sqrt(d_k))
+        if (seg == (L == 16 ? 1 : 0)) of[j][rloc] = fmaf(a, pq, nu * kq);
     };
 
     if (nst > 0) {
         issue(0);
-        commit();
+        commit(0);
         __syncthreads();
     }
     for (long long st = 0; st < nst; ++st) {
         const bool more = st + 1 < nst;
         if (more) issue(st + 1);
-        const int nvalid = (int)((T - st * TB) < TB ? (T - st * TB) : TB);
-        for (int j = 0; j < nvalid; ++j) {
-            const float4 *kp = reinterpret_cast<const float4 *>(&kf[j][seg * E]);
-            const float4 *qp = reinterpret_cast<const float4 *>(&qf[j][seg * E]);
-            const float4 k0 = kp[0], k1 = kp[1], q0 = qp[0], q1 = qp[1];
-            const float kk[E] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-            const float qq[E] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-            float u = 0.f, pq = 0.f;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                u = fmaf(s[e], kk[e], u);
-                pq = fmaf(s[e], qq[e], pq);
-            }
-            u = group_sum<L>(u);
-            pq = group_sum<L>(pq);
-            const float a = ga[j], bt = gb[j];
-            const float nu = bt * (vf[j][rloc] - a * u);
-#pragma unroll
-            for (int e = 0; e < E; ++e) s[e] = fmaf(nu, kk[e], a * s[e]);
-            if (seg == 0) of[j][rloc] = (a * pq + nu * gkq[j]) * p.scale;
+        // every stage runs all TB tokens (padding is a no-op); token j + 1's operands
+        // are read from LDS while token j is computed (the read after the last token
+        // wraps to token 0 of the same stage and is not used)
+        Tok A, B;
+        ld_tok(0, A);
+        for (int j = 0; j < TB; j += 2) {
+            ld_tok(j + 1, B);
+            step(j, A);
+            ld_tok((j + 2) % TB, A);
+            step(j + 1, B);
         }
         __syncthreads();
         // Write this stage's outputs: token j, rows [row0, row0 + rows).
+        const int nvalid = (int)((T - st * TB) < TB ? (T - st * TB) : TB);
         for (int idx = tid; idx < nvalid * rows; idx += nthr) {
             const int j = idx / rows, r = idx % rows;
-            const size_t e = ((size_t)(b * T + tok_of(st, j)) * H + h) * dv + row0 + r;
+            const size_t e = ((size_t)(b * T + tok_of(st * TB + j)) * H + h) * dv + row0 + r;
             const float o = of[j][r];
             if (p.out_mode == OUT_PARTIAL) {
                 partial[e] = o;
@@ -288,21 +359,40 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
                 store_out<BF16>(p.out, e, o);
             }
         }
-        if (more) commit();
+        if (more) commit(st + 1);
         __syncthreads();
     }
 
     if (p.state_out) {
-        float4 *sp = reinterpret_cast<float4 *>(p.state_out + srow);
-        sp[0] = make_float4(s[0], s[1], s[2], s[3]);
-        sp[1] = make_float4(s[4], s[5], s[6], s[7]);
+#pragma unroll
+        for (int i = 0; i < V4; ++i)
+            *reinterpret_cast<float4 *>(p.state_out + srow + 4 * (seg + L * i)) =
+                make_float4(s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]);
     }
 }
 
+template <int DK, int E, bool BF16, bool PRO>
+hipError_t launch_e(const PassArgs &a, const ScanParams &p, hipStream_t stream) {
+    constexpr int L = DK / E;
+    const int rows = (NT / L) < a.dv ? (NT / L) : a.dv;
+    dim3 grid(a.dv / rows, a.H, a.B * (a.both_dirs ? 2 : 1));
+    hipLaunchKernelGGL((scan_kernel<DK, E, BF16, PRO>), grid, dim3(rows * L), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int DK, int E>
+hipError_t launch_dk_e(const PassArgs &a, const ScanParams &p, hipStream_t stream) {
+    if (a.io_bf16)
+        return a.prologue ? launch_e<DK, E, true, true>(a, p, stream) : launch_e<DK, E, true, false>(a, p, stream);
+    return a.prologue ? launch_e<DK, E, false, true>(a, p, stream) : launch_e<DK, E, false, false>(a, p, stream);
+}
+
+// E = 8 state values per lane unless that puts more than two waves on a SIMD (256
+// CUs x 4): the second wave hides the latency of each token's dependent chain (dot
+// products, cross-lane sums, nu, update), which one wave alone leaves exposed.
+// With more work than that, E = 16 halves the cross-lane sums per state value.
 template <int DK>
 hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
-    constexpr int L = DK / 8;
-    const int rows = (NT / L) < a.dv ? (NT / L) : a.dv;
     ScanParams p;
     p.q = a.q; p.k = a.k; p.v = a.v; p.beta = a.beta; p.decay = a.decay;
     p.qk_ts = a.qk_ts; p.qk_bs = a.qk_bs; p.v_ts = a.v_ts; p.v_bs = a.v_bs;
@@ -311,17 +401,9 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.T = a.T; p.B = a.B; p.H = a.H; p.dv = a.dv; p.reverse = a.reverse; p.out_mode = a.out_mode;
     p.both_dirs = a.both_dirs;
     p.scale = (float)(1.0 / __builtin_sqrt((double)DK));
-    dim3 grid(a.dv / rows, a.H, a.B * (a.both_dirs ? 2 : 1));
-    dim3 block(rows * L);
-    if (a.io_bf16 && a.prologue)
-        hipLaunchKernelGGL((scan_kernel<DK, true, true>), grid, block, 0, stream, p);
-    else if (a.io_bf16)
-        hipLaunchKernelGGL((scan_kernel<DK, true, false>), grid, block, 0, stream, p);
-    else if (a.prologue)
-        hipLaunchKernelGGL((scan_kernel<DK, false, true>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((scan_kernel<DK, false, false>), grid, block, 0, stream, p);
-    return hipGetLastError();
+    const long long waves8 = (long long)a.B * a.H * (a.both_dirs ? 2 : 1) * a.dv * (DK / 8) / 64;
+    if (waves8 > 2048) return launch_dk_e<DK, 16>(a, p, stream);
+    return launch_dk_e<DK, 8>(a, p, stream);
 }
 
 // out = round(partial + partial_rev), 4 elements per thread.
