@@ -35,10 +35,11 @@ CHUNK_KERNEL = "tm_kernel + chunk_kernel"  # the two launches of one chunked gdn
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def algorithmic_bytes(B, T, H, dk, dv, es=2):
-    """q, k, v read and out written in the I/O dtype, beta and decay read in fp32, the
-    fp32 state read once and written once."""
-    return B * T * H * ((2 * dk + 2 * dv) * es + 8) + 2 * B * H * dk * dv * 4
+def algorithmic_bytes(B, T, H, dk, dv, es=2, es_out=None):
+    """q, k, v read in the input dtype (es bytes) and out written (es_out bytes, es by
+    default), beta and decay read in fp32, the fp32 state read once and written once."""
+    es_out = es if es_out is None else es_out
+    return B * T * H * ((2 * dk + dv) * es + dv * es_out + 8) + 2 * B * H * dk * dv * 4
 
 
 def chunk_flops(B, T, H, dk, dv, C=64):
@@ -269,6 +270,19 @@ def measure_forms(torch, gb, inputs, d, g, x):
                   "into the per-token decay factors, inverse q norms from diag(Q Q^T) on MFMA in the output "
                   "waves; sigmoid / exp(-softplus) of the logits in the gate wave"}
     gp.close()
+    del qkv, bl, dl
+
+    # FP8 (E4M3) q, k, v on the bench shape, out in bf16.
+    x8 = {k_: v_.cuda() for k_, v_ in inputs.make_inputs(B, T, H, dk, dv, "fp8", seed=0, a_mean=a_mean).items()}
+    g8 = gb.GDN(B, H, dk, dv, "fp8", max_T=T)
+    ms = timed(torch, lambda: gb.gdn_forward(g8.h, x8["q"], x8["k"], x8["v"], x8["beta"], x8["decay"], None, None,
+                                             out, T, 64, stream), 20)
+    ab8 = algorithmic_bytes(B, T, H, dk, dv, es=1, es_out=2)
+    forms["fp8_batched_d128"] = {
+        "ms": ms, "token_heads_per_s": B * H * T / (ms / 1e3), "algorithmic_bytes": ab8,
+        "hbm_gbs": ab8 / (ms / 1e3) / 1e9,
+        "design": "E4M3 rows widened exactly to bf16 by the loaders (v_cvt_scalef32_pk_bf16_fp8); bf16 MFMA"}
+    g8.close()
     return forms
 
 

@@ -29,6 +29,7 @@ STATUS_NAMES = {0: "GDN_OK", -1: "GDN_ERR_ARG", -2: "GDN_ERR_UNSUPPORTED", -3: "
                 -4: "GDN_ERR_ALIAS", -5: "GDN_ERR_DEVICE", -6: "GDN_ERR_OOM", -7: "GDN_ERR_LAUNCH"}
 GDN_F32 = 0
 GDN_BF16 = 1
+GDN_FP8 = 2
 GDN_FLAG_BIDI = 1
 
 
@@ -151,7 +152,7 @@ class GDN:
     def __init__(self, B, H, d_k, d_v, dtype="bf16", max_T=0, device=0, bidi=False):
         self.B, self.H, self.d_k, self.d_v = B, H, d_k, d_v
         self.dtype = dtype
-        self.io = {"bf16": GDN_BF16, "fp32": GDN_F32}[dtype]
+        self.io = {"bf16": GDN_BF16, "fp32": GDN_F32, "fp8": GDN_FP8}[dtype]
         self.max_T = max_T
         self.device = device
         self.h = None
@@ -179,8 +180,14 @@ class GDN:
             raise GDNError(st, gdn_last_error(self.h))
 
     def _torch_dtype(self):
+        """dtype of q, k, v (and qkv)."""
         import torch
-        return {"bf16": torch.bfloat16, "fp32": torch.float32}[self.dtype]
+        return {"bf16": torch.bfloat16, "fp32": torch.float32, "fp8": torch.float8_e4m3fn}[self.dtype]
+
+    def _out_dtype(self):
+        """dtype of out: fp32 for fp32 inputs, bf16 otherwise."""
+        import torch
+        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
 
     def _check_inputs(self, q, k, v, beta, decay):
         import torch
@@ -201,7 +208,7 @@ class GDN:
         import torch
         T = self._check_inputs(q, k, v, beta, decay)
         if out is None:
-            out = torch.empty((self.B, T, self.H, self.d_v), dtype=self._torch_dtype(), device=q.device)
+            out = torch.empty((self.B, T, self.H, self.d_v), dtype=self._out_dtype(), device=q.device)
         if state_out is None and return_state:
             state_out = torch.empty((self.B, self.H, self.d_v, self.d_k), dtype=torch.float32,
                                     device=q.device)
@@ -214,7 +221,7 @@ class GDN:
         import torch
         T = self._check_inputs(q, k, v, beta, decay)
         if out is None:
-            out = torch.empty((self.B, T, self.H, self.d_v), dtype=self._torch_dtype(), device=q.device)
+            out = torch.empty((self.B, T, self.H, self.d_v), dtype=self._out_dtype(), device=q.device)
         self._check(gdn_forward_bidi(self.h, q, k, v, beta, decay, out, T, chunk_len, current_stream()))
         return out
 
@@ -241,7 +248,7 @@ class GDN:
         import torch
         T, ts, bs = self._check_packed(qkv, beta_logit, decay_logit)
         if out is None:
-            out = torch.empty((self.B, T, self.H, self.d_v), dtype=self._torch_dtype(), device=qkv.device)
+            out = torch.empty((self.B, T, self.H, self.d_v), dtype=self._out_dtype(), device=qkv.device)
         if state_out is None and return_state:
             state_out = torch.empty((self.B, self.H, self.d_v, self.d_k), dtype=torch.float32,
                                     device=qkv.device)
@@ -254,7 +261,7 @@ class GDN:
         import torch
         T, ts, bs = self._check_packed(qkv, beta_logit, decay_logit)
         if out is None:
-            out = torch.empty((self.B, T, self.H, self.d_v), dtype=self._torch_dtype(), device=qkv.device)
+            out = torch.empty((self.B, T, self.H, self.d_v), dtype=self._out_dtype(), device=qkv.device)
         self._check(gdn_forward_bidi_packed(self.h, qkv, ts, bs, beta_logit, decay_logit, out, T, chunk_len,
                                             current_stream()))
         return out

@@ -28,6 +28,10 @@ struct gdn_ctx {
     long long tm_chunks = 0;   // their capacity: directions x B x H x ceil(max_T / 64)
 };
 
+static_assert((int)GDN_F32 == (int)gdn::IO_F32 && (int)GDN_BF16 == (int)gdn::IO_BF16 &&
+                  (int)GDN_FP8 == (int)gdn::IO_FP8,
+              "gdn_dtype values are the kernels' IoType values");
+
 namespace {
 
 thread_local std::string g_create_err;
@@ -133,10 +137,10 @@ int prepare_plain(gdn_ctx *h, const void *q, const void *k, const void *v, const
     const gdn_config &c = h->cfg;
     if (T < 0) return fail(h, GDN_ERR_ARG, "T = %lld is negative", T);
     if (T > c.max_T) return fail(h, GDN_ERR_ARG, "T = %lld exceeds max_T = %lld", T, c.max_T);
-    const size_t es = c.io_dtype == GDN_BF16 ? 2 : 4;
+    const size_t es = gdn::io_in_bytes(c.io_dtype);
     const size_t tok = (size_t)c.B * (size_t)T * (size_t)c.H;
     const size_t qk_bytes = tok * c.d_k * es, v_bytes = tok * c.d_v * es, g_bytes = tok * sizeof(float);
-    *out_bytes = v_bytes;
+    *out_bytes = tok * c.d_v * gdn::io_out_bytes(c.io_dtype);
     *in = Inputs{};
     in->q = q; in->k = k; in->v = v; in->beta = beta; in->decay = decay; in->prologue = 0;
     in->qk_ts = (long long)c.H * c.d_k; in->qk_bs = T * in->qk_ts;
@@ -184,13 +188,13 @@ int prepare_packed(gdn_ctx *h, const void *qkv, long long token_stride, long lon
     if (token_stride > MAX_TOKEN_STRIDE)
         return fail(h, GDN_ERR_UNSUPPORTED, "token_stride = %lld exceeds %lld elements", token_stride,
                     MAX_TOKEN_STRIDE);
-    const size_t es = c.io_dtype == GDN_BF16 ? 2 : 4;
+    const size_t es = gdn::io_in_bytes(c.io_dtype);
     if ((token_stride * (long long)es) % 16 || (batch_stride * (long long)es) % 16)
         return fail(h, GDN_ERR_ALIGN, "token_stride and batch_stride must be multiples of 16 bytes (%zu elements)",
                     16 / es);
     const size_t tok = (size_t)c.B * (size_t)T * (size_t)c.H;
     const size_t g_bytes = tok * sizeof(float);
-    *out_bytes = tok * c.d_v * es;
+    *out_bytes = tok * c.d_v * gdn::io_out_bytes(c.io_dtype);
     *in = Inputs{};
     const char *base = static_cast<const char *>(qkv);
     in->q = qkv;
@@ -257,7 +261,7 @@ int resolve_chunk(gdn_ctx *h, int chunk_len, int *C) {
         *C = 1;
         return GDN_OK;
     }
-    if (!gdn::chunk_supported(chunk_len, h->cfg.d_k, h->cfg.d_v, h->cfg.io_dtype == GDN_BF16))
+    if (!gdn::chunk_supported(chunk_len, h->cfg.d_k, h->cfg.d_v, h->cfg.io_dtype))
         return fail(h, GDN_ERR_UNSUPPORTED,
                     "chunk_len = %d is not supported for d_k = %d, d_v = %d, io_dtype = %d "
                     "(use 1 for the sequential scan, 16, 32, 64 or 128 (0 = 64) for the chunked form)",
@@ -280,8 +284,8 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
     if (!valid_dim(c.d_k) || !valid_dim(c.d_v))
         return fail_create(GDN_ERR_UNSUPPORTED, "d_k = %d, d_v = %d: each must be 16, 32, 64 or 128",
                            c.d_k, c.d_v);
-    if (c.io_dtype != GDN_F32 && c.io_dtype != GDN_BF16)
-        return fail_create(GDN_ERR_UNSUPPORTED, "io_dtype = %d is not GDN_F32 or GDN_BF16", c.io_dtype);
+    if (c.io_dtype != GDN_F32 && c.io_dtype != GDN_BF16 && c.io_dtype != GDN_FP8)
+        return fail_create(GDN_ERR_UNSUPPORTED, "io_dtype = %d is not GDN_F32, GDN_BF16 or GDN_FP8", c.io_dtype);
     if (c.max_T < 0) return fail_create(GDN_ERR_ARG, "max_T = %lld is negative", c.max_T);
     if (c.device < -1) return fail_create(GDN_ERR_ARG, "device = %d", c.device);
     if (c.flags & ~GDN_FLAG_BIDI) return fail_create(GDN_ERR_ARG, "unknown flags 0x%x", c.flags);
@@ -297,7 +301,7 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
     // The MFMA chunked kernel (bf16 I/O, chunk 64, d_k and d_v >= 32) forms each
     // chunk's triangular inverse in a pass of its own and reads it back.
     long long tm_chunks = 0;
-    if (gdn::chunk_mfma_supported(64, c.d_k, c.d_v, c.io_dtype == GDN_BF16))
+    if (gdn::chunk_mfma_supported(64, c.d_k, c.d_v, c.io_dtype))
         tm_chunks = ((c.flags & GDN_FLAG_BIDI) ? 2LL : 1LL) * c.B * c.H * ((c.max_T + 63) / 64);
     const size_t tm_bytes = gdn::chunk_mfma_tm_bytes(tm_chunks);
 
@@ -377,7 +381,7 @@ gdn::PassArgs pass_args(const gdn_ctx *h, const Inputs &in, long long T) {
     a.qk_ts = in.qk_ts; a.qk_bs = in.qk_bs; a.v_ts = in.v_ts; a.v_bs = in.v_bs;
     a.beta = in.beta; a.decay = in.decay; a.prologue = in.prologue;
     a.B = c.B; a.H = c.H; a.dk = c.d_k; a.dv = c.d_v; a.T = T;
-    a.io_bf16 = c.io_dtype == GDN_BF16;
+    a.io = c.io_dtype;  // gdn_dtype and gdn::IoType share their values
     a.tm = h->tm; a.tm_chunks = h->tm_chunks;
     return a;
 }
@@ -451,7 +455,7 @@ int run_bidi(gdn_ctx *h, const Inputs &in, void *out, size_t out_bytes, long lon
     a.out_mode = gdn::OUT_PARTIAL;
     hipError_t e = (C == 1) ? gdn::launch_scan(a, s) : gdn::launch_chunk(a, C, s);
     if ((st = launch_status(h, e, "bidirectional pass"))) return st;
-    e = gdn::launch_combine(out, a.partial, a.partial_rev, (long long)n_out, a.io_bf16, s);
+    e = gdn::launch_combine(out, a.partial, a.partial_rev, (long long)n_out, a.io, s);
     return launch_status(h, e, "bidirectional combine");
 }
 

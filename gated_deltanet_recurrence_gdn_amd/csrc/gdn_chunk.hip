@@ -82,6 +82,7 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int C = 64;     // chunk length
 constexpr int NT = 512;   // threads per block of the chunk kernel: 8 waves
@@ -161,13 +162,13 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // Per-block constants: base pointers already offset to (b, token 0, h), token
 // strides in elements, and the chunk walk.
 struct Ctx {
-    const uint16_t *q, *k, *v;  // v offset to the block's d_v tile
+    const char *q, *k, *v;      // bytes; v offset to the block's d_v tile
     const float *beta, *decay;
     const float *norms;         // prologue: the head's inverse k norms, C floats per chunk
     long long T;
     int nchunks;
-    int rs;   // q/k elements between consecutive tokens (H * d_k when contiguous)
-    int rsv;  // v elements between consecutive tokens (H * d_v when contiguous)
+    int rs;   // q/k bytes between consecutive tokens (H * d_k elements when contiguous)
+    int rsv;  // v bytes between consecutive tokens (H * d_v elements when contiguous)
     int rso;  // out elements between consecutive tokens: H * d_v
     int H;    // gate elements between consecutive tokens
     int reverse;
@@ -188,16 +189,16 @@ struct Ctx {
     }
 };
 
-// Row j of chunk c of a token-major tensor with `stride` elements per token:
-// one 64-bit base per chunk, then a 32-bit signed offset per row (clamped to the
+// Row j of chunk c of a token-major tensor with `stride` bytes per token: one
+// 64-bit base per chunk, then a 32-bit signed offset per row (clamped to the
 // chunk's last token as in Ctx::tok_clamped).
 struct ChunkRows {
-    const uint16_t *base;  // token 0 of the chunk
-    int step;              // +stride, or -stride when walking backwards
-    int last;              // ntok - 1
-    __device__ const uint16_t *row(int j) const { return base + (long long)((j < last ? j : last) * step); }
+    const char *base;  // token 0 of the chunk
+    int step;          // +stride, or -stride when walking backwards
+    int last;          // ntok - 1
+    __device__ const char *row(int j) const { return base + (long long)((j < last ? j : last) * step); }
 };
-__device__ __forceinline__ ChunkRows chunk_rows(const Ctx &x, const uint16_t *p, int c, int stride) {
+__device__ __forceinline__ ChunkRows chunk_rows(const Ctx &x, const char *p, int c, int stride) {
     ChunkRows r;
     r.base = p + x.tok(c, 0) * stride;
     r.step = x.reverse ? -stride : stride;
@@ -295,7 +296,7 @@ __device__ __forceinline__ GateVals gate_values(int lane, int ntok, float xb, fl
 // tm_kernel: Tm = (I + A)^{-1} of every chunk, in chain operand order.
 // =============================================================================
 struct TmParams {
-    const uint16_t *q, *k;
+    const char *k;
     const float *beta, *decay;
     uint16_t *tm;     // [dirs][B][H][nchunks][TM_ELEMS]
     float *norms;     // prologue: [dirs][B][H][nchunks][C] inverse norms of k
@@ -469,11 +470,9 @@ __device__ __forceinline__ void tm_column(uint16_t (*Tb)[LC], const uint16_t (*A
         for (int r = 0; r < 4; ++r) Tb[16 * rb + 4 * g16 + r][16 * CB + l16] = (uint16_t)f32_to_bf16_bits(-tout[rb][r]);
 }
 
-// Sum of squares of 8 bf16 values.
-__device__ __forceinline__ float sumsq8(const bf16x8_t &r) {
-    uint4 w;
-    __builtin_memcpy(&w, &r, 16);
-    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+// Sum of squares of 8 bf16 values (two per word).
+__device__ __forceinline__ float sumsq8(const u32x4_t &w) {
+    const uint32_t u[4] = {w[0], w[1], w[2], w[3]};
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -484,8 +483,29 @@ __device__ __forceinline__ float sumsq8(const bf16x8_t &r) {
     return s;
 }
 
+// Columns of a row that one 16-byte load holds: 8 bf16 or 16 FP8 values.
+template <int IO>
+__host__ __device__ constexpr int seg_cols() { return IO == IO_FP8 ? 16 : 8; }
+
+// One 16-byte row segment as loaded, widened to bf16 and stored at dst
+// (seg_cols<IO>() bf16 values); returns the sum of their squares if asked.
+template <int IO, bool SUMSQ>
+__device__ __forceinline__ float put_seg(uint16_t *dst, const u32x4_t &w) {
+    if constexpr (IO == IO_FP8) {
+        const uint2 a = fp8x4_to_bf16x4(w[0]), b = fp8x4_to_bf16x4(w[1]);
+        const uint2 c = fp8x4_to_bf16x4(w[2]), d = fp8x4_to_bf16x4(w[3]);
+        const u32x4_t lo = {a.x, a.y, b.x, b.y}, hi = {c.x, c.y, d.x, d.y};
+        *reinterpret_cast<u32x4_t *>(dst) = lo;
+        *reinterpret_cast<u32x4_t *>(dst + 8) = hi;
+        return SUMSQ ? sumsq8(lo) + sumsq8(hi) : 0.f;
+    } else {
+        *reinterpret_cast<u32x4_t *>(dst) = w;
+        return SUMSQ ? sumsq8(w) : 0.f;
+    }
+}
+
 // One block (4 waves) per (direction, b, h, chunk); up to 8 blocks per CU.
-template <int DK, bool PRO>
+template <int DK, int IO, bool PRO>
 __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
     __shared__ TmSmem<DK> sm;
     const int lane = threadIdx.x & 63;
@@ -500,26 +520,27 @@ __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
     const int b = (int)(L % p.B);
     const int dir = (int)(L / p.B);
 
+    constexpr int ES = io_in_bytes(IO);
     Ctx x;
     x.T = p.T;
     x.nchunks = p.nchunks;
-    x.rs = (int)p.qk_ts;
+    x.rs = (int)(p.qk_ts * ES);
     x.rsv = 0;
     x.rso = 0;
     x.H = p.H;
     x.reverse = p.reverse ^ dir;
     const size_t gtok0 = (size_t)b * p.T * p.H + h;  // (b, token 0, h) of the [B, T, H] gates
-    const size_t qk0 = (size_t)b * p.qk_bs + (size_t)h * DK;
     x.q = nullptr;
     x.v = nullptr;
-    x.k = p.k + qk0;
+    x.k = p.k + ((size_t)b * p.qk_bs + (size_t)h * DK) * ES;
     x.beta = p.beta + gtok0;
     x.decay = p.decay + gtok0;
     x.norms = nullptr;
 
-    // 1. K rows 16 wid .. 16 wid + 15 into LDS (row-coalesced: DK / 8 lanes per
-    //    row).  With the prologue the same lanes form every row's inverse L2 norm
-    //    (a sum over the row's lanes).  Wave 3 reads the gate inputs.
+    // 1. The chunk's K rows into LDS as bf16, row-coalesced (16 bytes per lane,
+    //    DK / seg_cols lanes per row, block-wide passes).  With the prologue the
+    //    same lanes form every row's inverse L2 norm (a sum over the row's lanes).
+    //    Wave 3 reads the gate inputs.
     float xb = 0.f, xa = 1.f;
     if (wid == 3) {
         const size_t o = (size_t)x.tok_clamped(c, lane) * x.H;
@@ -527,19 +548,22 @@ __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
         xa = x.decay[o];
     }
     {
-        constexpr int LPR = DK / 8, RPL = 64 / LPR, NLD = 16 / RPL;
-        const int r0 = 16 * wid + lane / LPR, col = 8 * (lane % LPR);
-        bf16x8_t r[NLD];
+        constexpr int SC = seg_cols<IO>(), LPR = DK / SC, RPB = 256 / LPR, NP = (C + RPB - 1) / RPB;
+        const int r0 = threadIdx.x / LPR, seg = threadIdx.x % LPR;
+        u32x4_t r[NP];
 #pragma unroll
-        for (int s = 0; s < NLD; ++s)
-            r[s] = *reinterpret_cast<const bf16x8_t *>(x.k + (size_t)x.tok_clamped(c, r0 + RPL * s) * x.rs + col);
+        for (int s = 0; s < NP; ++s)
+            if (r0 + RPB * s < C)
+                r[s] = *reinterpret_cast<const u32x4_t *>(x.k + (size_t)x.tok_clamped(c, r0 + RPB * s) * x.rs + 16 * seg);
 #pragma unroll
-        for (int s = 0; s < NLD; ++s) *reinterpret_cast<bf16x8_t *>(&sm.Ks[r0 + RPL * s][col]) = r[s];
-        if constexpr (PRO) {
-#pragma unroll
-            for (int s = 0; s < NLD; ++s) {
-                const float sk = group_sum<LPR>(sumsq8(r[s]));
-                if (lane % LPR == 0) sm.rk[r0 + RPL * s] = inv_norm(sk);
+        for (int s = 0; s < NP; ++s) {
+            const int row = r0 + RPB * s;
+            if (row < C) {
+                const float sk = put_seg<IO, PRO>(&sm.Ks[row][SC * seg], r[s]);
+                if constexpr (PRO) {
+                    const float t = group_sum<LPR>(sk);
+                    if (seg == 0) sm.rk[row] = inv_norm(t);
+                }
             }
         }
     }
@@ -600,7 +624,7 @@ __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
 // chunk_kernel: the chunks of a head in order.
 // =============================================================================
 struct ChunkParams {
-    const uint16_t *q, *k, *v;
+    const char *q, *k, *v;
     long long qk_ts, qk_bs, v_ts, v_bs;  // element strides between tokens / batch elements
     const float *beta, *decay;
     const float *norms;                  // prologue: written by tm_kernel
@@ -950,38 +974,37 @@ __device__ __forceinline__ void output_period(const Ctx &x, Smem<DK> &sm, const 
 }
 
 // ---- waves 4, 5: K and Q of a chunk, row-coalesced -----------------------------
-// DK / 8 lanes per row, each with 8 consecutive columns, 512 / DK rows per load
-// instruction, so every load reads whole rows.
-template <int DK>
+// 16 bytes per lane (8 bf16 or 16 FP8 columns), DK / seg_cols lanes per row, so
+// every load instruction reads whole rows; stored to LDS as bf16.
+template <int DK, int IO>
 struct Rows64 {
-    static constexpr int LPR = DK / 8;    // lanes per row
-    static constexpr int RPL = 64 / LPR;  // rows per load
-    static constexpr int NLD = C / RPL;   // loads per chunk
-    bf16x8_t r[NLD];
+    static constexpr int LPR = DK / seg_cols<IO>();  // lanes per row
+    static constexpr int RPL = 64 / LPR;             // rows per load
+    static constexpr int NLD = C / RPL;              // loads per chunk
+    u32x4_t r[NLD];
 };
 
 // Loads are unconditional per lane: rows past the end of a final short chunk
 // re-read token n-1 (finite data; those tokens carry b = 0 and a = 1, so every
 // product they enter is multiplied by 0 or never stored).
-template <int DK>
-__device__ __forceinline__ Rows64<DK> load_rows(const uint16_t *base, const Ctx &x, int c, int lane) {
-    using RB = Rows64<DK>;
+template <int DK, int IO>
+__device__ __forceinline__ Rows64<DK, IO> load_rows(const char *base, const Ctx &x, int c, int lane) {
+    using RB = Rows64<DK, IO>;
     RB d;
     const ChunkRows cr = chunk_rows(x, base, c, x.rs);
     const int r0 = lane / RB::LPR;
-    const int col = 8 * (lane % RB::LPR);
+    const int off = 16 * (lane % RB::LPR);
 #pragma unroll
-    for (int s = 0; s < RB::NLD; ++s)
-        d.r[s] = *reinterpret_cast<const bf16x8_t *>(cr.row(r0 + RB::RPL * s) + col);
+    for (int s = 0; s < RB::NLD; ++s) d.r[s] = *reinterpret_cast<const u32x4_t *>(cr.row(r0 + RB::RPL * s) + off);
     return d;
 }
-template <int DK, int PITCH>
-__device__ __forceinline__ void store_rows(uint16_t (*dst)[PITCH], const Rows64<DK> &blk, int lane) {
-    using RB = Rows64<DK>;
+template <int DK, int PITCH, int IO>
+__device__ __forceinline__ void store_rows(uint16_t (*dst)[PITCH], const Rows64<DK, IO> &blk, int lane) {
+    using RB = Rows64<DK, IO>;
     const int r0 = lane / RB::LPR;
-    const int col = 8 * (lane % RB::LPR);
+    const int col = seg_cols<IO>() * (lane % RB::LPR);
 #pragma unroll
-    for (int s = 0; s < RB::NLD; ++s) *reinterpret_cast<bf16x8_t *>(&dst[r0 + RB::RPL * s][col]) = blk.r[s];
+    for (int s = 0; s < RB::NLD; ++s) put_seg<IO, false>(&dst[r0 + RB::RPL * s][col], blk.r[s]);
 }
 
 // ---- waves 6, 7: gate vectors; V tiles -----------------------------------------
@@ -991,16 +1014,26 @@ struct GateRegs {
 };
 
 // The chunk's V tile (64 tokens x 32 d_v), row-coalesced: in w[s], lane l holds
-// token 16 s + l / 4, d_v columns 8 (l % 4) .. + 7.
+// token 16 s + l / 4, d_v columns 8 (l % 4) .. + 7 (16 bytes of bf16 or 8 of FP8).
+template <int IO>
 struct VRow {
-    u32x4_t w[4];
+    u32x4_t w[4];  // bf16: 8 columns; FP8: 8 columns in w[s][0..1]
 };
-__device__ __forceinline__ VRow load_v(const Ctx &x, int c, int lane) {
-    VRow d;
+template <int IO>
+__device__ __forceinline__ VRow<IO> load_v(const Ctx &x, int c, int lane) {
+    VRow<IO> d;
     const ChunkRows cr = chunk_rows(x, x.v, c, x.rsv);
+    constexpr int SEG = 8 * io_in_bytes(IO);  // bytes of 8 columns
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-        d.w[s] = *reinterpret_cast<const u32x4_t *>(cr.row(16 * s + (lane >> 2)) + 8 * (lane & 3));
+    for (int s = 0; s < 4; ++s) {
+        const char *src = cr.row(16 * s + (lane >> 2)) + SEG * (lane & 3);
+        if constexpr (IO == IO_FP8) {
+            const u32x2_t u = *reinterpret_cast<const u32x2_t *>(src);
+            d.w[s] = u32x4_t{u[0], u[1], 0u, 0u};
+        } else {
+            d.w[s] = *reinterpret_cast<const u32x4_t *>(src);
+        }
+    }
     return d;
 }
 // Unconditional (c is clamped into range by the caller), so that the count of
@@ -1028,25 +1061,34 @@ __device__ __forceinline__ void gates_store(const Ctx &x, Smem<DK> &sm, int c, i
     sm.glast[s3][lane] = v.glast;
 }
 
-template <int DK>
-__device__ __forceinline__ void store_bv(Smem<DK> &sm, int c, const VRow &v, int lane) {
+template <int DK, int IO>
+__device__ __forceinline__ void store_bv(Smem<DK> &sm, int c, const VRow<IO> &v, int lane) {
     const int d0 = 8 * (lane & 3);
 #pragma unroll
     for (int s_ = 0; s_ < 4; ++s_) {
         const int t = 16 * s_ + (lane >> 2);
         const float bt = sm.bet[c % 3][t];
         float *col = &sm.bVt[c & 1][d0][bv_slot(d0, t)];
-        const uint32_t w4[4] = {v.w[s_].x, v.w[s_].y, v.w[s_].z, v.w[s_].w};
+        float vv[8];
+        if constexpr (IO == IO_FP8) {
+            fp8x4_to_f32(v.w[s_][0], vv);
+            fp8x4_to_f32(v.w[s_][1], vv + 4);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            col[(2 * e) * (C + 4)] = bt * bf16_lo(w4[e]);
-            col[(2 * e + 1) * (C + 4)] = bt * bf16_hi(w4[e]);
+            for (int e = 0; e < 4; ++e) {
+                vv[2 * e] = bf16_lo(v.w[s_][e]);
+                vv[2 * e + 1] = bf16_hi(v.w[s_][e]);
+            }
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) col[e * (C + 4)] = bt * vv[e];
     }
 }
 
-template <int DK, bool BF16, bool PRO>
+template <int DK, int IO, bool PRO>
 __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
+    constexpr bool BF16 = true;  // out is bf16 for every input type this kernel takes
+    constexpr int ES = io_in_bytes(IO);
     static_assert(DK % 32 == 0 && DK <= 128, "d_k must be 32, 64 or 128");
     __shared__ Smem<DK> sm;
     const int tid = threadIdx.x;
@@ -1072,16 +1114,16 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     Ctx x;
     x.T = p.T;
     x.nchunks = (int)((p.T + C - 1) / C);
-    x.rs = (int)p.qk_ts;
-    x.rsv = (int)p.v_ts;
+    x.rs = (int)(p.qk_ts * ES);
+    x.rsv = (int)(p.v_ts * ES);
     x.rso = p.H * p.dv;
     x.H = p.H;
     x.reverse = p.reverse ^ dir;
     const size_t tok0 = (size_t)b * p.T * p.H + h;  // (b, token 0, h) of the [B, T, H] gates and out rows
-    const size_t qk0 = (size_t)b * p.qk_bs + (size_t)h * DK;
+    const size_t qk0 = ((size_t)b * p.qk_bs + (size_t)h * DK) * ES;
     x.q = p.q + qk0;
     x.k = p.k + qk0;
-    x.v = p.v + (size_t)b * p.v_bs + (size_t)h * p.dv + dv0;
+    x.v = p.v + ((size_t)b * p.v_bs + (size_t)h * p.dv + dv0) * ES;
     x.beta = p.beta + tok0;
     x.decay = p.decay + tok0;
     const int n = x.nchunks;
@@ -1145,20 +1187,20 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         // of loads in flight is the same on every path and the wait before a store
         // covers only the loads of the chunk being stored.
         const bool is_k = wid == 4;
-        const uint16_t *base = is_k ? x.k : x.q;
-        auto store = [&](int c, const Rows64<DK> &r) {
-            if (is_k) store_rows<DK, Smem<DK>::LKK>(sm.Ks[c & 1], r, lane);
-            else store_rows<DK, Smem<DK>::LKK>(sm.Qs[c & 1], r, lane);
+        const char *base = is_k ? x.k : x.q;
+        auto store = [&](int c, const Rows64<DK, IO> &r) {
+            if (is_k) store_rows<DK, Smem<DK>::LKK, IO>(sm.Ks[c & 1], r, lane);
+            else store_rows<DK, Smem<DK>::LKK, IO>(sm.Qs[c & 1], r, lane);
         };
-        Rows64<DK> rA, rB;
-        rA = load_rows<DK>(base, x, 0, lane);
+        Rows64<DK, IO> rA, rB;
+        rA = load_rows<DK, IO>(base, x, 0, lane);
         __syncthreads();
         for (int it = -2; it < n + 1; it += 2) {
             if (x.has(it + 1)) store(it + 1, rB);
-            rB = load_rows<DK>(base, x, it + 3 < n ? it + 3 : n - 1, lane);
+            rB = load_rows<DK, IO>(base, x, it + 3 < n ? it + 3 : n - 1, lane);
             __syncthreads();
             if (x.has(it + 2)) store(it + 2, rA);
-            rA = load_rows<DK>(base, x, it + 4 < n ? it + 4 : n - 1, lane);
+            rA = load_rows<DK, IO>(base, x, it + 4 < n ? it + 4 : n - 1, lane);
             __syncthreads();
         }
     } else if (wid == 6) {
@@ -1180,21 +1222,21 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         // b_t v_t of chunk c is stored in period c-1 from V register set c&1
         // (loaded in period c-3, unconditionally as for K and Q), with b_t from
         // the gate slot of chunk c.
-        VRow vA, vB;
-        vA = load_v(x, 0, lane);
+        VRow<IO> vA, vB;
+        vA = load_v<IO>(x, 0, lane);
         __syncthreads();
         for (int it = -2; it < n + 1; it += 2) {
-            if (x.has(it + 1)) store_bv(sm, it + 1, vB, lane);
-            vB = load_v(x, it + 3 < n ? it + 3 : n - 1, lane);
+            if (x.has(it + 1)) store_bv<DK, IO>(sm, it + 1, vB, lane);
+            vB = load_v<IO>(x, it + 3 < n ? it + 3 : n - 1, lane);
             __syncthreads();
-            if (x.has(it + 2)) store_bv(sm, it + 2, vA, lane);
-            vA = load_v(x, it + 4 < n ? it + 4 : n - 1, lane);
+            if (x.has(it + 2)) store_bv<DK, IO>(sm, it + 2, vA, lane);
+            vA = load_v<IO>(x, it + 4 < n ? it + 4 : n - 1, lane);
             __syncthreads();
         }
     }
 }
 
-template <int DK, bool PRO>
+template <int DK, int IO, bool PRO>
 hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     const int nchunks = (int)((a.T + C - 1) / C);
     const int dirs = a.both_dirs ? 2 : 1;
@@ -1204,21 +1246,20 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     float *norms = PRO ? reinterpret_cast<float *>(a.tm + (size_t)a.tm_chunks * TM_ELEMS) : nullptr;
 
     TmParams t;
-    t.q = static_cast<const uint16_t *>(a.q);
-    t.k = static_cast<const uint16_t *>(a.k);
+    t.k = static_cast<const char *>(a.k);
     t.beta = a.beta; t.decay = a.decay;
     t.tm = a.tm;
     t.norms = norms;
     t.T = a.T; t.qk_ts = a.qk_ts; t.qk_bs = a.qk_bs;
     t.B = a.B; t.H = a.H; t.nchunks = nchunks; t.reverse = a.reverse;
-    hipLaunchKernelGGL((tm_kernel<DK, PRO>), dim3((unsigned)ntm), dim3(256), 0, stream, t);
+    hipLaunchKernelGGL((tm_kernel<DK, IO, PRO>), dim3((unsigned)ntm), dim3(256), 0, stream, t);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
     ChunkParams p;
-    p.q = static_cast<const uint16_t *>(a.q);
-    p.k = static_cast<const uint16_t *>(a.k);
-    p.v = static_cast<const uint16_t *>(a.v);
+    p.q = static_cast<const char *>(a.q);
+    p.k = static_cast<const char *>(a.k);
+    p.v = static_cast<const char *>(a.v);
     p.qk_ts = a.qk_ts; p.qk_bs = a.qk_bs; p.v_ts = a.v_ts; p.v_bs = a.v_bs;
     p.beta = a.beta; p.decay = a.decay;
     p.norms = norms;
@@ -1232,20 +1273,21 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.reverse = a.reverse; p.out_mode = a.out_mode; p.both_dirs = a.both_dirs;
     p.scale = (float)(1.0 / __builtin_sqrt((double)DK));
     const int nblk = p.nblk_dir * dirs;
-    hipLaunchKernelGGL((chunk_kernel<DK, true, PRO>), dim3(nblk), dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO>), dim3(nblk), dim3(NT), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int DK>
 hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
-    return a.prologue ? launch_dk<DK, true>(a, stream) : launch_dk<DK, false>(a, stream);
+    if (a.io == IO_FP8) return a.prologue ? launch_dk<DK, IO_FP8, true>(a, stream) : launch_dk<DK, IO_FP8, false>(a, stream);
+    return a.prologue ? launch_dk<DK, IO_BF16, true>(a, stream) : launch_dk<DK, IO_BF16, false>(a, stream);
 }
 
 }  // namespace
 
-bool chunk_mfma_supported(int C_, int dk, int dv, int io_bf16) {
+bool chunk_mfma_supported(int C_, int dk, int dv, int io) {
     const bool dims = (dk == 32 || dk == 64 || dk == 128) && (dv == 32 || dv == 64 || dv == 128);
-    return C_ == C && dims && io_bf16;
+    return C_ == C && dims && (io == IO_BF16 || io == IO_FP8);
 }
 
 size_t chunk_mfma_tm_bytes(long long chunks) {
@@ -1253,7 +1295,7 @@ size_t chunk_mfma_tm_bytes(long long chunks) {
 }
 
 hipError_t launch_chunk_mfma(const PassArgs &a, int C_, hipStream_t stream) {
-    if (!chunk_mfma_supported(C_, a.dk, a.dv, a.io_bf16)) return hipErrorInvalidValue;
+    if (!chunk_mfma_supported(C_, a.dk, a.dv, a.io)) return hipErrorInvalidValue;
     switch (a.dk) {
         case 32: return launch_dk<32>(a, stream);
         case 64: return launch_dk<64>(a, stream);

@@ -1,6 +1,6 @@
 // gdn_chunk_gen.hip -- the chunked (UT-transform) form for every supported
 // shape: chunk length C in {16, 32, 64, 128}, d_k and d_v in {16, 32, 64, 128},
-// fp32 or bf16 I/O, all arithmetic in fp32 on the vector ALUs.
+// fp32, bf16 or FP8 inputs, all arithmetic in fp32 on the vector ALUs.
 //
 // It computes the same per-chunk quantities as the bf16 MFMA kernel: with
 // g_i = sum_{r<=i} log2 a_r over the chunk, gam_i = 2^{g_i} and
@@ -59,17 +59,22 @@ struct GenParams {
     float scale;
 };
 
-template <bool BF16>
+template <int IO>
 __device__ __forceinline__ float ld_io(const void *p, size_t i) {
-    if constexpr (BF16)
+    if constexpr (IO == IO_BF16) {
         return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(p)[i] << 16);
-    else
+    } else if constexpr (IO == IO_FP8) {
+        float f[4];
+        fp8x4_to_f32(reinterpret_cast<const uint8_t *>(p)[i], f);  // the byte in bits 0-7
+        return f[0];
+    } else {
         return reinterpret_cast<const float *>(p)[i];
+    }
 }
 
-template <bool BF16>
+template <int IO>
 __device__ __forceinline__ void st_io(void *p, size_t i, float x) {
-    if constexpr (BF16)
+    if constexpr (IO != IO_F32)
         reinterpret_cast<uint16_t *>(p)[i] = (uint16_t)f32_to_bf16_bits(x);
     else
         reinterpret_cast<float *>(p)[i] = x;
@@ -85,7 +90,7 @@ __host__ __device__ inline size_t gen_lds_bytes(int C, int dk, int dvt) {
            + (size_t)C * dvt * sizeof(float);               // R, then N
 }
 
-template <bool BF16, bool PRO>
+template <int IO, bool PRO>
 __global__ __launch_bounds__(GT) void chunk_gen_kernel(GenParams p) {
     extern __shared__ double smem_d[];
     const int C = p.C, dk = p.dk, dvt = p.dvt;
@@ -131,7 +136,7 @@ __global__ __launch_bounds__(GT) void chunk_gen_kernel(GenParams p) {
 
         for (int idx = tid; idx < n * dk; idx += GT) {
             const int i = idx / dk, f = idx - i * dk;
-            Ks[i * PK + f] = ld_io<BF16>(p.k, qk_row(tok(i)) + f);
+            Ks[i * PK + f] = ld_io<IO>(p.k, qk_row(tok(i)) + f);
         }
         if (tid < n) {
             const size_t r = row(tok(tid));
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(GT) void chunk_gen_kernel(GenParams p) {
             const size_t qr = qk_row(tok(tid));
             float sk = 0.0f, sq = 0.0f;
             for (int f = 0; f < dk; ++f) {
-                const float kf = Ks[tid * PK + f], qf = ld_io<BF16>(p.q, qr + f);
+                const float kf = Ks[tid * PK + f], qf = ld_io<IO>(p.q, qr + f);
                 sk = fmaf(kf, kf, sk);
                 sq = fmaf(qf, qf, sq);
             }
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(GT) void chunk_gen_kernel(GenParams p) {
             const int i = idx / dvt, e = idx - i * dvt;
             float x = 0.0f;
             for (int f = 0; f < dk; ++f) x = fmaf(Ks[i * PK + f], Ss[e * PK + f], x);
-            const float vv = ld_io<BF16>(p.v, v_row(tok(i)) + dv0 + e);
+            const float vv = ld_io<IO>(p.v, v_row(tok(i)) + dv0 + e);
             Rs[i * dvt + e] = bet[i] * (vv - gam[i] * x);
         }
         __syncthreads();
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(GT) void chunk_gen_kernel(GenParams p) {
             if (j <= i) {
                 const size_t qr = qk_row(tok(i));
                 float s = 0.0f;
-                for (int f = 0; f < dk; ++f) s = fmaf(ld_io<BF16>(p.q, qr + f), Ks[j * PK + f], s);
+                for (int f = 0; f < dk; ++f) s = fmaf(ld_io<IO>(p.q, qr + f), Ks[j * PK + f], s);
                 if constexpr (PRO) s *= rq[i];
                 Bf[i * PC + j] = s * exp2f((float)(g[i] - g[j]));
             }
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(GT) void chunk_gen_kernel(GenParams p) {
             const size_t r = row(tok(i));
             const size_t qr = qk_row(tok(i));
             float y = 0.0f;
-            for (int f = 0; f < dk; ++f) y = fmaf(ld_io<BF16>(p.q, qr + f), Ss[e * PK + f], y);
+            for (int f = 0; f < dk; ++f) y = fmaf(ld_io<IO>(p.q, qr + f), Ss[e * PK + f], y);
             if constexpr (PRO) y *= rq[i];
             float s = gam[i] * y;
             for (int j = 0; j <= i; ++j) s = fmaf(Bf[i * PC + j], Rs[j * dvt + e], s);
@@ -264,7 +269,7 @@ __global__ __launch_bounds__(GT) void chunk_gen_kernel(GenParams p) {
             if (p.out_mode == OUT_PARTIAL)
                 part[o] = s;
             else
-                st_io<BF16>(out, o, s);
+                st_io<IO>(out, o, s);
         }
         __syncthreads();
         // S = gam_{n-1} S0 + N^T diag(G_{n-1,.}) K
@@ -285,15 +290,20 @@ __global__ __launch_bounds__(GT) void chunk_gen_kernel(GenParams p) {
     }
 }
 
-template <bool BF16, bool PRO>
+template <int IO, bool PRO>
 hipError_t launch_gen(const GenParams &p, hipStream_t stream) {
     const size_t lds = gen_lds_bytes(p.C, p.dk, p.dvt);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_gen_kernel<BF16, PRO>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_gen_kernel<IO, PRO>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const dim3 grid(p.dv / p.dvt, p.H, p.B * (p.both_dirs ? 2 : 1));
-    hipLaunchKernelGGL((chunk_gen_kernel<BF16, PRO>), grid, dim3(GT), lds, stream, p);
+    hipLaunchKernelGGL((chunk_gen_kernel<IO, PRO>), grid, dim3(GT), lds, stream, p);
     return hipGetLastError();
+}
+
+template <int IO>
+hipError_t launch_gen_io(const GenParams &p, int prologue, hipStream_t stream) {
+    return prologue ? launch_gen<IO, true>(p, stream) : launch_gen<IO, false>(p, stream);
 }
 
 bool pow2_16_128(int x) { return x == 16 || x == 32 || x == 64 || x == 128; }
@@ -317,8 +327,11 @@ hipError_t launch_chunk_general(const PassArgs &a, int C, hipStream_t stream) {
     p.dvt = a.dv < GDVT ? a.dv : GDVT;
     p.reverse = a.reverse; p.out_mode = a.out_mode; p.both_dirs = a.both_dirs;
     p.scale = (float)(1.0 / __builtin_sqrt((double)a.dk));
-    if (a.prologue) return a.io_bf16 ? launch_gen<true, true>(p, stream) : launch_gen<false, true>(p, stream);
-    return a.io_bf16 ? launch_gen<true, false>(p, stream) : launch_gen<false, false>(p, stream);
+    switch (a.io) {
+        case IO_BF16: return launch_gen_io<IO_BF16>(p, a.prologue, stream);
+        case IO_FP8: return launch_gen_io<IO_FP8>(p, a.prologue, stream);
+        default: return launch_gen_io<IO_F32>(p, a.prologue, stream);
+    }
 }
 
 }  // namespace gdn

@@ -30,6 +30,27 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return u;
 }
 
+// OCP FP8 E4M3 -> bf16 / fp32 with gfx950's conversion instructions at scale 1.
+// Every finite E4M3 value is exactly a bf16 (3 mantissa bits, exponents 2^-9 ..
+// 2^8), so the widening is exact; NaN stays NaN.
+// fp8x4_to_bf16x4: bytes 0-3 of w -> four bf16, two per returned word.
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
+    const gdn_bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const gdn_bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    uint2 r;
+    __builtin_memcpy(&r.x, &lo, 4);
+    __builtin_memcpy(&r.y, &hi, 4);
+    return r;
+}
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float *f) {
+    const gdn_f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    const gdn_f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    f[0] = lo[0];
+    f[1] = lo[1];
+    f[2] = hi[0];
+    f[3] = hi[1];
+}
+
 // Cross-lane data movement inside a row of 16 lanes (DPP).
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {

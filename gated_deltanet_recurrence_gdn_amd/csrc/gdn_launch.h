@@ -9,6 +9,15 @@
 
 namespace gdn {
 
+// Element type of q, k, v.  out is fp32 for IO_F32 and bf16 otherwise.
+enum IoType : int {
+    IO_F32 = 0,   // fp32
+    IO_BF16 = 1,  // bf16
+    IO_FP8 = 2,   // OCP FP8 E4M3 (widened exactly to bf16 / fp32 at load)
+};
+__host__ __device__ constexpr int io_in_bytes(int io) { return io == IO_F32 ? 4 : io == IO_BF16 ? 2 : 1; }
+__host__ __device__ constexpr int io_out_bytes(int io) { return io == IO_F32 ? 4 : 2; }
+
 // What a pass does with the per-token outputs o_t.
 enum OutMode : int {
     OUT_STORE = 0,    // out[t] = round(o_t) in the I/O dtype
@@ -31,12 +40,12 @@ struct PassArgs {
                             //    b = sigmoid(beta), a = exp(-softplus(decay))
     const float *state_in;  // [B,H,dv,dk] or nullptr (zeros)
     float *state_out;       // [B,H,dv,dk] or nullptr; may equal state_in
-    void *out;              // [B,T,H,dv] io dtype (OUT_STORE)
+    void *out;              // [B,T,H,dv] fp32 or bf16 (OUT_STORE), see IoType
     float *partial;         // [B,T,H,dv] fp32 (OUT_PARTIAL)
     float *partial_rev;     // [B,T,H,dv] fp32, reverse direction's partial (both_dirs)
     int B, H, dk, dv;
     long long T;
-    int io_bf16;            // 1: bf16 I/O, 0: fp32 I/O
+    int io;                 // IoType of q, k, v
     int reverse;            // 1: walk tokens T-1 .. 0
     int out_mode;           // OutMode
     int both_dirs;          // 1: one launch runs both directions (OUT_PARTIAL into
@@ -56,31 +65,32 @@ inline void contiguous_strides(PassArgs &a) {
 // Sequential per-token scan (the chunk_len = 1 form).
 hipError_t launch_scan(const PassArgs &a, hipStream_t stream);
 
-// Chunked (UT-transform) form, bf16 MFMA kernel: C = 64, bf16 I/O,
+// Chunked (UT-transform) form, bf16 MFMA kernel: C = 64, bf16 or FP8 inputs,
 // d_k, d_v in {32, 64, 128}.
 // It needs PassArgs::tm: chunk_mfma_tm_bytes(n) bytes hold the triangular
 // inverses of n chunks (one per direction, b, h and chunk) and, for the
-// prologue, their tokens' inverse q and k norms.
-bool chunk_mfma_supported(int C, int dk, int dv, int io_bf16);
+// prologue, their tokens' inverse k norms.
+bool chunk_mfma_supported(int C, int dk, int dv, int io);
 size_t chunk_mfma_tm_bytes(long long chunks);
 hipError_t launch_chunk_mfma(const PassArgs &a, int C, hipStream_t stream);
 
-// Chunked form, general fp32 kernel: C, d_k, d_v in {16, 32, 64, 128}, fp32 or
-// bf16 I/O.
+// Chunked form, general fp32 kernel: C, d_k, d_v in {16, 32, 64, 128}, every
+// IoType.
 bool chunk_general_supported(int C, int dk, int dv);
 hipError_t launch_chunk_general(const PassArgs &a, int C, hipStream_t stream);
 
-// out[e] = round(partial[e] + partial_rev[e]) over n elements (n % 4 == 0).
+// out[e] = round(partial[e] + partial_rev[e]) over n elements (n % 4 == 0), out
+// in fp32 for IO_F32 and bf16 otherwise.
 hipError_t launch_combine(void *out, const float *partial, const float *partial_rev, long long n,
-                          int io_bf16, hipStream_t stream);
+                          int io, hipStream_t stream);
 
 // Chunked form with chunk length C: the MFMA kernel where it applies, else the
 // general one.  hipErrorInvalidValue for a (C, dk, dv, dtype) neither covers.
-inline bool chunk_supported(int C, int dk, int dv, int io_bf16) {
-    return chunk_mfma_supported(C, dk, dv, io_bf16) || chunk_general_supported(C, dk, dv);
+inline bool chunk_supported(int C, int dk, int dv, int io) {
+    return chunk_mfma_supported(C, dk, dv, io) || chunk_general_supported(C, dk, dv);
 }
 inline hipError_t launch_chunk(const PassArgs &a, int C, hipStream_t stream) {
-    if (chunk_mfma_supported(C, a.dk, a.dv, a.io_bf16)) return launch_chunk_mfma(a, C, stream);
+    if (chunk_mfma_supported(C, a.dk, a.dv, a.io)) return launch_chunk_mfma(a, C, stream);
     return launch_chunk_general(a, C, stream);
 }
 

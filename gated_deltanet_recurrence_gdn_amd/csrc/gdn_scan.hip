@@ -50,16 +50,15 @@ struct ScanParams {
     float scale;
 };
 
-template <bool BF16>
-struct Chunk8;  // 8 consecutive I/O elements held in registers
+template <int IO>
+struct Chunk8;  // 8 consecutive input elements held in registers
 
 template <>
-struct Chunk8<true> {
+struct Chunk8<IO_BF16> {
     uint4 w;
     __device__ void load(const void *base, size_t elem) {
         w = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + elem);
     }
-    __device__ void zero() { w = make_uint4(0, 0, 0, 0); }
     __device__ void to_f32(float f[8]) const {
         f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
         f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
@@ -67,14 +66,25 @@ struct Chunk8<true> {
 };
 
 template <>
-struct Chunk8<false> {
+struct Chunk8<IO_FP8> {
+    uint2 w;
+    __device__ void load(const void *base, size_t elem) {
+        w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(base) + elem);
+    }
+    __device__ void to_f32(float f[8]) const {
+        fp8x4_to_f32(w.x, f);
+        fp8x4_to_f32(w.y, f + 4);
+    }
+};
+
+template <>
+struct Chunk8<IO_F32> {
     float4 a, b;
     __device__ void load(const void *base, size_t elem) {
         const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + elem);
         a = p[0];
         b = p[1];
     }
-    __device__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
     __device__ void to_f32(float f[8]) const {
         f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
         f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
@@ -96,9 +106,9 @@ __device__ __forceinline__ float row16_sum2(float u, float &p, bool odd) {
     return dpp_mov<0xA0>(t);  // quad_perm [0,0,2,2]: the even lane's sum
 }
 
-template <bool BF16>
+template <int IO>
 __device__ __forceinline__ void store_out(void *out, size_t elem, float x) {
-    if constexpr (BF16)
+    if constexpr (IO != IO_F32)
         reinterpret_cast<uint16_t *>(out)[elem] = (uint16_t)f32_to_bf16_bits(x);
     else
         reinterpret_cast<float *>(out)[elem] = x;
@@ -108,7 +118,7 @@ __device__ __forceinline__ void store_out(void *out, size_t elem, float x) {
 // live in the VGPRs of L = DK / E lanes: lane `seg` of the row holds d_k indices
 // 4 (seg + L i) + m (i < E / 4, m < 4), so the row's lanes read one contiguous
 // run of LDS per float4 and every row reads the same addresses (a broadcast).
-template <int DK, int E, bool BF16, bool PRO>
+template <int DK, int E, int IO, bool PRO>
 __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
     constexpr int L = DK / E;            // lanes per state row
     constexpr int V4 = E / 4;            // float4 of k (and of q) per lane and token
@@ -159,7 +169,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
     __builtin_amdgcn_s_waitcnt(0);
 
     const long long nst = (T + TB - 1) / TB;
-    Chunk8<BF16> kr[KPT], qr[KPT], vr[VPT];
+    Chunk8<IO> kr[KPT], qr[KPT], vr[VPT];
     float br = 0.f, ar = 1.f;
 
     // Token at walk position sidx, clamped to the last one: the loads are
@@ -356,7 +366,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
             if (p.out_mode == OUT_PARTIAL) {
                 partial[e] = o;
             } else {
-                store_out<BF16>(p.out, e, o);
+                store_out<IO>(p.out, e, o);
             }
         }
         if (more) commit(st + 1);
@@ -371,20 +381,27 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
     }
 }
 
-template <int DK, int E, bool BF16, bool PRO>
+template <int DK, int E, int IO, bool PRO>
 hipError_t launch_e(const PassArgs &a, const ScanParams &p, hipStream_t stream) {
     constexpr int L = DK / E;
     const int rows = (NT / L) < a.dv ? (NT / L) : a.dv;
     dim3 grid(a.dv / rows, a.H, a.B * (a.both_dirs ? 2 : 1));
-    hipLaunchKernelGGL((scan_kernel<DK, E, BF16, PRO>), grid, dim3(rows * L), 0, stream, p);
+    hipLaunchKernelGGL((scan_kernel<DK, E, IO, PRO>), grid, dim3(rows * L), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int DK, int E, int IO>
+hipError_t launch_dk_io(const PassArgs &a, const ScanParams &p, hipStream_t stream) {
+    return a.prologue ? launch_e<DK, E, IO, true>(a, p, stream) : launch_e<DK, E, IO, false>(a, p, stream);
 }
 
 template <int DK, int E>
 hipError_t launch_dk_e(const PassArgs &a, const ScanParams &p, hipStream_t stream) {
-    if (a.io_bf16)
-        return a.prologue ? launch_e<DK, E, true, true>(a, p, stream) : launch_e<DK, E, true, false>(a, p, stream);
-    return a.prologue ? launch_e<DK, E, false, true>(a, p, stream) : launch_e<DK, E, false, false>(a, p, stream);
+    switch (a.io) {
+        case IO_BF16: return launch_dk_io<DK, E, IO_BF16>(a, p, stream);
+        case IO_FP8: return launch_dk_io<DK, E, IO_FP8>(a, p, stream);
+        default: return launch_dk_io<DK, E, IO_F32>(a, p, stream);
+    }
 }
 
 // E = 8 state values per lane unless that puts more than two waves on a SIMD (256
@@ -433,14 +450,14 @@ hipError_t launch_scan(const PassArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_combine(void *out, const float *partial, const float *partial_rev, long long n,
-                          int io_bf16, hipStream_t stream) {
+                          int io, hipStream_t stream) {
     const long long n4 = n / 4;
     if (n4 == 0) return hipSuccess;
     long long nb = (n4 + 255) / 256;
     if (nb > 256 * 64) nb = 256 * 64;
     const float4 *pa = reinterpret_cast<const float4 *>(partial);
     const float4 *pb = reinterpret_cast<const float4 *>(partial_rev);
-    if (io_bf16)
+    if (io != IO_F32)
         hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)nb), dim3(256), 0, stream, out, pa, pb, n4);
     else
         hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)nb), dim3(256), 0, stream, out, pa, pb, n4);

@@ -15,8 +15,8 @@ Recipe: one torch CPU ``Generator`` seeded with ``seed``, float32 draws in the
 order q, k, v, x_b, x_a with shapes [B,T,H,d_k], [B,T,H,d_k], [B,T,H,d_v],
 [B,T,H], [B,T,H]; q and k are divided by max(||x||_2, 1e-12) over the last
 axis; b = sigmoid(x_b + b_mean), a = exp(-softplus(x_a + a_mean)); q, k, v are
-then rounded to bf16 (round-to-nearest-even) when the workload is bf16.  beta
-and decay stay float32.
+then rounded to bf16 or to FP8 E4M3 (round-to-nearest-even) for those I/O types.
+beta and decay stay float32.
 """
 from __future__ import annotations
 
@@ -26,6 +26,10 @@ from dataclasses import dataclass, field
 import torch
 
 TOKENS_PER_FRAME = 30 * 52  # 480x832 video at a 16x spatial reduction
+
+# q, k, v element types: fp8 is OCP FP8 E4M3 (torch.float8_e4m3fn, round to nearest
+# even from fp32; every draw here is far inside its +-448 range).
+IO_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 
 
 @dataclass(frozen=True)
@@ -83,7 +87,7 @@ def make_inputs(B: int, T: int, H: int, dk: int, dv: int, io: str = "bf16", seed
     k = torch.nn.functional.normalize(k, p=2.0, dim=-1, eps=1e-12)
     beta = torch.sigmoid(xb + b_mean)
     decay = torch.exp(-torch.nn.functional.softplus(xa + a_mean))
-    dt = {"fp32": torch.float32, "bf16": torch.bfloat16}[io]
+    dt = IO_DTYPES[io]
     return {"q": q.to(dt).contiguous(), "k": k.to(dt).contiguous(), "v": v.to(dt).contiguous(),
             "beta": beta.contiguous(), "decay": decay.contiguous()}
 
@@ -106,7 +110,7 @@ def make_packed_inputs(B: int, T: int, H: int, dk: int, dv: int, io: str = "bf16
     v = torch.randn((B, T, H * dv), generator=g, dtype=torch.float32)
     xb = torch.randn((B, T, H), generator=g, dtype=torch.float32)
     xa = torch.randn((B, T, H), generator=g, dtype=torch.float32)
-    dt = {"fp32": torch.float32, "bf16": torch.bfloat16}[io]
+    dt = IO_DTYPES[io]
     W = 2 * H * dk + H * dv
     buf = torch.full((B, T + gap, W + pad), float("nan"), dtype=dt)
     buf[:, :T, :W] = torch.cat([q, k, v], dim=-1).to(dt)

@@ -27,7 +27,8 @@
  * Layouts.  Every tensor pointer is a DEVICE pointer to a contiguous,
  * row-major array on the handle's device:
  *     q, k       [B, T, H, d_k]   io_dtype
- *     v, out     [B, T, H, d_v]   io_dtype
+ *     v          [B, T, H, d_v]   io_dtype
+ *     out        [B, T, H, d_v]   fp32 (GDN_F32) or bf16 (GDN_BF16, GDN_FP8)
  *     beta,decay [B, T, H]        float32
  *     state      [B, H, d_v, d_k] float32  (row i is output channel i: o = S q)
  * q, k, v, out and the states must be 16-byte aligned; beta and decay 4-byte.
@@ -69,7 +70,14 @@ typedef enum {
     GDN_ERR_LAUNCH = -7       /* kernel launch was rejected                     */
 } gdn_status;
 
-typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+/* Element type of q, k, v (and qkv).  out is fp32 for GDN_F32 and bf16 for the
+ * others; beta, decay and the state are always fp32.  GDN_FP8 is OCP FP8 E4M3
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, NaN =
+ * S.1111.111), widened exactly to bf16 / fp32 inside the kernels: halving the
+ * bytes of q, k and v; the FlashDreams SANA-WM page (section "Developer Details",
+ * the precision bullet) lists FP8 inference beside the bf16 default.  Its
+ * arithmetic is that of the bf16 path. */
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8 = 2 } gdn_dtype;
 
 /* Request the scratch that gdn_forward_bidi needs (B * max_T * H * d_v fp32). */
 #define GDN_FLAG_BIDI 1u
@@ -78,7 +86,7 @@ typedef struct {
     int device;        /* HIP device ordinal; -1 = dry run (validate only, no GPU) */
     int B, H;          /* batch and heads, >= 1                                   */
     int d_k, d_v;      /* head dims, each in {16, 32, 64, 128}                    */
-    int io_dtype;      /* gdn_dtype of q, k, v and out                            */
+    int io_dtype;      /* gdn_dtype of q, k, v (out: fp32 or bf16, see gdn_dtype) */
     long long max_T;   /* largest T any call on this handle will pass, >= 0       */
     unsigned flags;    /* GDN_FLAG_* bits                                         */
 } gdn_config;
@@ -99,10 +107,10 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h);
  *   state_out  NULL = final state discarded; may equal state_in (in-place carry).
  *   chunk_len  1 = sequential scan; 16, 32, 64 or 128 = chunked (UT-transform)
  *              form with chunks of that many tokens; 0 = default (64).  Others
- *              return GDN_ERR_UNSUPPORTED.  bf16 I/O with chunk_len 64 and
- *              d_k, d_v >= 32 runs on bf16 MFMA with fp32 accumulation; every
- *              other chunked request (fp32 I/O, other chunk lengths, d = 16)
- *              runs a kernel that computes in fp32 throughout.
+ *              return GDN_ERR_UNSUPPORTED.  bf16 or FP8 inputs with chunk_len 64
+ *              and d_k, d_v >= 32 run on bf16 MFMA with fp32 accumulation;
+ *              every other chunked request (fp32 I/O, other chunk lengths,
+ *              d = 16) runs a kernel that computes in fp32 throughout.
  *   hip_stream a hipStream_t (NULL = the null stream of the handle's device).
  * Streaming: calling with consecutive token ranges and state_out of one call
  * as state_in of the next reproduces a single call over the whole range.

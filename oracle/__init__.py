@@ -87,8 +87,8 @@ def _as(x, dtype):
     if hasattr(x, "detach"):  # torch tensor
         import torch
         x = x.detach().to("cpu")
-        if x.dtype == torch.bfloat16 or x.dtype == torch.float16:
-            x = x.float()
+        if x.dtype in (torch.bfloat16, torch.float16, torch.float8_e4m3fn, torch.float8_e5m2):
+            x = x.float()  # exact: every value of these types is an fp32
         x = x.numpy()
     return np.ascontiguousarray(np.asarray(x), dtype=dtype)
 

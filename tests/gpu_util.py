@@ -7,8 +7,10 @@ import torch
 
 import oracle
 
-# rel-L2 bars against the float64 oracle, by I/O dtype.
-TOL = {"fp32": 1e-5, "bf16": 1e-2}
+# rel-L2 bars against the float64 oracle, by I/O dtype.  The oracle reads the very
+# bf16 / FP8 values the GPU receives, so the bar covers only the kernel arithmetic
+# and the output rounding, which are the same for bf16 and FP8 inputs.
+TOL = {"fp32": 1e-5, "bf16": 1e-2, "fp8": 1e-2}
 
 
 def dev(x: dict, device="cuda:0") -> dict:

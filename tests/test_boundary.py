@@ -192,6 +192,32 @@ def test_torch_wrapper_checks_packed_shapes():
     g.close()
 
 
+def test_fp8_dry_run_sizes():
+    """FP8 inputs are 1 byte, out is bf16: the aliasing extents follow."""
+    st, h = gb.gdn_create(-1, 1, 2, 64, 64, gb.GDN_FP8, 100, 0)
+    assert st == gb.GDN_OK
+    T = 100
+    in_bytes = T * 2 * 64        # q, k or v
+    out_bytes = T * 2 * 64 * 2   # bf16
+    a = dict(ADDR)
+    ok = gb.gdn_forward(h, a["q"], a["k"], a["v"], a["beta"], a["decay"], None, None, a["q"] + in_bytes, T, 64)
+    assert ok == gb.GDN_OK
+    bad = gb.gdn_forward(h, a["q"], a["k"], a["v"], a["beta"], a["decay"], None, None, a["q"] + in_bytes - 16, T, 64)
+    assert bad == gb.GDN_ERR_ALIAS
+    # out ends exactly where k begins
+    ok = gb.gdn_forward(h, a["q"], a["k"], a["v"], a["beta"], a["decay"], None, None, a["k"] - out_bytes, T, 64)
+    assert ok == gb.GDN_OK
+    # packed rows: strides are multiples of 16 bytes = 16 FP8 elements
+    row = 2 * 2 * 64 + 2 * 64
+    assert gb.gdn_forward_packed(h, a["q"], row + 16, 0, a["beta"], a["decay"], None, None, a["out"], T, 1) == gb.GDN_OK
+    assert gb.gdn_forward_packed(h, a["q"], row + 8, 0, a["beta"], a["decay"], None, None, a["out"], T, 1) == \
+        gb.GDN_ERR_ALIGN
+    for chunk in (0, 1, 16, 32, 64, 128):
+        assert gb.gdn_forward(h, a["q"], a["k"], a["v"], a["beta"], a["decay"], None, None, a["out"], T,
+                              chunk) == gb.GDN_OK
+    gb.gdn_free(h)
+
+
 @pytest.mark.parametrize("args,code", [
     ((-1, 0, 1, 16, 16, gb.GDN_F32, 10, 0), gb.GDN_ERR_ARG),
     ((-1, 1, 0, 16, 16, gb.GDN_F32, 10, 0), gb.GDN_ERR_ARG),

@@ -102,3 +102,20 @@ def test_generator_distributions():
     # the strong-decay workload: a = exp(-softplus(N(2,1))) has mean ~0.13
     y = inputs.make_inputs(1, 500, 4, 16, 16, "bf16", seed=0, a_mean=2.0)
     assert 0.08 < float(y["decay"].mean()) < 0.2
+
+
+def test_fp8_inputs_widen_to_the_e4m3_definition():
+    """The oracle reads FP8 inputs as the OCP E4M3 values themselves: sign s, exponent
+    e (bias 7), mantissa m give (-1)^s 2^(e-7) (1 + m/8) for e > 0 and (-1)^s 2^-6 m/8
+    for e = 0; S.1111.111 is NaN and there are no infinities."""
+    import torch
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    got = oracle._as(codes.view(torch.float8_e4m3fn), np.float64)
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            assert np.isnan(got[c]), c
+            continue
+        mag = 2.0 ** (e - 7) * (1 + m / 8) if e > 0 else 2.0 ** -6 * (m / 8)
+        assert got[c] == (-mag if s else mag), (c, got[c])
+    assert np.nanmax(got) == 448.0 and got[1] == 2.0 ** -9
