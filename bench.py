@@ -202,6 +202,26 @@ def timed(torch, fn, reps, warm=10):
     return e0.elapsed_time(e1) / reps
 
 
+def per_call(torch, fn, reps, warm=10, flush=None):
+    """Median and min ms of single calls, each bracketed by its own HIP events on the
+    current stream; `flush` (if given) runs before each call, outside the events."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    return {"median_ms": ts[len(ts) // 2], "min_ms": ts[0], "runs": reps}
+
+
 def measure_forms(torch, gb, inputs, d, g, x):
     forms = {}
     B, T, H, dk = d["q"].shape
@@ -229,17 +249,41 @@ def measure_forms(torch, gb, inputs, d, g, x):
     state = torch.zeros((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
     outs = [torch.empty((w.B, n, w.H, w.dv), dtype=torch.bfloat16, device="cuda") for _ in range(w.calls)]
     out1 = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
-    per_call = []
+    per_call_ms = []
     for i in range(w.calls):
         pi = parts[i]
-        per_call.append(timed(torch, lambda: gb.gdn_forward(gs.h, pi["q"], pi["k"], pi["v"], pi["beta"],
+        per_call_ms.append(timed(torch, lambda: gb.gdn_forward(gs.h, pi["q"], pi["k"], pi["v"], pi["beta"],
                                                             pi["decay"], state, state, outs[i], n, 64, stream), 5))
     one = timed(torch, lambda: gb.gdn_forward(gs.h, xs["q"], xs["k"], xs["v"], xs["beta"], xs["decay"], None,
                                               state, out1, w.T, 64, stream), 5)
-    forms["streaming_bf16_d128"] = {"per_call_ms": per_call, "sum_ms": sum(per_call), "one_shot_ms": one,
-                                    "token_heads_per_s": w.B * w.H * w.T / (sum(per_call) / 1e3)}
+    # Cold: a 512 MiB device write before each call evicts L2 and the 256 MB MALL.
+    flush_buf = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
+    flush = lambda: flush_buf.fill_(1)
+    cold = [per_call(torch, lambda: gb.gdn_forward(gs.h, parts[i]["q"], parts[i]["k"], parts[i]["v"],
+                                                   parts[i]["beta"], parts[i]["decay"], state, state, outs[i], n,
+                                                   64, stream), 10, warm=2, flush=flush)["median_ms"]
+            for i in range(w.calls)]
+    forms["streaming_bf16_d128"] = {"per_call_ms": per_call_ms, "sum_ms": sum(per_call_ms), "one_shot_ms": one,
+                                    "cold_per_call_median_ms": cold, "cold_sum_ms": sum(cold),
+                                    "token_heads_per_s": w.B * w.H * w.T / (sum(per_call_ms) / 1e3)}
     gs.close()
     del xs, parts
+
+    # 3 frames at d = 64 (B=1, H=16, T=4680), warm and cold.
+    w1 = inputs.WORKLOADS["causal_bf16_d64"]
+    x1 = {k_: v_.cuda() for k_, v_ in inputs.make_workload(w1).items()}
+    g1 = gb.GDN(w1.B, w1.H, w1.dk, w1.dv, "bf16", max_T=w1.T)
+    o1 = torch.empty((w1.B, w1.T, w1.H, w1.dv), dtype=torch.bfloat16, device="cuda")
+    f1 = lambda: gb.gdn_forward(g1.h, x1["q"], x1["k"], x1["v"], x1["beta"], x1["decay"], None, None, o1, w1.T,
+                                64, stream)
+    warm1 = per_call(torch, f1, 20)
+    cold1 = per_call(torch, f1, 10, warm=2, flush=flush)
+    th1 = w1.B * w1.H * w1.T
+    forms["causal_bf16_d64"] = {"warm": warm1, "cold": cold1,
+                                "token_heads_per_s_warm": th1 / (warm1["median_ms"] / 1e3),
+                                "token_heads_per_s_cold": th1 / (cold1["median_ms"] / 1e3)}
+    g1.close()
+    del x1, o1, flush_buf
 
     # Bidirectional form, 21 frames.
     wb = inputs.WORKLOADS["bidi_bf16_d128"]
