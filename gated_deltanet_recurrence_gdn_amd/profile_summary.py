@@ -10,6 +10,11 @@ written into the summaries):
   write bytes:   rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o write -- \\
                      python bench.py --steps 2 --warmup 1 --no-cpu --no-forms --calib-copy
 
+and, for --forms-only, a kernel trace of the bench with its secondary forms:
+
+  forms:         rocprofv3 --kernel-trace --stats --output-format csv -d DIR/forms -o forms -- \\
+                     python bench.py --no-cpu --steps 5 --warmup 5
+
     python -m gated_deltanet_recurrence_gdn_amd.profile_summary DIR [--workload NAME]
 
 One chunked gdn_forward is two launches, tm_kernel (the per-chunk triangular
@@ -95,14 +100,44 @@ def counter_per_dispatch(d, sub, counter):
     return per, statistics.mean(copy)
 
 
+FORMS_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d {d}/forms -o forms -- "
+             "python bench.py --no-cpu --steps 5 --warmup 5")
+
+
+def forms_summary(d):
+    """Per-kernel-instantiation stats of a bench run with its secondary forms."""
+    rows = _csv(os.path.join(d, "forms", "**", "*kernel_stats.csv"))
+    lines = ["rocprofv3 kernel trace: bench.py with its secondary forms (scan, 5-call streaming warm and",
+             "cold, 3-frame d=64 warm and cold, bidirectional, fused prologue from packed qkv, FP8 inputs)",
+             "", "command (MI355X, repo root, TMPDIR=/tmp):", "  " + FORMS_CMD.format(d="gpurun_out/prof"),
+             f"kernel source sha256[:16] (gdn_chunk.hip): {src_hash()}", "",
+             "template arguments: chunk_kernel<d_k, input type (1 bf16, 2 FP8), prologue>, tm_kernel<same>,",
+             "scan_kernel<d_k, state values per lane, input type (0 fp32, 1 bf16, 2 FP8), prologue>", "",
+             f"  {'kernel':78s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
+    for r in rows:
+        name = r["Name"].replace("void gdn::(anonymous namespace)::", "")
+        name = name.split("(gdn::")[0].split("(void*")[0]
+        lines.append(f"  {name[:78]:78s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
+                     f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f}")
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("dir", help="directory holding the kt/, fetch/ and write/ rocprofv3 outputs")
+    ap.add_argument("--forms-only", action="store_true",
+                    help="only summarise DIR/forms (the kernel trace of a bench run with its secondary forms)")
     ap.add_argument("--workload", default="batched_bf16_d128")
     ap.add_argument("--algorithmic-bytes", type=float, default=None,
                     help="algorithmic bytes per launch (default: bench.py's formula for the workload)")
     a = ap.parse_args()
     os.makedirs(PROFILES, exist_ok=True)
+    if a.forms_only:
+        lines = forms_summary(a.dir)
+        with open(os.path.join(PROFILES, "forms_batched_bf16_d128.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return
     import sys
     sys.path.insert(0, ROOT)
     import bench
