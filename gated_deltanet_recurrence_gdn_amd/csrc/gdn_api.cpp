@@ -298,7 +298,7 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
 
     size_t scratch_bytes = 0;
     if (c.flags & GDN_FLAG_BIDI) scratch_bytes = 2 * (size_t)c.B * (size_t)c.max_T * c.H * c.d_v * sizeof(float);
-    // The MFMA chunked kernel (bf16 I/O, chunk 64, d_k and d_v >= 32) forms each
+    // The MFMA chunked kernel (bf16 or FP8 inputs, chunk 64, d_k and d_v >= 32) forms each
     // chunk's triangular inverse in a pass of its own and reads it back.
     long long tm_chunks = 0;
     if (gdn::chunk_mfma_supported(64, c.d_k, c.d_v, c.io_dtype))

@@ -32,14 +32,15 @@
  *     beta,decay [B, T, H]        float32
  *     state      [B, H, d_v, d_k] float32  (row i is output channel i: o = S q)
  * q, k, v, out and the states must be 16-byte aligned; beta and decay 4-byte.
+ * FP8 inputs are one byte per element, so their rows are 16-byte multiples too.
  *
  * Ownership.  The caller owns every tensor and the stream.  The library owns
  * the handle and its device scratch, allocated once in gdn_create and freed in
  * gdn_free: the two fp32 partials of gdn_forward_bidi (GDN_FLAG_BIDI), and, on
- * handles the bf16 chunked kernel can serve (bf16 I/O, d_k and d_v >= 32), the
- * per-chunk triangular inverses of that kernel and, for the packed entry
- * points, each token's inverse k norm (6.25 KiB per direction, b, h and 64-token
- * chunk up to max_T).  The forward calls allocate nothing, never
+ * handles the bf16 MFMA chunked kernel can serve (bf16 or FP8 inputs, d_k and
+ * d_v >= 32), the per-chunk triangular inverses of that kernel and, for the
+ * packed entry points, each token's inverse k norm (6.25 KiB per direction, b,
+ * h and 64-token chunk up to max_T).  The forward calls allocate nothing, never
  * synchronise and never copy between host and device: they validate, enqueue
  * kernels on the given stream and return.  Device faults surface at the
  * caller's next synchronisation, as with any HIP launch.  A handle must be
