@@ -122,8 +122,48 @@ def forms_summary(d):
     return lines
 
 
+# Hardware-counter passes (one rocprofv3 --pmc run each) over the bench's chunked call.
+COUNTER_SETS = [
+    "TA_BUSY_avr TA_ADDR_STALLED_BY_TC_CYCLES_sum",
+    "TA_DATA_STALLED_BY_TC_CYCLES_sum TA_TA_BUSY_sum",
+    "TCC_HIT_sum TCC_MISS_sum",
+    "TCP_PENDING_STALL_CYCLES_sum TCP_TOTAL_CACHE_ACCESSES_sum",
+    "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_INSTS_VMEM_RD SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT "
+    "SQ_INSTS_VALU SQ_INSTS_MFMA",
+]
+CTR_CMD = ("rocprofv3 --pmc {c} --output-format csv -d {d}/ctr_{i} -o ctr -- "
+           "python bench.py --steps 2 --warmup 1 --no-cpu --no-forms")
+
+
+def counters_summary(d):
+    """Mean per-dispatch counter values of tm_kernel and chunk_kernel from the DIR/ctr_<i> passes."""
+    vals = {kn: {} for kn in KERNELS}
+    for i in range(len(COUNTER_SETS)):
+        rows = _csv(os.path.join(d, f"ctr_{i}", "**", "*counter_collection.csv"))
+        acc = {}
+        for r in rows:
+            for kn in KERNELS:
+                if kn in r["Kernel_Name"]:
+                    acc.setdefault((kn, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+        for (kn, cn), v in acc.items():
+            vals[kn][cn] = statistics.mean(v)
+    lines = ["rocprofv3 hardware counters: chunked GDN forward (tm_kernel + chunk_kernel), workload "
+             "batched_bf16_d128", "(mean per dispatch; *_sum counters are summed over the 256 CUs' "
+             "instances, *_avr averaged over them)", "",
+             "commands (MI355X, repo root, TMPDIR=/tmp), one counter set per run:"]
+    lines += ["  " + CTR_CMD.format(c=c, d="gpurun_out/prof", i=i) for i, c in enumerate(COUNTER_SETS)]
+    lines += [f"kernel source sha256[:16]: {src_hash()}", ""]
+    for kn in KERNELS:
+        lines.append(f"{kn}:")
+        for cn in sorted(vals[kn]):
+            lines.append(f"  {cn:42s} {vals[kn][cn]:16.6g}")
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser()
+    ap.add_argument("--counters-only", action="store_true",
+                    help="only summarise the DIR/ctr_<i> hardware-counter passes")
     ap.add_argument("dir", help="directory holding the kt/, fetch/ and write/ rocprofv3 outputs")
     ap.add_argument("--forms-only", action="store_true",
                     help="only summarise DIR/forms (the kernel trace of a bench run with its secondary forms)")
@@ -132,6 +172,12 @@ def main():
                     help="algorithmic bytes per launch (default: bench.py's formula for the workload)")
     a = ap.parse_args()
     os.makedirs(PROFILES, exist_ok=True)
+    if a.counters_only:
+        lines = counters_summary(a.dir)
+        with open(os.path.join(PROFILES, "chunk_kernel_batched_bf16_d128_counters.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return
     if a.forms_only:
         lines = forms_summary(a.dir)
         with open(os.path.join(PROFILES, "forms_batched_bf16_d128.txt"), "w") as f:
