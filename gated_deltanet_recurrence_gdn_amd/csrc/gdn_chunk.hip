@@ -20,7 +20,10 @@
 // tm_kernel (throughput): Tm depends only on K and the gates, so it is formed
 // once per (direction, b, h, chunk) -- one block each, all chunks in parallel --
 // and written as bf16 in exactly the register order in which the state chain
-// uses it as an MFMA operand (6 KiB per chunk).  That costs extra HBM traffic
+// uses it as an MFMA operand (6 KiB per chunk), with the chunk's gate records
+// (1 KiB: b, log2 a and 1/||k|| of each token, so that chunk_kernel reads its
+// gates in one coalesced load instead of two loads whose lanes all fall on
+// different cache lines).  That costs extra HBM traffic
 // (K read again, Tm written and read back) and takes the Gram products, the
 // decay epilogues and the triangular inverse off the sequential path, where
 // every d_v tile of a head would otherwise redo them.
@@ -46,10 +49,11 @@
 //               O^T = gam .* (S Q^T) + N^T P^T, written as 8-byte row segments.
 //   waves 4, 5  K and Q of chunk c+1 (HBM -> registers -> LDS), loaded in
 //               period c-2 (two register sets alternate).
-//   wave 6      gate vectors of chunk c+2: float64 prefix sum of log2 a (DPP
-//               within 16-lane rows, then the row carries), 2^g, b 2^g,
-//               2^{g_last - g}, b, and the factors of the off-diagonal 32x32
-//               block.
+//   wave 6      gate vectors of chunk c+2 from the chunk's gate records (b,
+//               log2 a, 1/||k|| per token, written contiguously by tm_kernel
+//               from the strided [B, T, H] gates): float64 prefix sum of log2 a
+//               (DPP within 16-lane rows, then the row carries), 2^g, b 2^g,
+//               2^{g_last - g}, b.
 //   wave 7      b_t v_t of chunk c+1 (fp32, d_v-major) for R.
 //
 // Fused input prologue (template flag PRO): q, k, v are read in place from a
@@ -164,7 +168,7 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 struct Ctx {
     const char *q, *k, *v;      // bytes; v offset to the block's d_v tile
     const float *beta, *decay;
-    const float *norms;         // prologue: the head's inverse k norms, C floats per chunk
+    const float4 *grec;         // the head's gate records (b, log2 a, 1/||k||, 0), C per chunk
     long long T;
     int nchunks;
     int rs;   // q/k bytes between consecutive tokens (H * d_k elements when contiguous)
@@ -269,11 +273,10 @@ __device__ __forceinline__ void gate_in(float xb, float xa, float &b, float &l2a
     }
     if (!(l2a > -200.0f)) l2a = -200.0f;
 }
+// From b_t and log2 a_t (gate_in) and the inverse k norm of every token.
 template <bool PRO>
-__device__ __forceinline__ GateVals gate_values(int lane, int ntok, float xb, float xa, float rk) {
+__device__ __forceinline__ GateVals gate_values(int lane, int ntok, float b, float l2, float rk) {
     const bool real = lane < ntok;
-    float b, l2;
-    gate_in<PRO>(xb, xa, b, l2);
     if (!real) l2 = 0.0f;  // padding: a = 1
     const double xs = prefix_sum64(lane, (double)l2);
     const double xl = lane_value(xs, 63);
@@ -299,7 +302,7 @@ struct TmParams {
     const char *k;
     const float *beta, *decay;
     uint16_t *tm;     // [dirs][B][H][nchunks][TM_ELEMS]
-    float *norms;     // prologue: [dirs][B][H][nchunks][C] inverse norms of k
+    float4 *grec;     // [dirs][B][H][nchunks][C] gate records (b, log2 a, 1/||k||, 0)
     long long T;
     long long qk_ts, qk_bs;
     int B, H, nchunks, reverse;
@@ -535,7 +538,7 @@ __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
     x.k = p.k + ((size_t)b * p.qk_bs + (size_t)h * DK) * ES;
     x.beta = p.beta + gtok0;
     x.decay = p.decay + gtok0;
-    x.norms = nullptr;
+    x.grec = nullptr;
 
     // 1. The chunk's K rows into LDS as bf16, row-coalesced (16 bytes per lane,
     //    DK / seg_cols lanes per row, block-wide passes).  With the prologue the
@@ -590,12 +593,15 @@ __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
     } else {
         // wave 3: the gate vectors (the prologue's factors need every row's norm)
         const float rk = PRO ? sm.rk[lane] : 1.f;
-        const GateVals gv = gate_values<PRO>(lane, x.ntok(c), xb, xa, rk);
+        float bt, l2;
+        gate_in<PRO>(xb, xa, bt, l2);
+        const GateVals gv = gate_values<PRO>(lane, x.ntok(c), bt, l2, rk);
         sm.g[lane] = gv.g;
         sm.gk[lane] = gv.gk;
         sm.bk[lane] = gv.bk;
         sm.xf[lane] = gv.xf;
-        if constexpr (PRO) p.norms[((size_t)((dir * p.B + b) * p.H + h) * p.nchunks + c) * C + lane] = rk;
+        // the chunk's gate record, one 16-byte entry per token, contiguous for chunk_kernel
+        p.grec[((size_t)((dir * p.B + b) * p.H + h) * p.nchunks + c) * C + lane] = make_float4(bt, l2, rk, 0.f);
     }
     __syncthreads();  // K is read; Tm and A overwrite it
     if (wid < 2) a_diag_block(sm, g0, wid, lane);
@@ -626,8 +632,7 @@ __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
 struct ChunkParams {
     const char *q, *k, *v;
     long long qk_ts, qk_bs, v_ts, v_bs;  // element strides between tokens / batch elements
-    const float *beta, *decay;
-    const float *norms;                  // prologue: written by tm_kernel
+    const float4 *grec;                  // gate records written by tm_kernel
     const float *state_in;
     float *state_out;
     void *out;
@@ -1009,8 +1014,7 @@ __device__ __forceinline__ void store_rows(uint16_t (*dst)[PITCH], const Rows64<
 
 // ---- waves 6, 7: gate vectors; V tiles -----------------------------------------
 struct GateRegs {
-    float b, a;  // gate inputs (values, or logits with the prologue)
-    float rk;    // prologue: inverse norm of k_t (from tm_kernel)
+    float4 r;  // the token's gate record from tm_kernel: b, log2 a, 1/||k|| (1 without the prologue)
 };
 
 // The chunk's V tile (64 tokens x 32 d_v), row-coalesced: in w[s], lane l holds
@@ -1036,22 +1040,17 @@ __device__ __forceinline__ VRow<IO> load_v(const Ctx &x, int c, int lane) {
     }
     return d;
 }
-// Unconditional (c is clamped into range by the caller), so that the count of
-// loads in flight is the same on every path.
-template <bool PRO>
+// One 16-byte record per lane from a contiguous 1 KiB per chunk (the strided
+// [B, T, H] gates were read, activated and clamped by tm_kernel).  Unconditional
+// (c is clamped into range by the caller), so that the count of loads in flight
+// is the same on every path.
 __device__ __forceinline__ void load_gates(const Ctx &x, int c, int lane, GateRegs &g) {
-    const size_t o = (size_t)x.tok_clamped(c, lane) * x.H;
-    g.b = x.beta[o];
-    g.a = x.decay[o];
-    if constexpr (PRO)
-        g.rk = x.norms[(size_t)c * C + lane];
-    else
-        g.rk = 1.f;
+    g.r = x.grec[(size_t)c * C + lane];
 }
 
 template <int DK, bool PRO>
 __device__ __forceinline__ void gates_store(const Ctx &x, Smem<DK> &sm, int c, int lane, const GateRegs &gr) {
-    const GateVals v = gate_values<PRO>(lane, x.ntok(c), gr.b, gr.a, gr.rk);
+    const GateVals v = gate_values<PRO>(lane, x.ntok(c), gr.r.x, gr.r.y, gr.r.z);
     const int s3 = c % 3;
     sm.g[s3][lane] = v.g;
     sm.gk[s3][lane] = v.gk;
@@ -1124,10 +1123,9 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     x.q = p.q + qk0;
     x.k = p.k + qk0;
     x.v = p.v + ((size_t)b * p.v_bs + (size_t)h * p.dv + dv0) * ES;
-    x.beta = p.beta + tok0;
-    x.decay = p.decay + tok0;
+    x.beta = x.decay = nullptr;  // the gates arrive as tm_kernel's records (x.grec)
     const int n = x.nchunks;
-    x.norms = PRO ? p.norms + (size_t)((dir * p.B + b) * p.H + h) * n * C : nullptr;
+    x.grec = p.grec + (size_t)((dir * p.B + b) * p.H + h) * n * C;
 
     // Every role walks the same periods it = -2 .. n (the last one finishes the
     // outputs of chunk n-1), two per loop trip so that register sets alternate at
@@ -1207,15 +1205,15 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         // Gates of chunk c are computed in period c-2 from register set c&1
         // (loaded in period c-4).
         GateRegs gA, gB;
-        load_gates<PRO>(x, 0, lane, gA);
-        load_gates<PRO>(x, 1 < n ? 1 : n - 1, lane, gB);
+        load_gates(x, 0, lane, gA);
+        load_gates(x, 1 < n ? 1 : n - 1, lane, gB);
         __syncthreads();
         for (int it = -2; it < n + 1; it += 2) {
             if (x.has(it + 2)) gates_store<DK, PRO>(x, sm, it + 2, lane, gA);
-            load_gates<PRO>(x, it + 4 < n ? it + 4 : n - 1, lane, gA);
+            load_gates(x, it + 4 < n ? it + 4 : n - 1, lane, gA);
             __syncthreads();
             if (x.has(it + 3)) gates_store<DK, PRO>(x, sm, it + 3, lane, gB);
-            load_gates<PRO>(x, it + 5 < n ? it + 5 : n - 1, lane, gB);
+            load_gates(x, it + 5 < n ? it + 5 : n - 1, lane, gB);
             __syncthreads();
         }
     } else {
@@ -1242,14 +1240,14 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     const int dirs = a.both_dirs ? 2 : 1;
     const long long ntm = (long long)dirs * a.B * a.H * nchunks;
     if (!a.tm || ntm > a.tm_chunks || ntm > 0x7fffffffLL) return hipErrorInvalidValue;
-    // The inverse norms follow the Tm blocks of the handle's whole capacity.
-    float *norms = PRO ? reinterpret_cast<float *>(a.tm + (size_t)a.tm_chunks * TM_ELEMS) : nullptr;
+    // The gate records follow the Tm blocks of the handle's whole capacity.
+    float4 *grec = reinterpret_cast<float4 *>(a.tm + (size_t)a.tm_chunks * TM_ELEMS);
 
     TmParams t;
     t.k = static_cast<const char *>(a.k);
     t.beta = a.beta; t.decay = a.decay;
     t.tm = a.tm;
-    t.norms = norms;
+    t.grec = grec;
     t.T = a.T; t.qk_ts = a.qk_ts; t.qk_bs = a.qk_bs;
     t.B = a.B; t.H = a.H; t.nchunks = nchunks; t.reverse = a.reverse;
     hipLaunchKernelGGL((tm_kernel<DK, IO, PRO>), dim3((unsigned)ntm), dim3(256), 0, stream, t);
@@ -1261,8 +1259,7 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.k = static_cast<const char *>(a.k);
     p.v = static_cast<const char *>(a.v);
     p.qk_ts = a.qk_ts; p.qk_bs = a.qk_bs; p.v_ts = a.v_ts; p.v_bs = a.v_bs;
-    p.beta = a.beta; p.decay = a.decay;
-    p.norms = norms;
+    p.grec = grec;
     p.state_in = a.state_in; p.state_out = a.state_out; p.out = a.out;
     p.partial = a.partial; p.partial_rev = a.partial_rev;
     p.tm = a.tm;
@@ -1291,7 +1288,7 @@ bool chunk_mfma_supported(int C_, int dk, int dv, int io) {
 }
 
 size_t chunk_mfma_tm_bytes(long long chunks) {
-    return (size_t)chunks * (TM_ELEMS * sizeof(uint16_t) + C * sizeof(float));
+    return (size_t)chunks * (TM_ELEMS * sizeof(uint16_t) + C * sizeof(float4));
 }
 
 hipError_t launch_chunk_mfma(const PassArgs &a, int C_, hipStream_t stream) {

@@ -68,8 +68,8 @@ hipError_t launch_scan(const PassArgs &a, hipStream_t stream);
 // Chunked (UT-transform) form, bf16 MFMA kernel: C = 64, bf16 or FP8 inputs,
 // d_k, d_v in {32, 64, 128}.
 // It needs PassArgs::tm: chunk_mfma_tm_bytes(n) bytes hold the triangular
-// inverses of n chunks (one per direction, b, h and chunk) and, for the
-// prologue, their tokens' inverse k norms.
+// inverses of n chunks (one per direction, b, h and chunk) and their tokens'
+// gate records.
 bool chunk_mfma_supported(int C, int dk, int dv, int io);
 size_t chunk_mfma_tm_bytes(long long chunks);
 hipError_t launch_chunk_mfma(const PassArgs &a, int C, hipStream_t stream);

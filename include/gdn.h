@@ -38,9 +38,10 @@
  * the handle and its device scratch, allocated once in gdn_create and freed in
  * gdn_free: the two fp32 partials of gdn_forward_bidi (GDN_FLAG_BIDI), and, on
  * handles the bf16 MFMA chunked kernel can serve (bf16 or FP8 inputs, d_k and
- * d_v >= 32), the per-chunk triangular inverses of that kernel and, for the
- * packed entry points, each token's inverse k norm (6.25 KiB per direction, b,
- * h and 64-token chunk up to max_T).  The forward calls allocate nothing, never
+ * d_v >= 32), the per-chunk triangular inverses of that kernel and each
+ * token's gate record (b, log2 a and, for the packed entry points, the inverse
+ * k norm): 7 KiB per direction, b, h and 64-token chunk up to max_T.  The
+ * forward calls allocate nothing, never
  * synchronise and never copy between host and device: they validate, enqueue
  * kernels on the given stream and return.  Device faults surface at the
  * caller's next synchronisation, as with any HIP launch.  A handle must be
