@@ -660,6 +660,11 @@ struct __align__(16) Smem {
     float gam[3][C];
     float bg[3][C];
     float glast[3][C];
+    // Output staging, one 16-query tile per output wave and query block.  The
+    // pitch of 36 floats keeps both the writes (16-byte columns of 16 rows) and the
+    // row-major reads free of bank conflicts.
+    static constexpr int LOT = DVT + 4;
+    float Ot[4][16][LOT];
 };
 
 // Column d of bVt holds token t at position t + 16 (d / 8), mod 64: the four
@@ -905,25 +910,50 @@ __device__ __forceinline__ void out_pn(const Smem<DK> &sm, int slot, int q, int 
     }
 }
 
-template <int DK, bool BF16, bool PRO>
-__device__ __forceinline__ void out_store(const Ctx &x, const ChunkParams &p, int c, int q, int lane,
-                                          const f32x4_t (&o)[2], float rq, void *out_b, float *part_b) {
-    const int g4 = lane >> 4, qi = 16 * q + (lane & 15);
-    if (qi >= x.ntok(c)) return;
-    const size_t e0 = (size_t)x.tok(c, qi) * x.rso + 4 * g4;
+// Stores of a 16-query block.  In the accumulators lane (g, r) holds query r,
+// columns 4g .. 4g + 3 and 16 + 4g .. + 3, so 16 consecutive lanes address 16
+// different output rows and every lane of a store instruction touches its own
+// 64-byte segment.  The block goes through a wave-private LDS tile instead and is
+// read back row-major, so that the lanes of one store instruction write whole
+// 64-byte row segments (4 lanes per row for bf16 out, 8 per row for the fp32
+// partials): a quarter of the address work of the per-lane stores.
+__device__ __forceinline__ void wave_lds_sync() {
+    // ds instructions of one wave execute in order; this only keeps the compiler
+    // from moving the reads above the writes of other lanes.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int DK, bool PRO>
+__device__ __forceinline__ void out_store(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int c, int q,
+                                          int slot, int lane, const f32x4_t (&o)[2], float rq, void *out_b,
+                                          float *part_b) {
+    const int g4 = lane >> 4, r16 = lane & 15;
     const float sc = PRO ? p.scale * rq : p.scale;
+    float(*tile)[Smem<DK>::LOT] = sm.Ot[slot];
 #pragma unroll
-    for (int dvb = 0; dvb < 2; ++dvb) {
-        const size_t e = e0 + 16 * dvb;
-        const float o0 = o[dvb][0] * sc, o1 = o[dvb][1] * sc;
-        const float o2 = o[dvb][2] * sc, o3 = o[dvb][3] * sc;
-        if (p.out_mode == OUT_PARTIAL) {
-            *reinterpret_cast<float4 *>(part_b + e) = make_float4(o0, o1, o2, o3);
-        } else {
-            if constexpr (BF16)
-                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out_b) + e) = pack4(o0, o1, o2, o3);
-            else
-                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out_b) + e) = make_float4(o0, o1, o2, o3);
+    for (int dvb = 0; dvb < 2; ++dvb)
+        *reinterpret_cast<float4 *>(&tile[r16][16 * dvb + 4 * g4]) =
+            make_float4(o[dvb][0] * sc, o[dvb][1] * sc, o[dvb][2] * sc, o[dvb][3] * sc);
+    wave_lds_sync();
+    const int n = x.ntok(c);
+    if (p.out_mode == OUT_PARTIAL) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row = (lane >> 3) + 8 * i, col = 4 * (lane & 7);
+            const float4 v = *reinterpret_cast<const float4 *>(&tile[row][col]);
+            if (16 * q + row < n)
+                *reinterpret_cast<float4 *>(part_b + (size_t)x.tok(c, 16 * q + row) * x.rso + col) = v;
+        }
+    } else {
+        const int row = lane >> 2, col = 8 * (lane & 3);
+        const float4 a = *reinterpret_cast<const float4 *>(&tile[row][col]);
+        const float4 b = *reinterpret_cast<const float4 *>(&tile[row][col + 4]);
+        if (16 * q + row < n) {
+            const uint2 lo = pack4(a.x, a.y, a.z, a.w), hi = pack4(b.x, b.y, b.z, b.w);
+            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out_b) + (size_t)x.tok(c, 16 * q + row) * x.rso +
+                                       col) = make_uint4(lo.x, lo.y, hi.x, hi.y);
         }
     }
 }
@@ -953,28 +983,28 @@ __device__ __forceinline__ void out_products_step(Smem<DK> &sm, int c, int lane,
     out_products<DK, PRO>(sm, s2, s3, QB, lane, sa, r.ob, r.pb, r.rb);
 }
 
-template <int DK, bool BF16, int W, bool PRO>
-__device__ __forceinline__ void out_finish_step(const Ctx &x, const Smem<DK> &sm, const ChunkParams &p, int c,
+template <int DK, int W, bool PRO>
+__device__ __forceinline__ void out_finish_step(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int c,
                                                 int lane, OutRegs &r, void *out_b, float *part_b) {
     constexpr int QA = W ? 1 : 0, QB = W ? 2 : 3;
     out_pn(sm, c & 1, QA, lane, r.oa, r.pa);
     out_pn(sm, c & 1, QB, lane, r.ob, r.pb);
-    out_store<DK, BF16, PRO>(x, p, c, QA, lane, r.oa, r.ra, out_b, part_b);
-    out_store<DK, BF16, PRO>(x, p, c, QB, lane, r.ob, r.rb, out_b, part_b);
+    out_store<DK, PRO>(x, sm, p, c, QA, 2 * W, lane, r.oa, r.ra, out_b, part_b);
+    out_store<DK, PRO>(x, sm, p, c, QB, 2 * W + 1, lane, r.ob, r.rb, out_b, part_b);
 }
 
 // Period c of an output wave: finish chunk c - 1, then the products of chunk c.
-template <int DK, bool BF16, int W, bool PRO>
+template <int DK, int W, bool PRO>
 __device__ __forceinline__ void output_period(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int c, int lane,
                                               OutRegs &r, void *out_b, float *part_b) {
     const bool fin = x.has(c - 1), run = x.has(c);
     if (fin && run) {
-        out_finish_step<DK, BF16, W, PRO>(x, sm, p, c - 1, lane, r, out_b, part_b);
+        out_finish_step<DK, W, PRO>(x, sm, p, c - 1, lane, r, out_b, part_b);
         out_products_step<DK, W, PRO>(sm, c, lane, r);
     } else if (run) {
         out_products_step<DK, W, PRO>(sm, c, lane, r);
     } else if (fin) {
-        out_finish_step<DK, BF16, W, PRO>(x, sm, p, c - 1, lane, r, out_b, part_b);
+        out_finish_step<DK, W, PRO>(x, sm, p, c - 1, lane, r, out_b, part_b);
     }
 }
 
@@ -1086,7 +1116,6 @@ __device__ __forceinline__ void store_bv(Smem<DK> &sm, int c, const VRow<IO> &v,
 
 template <int DK, int IO, bool PRO>
 __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
-    constexpr bool BF16 = true;  // out is bf16 for every input type this kernel takes
     constexpr int ES = io_in_bytes(IO);
     static_assert(DK % 32 == 0 && DK <= 128, "d_k must be 32, 64 or 128");
     __shared__ Smem<DK> sm;
@@ -1130,8 +1159,8 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     // Every role walks the same periods it = -2 .. n (the last one finishes the
     // outputs of chunk n-1), two per loop trip so that register sets alternate at
     // compile time, with one barrier each.
-    void *out_b = BF16 ? (void *)(reinterpret_cast<uint16_t *>(p.out) + tok0 * p.dv + dv0)
-                       : (void *)(reinterpret_cast<float *>(p.out) + tok0 * p.dv + dv0);
+    // out is bf16 for every input type this kernel takes
+    void *out_b = reinterpret_cast<uint16_t *>(p.out) + tok0 * p.dv + dv0;
     float *part = dir ? p.partial_rev : p.partial;
     float *part_b = part ? part + tok0 * p.dv + dv0 : nullptr;
     if (wid < 2) {
@@ -1164,18 +1193,18 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         OutRegs r;
         __syncthreads();
         for (int it = -2; it < n + 1; it += 2) {
-            output_period<DK, BF16, 0, PRO>(x, sm, p, it, lane, r, out_b, part_b);
+            output_period<DK, 0, PRO>(x, sm, p, it, lane, r, out_b, part_b);
             __syncthreads();
-            output_period<DK, BF16, 0, PRO>(x, sm, p, it + 1, lane, r, out_b, part_b);
+            output_period<DK, 0, PRO>(x, sm, p, it + 1, lane, r, out_b, part_b);
             __syncthreads();
         }
     } else if (wid == 3) {
         OutRegs r;
         __syncthreads();
         for (int it = -2; it < n + 1; it += 2) {
-            output_period<DK, BF16, 1, PRO>(x, sm, p, it, lane, r, out_b, part_b);
+            output_period<DK, 1, PRO>(x, sm, p, it, lane, r, out_b, part_b);
             __syncthreads();
-            output_period<DK, BF16, 1, PRO>(x, sm, p, it + 1, lane, r, out_b, part_b);
+            output_period<DK, 1, PRO>(x, sm, p, it + 1, lane, r, out_b, part_b);
             __syncthreads();
         }
     } else if (wid < 6) {
