@@ -19,7 +19,6 @@ the same inputs, and secondary measurements of the other forms (sequential scan,
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -54,21 +53,16 @@ def scan_flops(B, T, H, dk, dv):
     return B * T * H * 6 * dk * dv
 
 
-def src_hash(name):
-    p = os.path.join(ROOT, "gated_deltanet_recurrence_gdn_amd", "csrc", name)
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
 def load_traffic(workload):
     """HBM bytes per launch of the chunked kernel from the committed rocprofv3 --pmc
-    summary, if it was taken on the current kernel source; else None."""
+    summary, if it was taken on the current kernel code (comments aside); else None."""
     p = os.path.join(PROFILES, f"chunk_kernel_{workload}_traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("kernel_src_sha256_16") != src_hash("gdn_chunk.hip"):
+    from gated_deltanet_recurrence_gdn_amd.srchash import code_hash
+    if t.get("kernel_code_sha256_16") != code_hash("gdn_chunk.hip"):
         return None
     return t
 

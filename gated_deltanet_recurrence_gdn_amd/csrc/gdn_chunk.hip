@@ -58,11 +58,12 @@
 //
 // Fused input prologue (template flag PRO): q, k, v are read in place from a
 // packed token-major projection (token and batch strides), the gate inputs are
-// logits (b = sigmoid(x_b), log2 a = -softplus(x_a) / ln 2, in the gate
-// function), and q, k are L2-normalised without touching the bf16 operands:
-// tm_kernel forms each token's 1 / ||k|| from the K rows it loads and folds it
-// into A's row and column factors (and writes it for chunk_kernel, which folds
-// it into the per-token factors of R, the state update and P); the output waves
+// logits (b = sigmoid(x_b), log2 a = -softplus(x_a) / ln 2, applied by tm_kernel
+// as it reads them), and q, k are L2-normalised without touching the bf16
+// operands: tm_kernel forms each token's 1 / ||k|| from the K rows it loads and
+// folds it into A's row and column factors (and puts it in the gate record, from
+// which chunk_kernel folds it into the per-token factors of R, the state update
+// and P); the output waves
 // form 1 / ||q|| from diag(Q Q^T) on MFMA and apply it with the 1/sqrt(d_k)
 // scale.  Only per-token factors change, so without the prologue every factor is
 // bit for bit the plain one.

@@ -31,13 +31,16 @@ from __future__ import annotations
 import argparse
 import csv
 import glob
-import hashlib
 import json
 import os
 import statistics
+import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+from gated_deltanet_recurrence_gdn_amd.srchash import code_hash  # noqa: E402
 PROFILES = os.path.join(ROOT, "profiles")
 CHUNK = "chunk_kernel"
 TM = "tm_kernel"
@@ -61,8 +64,7 @@ def _csv(path_glob):
 
 
 def src_hash():
-    with open(os.path.join(PKG, "csrc", "gdn_chunk.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    return code_hash("gdn_chunk.hip")
 
 
 def kernel_stats(d):
@@ -110,7 +112,7 @@ def forms_summary(d):
     lines = ["rocprofv3 kernel trace: bench.py with its secondary forms (scan, 5-call streaming warm and",
              "cold, 3-frame d=64 warm and cold, bidirectional, fused prologue from packed qkv, FP8 inputs)",
              "", "command (MI355X, repo root, TMPDIR=/tmp):", "  " + FORMS_CMD.format(d="gpurun_out/prof"),
-             f"kernel source sha256[:16] (gdn_chunk.hip): {src_hash()}", "",
+             f"kernel code sha256[:16] (gdn_chunk.hip, comments and whitespace removed): {src_hash()}", "",
              "template arguments: chunk_kernel<d_k, input type (1 bf16, 2 FP8), prologue>, tm_kernel<same>,",
              "scan_kernel<d_k, state values per lane, input type (0 fp32, 1 bf16, 2 FP8), prologue>", "",
              f"  {'kernel':78s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
@@ -152,7 +154,7 @@ def counters_summary(d):
              "instances, *_avr averaged over them)", "",
              "commands (MI355X, repo root, TMPDIR=/tmp), one counter set per run:"]
     lines += ["  " + CTR_CMD.format(c=c, d="gpurun_out/prof", i=i) for i, c in enumerate(COUNTER_SETS)]
-    lines += [f"kernel source sha256[:16]: {src_hash()}", ""]
+    lines += [f"kernel code sha256[:16] (comments and whitespace removed): {src_hash()}", ""]
     for kn in KERNELS:
         lines.append(f"{kn}:")
         for cn in sorted(vals[kn]):
@@ -184,8 +186,6 @@ def main():
             f.write("\n".join(lines) + "\n")
         print("\n".join(lines))
         return
-    import sys
-    sys.path.insert(0, ROOT)
     import bench
     from gated_deltanet_recurrence_gdn_amd import inputs
     w = inputs.WORKLOADS[a.workload]
@@ -195,7 +195,7 @@ def main():
     lines = [f"rocprofv3 kernel trace: chunked GDN forward (tm_kernel + chunk_kernel), workload {w.name}",
              f"(B={w.B}, H={w.H}, T={w.T}, d_k={w.dk}, d_v={w.dv}, bf16 I/O, chunk_len=64, fp32 state in/out)",
              "", "command (MI355X, repo root, TMPDIR=/tmp):", "  " + KT_CMD.format(d="gpurun_out/prof"),
-             f"kernel source sha256[:16]: {src_hash()}", "",
+             f"kernel code sha256[:16] (comments and whitespace removed): {src_hash()}", "",
              "kernel stats (durations in ns):",
              f"  {'name':60s} {'calls':>6s} {'total_ns':>14s} {'avg_ns':>12s} {'pct':>7s}"]
     for n, c, t, av, pc in stats:
@@ -221,7 +221,7 @@ def main():
     w_scale = COPY_BYTES / (write_c * 1024.0)
     fetch_b = sum(fetch[kn][0] for kn in KERNELS) * 1024.0 * f_scale
     write_b = sum(write[kn][0] for kn in KERNELS) * 1024.0 * w_scale
-    rec = {"workload": w.name, "kernel_src_sha256_16": src_hash(),
+    rec = {"workload": w.name, "kernel_code_sha256_16": src_hash(),
            "bytes_per_launch": fetch_b + write_b, "fetch_bytes": fetch_b, "write_bytes": write_b,
            "per_kernel_kib_raw": {kn: {"fetch": fetch[kn][0], "write": write[kn][0]} for kn in KERNELS},
            "copy_fetch_kib": fetch_c, "copy_write_kib": write_c,
@@ -234,7 +234,7 @@ def main():
           "commands (MI355X, repo root, TMPDIR=/tmp), one counter per run:",
           "  " + PMC_CMD.format(c="FETCH_SIZE", d="gpurun_out/prof", n="fetch"),
           "  " + PMC_CMD.format(c="WRITE_SIZE", d="gpurun_out/prof", n="write"),
-          f"kernel source sha256[:16]: {src_hash()}", "",
+          f"kernel code sha256[:16] (comments and whitespace removed): {src_hash()}", "",
           "scale: the run's plain 512 MiB device copy (--calib-copy) reads and writes 512 MiB;",
           f"  FETCH_SIZE reads {fetch_c:.0f} KiB for it -> scale {f_scale:.3f}",
           f"  WRITE_SIZE reads {write_c:.0f} KiB for it -> scale {w_scale:.3f}", ""]
