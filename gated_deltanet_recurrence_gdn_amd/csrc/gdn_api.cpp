@@ -422,8 +422,12 @@ int run_forward(gdn_ctx *h, const Inputs &in, const float *state_in, float *stat
     a.state_in = state_in; a.state_out = state_out; a.out = out; a.partial = nullptr;
     a.reverse = 0; a.out_mode = gdn::OUT_STORE;
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-    hipError_t e = (C == 1) ? gdn::launch_scan(a, s) : gdn::launch_chunk(a, C, s);
-    return launch_status(h, e, C == 1 ? "scan" : "chunked");
+    // With no tokens only the state is written (state_in copied, or zeros).  The
+    // scan kernel does exactly that for every shape and input type without reading
+    // q, k, v or the gates; the chunked kernels need at least one token.
+    const bool scan = C == 1 || !tok;
+    hipError_t e = scan ? gdn::launch_scan(a, s) : gdn::launch_chunk(a, C, s);
+    return launch_status(h, e, scan ? "scan" : "chunked");
 }
 
 int run_bidi(gdn_ctx *h, const Inputs &in, void *out, size_t out_bytes, long long T, int chunk_len,

@@ -90,6 +90,7 @@ inline bool chunk_supported(int C, int dk, int dv, int io) {
     return chunk_mfma_supported(C, dk, dv, io) || chunk_general_supported(C, dk, dv);
 }
 inline hipError_t launch_chunk(const PassArgs &a, int C, hipStream_t stream) {
+    if (a.T <= 0) return hipErrorInvalidValue;  // the chunked kernels read at least one token
     if (chunk_mfma_supported(C, a.dk, a.dv, a.io)) return launch_chunk_mfma(a, C, stream);
     return launch_chunk_general(a, C, stream);
 }
