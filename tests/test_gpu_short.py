@@ -1,12 +1,18 @@
-"""A call with T = 0 writes only the state, on every path: state_in is copied to
-state_out exactly (zeros without state_in), out is left untouched, and q, k, v and
-the gates may be NULL.  The chunk length and input type select the bf16 MFMA
-chunked kernel, the fp32 general chunked kernel or the scan for T > 0; with no
-tokens every one of them must behave the same."""
+"""Short sequences on every path (the bf16 MFMA chunked kernel, the fp32 general
+chunked kernel and the scan, selected by chunk length and input type).
+
+* T = 0 writes only the state: state_in is copied to state_out exactly (zeros
+  without state_in), out is left untouched, and q, k, v and the gates may be NULL.
+* The bidirectional form at T = 1, 2, 63, 64, 65 (one partial chunk, one full
+  chunk, a full chunk and one token) equals the float64 oracle's sum of the
+  forward and the reverse recurrence within the bar."""
 import pytest
 import torch
 
+import oracle
+from gated_deltanet_recurrence_gdn_amd import inputs
 from gated_deltanet_recurrence_gdn_amd import binding as gb
+from gpu_util import TOL, dev, rel
 
 pytestmark = pytest.mark.gpu
 
@@ -36,3 +42,18 @@ def test_zero_tokens_write_only_the_state(io, chunk, d):
     torch.cuda.synchronize()
     assert torch.equal(st, s0)
     g.close()
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65])
+@pytest.mark.parametrize("io,chunk,d", [("bf16", 64, 64), ("fp8", 64, 32), ("fp32", 32, 32), ("fp32", 1, 32)])
+def test_bidi_short(io, chunk, d, T):
+    B, H = 1, 2
+    x = inputs.make_inputs(B, T, H, d, d, io, seed=100 + T)
+    dx = dev(x)
+    g = gb.GDN(B, H, d, d, io, max_T=T, bidi=True)
+    out = g.forward_bidi(dx["q"], dx["k"], dx["v"], dx["beta"], dx["decay"], chunk_len=chunk)
+    torch.cuda.synchronize()
+    g.close()
+    r = rel(out, oracle.bidi(**x))
+    print(f"bidi {io} C={chunk} d={d} T={T}: rel-L2 {r:.3e}")
+    assert r <= TOL[io]
