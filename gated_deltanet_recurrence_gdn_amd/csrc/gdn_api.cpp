@@ -110,6 +110,7 @@ struct DeviceGuard {
 // Largest token stride (elements) of q, k, v: the kernels address up to 64
 // tokens of a chunk with 32-bit offsets from the chunk's first token.
 constexpr long long MAX_TOKEN_STRIDE = 1LL << 24;
+constexpr int MAX_B = 32767;  // (directions x B) <= 65535
 
 // The token inputs of one call: contiguous [B,T,H,d] tensors, or views into a
 // packed qkv projection with the prologue applied in the kernels.
@@ -281,6 +282,9 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
     if (!cfg || !out_h) return fail_create(GDN_ERR_ARG, "cfg and out_h must be non-NULL");
     const gdn_config c = *cfg;
     if (c.B < 1 || c.H < 1) return fail_create(GDN_ERR_ARG, "B = %d and H = %d must be >= 1", c.B, c.H);
+    // The scan and the general chunked kernel index (direction, b) by the grid's z
+    // dimension, at most 65535: two directions per b on bidirectional handles.
+    if (c.B > MAX_B) return fail_create(GDN_ERR_UNSUPPORTED, "B = %d is too large (at most %d)", c.B, MAX_B);
     if (!valid_dim(c.d_k) || !valid_dim(c.d_v))
         return fail_create(GDN_ERR_UNSUPPORTED, "d_k = %d, d_v = %d: each must be 16, 32, 64 or 128",
                            c.d_k, c.d_v);

@@ -86,7 +86,8 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8 = 2 } gdn_dtype;
 
 typedef struct {
     int device;        /* HIP device ordinal; -1 = dry run (validate only, no GPU) */
-    int B, H;          /* batch and heads, >= 1                                   */
+    int B, H;          /* batch (1 .. 32767) and heads (>= 1, H * max(d_k, d_v)   *
+                        * at most 2^24 / 3)                                     */
     int d_k, d_v;      /* head dims, each in {16, 32, 64, 128}                    */
     int io_dtype;      /* gdn_dtype of q, k, v (out: fp32 or bf16, see gdn_dtype) */
     long long max_T;   /* largest T any call on this handle will pass, >= 0       */

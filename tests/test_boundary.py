@@ -221,6 +221,7 @@ def test_fp8_dry_run_sizes():
 @pytest.mark.parametrize("args,code", [
     ((-1, 0, 1, 16, 16, gb.GDN_F32, 10, 0), gb.GDN_ERR_ARG),
     ((-1, 1, 0, 16, 16, gb.GDN_F32, 10, 0), gb.GDN_ERR_ARG),
+    ((-1, 32768, 1, 16, 16, gb.GDN_F32, 10, 0), gb.GDN_ERR_UNSUPPORTED),
     ((-1, 1, 1, 24, 16, gb.GDN_F32, 10, 0), gb.GDN_ERR_UNSUPPORTED),
     ((-1, 1, 1, 16, 256, gb.GDN_F32, 10, 0), gb.GDN_ERR_UNSUPPORTED),
     ((-1, 1, 1, 16, 16, 7, 10, 0), gb.GDN_ERR_UNSUPPORTED),
