@@ -91,6 +91,8 @@ inline bool chunk_supported(int C, int dk, int dv, int io) {
 }
 inline hipError_t launch_chunk(const PassArgs &a, int C, hipStream_t stream) {
     if (a.T <= 0) return hipErrorInvalidValue;  // the chunked kernels read at least one token
+    // Block counts of the chunked grids (at most two directions x B x H x d_v) are ints.
+    if (2LL * a.B * a.H * a.dv > 0x7fffffffLL) return hipErrorInvalidValue;
     if (chunk_mfma_supported(C, a.dk, a.dv, a.io)) return launch_chunk_mfma(a, C, stream);
     return launch_chunk_general(a, C, stream);
 }
