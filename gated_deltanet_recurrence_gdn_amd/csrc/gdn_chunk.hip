@@ -42,11 +42,13 @@
 //               operand if the k index is permuted (slots 0-3 = rows 4g .. 4g+3 of
 //               the first block, slots 4-7 = the same rows of the second); the A
 //               operand is read from LDS (or Tm from HBM) under the same
-//               permutation.  Each publishes its columns of N (behind an LDS
-//               counter) and a bf16 copy of its S columns for the outputs.
-//   waves 2, 3  outputs of chunk c, one 32-token half each: P of the half's query
-//               rows in registers (formed while the chain works on N), then
-//               O^T = gam .* (S Q^T) + N^T P^T, written as 8-byte row segments.
+//               permutation.  Each publishes its columns of N and a bf16 copy
+//               of its S columns for the outputs in double-buffered LDS slots
+//               (read after the period's barrier).
+//   waves 2, 3  outputs, query blocks {0, 3} and {1, 2} (16 queries each, the
+//               same work): in period c, gam .* (S Q^T) and P of chunk c in
+//               registers; in period c+1, + N^T P^T, staged through a
+//               wave-private LDS tile and stored as whole 64-byte row segments.
 //   waves 4, 5  K and Q of chunk c+1 (HBM -> registers -> LDS), loaded in
 //               period c-2 (two register sets alternate).
 //   wave 6      gate vectors of chunk c+2 from the chunk's gate records (b,
