@@ -305,8 +305,8 @@ def measure_forms(torch, gb, inputs, d, g, x):
     forms["packed_prologue_batched_bf16_d128"] = {
         "ms": ms, "token_heads_per_s": B * H * T / (ms / 1e3),
         "design": "strided reads of the packed rows; inverse k norms formed in the inverse pass and folded "
-                  "into the per-token decay factors, inverse q norms from diag(Q Q^T) on MFMA in the output "
-                  "waves; sigmoid / exp(-softplus) of the logits in the gate wave"}
+                  "into the per-token decay factors, inverse q norms in the output waves from the Q operands they "
+                  "hold (v_dot2, two lane swaps, v_rsq); sigmoid / exp(-softplus) of the logits in the inverse pass"}
     gp.close()
     del qkv, bl, dl
 

@@ -66,7 +66,8 @@
 // folds it into A's row and column factors (and puts it in the gate record, from
 // which chunk_kernel folds it into the per-token factors of R, the state update
 // and P); the output waves
-// form 1 / ||q|| from diag(Q Q^T) on MFMA and apply it with the 1/sqrt(d_k)
+// form 1 / ||q|| from the Q operands they hold (v_dot2 and two lane swaps) and
+// apply it with the 1/sqrt(d_k)
 // scale.  Only per-token factors change, so without the prologue every factor is
 // bit for bit the plain one.
 //
@@ -90,6 +91,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int C = 64;     // chunk length
 constexpr int NT = 512;   // threads per block of the chunk kernel: 8 waves
@@ -251,8 +253,8 @@ __device__ __forceinline__ double prefix_sum64(int lane, double x) {
 //   S    = gam_{C-1} S0 + N^T diag(2^{g_{C-1} - gk}) K,
 //   O_i  = rq_i (gam_i (Q S0^T)_i + sum_j 2^{g_i - gk_j} (q_i . k_j) N_j)  (times 1/sqrt(d_k)),
 // and the bf16 operands stay the inputs as given.  rk comes from the inverse
-// pass (which reads K anyway); rq is formed by the output waves (diag(Q Q^T) of
-// the Q operands they hold).  Without the prologue rk = 1 and gk = g.
+// pass (which reads K anyway); rq is formed by the output waves from the Q
+// operands they hold.  Without the prologue rk = 1 and gk = g.
 struct GateVals {
     float g;      // cumulative log2 decay g_i (summed in float64)
     float gk;     // g_j - log2 rk_j: key-side exponent of A and P
@@ -839,10 +841,14 @@ __device__ __forceinline__ TmOps load_tm(const uint16_t *tm_head, int c, int n, 
 // its B operand (the permuted k order of the chain) and N^T, whose keys the
 // chain stores in the matching order, as its A operand.  Query blocks {0, 3} and
 // {1, 2} need five key blocks each, so the two waves do the same work.
-// With the prologue, rq is set to this lane's query's inverse L2 norm: diag(Q Q^T)
-// of the block on MFMA from the Q operands already held (bf16 products are exact in
-// fp32), the diagonal entry of query r taken from the lane that holds it (lane
-// 16 (r / 4) + r, slot r % 4).
+// With the prologue, rq is set to this lane's query's inverse L2 norm.  The lane
+// holds d_k / 4 values of its query r in the Q operands (the other lanes of the
+// query are r + 16, r + 32, r + 48): it sums their squares with v_dot2_f32_bf16
+// (bf16 products are exact in fp32), adds the partner lanes' sums with
+// v_permlane16_swap and v_permlane32_swap, and takes v_rsq_f32 of max(sum,
+// 1e-24), which is 1 / max(||q||, 1e-12) to within an ulp.  These are short VALU
+// chains: the first version formed diag(Q Q^T) with four chained MFMAs and read
+// it back through ds_bpermute, which cost 8% of the call.
 template <int DK, bool PRO>
 __device__ __forceinline__ void out_products(const Smem<DK> &sm, int s2, int s3, int q, int lane,
                                              const bf16x8_t (&sa)[2][DK / 32], f32x4_t (&o)[2], f32x4_t (&pk)[4],
@@ -853,13 +859,26 @@ __device__ __forceinline__ void out_products(const Smem<DK> &sm, int s2, int s3,
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qo[ks] = lds16(&sm.Qs[s2][16 * q + r16][32 * ks + 8 * g4]);
     if constexpr (PRO) {
-        f32x4_t nn = zero4();
+        float d0 = 0.f, d1 = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) nn = mfma16k32(qo[ks], qo[ks], nn);
-        const int m = r16 - 4 * g4;  // nn[m] = (Q Q^T)[4 g4 + m][r16]
-        const float d = m == 0 ? nn[0] : m == 1 ? nn[1] : m == 2 ? nn[2] : m == 3 ? nn[3] : 0.f;
-        const int src = 16 * (r16 >> 2) + r16;
-        rq = inv_norm(__int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(d))));
+        for (int ks = 0; ks < NKS; ++ks) {
+            u32x4_t w;
+            __builtin_memcpy(&w, &qo[ks], 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t we = w[e];
+                bf16x2_t x;
+                __builtin_memcpy(&x, &we, 4);
+                if (e & 1) d1 = __builtin_amdgcn_fdot2_f32_bf16(x, x, d1, false);
+                else d0 = __builtin_amdgcn_fdot2_f32_bf16(x, x, d0, false);
+            }
+        }
+        float d = d0 + d1;
+        const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(d), __float_as_uint(d), false, false);
+        d = __uint_as_float(x16[0]) + __uint_as_float(x16[1]);  // lanes l and l ^ 16
+        const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(d), __float_as_uint(d), false, false);
+        d = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);  // and l ^ 32: all four lanes of query r16
+        rq = __builtin_amdgcn_rsqf(fmaxf(d, 1e-24f));
     }
     o[0] = zero4();
     o[1] = zero4();
