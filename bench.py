@@ -83,7 +83,7 @@ def main():
                          "reference dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported "
               "(the per-head recurrence shards over (b, h) with no exchange, but no "
               "multi-GPU path is built)", file=sys.stderr)
         sys.exit(2)

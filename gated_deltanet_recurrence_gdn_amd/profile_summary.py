@@ -106,12 +106,19 @@ FORMS_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d {d}/forms 
              "python bench.py --no-cpu --steps 5 --warmup 5")
 
 
+def rel_dir(d):
+    """The output directory the profiled commands were given, relative to the repo root
+    when it lies inside it (the commands run from there)."""
+    a = os.path.abspath(d)
+    return os.path.relpath(a, ROOT) if a.startswith(ROOT + os.sep) else a
+
+
 def forms_summary(d):
     """Per-kernel-instantiation stats of a bench run with its secondary forms."""
     rows = _csv(os.path.join(d, "forms", "**", "*kernel_stats.csv"))
     lines = ["rocprofv3 kernel trace: bench.py with its secondary forms (scan, 5-call streaming warm and",
              "cold, 3-frame d=64 warm and cold, bidirectional, fused prologue from packed qkv, FP8 inputs)",
-             "", "command (MI355X, repo root, TMPDIR=/tmp):", "  " + FORMS_CMD.format(d="gpurun_out/prof"),
+             "", "command (MI355X, repo root, TMPDIR=/tmp):", "  " + FORMS_CMD.format(d=rel_dir(d)),
              f"kernel code sha256[:16] (gdn_chunk.hip, comments and whitespace removed): {src_hash()}", "",
              "template arguments: chunk_kernel<d_k, input type (1 bf16, 2 FP8), prologue>, tm_kernel<same>,",
              "scan_kernel<d_k, state values per lane, input type (0 fp32, 1 bf16, 2 FP8), prologue>", "",
@@ -153,7 +160,7 @@ def counters_summary(d):
              "batched_bf16_d128", "(mean per dispatch; *_sum counters are summed over the 256 CUs' "
              "instances, *_avr averaged over them)", "",
              "commands (MI355X, repo root, TMPDIR=/tmp), one counter set per run:"]
-    lines += ["  " + CTR_CMD.format(c=c, d="gpurun_out/prof", i=i) for i, c in enumerate(COUNTER_SETS)]
+    lines += ["  " + CTR_CMD.format(c=c, d=rel_dir(d), i=i) for i, c in enumerate(COUNTER_SETS)]
     lines += [f"kernel code sha256[:16] (comments and whitespace removed): {src_hash()}", ""]
     for kn in KERNELS:
         lines.append(f"{kn}:")
@@ -194,7 +201,7 @@ def main():
     stats = kernel_stats(a.dir)
     lines = [f"rocprofv3 kernel trace: chunked GDN forward (tm_kernel + chunk_kernel), workload {w.name}",
              f"(B={w.B}, H={w.H}, T={w.T}, d_k={w.dk}, d_v={w.dv}, bf16 I/O, chunk_len=64, fp32 state in/out)",
-             "", "command (MI355X, repo root, TMPDIR=/tmp):", "  " + KT_CMD.format(d="gpurun_out/prof"),
+             "", "command (MI355X, repo root, TMPDIR=/tmp):", "  " + KT_CMD.format(d=rel_dir(a.dir)),
              f"kernel code sha256[:16] (comments and whitespace removed): {src_hash()}", "",
              "kernel stats (durations in ns):",
              f"  {'name':60s} {'calls':>6s} {'total_ns':>14s} {'avg_ns':>12s} {'pct':>7s}"]
@@ -232,8 +239,8 @@ def main():
         json.dump(rec, f, indent=1)
     tl = [f"rocprofv3 HBM traffic counters: chunked GDN forward (tm_kernel + chunk_kernel), workload {w.name}", "",
           "commands (MI355X, repo root, TMPDIR=/tmp), one counter per run:",
-          "  " + PMC_CMD.format(c="FETCH_SIZE", d="gpurun_out/prof", n="fetch"),
-          "  " + PMC_CMD.format(c="WRITE_SIZE", d="gpurun_out/prof", n="write"),
+          "  " + PMC_CMD.format(c="FETCH_SIZE", d=rel_dir(a.dir), n="fetch"),
+          "  " + PMC_CMD.format(c="WRITE_SIZE", d=rel_dir(a.dir), n="write"),
           f"kernel code sha256[:16] (comments and whitespace removed): {src_hash()}", "",
           "scale: the run's plain 512 MiB device copy (--calib-copy) reads and writes 512 MiB;",
           f"  FETCH_SIZE reads {fetch_c:.0f} KiB for it -> scale {f_scale:.3f}",
