@@ -181,12 +181,23 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def timed(torch, fn, reps, warm=10):
-    """Average ms of `reps` back-to-back calls after `warm` untimed ones (the clock
-    ramps back up after the host-side input generation between forms)."""
-    for _ in range(warm):
+def warm_up(torch, fn, calls, min_ms=100.0):
+    """Untimed calls: at least `calls` of them and at least `min_ms` of wall time.  The
+    GPU clock drops while the host generates a form's inputs and needs tens of
+    milliseconds of load to come back, which a fixed count of short calls may not give."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < calls or (time.perf_counter() - t0) * 1e3 < min_ms:
         fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+
+
+def timed(torch, fn, reps, warm=10):
+    """Average ms of `reps` back-to-back calls after the warm-up."""
+    warm_up(torch, fn, warm)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -199,9 +210,7 @@ def timed(torch, fn, reps, warm=10):
 def per_call(torch, fn, reps, warm=10, flush=None):
     """Median and min ms of single calls, each bracketed by its own HIP events on the
     current stream; `flush` (if given) runs before each call, outside the events."""
-    for _ in range(warm):
-        fn()
-    torch.cuda.synchronize()
+    warm_up(torch, fn, warm)
     ts = []
     for _ in range(reps):
         if flush is not None:
