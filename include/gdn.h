@@ -161,7 +161,9 @@ int gdn_forward_bidi(gdn_handle h, const void *q, const void *k, const void *v,
  *     q <- q / max(||q||_2, 1e-12),  k <- k / max(||k||_2, 1e-12),
  *     b_t = sigmoid(x_b) = 1 / (1 + e^{-x_b}),
  *     a_t = exp(-softplus(x_a)) = 1 / (1 + e^{x_a}),
- * computed in fp32 from the inputs as given (the sglang SANA-WM record widens
+ * computed in fp32 from the inputs as given (the chunked bf16 / FP8 kernel takes
+ * 1 / max(||q||, 1e-12) with the hardware reciprocal square root, to within an
+ * ulp; the sglang SANA-WM record widens
  * q, k, v with .float().contiguous() in a separate pass before its scan; here
  * nothing is materialised).  out (contiguous [B, T, H, d_v]) and state_out
  * must not overlap the byte range qkv spans.  Errors as for gdn_forward, plus
