@@ -423,17 +423,26 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     return launch_dk_e<DK, 8>(a, p, stream);
 }
 
-// out = round(partial + partial_rev), 4 elements per thread.
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
+
+// out = round(partial + partial_rev), 4 elements per thread.  Every byte is read
+// or written once, so the loads and stores are non-temporal (no cache
+// allocation for data that is not used again): 3% of the bidirectional call.
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(void *out, const float4 *pa, const float4 *pb, long long n4) {
     const long long stride = (long long)gridDim.x * blockDim.x;
+    const f32x4v_t *va = reinterpret_cast<const f32x4v_t *>(pa);
+    const f32x4v_t *vb = reinterpret_cast<const f32x4v_t *>(pb);
     for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-        const float4 x = pa[i], y = pb[i];
-        const float o0 = x.x + y.x, o1 = x.y + y.y, o2 = x.z + y.z, o3 = x.w + y.w;
-        if constexpr (BF16)
-            reinterpret_cast<uint2 *>(out)[i] = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
-        else
-            reinterpret_cast<float4 *>(out)[i] = make_float4(o0, o1, o2, o3);
+        const f32x4v_t x = __builtin_nontemporal_load(va + i), y = __builtin_nontemporal_load(vb + i);
+        const f32x4v_t o = x + y;
+        if constexpr (BF16) {
+            const u32x2v_t w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x2v_t *>(out) + i);
+        } else {
+            __builtin_nontemporal_store(o, reinterpret_cast<f32x4v_t *>(out) + i);
+        }
     }
 }
 
