@@ -965,8 +965,12 @@ __device__ __forceinline__ void out_store(const Ctx &x, Smem<DK> &sm, const Chun
         for (int i = 0; i < 2; ++i) {
             const int row = (lane >> 3) + 8 * i, col = 4 * (lane & 7);
             const float4 v = *reinterpret_cast<const float4 *>(&tile[row][col]);
+            // non-temporal: the combine reads each partial once, much later
             if (16 * q + row < n)
-                *reinterpret_cast<float4 *>(part_b + (size_t)x.tok(c, 16 * q + row) * x.rso + col) = v;
+                __builtin_nontemporal_store(u32x4_t{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                                                    __float_as_uint(v.w)},
+                                            reinterpret_cast<u32x4_t *>(part_b + (size_t)x.tok(c, 16 * q + row) * x.rso +
+                                                                        col));
         }
     } else {
         const int row = lane >> 2, col = 8 * (lane & 3);
