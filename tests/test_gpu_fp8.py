@@ -114,12 +114,12 @@ def test_streaming_split_bit_identical(chunk):
     assert torch.equal(torch.cat(outs, dim=1), o1) and torch.equal(state, st1)
 
 
-@pytest.mark.parametrize("chunk", [64, 1])
-def test_packed_prologue(chunk):
+@pytest.mark.parametrize("chunk,d", [(64, 128), (64, 64), (64, 32), (1, 128)])
+def test_packed_prologue(chunk, d):
     """FP8 packed projection with the fused prologue (normalisation of the FP8 q, k
     in the kernels), padded token stride and a gap between batch elements."""
-    B, T, H, d = 2, 170, 3, 128
-    x = inputs.make_packed_inputs(B, T, H, d, d, "fp8", seed=12, pad=32, gap=3)
+    B, T, H = 2, 170, 3
+    x = inputs.make_packed_inputs(B, T, H, d, d, "fp8", seed=12 + d, pad=32, gap=3)
     g0 = torch.Generator().manual_seed(77)
     s0 = 0.3 * torch.randn((B, H, d, d), generator=g0, dtype=torch.float32)
     buf = x["qkv_buf"].cuda()
@@ -131,7 +131,7 @@ def test_packed_prologue(chunk):
     g.close()
     o64, s64 = oracle.forward_packed(x["qkv"], x["beta_logit"], x["decay_logit"], H, d, d, state_in=s0)
     r1, r2 = oracle.rel_l2(host(out), o64), oracle.rel_l2(host(st), s64)
-    print(f"packed fp8 C={chunk}: rel-L2 out {r1:.3e} state {r2:.3e}")
+    print(f"packed fp8 C={chunk} d={d}: rel-L2 out {r1:.3e} state {r2:.3e}")
     assert r1 <= TOL["fp8"] and r2 <= TOL["fp8"]
 
 
