@@ -181,3 +181,26 @@ def test_full_size_sampled_heads():
         r2 = oracle.rel_l2(host(st[b:b + 1, hs]), s64)
         print(f"packed full size b={b} heads={hs}: rel-L2 out {r1:.3e} state {r2:.3e}")
         assert r1 <= TOL["bf16"] and r2 <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("io,chunk", [("bf16", 64), ("bf16", 1), ("fp32", 32)])
+def test_normalisation_makes_scale_irrelevant(io, chunk):
+    """q and k are L2-normalised inside the kernels, so scaling every q row by 2^-9 and
+    every k row by 2^7 (exact in bf16 and fp32) leaves out and the state unchanged up to
+    rounding: the norms, and the exponents of the decay factors that carry 1/||k||, can
+    round differently, which may move a few bf16 outputs by one unit (a missing
+    normalisation would show as a factor of 2^9)."""
+    B, T, H, d = 1, 200, 2, 128 if io == "bf16" else 64
+    x, s0 = make(B, T, H, d, d, io, seed=31, pad=8, state=True)
+    out, st = run(x, s0, B, H, d, d, io, chunk)
+    y = dict(x)
+    buf = x["qkv_buf"].clone()
+    buf[:, :, :H * d] *= 2.0 ** -9
+    buf[:, :, H * d:2 * H * d] *= 2.0 ** 7
+    y["qkv_buf"] = buf
+    out2, st2 = run(y, s0, B, H, d, d, io, chunk)
+    r1 = oracle.rel_l2(host(out2), host(out))
+    r2 = oracle.rel_l2(host(st2), host(st))
+    print(f"{io} C={chunk}: rel-L2 scaled vs unscaled out {r1:.3e} state {r2:.3e}")
+    tol = 1e-3 if io == "bf16" else 1e-6
+    assert r1 <= tol and r2 <= tol
