@@ -1,7 +1,8 @@
 """Full-size parity on the d=128 workloads, in the launch configuration bench.py
 times.  The oracle recomputes sampled (b, h) pairs over the whole sequence (pairs
 are independent, so slicing the head axis is exact); properties that hold at any
-size (reversal symmetry) are checked on every output."""
+size (reversal symmetry, closed forms of two gate settings) are checked on every
+output."""
 import numpy as np
 import pytest
 import torch
@@ -59,3 +60,46 @@ def test_bidi_full_size():
     rr = oracle.rel_l2(host(out[:, :, hs]), ob)
     print(f"bidi heads {hs}: rel-L2 {rr:.3e}")
     assert rr <= TOL["bf16"]
+
+
+def _rel(a, b):
+    a, b = a.double(), b.double()
+    return float(torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b))
+
+
+@pytest.mark.parametrize("chunk", [64, 1])
+def test_full_size_closed_forms(batched, chunk):
+    """Two gate settings with closed forms over every output at the full bench size
+    (the reference is computed on the GPU in float32 from the same inputs):
+    * b = 0, a = 1 from a random state: nothing is written or decayed, so state_out
+      equals state_in bit for bit and o_t = S_0 q_t / sqrt(d_k);
+    * a = 0 at every token: each token starts from S = 0, so
+      o_t = b_t (k_t . q_t) v_t / sqrt(d_k) and the final state is b_T v_T k_T^T."""
+    w, _, d = batched
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    g = gb.GDN(B, H, dk, dv, "bf16", max_T=T)
+    s0 = 0.3 * torch.randn((B, H, dv, dk), device="cuda", generator=torch.Generator("cuda").manual_seed(5))
+    q, k, v = d["q"].float(), d["k"].float(), d["v"].float()
+
+    out, st = g.forward(d["q"], d["k"], d["v"], torch.zeros_like(d["beta"]), torch.ones_like(d["decay"]),
+                        state_in=s0, chunk_len=chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(st, s0)
+    # o[b, t, h, :] = S0[b, h] q[b, t, h, :] / sqrt(dk), per (b, h) as one matmul
+    ref = torch.matmul(q.permute(0, 2, 1, 3).contiguous(), s0.transpose(2, 3).contiguous()).permute(0, 2, 1, 3)
+    r1 = _rel(out.float(), ref / dk ** 0.5)
+    print(f"chunk={chunk} b=0, a=1: rel-L2 out {r1:.3e}")
+    assert r1 <= TOL["bf16"]
+    del ref
+
+    out, st = g.forward(d["q"], d["k"], d["v"], d["beta"], torch.zeros_like(d["decay"]), state_in=s0,
+                        chunk_len=chunk)
+    torch.cuda.synchronize()
+    g.close()
+    kq = (k * q).sum(-1, keepdim=True)
+    ref = d["beta"].unsqueeze(-1) * kq * v / dk ** 0.5
+    r2 = _rel(out.float(), ref)
+    sref = d["beta"][:, -1].reshape(B, H, 1, 1) * v[:, -1].unsqueeze(-1) * k[:, -1].unsqueeze(-2)
+    r3 = _rel(st, sref)
+    print(f"chunk={chunk} a=0: rel-L2 out {r2:.3e} state {r3:.3e}")
+    assert r2 <= TOL["bf16"] and r3 <= TOL["bf16"]
