@@ -202,11 +202,23 @@ class GDN:
                 raise ValueError(f"{name}: expected contiguous {want} {shape}, got {x.dtype} {tuple(x.shape)}")
         return T
 
+    def _check_given(self, T, out=None, state_in=None, state_out=None):
+        """Shape, dtype and layout of the caller's out and states.  The C ABI takes raw
+        pointers and cannot know their extents, so a wrong shape is refused here."""
+        import torch
+        st = (self.B, self.H, self.d_v, self.d_k)
+        for name, x, shape, want in (("out", out, (self.B, T, self.H, self.d_v), self._out_dtype()),
+                                     ("state_in", state_in, st, torch.float32),
+                                     ("state_out", state_out, st, torch.float32)):
+            if x is not None and (tuple(x.shape) != shape or x.dtype != want or not x.is_contiguous()):
+                raise ValueError(f"{name}: expected contiguous {want} {shape}, got {x.dtype} {tuple(x.shape)}")
+
     def forward(self, q, k, v, beta, decay, state_in=None, state_out=None, out=None,
                 chunk_len=64, return_state=True):
         """Causal recurrence.  Returns (out, state_out)."""
         import torch
         T = self._check_inputs(q, k, v, beta, decay)
+        self._check_given(T, out, state_in, state_out)
         if out is None:
             out = torch.empty((self.B, T, self.H, self.d_v), dtype=self._out_dtype(), device=q.device)
         if state_out is None and return_state:
@@ -220,6 +232,7 @@ class GDN:
         """Bidirectional form.  Returns out."""
         import torch
         T = self._check_inputs(q, k, v, beta, decay)
+        self._check_given(T, out)
         if out is None:
             out = torch.empty((self.B, T, self.H, self.d_v), dtype=self._out_dtype(), device=q.device)
         self._check(gdn_forward_bidi(self.h, q, k, v, beta, decay, out, T, chunk_len, current_stream()))
@@ -247,6 +260,7 @@ class GDN:
         sigmoid / exp(-softplus) gates applied in the kernels).  Returns (out, state_out)."""
         import torch
         T, ts, bs = self._check_packed(qkv, beta_logit, decay_logit)
+        self._check_given(T, out, state_in, state_out)
         if out is None:
             out = torch.empty((self.B, T, self.H, self.d_v), dtype=self._out_dtype(), device=qkv.device)
         if state_out is None and return_state:
@@ -260,6 +274,7 @@ class GDN:
         """Bidirectional form with the fused prologue.  Returns out."""
         import torch
         T, ts, bs = self._check_packed(qkv, beta_logit, decay_logit)
+        self._check_given(T, out)
         if out is None:
             out = torch.empty((self.B, T, self.H, self.d_v), dtype=self._out_dtype(), device=qkv.device)
         self._check(gdn_forward_bidi_packed(self.h, qkv, ts, bs, beta_logit, decay_logit, out, T, chunk_len,

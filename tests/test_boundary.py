@@ -182,6 +182,30 @@ def test_packed_bidi_dry_run(dry):
     gb.gdn_free(h)
 
 
+def test_torch_wrapper_checks_given_outputs_and_states():
+    """out and the states reach the C ABI as raw pointers, so their shapes are checked
+    in the wrapper: a state or out of the wrong shape, dtype or layout is refused."""
+    import torch
+    g = gb.GDN(1, 2, 32, 16, "fp32", max_T=10, device=-1, bidi=True)
+    x, v = torch.zeros(1, 4, 2, 32), torch.zeros(1, 4, 2, 16)
+    gates = torch.zeros(1, 4, 2)
+    for kw in ({"state_in": torch.zeros(1, 2, 32, 16)},          # d_k x d_v instead of d_v x d_k
+               {"state_out": torch.zeros(1, 2, 16, 32, dtype=torch.float64)},
+               {"state_in": torch.zeros(1, 2, 32, 16).transpose(2, 3)},  # right shape, not contiguous
+               {"out": torch.zeros(1, 4, 2, 32)},
+               {"out": torch.zeros(1, 4, 2, 16, dtype=torch.bfloat16)}):
+        with pytest.raises(ValueError):
+            g.forward(x, x, v, gates, gates, **kw)
+    with pytest.raises(ValueError):
+        g.forward_bidi(x, x, v, gates, gates, out=torch.zeros(1, 3, 2, 16))
+    qkv = torch.zeros(1, 4, 2 * 2 * 32 + 2 * 16)
+    with pytest.raises(ValueError):
+        g.forward_packed(qkv, gates, gates, state_in=torch.zeros(2, 16, 32))
+    with pytest.raises(ValueError):
+        g.forward_bidi_packed(qkv, gates, gates, out=torch.zeros(1, 4, 2, 17))
+    g.close()
+
+
 def test_torch_wrapper_checks_packed_shapes():
     import torch
     g = gb.GDN(1, 2, 16, 16, "fp32", max_T=10, device=-1)
