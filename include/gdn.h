@@ -45,7 +45,10 @@
  * synchronise and never copy between host and device: they validate, enqueue
  * kernels on the given stream and return.  Device faults surface at the
  * caller's next synchronisation, as with any HIP launch.  A handle must be
- * used by one host thread at a time; separate handles are independent.
+ * used by one host thread at a time, and its calls must not overlap on the
+ * device, since they share the handle's scratch: enqueue them on one stream,
+ * or order streams with events.  Separate handles are independent and may run
+ * concurrently on different streams.
  *
  * Errors.  Every call returns GDN_OK (0) or a negative gdn_status; nothing is
  * thrown across this boundary and no call silently falls back to another
