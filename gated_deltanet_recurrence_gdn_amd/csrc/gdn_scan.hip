@@ -128,6 +128,8 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
     // a block has rows * L >= 16 L threads (d_v >= 16)
     constexpr int KPT = (KCH + 16 * L - 1) / (16 * L);
     constexpr int VPT = (TB / 8 + L - 1) / L;
+    // gate loads per thread: a block can have as few as 16 threads (L = 1, d_v = 16)
+    constexpr int GPT = (TB + 16 * L - 1) / (16 * L);
 
     __shared__ __align__(16) float kf[TB][DK];
     __shared__ __align__(16) float qf[TB][DK];
@@ -170,7 +172,12 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
 
     const long long nst = (T + TB - 1) / TB;
     Chunk8<IO> kr[KPT], qr[KPT], vr[VPT];
-    float br = 0.f, ar = 1.f;
+    float br[GPT], ar[GPT];
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+        br[i] = 0.f;
+        ar[i] = 1.f;
+    }
 
     // Token at walk position sidx, clamped to the last one: the loads are
     // unconditional (past the end they re-read a real token), and commit()
@@ -197,10 +204,14 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
                 vr[i].load(p.v, (size_t)b * p.v_bs + (size_t)tok_of(st * TB + c / vpt_tok) * p.v_ts +
                                     (size_t)h * dv + row0 + (c % vpt_tok) * 8);
         }
-        if (tid < TB) {
-            const size_t g = (size_t)(b * T + tok_of(st * TB + tid)) * H + h;
-            br = p.beta[g];
-            ar = p.decay[g];
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) {
+            const int j = tid + i * nthr;
+            if (j < TB) {
+                const size_t g = (size_t)(b * T + tok_of(st * TB + j)) * H + h;
+                br[i] = p.beta[g];
+                ar[i] = p.decay[g];
+            }
         }
     };
     // Registers -> LDS in fp32.  Tokens past T become b = 0, a = 1, q = k = v = 0:
@@ -258,15 +269,19 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
                 for (int e = 0; e < 8; ++e) vf[j][part * 8 + e] = real ? vv[e] : 0.f;
             }
         }
-        if (tid < TB) {
-            const bool real = st * TB + tid < T;
-            float bb = br, aa = ar;
-            if constexpr (PRO) {
-                bb = sigmoid_f32(br);
-                aa = decay_from_logit(ar);
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) {
+            const int j = tid + i * nthr;
+            if (j < TB) {
+                const bool real = st * TB + j < T;
+                float bb = br[i], aa = ar[i];
+                if constexpr (PRO) {
+                    bb = sigmoid_f32(br[i]);
+                    aa = decay_from_logit(ar[i]);
+                }
+                gt[j][0] = real ? aa : 1.f;
+                gt[j][1] = real ? bb : 0.f;
             }
-            gt[tid][0] = real ? aa : 1.f;
-            gt[tid][1] = real ? bb : 0.f;
         }
     };
 

@@ -12,8 +12,9 @@ pytestmark = pytest.mark.gpu
 EXE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_check")
 
 
-@pytest.mark.skipif(not os.path.exists(EXE), reason="tests/c_abi_check is not built (__graft_entry__.build())")
 def test_c_abi_from_cpp():
+    # a missing checker is a failure, not a skip: build() compiles it with the library
+    assert os.path.exists(EXE), "tests/c_abi_check is not built (run __graft_entry__.build())"
     r = subprocess.run([EXE], capture_output=True, text=True, timeout=120)
     print(r.stdout)
     print(r.stderr)
