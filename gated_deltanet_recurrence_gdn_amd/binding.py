@@ -5,8 +5,8 @@ kernels.  PyTorch is used for device memory and streams.  If libgdn.so is missin
 the import of this module raises: there is no fallback implementation.
 
 Raw functions (``gdn_create``, ``gdn_forward``, ``gdn_forward_bidi``,
-``gdn_forward_packed``, ``gdn_forward_bidi_packed``, ``gdn_free``, ``gdn_last_error``,
-``gdn_version``) take device pointers as ints or torch tensors and return the C
+``gdn_forward_packed``, ``gdn_forward_bidi_packed``, ``gdn_forward_noalloc``, ``gdn_free``,
+``gdn_last_error``, ``gdn_version``) take device pointers as ints or torch tensors and return the C
 status.  ``GDN`` wraps a handle for torch callers.
 """
 from __future__ import annotations
@@ -66,6 +66,8 @@ def _load():
     lib.gdn_forward_packed.restype = I
     lib.gdn_forward_bidi_packed.argtypes = [P, P, LL, LL, P, P, P, LL, I, P]
     lib.gdn_forward_bidi_packed.restype = I
+    lib.gdn_forward_noalloc.argtypes = [ctypes.POINTER(gdn_config), P, P, P, P, P, P, P, P, LL, I, P]
+    lib.gdn_forward_noalloc.restype = I
     lib.gdn_free.argtypes = [P]
     lib.gdn_free.restype = None
     lib.gdn_last_error.argtypes = [P]
@@ -133,6 +135,14 @@ def gdn_forward_bidi_packed(h, qkv, token_stride: int, batch_stride: int, beta_l
                             T: int, chunk_len: int, stream=None) -> int:
     return _lib.gdn_forward_bidi_packed(h, _p(qkv), int(token_stride), int(batch_stride), _p(beta_logit),
                                         _p(decay_logit), _p(out), int(T), int(chunk_len), stream)
+
+
+def gdn_forward_noalloc(cfg: gdn_config, q, k, v, beta, decay, state_in, state_out, out, T: int,
+                        chunk_len: int, stream=None) -> int:
+    """No handle, no allocation: cfg (a gdn_config) comes with every call; errors are
+    read with gdn_last_error(None)."""
+    return _lib.gdn_forward_noalloc(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(beta), _p(decay), _p(state_in),
+                                    _p(state_out), _p(out), int(T), int(chunk_len), stream)
 
 
 def current_stream():

@@ -17,11 +17,13 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
-#include <string>
+
+// Messages live in fixed buffers, so no call but gdn_create allocates host memory.
+constexpr size_t ERR_LEN = 512;
 
 struct gdn_ctx {
     gdn_config cfg{};
-    std::string err;
+    char err[ERR_LEN] = {0};
     float *scratch = nullptr;  // two fp32 [B, max_T, H, d_v] partials for the bidirectional form
     size_t scratch_bytes = 0;
     uint16_t *tm = nullptr;    // per-chunk triangular inverses of the MFMA chunked kernel
@@ -34,12 +36,11 @@ static_assert((int)GDN_F32 == (int)gdn::IO_F32 && (int)GDN_BF16 == (int)gdn::IO_
 
 namespace {
 
-thread_local std::string g_create_err;
+// Last failure of gdn_create, or of a call that takes no handle, on this thread.
+thread_local char g_create_err[ERR_LEN];
 
-int set_err(std::string &dst, int code, const char *fmt, va_list ap) {
-    char buf[512];
-    vsnprintf(buf, sizeof(buf), fmt, ap);
-    dst = buf;
+int set_err(char *dst, int code, const char *fmt, va_list ap) {
+    vsnprintf(dst, ERR_LEN, fmt, ap);
     return code;
 }
 
@@ -56,7 +57,7 @@ int fail_create(int code, const char *fmt, ...) {
     va_start(ap, fmt);
     set_err(g_create_err, code, fmt, ap);
     va_end(ap);
-    fprintf(stderr, "gdn_create failed: %s\n", g_create_err.c_str());
+    fprintf(stderr, "gdn_create failed: %s\n", g_create_err);
     return code;
 }
 
@@ -271,34 +272,50 @@ int resolve_chunk(gdn_ctx *h, int chunk_len, int *C) {
     return GDN_OK;
 }
 
+// The checks of a configuration that need no device: shapes, dtype, flags (any
+// bit outside `allowed` is refused), sizes.  Returns a status; the message goes to err.
+int check_config(const gdn_config &c, unsigned allowed, char *err) {
+    auto bad = [err](int code, const char *fmt, ...) {
+        va_list ap;
+        va_start(ap, fmt);
+        set_err(err, code, fmt, ap);
+        va_end(ap);
+        return code;
+    };
+    if (c.B < 1 || c.H < 1) return bad(GDN_ERR_ARG, "B = %d and H = %d must be >= 1", c.B, c.H);
+    // The scan and the general chunked kernel index (direction, b) by the grid's z
+    // dimension, at most 65535: two directions per b on bidirectional handles.
+    if (c.B > MAX_B) return bad(GDN_ERR_UNSUPPORTED, "B = %d is too large (at most %d)", c.B, MAX_B);
+    if (!valid_dim(c.d_k) || !valid_dim(c.d_v))
+        return bad(GDN_ERR_UNSUPPORTED, "d_k = %d, d_v = %d: each must be 16, 32, 64 or 128", c.d_k, c.d_v);
+    if (c.io_dtype != GDN_F32 && c.io_dtype != GDN_BF16 && c.io_dtype != GDN_FP8)
+        return bad(GDN_ERR_UNSUPPORTED, "io_dtype = %d is not GDN_F32, GDN_BF16 or GDN_FP8", c.io_dtype);
+    if (c.max_T < 0) return bad(GDN_ERR_ARG, "max_T = %lld is negative", c.max_T);
+    if (c.device < -1) return bad(GDN_ERR_ARG, "device = %d", c.device);
+    if (c.flags & ~allowed) return bad(GDN_ERR_ARG, "unknown or unsupported flags 0x%x", c.flags);
+    if ((long long)c.H * (c.d_k > c.d_v ? c.d_k : c.d_v) > MAX_TOKEN_STRIDE / 3)
+        return bad(GDN_ERR_UNSUPPORTED, "H = %d is too large (H * max(d_k, d_v) * 3 must be <= %lld)", c.H,
+                   MAX_TOKEN_STRIDE);
+    // Element count guard: B*T*H*d must fit comfortably in 64-bit byte offsets.
+    const double elems = (double)c.B * (double)c.max_T * (double)c.H * 128.0 * 4.0;
+    if (elems > 9.0e18) return bad(GDN_ERR_ARG, "B*max_T*H is too large");
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-const char *gdn_version(void) { return "0.1.0"; }
+const char *gdn_version(void) { return "0.2.0"; }
 
 int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
     if (out_h) *out_h = nullptr;
     if (!cfg || !out_h) return fail_create(GDN_ERR_ARG, "cfg and out_h must be non-NULL");
     const gdn_config c = *cfg;
-    if (c.B < 1 || c.H < 1) return fail_create(GDN_ERR_ARG, "B = %d and H = %d must be >= 1", c.B, c.H);
-    // The scan and the general chunked kernel index (direction, b) by the grid's z
-    // dimension, at most 65535: two directions per b on bidirectional handles.
-    if (c.B > MAX_B) return fail_create(GDN_ERR_UNSUPPORTED, "B = %d is too large (at most %d)", c.B, MAX_B);
-    if (!valid_dim(c.d_k) || !valid_dim(c.d_v))
-        return fail_create(GDN_ERR_UNSUPPORTED, "d_k = %d, d_v = %d: each must be 16, 32, 64 or 128",
-                           c.d_k, c.d_v);
-    if (c.io_dtype != GDN_F32 && c.io_dtype != GDN_BF16 && c.io_dtype != GDN_FP8)
-        return fail_create(GDN_ERR_UNSUPPORTED, "io_dtype = %d is not GDN_F32, GDN_BF16 or GDN_FP8", c.io_dtype);
-    if (c.max_T < 0) return fail_create(GDN_ERR_ARG, "max_T = %lld is negative", c.max_T);
-    if (c.device < -1) return fail_create(GDN_ERR_ARG, "device = %d", c.device);
-    if (c.flags & ~GDN_FLAG_BIDI) return fail_create(GDN_ERR_ARG, "unknown flags 0x%x", c.flags);
-    if ((long long)c.H * (c.d_k > c.d_v ? c.d_k : c.d_v) > MAX_TOKEN_STRIDE / 3)
-        return fail_create(GDN_ERR_UNSUPPORTED, "H = %d is too large (H * max(d_k, d_v) * 3 must be <= %lld)", c.H,
-                           MAX_TOKEN_STRIDE);
-    // Element count guard: B*T*H*d must fit comfortably in 64-bit byte offsets.
-    const double elems = (double)c.B * (double)c.max_T * (double)c.H * 128.0 * 4.0;
-    if (elems > 9.0e18) return fail_create(GDN_ERR_ARG, "B*max_T*H is too large");
+    if (int st = check_config(c, GDN_FLAG_BIDI, g_create_err)) {
+        fprintf(stderr, "gdn_create failed: %s\n", g_create_err);
+        return st;
+    }
 
     size_t scratch_bytes = 0;
     if (c.flags & GDN_FLAG_BIDI) scratch_bytes = 2 * (size_t)c.B * (size_t)c.max_T * c.H * c.d_v * sizeof(float);
@@ -358,7 +375,7 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
     h->tm = tm;
     h->tm_chunks = tm ? tm_chunks : 0;
     *out_h = h;
-    g_create_err.clear();
+    g_create_err[0] = 0;
     return GDN_OK;
 }
 
@@ -372,7 +389,7 @@ void gdn_free(gdn_handle h) {
     delete h;
 }
 
-const char *gdn_last_error(gdn_handle h) { return h ? h->err.c_str() : g_create_err.c_str(); }
+const char *gdn_last_error(gdn_handle h) { return h ? h->err : g_create_err; }
 
 }  // extern "C"
 
@@ -481,10 +498,10 @@ int gdn_forward(gdn_handle h, const void *q, const void *k, const void *v, const
                 const float *decay, const float *state_in, float *state_out, void *out, long long T,
                 int chunk_len, void *hip_stream) {
     if (!h) {
-        g_create_err = "gdn_forward: NULL handle";
+        snprintf(g_create_err, ERR_LEN, "gdn_forward: NULL handle");
         return GDN_ERR_ARG;
     }
-    h->err.clear();
+    h->err[0] = 0;
     Inputs in;
     size_t out_bytes;
     int st = prepare_plain(h, q, k, v, beta, decay, out, T, &in, &out_bytes);
@@ -496,10 +513,10 @@ int gdn_forward_packed(gdn_handle h, const void *qkv, long long token_stride, lo
                        const float *beta_logit, const float *decay_logit, const float *state_in,
                        float *state_out, void *out, long long T, int chunk_len, void *hip_stream) {
     if (!h) {
-        g_create_err = "gdn_forward_packed: NULL handle";
+        snprintf(g_create_err, ERR_LEN, "gdn_forward_packed: NULL handle");
         return GDN_ERR_ARG;
     }
-    h->err.clear();
+    h->err[0] = 0;
     Inputs in;
     size_t out_bytes;
     int st = prepare_packed(h, qkv, token_stride, batch_stride, beta_logit, decay_logit, out, T, &in, &out_bytes);
@@ -510,10 +527,10 @@ int gdn_forward_packed(gdn_handle h, const void *qkv, long long token_stride, lo
 int gdn_forward_bidi(gdn_handle h, const void *q, const void *k, const void *v, const float *beta,
                      const float *decay, void *out, long long T, int chunk_len, void *hip_stream) {
     if (!h) {
-        g_create_err = "gdn_forward_bidi: NULL handle";
+        snprintf(g_create_err, ERR_LEN, "gdn_forward_bidi: NULL handle");
         return GDN_ERR_ARG;
     }
-    h->err.clear();
+    h->err[0] = 0;
     int st = need_bidi(h, "gdn_forward_bidi");
     if (st) return st;
     Inputs in;
@@ -526,10 +543,10 @@ int gdn_forward_bidi_packed(gdn_handle h, const void *qkv, long long token_strid
                             const float *beta_logit, const float *decay_logit, void *out, long long T,
                             int chunk_len, void *hip_stream) {
     if (!h) {
-        g_create_err = "gdn_forward_bidi_packed: NULL handle";
+        snprintf(g_create_err, ERR_LEN, "gdn_forward_bidi_packed: NULL handle");
         return GDN_ERR_ARG;
     }
-    h->err.clear();
+    h->err[0] = 0;
     int st = need_bidi(h, "gdn_forward_bidi_packed");
     if (st) return st;
     Inputs in;
@@ -538,6 +555,61 @@ int gdn_forward_bidi_packed(gdn_handle h, const void *qkv, long long token_strid
                              &out_bytes)))
         return st;
     return run_bidi(h, in, out, out_bytes, T, chunk_len, hip_stream);
+}
+
+// No handle and no allocation: the configuration comes with the call and the
+// MFMA chunked kernel's per-chunk scratch is the fixed device array of
+// gdn_static.hip.  Messages go to the thread's handle-less buffer
+// (gdn_last_error(NULL)).
+int gdn_forward_noalloc(const gdn_config *cfg, const void *q, const void *k, const void *v, const float *beta,
+                        const float *decay, const float *state_in, float *state_out, void *out, long long T,
+                        int chunk_len, void *hip_stream) {
+    if (!cfg) {
+        snprintf(g_create_err, ERR_LEN, "gdn_forward_noalloc: cfg must be non-NULL");
+        return GDN_ERR_ARG;
+    }
+    gdn_ctx ctx;
+    ctx.cfg = *cfg;
+    ctx.cfg.max_T = T < 0 ? 0 : T;  // the limit is the fixed scratch, checked below
+    g_create_err[0] = 0;
+    int st = check_config(ctx.cfg, 0u, g_create_err);
+    if (st) return st;
+    const gdn_config &c = ctx.cfg;
+    const int C = chunk_len == 0 ? 64 : chunk_len;
+    const long long per_chunk = (long long)gdn::chunk_mfma_tm_bytes(1);
+    const long long capacity = (long long)gdn::STATIC_SCRATCH_BYTES / per_chunk;
+    if (T > 0 && C != 1 && gdn::chunk_mfma_supported(C, c.d_k, c.d_v, c.io_dtype)) {
+        const long long need = (long long)c.B * c.H * ((T + 63) / 64);
+        if (need > capacity) {
+            snprintf(g_create_err, ERR_LEN,
+                     "gdn_forward_noalloc: B * H * ceil(T / 64) = %lld chunks need %lld bytes of scratch; the fixed "
+                     "array holds %zu bytes (%lld chunks): split the call over tokens or heads, or use gdn_forward",
+                     need, need * per_chunk, gdn::STATIC_SCRATCH_BYTES, capacity);
+            return GDN_ERR_UNSUPPORTED;
+        }
+    }
+    if (c.device >= 0) {
+        void *ptr = nullptr;
+        bool gfx950 = false;
+        const hipError_t e = gdn::static_scratch(c.device, &ptr, &gfx950);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            snprintf(g_create_err, ERR_LEN, "gdn_forward_noalloc: device %d: %s", c.device, hipGetErrorString(e));
+            return GDN_ERR_DEVICE;
+        }
+        if (!gfx950) {
+            snprintf(g_create_err, ERR_LEN, "gdn_forward_noalloc: device %d is not a gfx950", c.device);
+            return GDN_ERR_DEVICE;
+        }
+        ctx.tm = static_cast<uint16_t *>(ptr);
+        ctx.tm_chunks = capacity;
+    }
+    Inputs in;
+    size_t out_bytes;
+    st = prepare_plain(&ctx, q, k, v, beta, decay, out, T, &in, &out_bytes);
+    if (!st) st = run_forward(&ctx, in, state_in, state_out, out, out_bytes, T, chunk_len, hip_stream);
+    if (st) snprintf(g_create_err, ERR_LEN, "%s", ctx.err);
+    return st;
 }
 
 }  // extern "C"

@@ -84,6 +84,13 @@ hipError_t launch_chunk_general(const PassArgs &a, int C, hipStream_t stream);
 hipError_t launch_combine(void *out, const float *partial, const float *partial_rev, long long n,
                           int io, hipStream_t stream);
 
+// The fixed device array behind gdn_forward_noalloc (gdn_static.hip): its size,
+// and its device address on `device` (resolved on the first call for that device,
+// with the device made current for it; *is_gfx950 is false, and *ptr NULL, for a
+// device of another architecture).
+constexpr size_t STATIC_SCRATCH_BYTES = 64ull << 20;
+hipError_t static_scratch(int device, void **ptr, bool *is_gfx950);
+
 // Chunked form with chunk length C: the MFMA kernel where it applies, else the
 // general one.  hipErrorInvalidValue for a (C, dk, dv, dtype) neither covers.
 inline bool chunk_supported(int C, int dk, int dv, int io) {

@@ -186,6 +186,30 @@ int gdn_forward_bidi_packed(gdn_handle h, const void *qkv, long long token_strid
                             const float *decay_logit, void *out, long long T,
                             int chunk_len, void *hip_stream);
 
+/*
+ * For callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  gdn_forward's causal
+ * form (same arguments, layouts, state, chunk_len and stream rules), with no
+ * handle: *cfg is a configuration as for gdn_create (flags must be 0; max_T is
+ * not used).  The call allocates nothing, on the device or the host.  The
+ * scratch of the bf16 / FP8 MFMA chunked kernel (chunk_len 64, d_k, d_v >= 32:
+ * 7 KiB per b, h and 64-token chunk) is one fixed 64 MiB device array inside the
+ * library, one per GPU, held until the process ends; a call whose
+ * B * H * ceil(T / 64) exceeds 9,362 chunks is refused with
+ * GDN_ERR_UNSUPPORTED before anything is launched (B = 1, H = 20 allows
+ * T <= 29,952).  The other paths (scan, fp32 chunked kernel) need no scratch.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on the
+ * device (streams not ordered by events) race and give wrong results.  The
+ * first call on a device resolves the array's address and checks the device
+ * (hipGetSymbolAddress, hipGetDeviceProperties): make it outside graph capture.
+ * Errors as for gdn_forward, GDN_ERR_DEVICE for a device that is not a gfx950;
+ * the message is read with gdn_last_error(NULL).  device = -1 validates only.
+ */
+int gdn_forward_noalloc(const gdn_config *cfg, const void *q, const void *k,
+                        const void *v, const float *beta, const float *decay,
+                        const float *state_in, float *state_out, void *out,
+                        long long T, int chunk_len, void *hip_stream);
+
 /* Release the handle and its scratch.  NULL is a no-op. */
 void gdn_free(gdn_handle h);
 

@@ -289,3 +289,37 @@ def test_torch_wrapper_checks_shapes():
         g.forward(x, x, x, torch.zeros(1, 4, 3), torch.zeros(1, 4, 2), out=x, state_out=None,
                   return_state=False)
     g.close()
+
+
+def noalloc(T=100, chunk=64, B=2, H=3, dk=64, dv=32, io=gb.GDN_BF16, flags=0, device=-1, **over):
+    cfg = gb.gdn_config(device, B, H, dk, dv, io, 0, flags)
+    a = dict(ADDR)
+    a.update(over)
+    return gb.gdn_forward_noalloc(cfg, a["q"], a["k"], a["v"], a["beta"], a["decay"], a["s_in"], a["s_out"],
+                                  a["out"], T, chunk)
+
+
+def test_noalloc_dry_run():
+    """gdn_forward_noalloc validates like gdn_forward (dry run: device = -1) and refuses
+    a request whose MFMA-kernel scratch exceeds the fixed array before anything else."""
+    assert noalloc() == gb.GDN_OK
+    assert noalloc(s_in=None, s_out=None, chunk=1) == gb.GDN_OK
+    assert noalloc(s_out=ADDR["s_in"]) == gb.GDN_OK
+    assert noalloc(T=0, q=None, k=None, v=None, beta=None, decay=None, out=None) == gb.GDN_OK
+    assert noalloc(chunk=3) == gb.GDN_ERR_UNSUPPORTED
+    assert noalloc(flags=gb.GDN_FLAG_BIDI) == gb.GDN_ERR_ARG
+    assert noalloc(out=ADDR["q"]) == gb.GDN_ERR_ALIAS
+    assert noalloc(q=ADDR["q"] + 2) == gb.GDN_ERR_ALIGN
+    assert noalloc(T=-1) == gb.GDN_ERR_ARG
+    assert noalloc(dk=48) == gb.GDN_ERR_UNSUPPORTED
+    assert gb.gdn_last_error(None) != ""
+    # capacity: B * H * ceil(T / 64) <= 9,362 chunks on the MFMA kernel
+    assert noalloc(B=1, H=20, dk=128, dv=128, T=29952) == gb.GDN_OK
+    assert noalloc(B=1, H=20, dk=128, dv=128, T=29953) == gb.GDN_ERR_UNSUPPORTED
+    assert "scratch" in gb.gdn_last_error(None)
+    # the paths that use no scratch have no such limit
+    assert noalloc(B=1, H=20, dk=128, dv=128, T=100000, chunk=1) == gb.GDN_OK
+    assert noalloc(B=1, H=20, dk=128, dv=128, T=100000, chunk=32) == gb.GDN_OK
+    assert noalloc(B=1, H=20, dk=128, dv=128, T=100000, chunk=64, io=gb.GDN_F32) == gb.GDN_OK
+    assert gb.library().gdn_forward_noalloc(None, None, None, None, None, None, None, None, None, 0, 1,
+                                            None) == gb.GDN_ERR_ARG
