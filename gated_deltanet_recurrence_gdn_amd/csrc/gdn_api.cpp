@@ -24,7 +24,8 @@ constexpr size_t ERR_LEN = 512;
 struct gdn_ctx {
     gdn_config cfg{};
     char err[ERR_LEN] = {0};
-    float *scratch = nullptr;  // two fp32 [B, max_T, H, d_v] partials for the bidirectional form
+    float *scratch = nullptr;  // bidirectional form: two fp32 [B, max_T, H, d_v] partials, then
+                               // two fp32 [B, H, d_v, d_k] states (the MFMA kernel's split sweep)
     size_t scratch_bytes = 0;
     uint16_t *tm = nullptr;    // per-chunk triangular inverses of the MFMA chunked kernel
     long long tm_chunks = 0;   // their capacity: directions x B x H x ceil(max_T / 64)
@@ -318,7 +319,9 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
     }
 
     size_t scratch_bytes = 0;
-    if (c.flags & GDN_FLAG_BIDI) scratch_bytes = 2 * (size_t)c.B * (size_t)c.max_T * c.H * c.d_v * sizeof(float);
+    if (c.flags & GDN_FLAG_BIDI)
+        scratch_bytes = 2 * (size_t)c.B * (size_t)c.max_T * c.H * c.d_v * sizeof(float) +
+                        2 * (size_t)c.B * c.H * c.d_v * c.d_k * sizeof(float);
     // The MFMA chunked kernel (bf16 or FP8 inputs, chunk 64, d_k and d_v >= 32) forms each
     // chunk's triangular inverse in a pass of its own and reads it back.
     long long tm_chunks = 0;
@@ -469,17 +472,23 @@ int run_bidi(gdn_ctx *h, const Inputs &in, void *out, size_t out_bytes, long lon
     const size_t n_out = (size_t)c.B * (size_t)T * c.H * c.d_v;
     a.state_in = nullptr; a.state_out = nullptr; a.out = out;
     a.partial = h->scratch;
-    a.partial_rev = h->scratch + n_out;
+    a.partial_rev = h->scratch + (size_t)c.B * (size_t)c.max_T * c.H * c.d_v;
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-    // Both directions in one launch, each into its own fp32 partial (the reverse
-    // direction walks the tokens from T-1 down, chunk grid anchored there), then
-    // out = round(partial + partial_rev): one rounding, and fp32 addition is
-    // commutative, so reversing the inputs reverses the output exactly.
+    // Both directions run concurrently, each writing fp32 outputs (the reverse
+    // direction walks the tokens from T-1 down, chunk grid anchored there), and
+    // out = round(forward + reverse): one rounding, and fp32 addition is
+    // commutative, so reversing the inputs reverses the output exactly.  The MFMA
+    // chunked kernel splits its sweeps at the middle chunk and adds the other
+    // direction's output itself; the other kernels write both partials in one
+    // launch and a combine pass adds them.
     a.reverse = 0;
     a.both_dirs = 1;
     a.out_mode = gdn::OUT_PARTIAL;
+    const bool split = C != 1 && gdn::chunk_mfma_supported(C, c.d_k, c.d_v, c.io_dtype);
+    if (split) a.bidi_state = a.partial_rev + (size_t)c.B * (size_t)c.max_T * c.H * c.d_v;
     hipError_t e = (C == 1) ? gdn::launch_scan(a, s) : gdn::launch_chunk(a, C, s);
     if ((st = launch_status(h, e, "bidirectional pass"))) return st;
+    if (split) return GDN_OK;
     e = gdn::launch_combine(out, a.partial, a.partial_rev, (long long)n_out, a.io, s);
     return launch_status(h, e, "bidirectional combine");
 }

@@ -176,12 +176,16 @@ struct Ctx {
     const float4 *grec;         // the head's gate records (b, log2 a, 1/||k||, 0), C per chunk
     long long T;
     int nchunks;
+    int c0 = 0, c1 = 0;  // the chunks this launch walks: [c0, c1) (chunk_kernel)
     int rs;   // q/k bytes between consecutive tokens (H * d_k elements when contiguous)
     int rsv;  // v bytes between consecutive tokens (H * d_v elements when contiguous)
     int rso;  // out elements between consecutive tokens: H * d_v
     int H;    // gate elements between consecutive tokens
     int reverse;
-    __device__ bool has(int c) const { return c >= 0 && c < nchunks; }
+    __device__ bool has(int c) const { return c >= c0 && c < c1; }
+    // c clamped into [c0, c1 - 1]: the prefetches are unconditional, so past the end
+    // of the range they re-read its last chunk
+    __device__ int clamp(int c) const { return c < c1 ? c : c1 - 1; }
     __device__ int ntok(int c) const {
         const long long r = T - (long long)c * C;
         return r < C ? (int)r : C;
@@ -532,6 +536,8 @@ __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
     Ctx x;
     x.T = p.T;
     x.nchunks = p.nchunks;
+    x.c0 = 0;
+    x.c1 = p.nchunks;
     x.rs = (int)(p.qk_ts * ES);
     x.rsv = 0;
     x.rso = 0;
@@ -644,8 +650,10 @@ struct ChunkParams {
     float *partial, *partial_rev;
     const uint16_t *tm;
     long long T;
+    long long state_dir_stride;  // elements between the two directions' states (both_dirs)
     int B, H, dv, ntile, nblk_dir;
     int reverse, out_mode, xcd_remap, both_dirs;
+    int c0, c1;                  // the chunks of this launch: [c0, c1)
     float scale;
 };
 
@@ -670,6 +678,9 @@ struct __align__(16) Smem {
     // row-major reads free of bank conflicts.
     static constexpr int LOT = DVT + 4;
     float Ot[4][16][LOT];
+    // OUT_ADD_PARTIAL: the other direction's fp32 outputs of the chunk's tokens
+    // (chunk parity), staged by the gate wave
+    float Pt[2][C][LOT];
 };
 
 // Column d of bVt holds token t at position t + 16 (d / 8), mod 64: the four
@@ -720,7 +731,7 @@ struct Chain16 {
                 sacc[db][0] = s4.x; sacc[db][1] = s4.y; sacc[db][2] = s4.z; sacc[db][3] = s4.w;
             }
         }
-        publish_state(sm, 0, col, g4);
+        publish_state(sm, p.c0 & 1, col, g4);  // the slot of the launch's first chunk
     }
 
     // K^T as the A operands of the update: row r of block db is d_k
@@ -825,7 +836,7 @@ struct Chain16 {
 // Tm operands of chunk c (clamped into range: the load is unconditional and
 // its result unused past the last chunk).
 __device__ __forceinline__ TmOps load_tm(const uint16_t *tm_head, int c, int n, int lane) {
-    const int cc = c < n ? c : n - 1;
+    const int cc = c < n ? c : n - 1;  // n: one past the last chunk of the launch
     const uint16_t *src = tm_head + (size_t)cc * TM_ELEMS + (size_t)lane * 8;
     TmOps t;
 #pragma unroll
@@ -950,7 +961,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 template <int DK, bool PRO>
 __device__ __forceinline__ void out_store(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int c, int q,
                                           int slot, int lane, const f32x4_t (&o)[2], float rq, void *out_b,
-                                          float *part_b) {
+                                          float *part_b, const float *other_b) {
     const int g4 = lane >> 4, r16 = lane & 15;
     const float sc = PRO ? p.scale * rq : p.scale;
     float(*tile)[Smem<DK>::LOT] = sm.Ot[slot];
@@ -974,9 +985,17 @@ __device__ __forceinline__ void out_store(const Ctx &x, Smem<DK> &sm, const Chun
         }
     } else {
         const int row = lane >> 2, col = 8 * (lane & 3);
-        const float4 a = *reinterpret_cast<const float4 *>(&tile[row][col]);
-        const float4 b = *reinterpret_cast<const float4 *>(&tile[row][col + 4]);
+        float4 a = *reinterpret_cast<const float4 *>(&tile[row][col]);
+        float4 b = *reinterpret_cast<const float4 *>(&tile[row][col + 4]);
         if (16 * q + row < n) {
+            if (p.out_mode == OUT_ADD_PARTIAL) {
+                // the other direction's fp32 output of this token (written by the
+                // previous launch, staged in LDS): the sum is rounded once
+                const float4 u = *reinterpret_cast<const float4 *>(&sm.Pt[c & 1][16 * q + row][col]);
+                const float4 w = *reinterpret_cast<const float4 *>(&sm.Pt[c & 1][16 * q + row][col + 4]);
+                a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+                b.x += w.x; b.y += w.y; b.z += w.z; b.w += w.w;
+            }
             const uint2 lo = pack4(a.x, a.y, a.z, a.w), hi = pack4(b.x, b.y, b.z, b.w);
             *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out_b) + (size_t)x.tok(c, 16 * q + row) * x.rso +
                                        col) = make_uint4(lo.x, lo.y, hi.x, hi.y);
@@ -1011,26 +1030,27 @@ __device__ __forceinline__ void out_products_step(Smem<DK> &sm, int c, int lane,
 
 template <int DK, int W, bool PRO>
 __device__ __forceinline__ void out_finish_step(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int c,
-                                                int lane, OutRegs &r, void *out_b, float *part_b) {
+                                                int lane, OutRegs &r, void *out_b, float *part_b,
+                                                const float *other_b) {
     constexpr int QA = W ? 1 : 0, QB = W ? 2 : 3;
     out_pn(sm, c & 1, QA, lane, r.oa, r.pa);
     out_pn(sm, c & 1, QB, lane, r.ob, r.pb);
-    out_store<DK, PRO>(x, sm, p, c, QA, 2 * W, lane, r.oa, r.ra, out_b, part_b);
-    out_store<DK, PRO>(x, sm, p, c, QB, 2 * W + 1, lane, r.ob, r.rb, out_b, part_b);
+    out_store<DK, PRO>(x, sm, p, c, QA, 2 * W, lane, r.oa, r.ra, out_b, part_b, other_b);
+    out_store<DK, PRO>(x, sm, p, c, QB, 2 * W + 1, lane, r.ob, r.rb, out_b, part_b, other_b);
 }
 
 // Period c of an output wave: finish chunk c - 1, then the products of chunk c.
 template <int DK, int W, bool PRO>
 __device__ __forceinline__ void output_period(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int c, int lane,
-                                              OutRegs &r, void *out_b, float *part_b) {
+                                              OutRegs &r, void *out_b, float *part_b, const float *other_b) {
     const bool fin = x.has(c - 1), run = x.has(c);
     if (fin && run) {
-        out_finish_step<DK, W, PRO>(x, sm, p, c - 1, lane, r, out_b, part_b);
+        out_finish_step<DK, W, PRO>(x, sm, p, c - 1, lane, r, out_b, part_b, other_b);
         out_products_step<DK, W, PRO>(sm, c, lane, r);
     } else if (run) {
         out_products_step<DK, W, PRO>(sm, c, lane, r);
     } else if (fin) {
-        out_finish_step<DK, W, PRO>(x, sm, p, c - 1, lane, r, out_b, part_b);
+        out_finish_step<DK, W, PRO>(x, sm, p, c - 1, lane, r, out_b, part_b, other_b);
     }
 }
 
@@ -1104,6 +1124,31 @@ __device__ __forceinline__ void load_gates(const Ctx &x, int c, int lane, GateRe
     g.r = x.grec[(size_t)c * C + lane];
 }
 
+// The other direction's fp32 outputs of a chunk's tokens for this block's 32 d_v
+// columns: lane l holds row 8 s + l / 8, columns 4 (l % 8) .. + 3 (rows past the
+// end of a short final chunk re-read its last token; they are never used).
+struct PartRows {
+    float4 r[8];
+};
+__device__ __forceinline__ PartRows load_part(const Ctx &x, const float *other_b, int c, int lane) {
+    PartRows d;
+    const int nt = x.ntok(c);
+#pragma unroll
+    for (int s_ = 0; s_ < 8; ++s_) {
+        const int j = 8 * s_ + (lane >> 3);
+        const float *src = other_b + (size_t)x.tok(c, j < nt ? j : nt - 1) * x.rso + 4 * (lane & 7);
+        const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(src));
+        d.r[s_] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    return d;
+}
+template <int DK>
+__device__ __forceinline__ void store_part(Smem<DK> &sm, int c, const PartRows &d, int lane) {
+#pragma unroll
+    for (int s_ = 0; s_ < 8; ++s_)
+        *reinterpret_cast<float4 *>(&sm.Pt[c & 1][8 * s_ + (lane >> 3)][4 * (lane & 7)]) = d.r[s_];
+}
+
 template <int DK, bool PRO>
 __device__ __forceinline__ void gates_store(const Ctx &x, Smem<DK> &sm, int c, int lane, const GateRegs &gr) {
     const GateVals v = gate_values<PRO>(lane, x.ntok(c), gr.r.x, gr.r.y, gr.r.z);
@@ -1168,6 +1213,8 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     Ctx x;
     x.T = p.T;
     x.nchunks = (int)((p.T + C - 1) / C);
+    x.c0 = p.c0;
+    x.c1 = p.c1;
     x.rs = (int)(p.qk_ts * ES);
     x.rsv = (int)(p.v_ts * ES);
     x.rso = p.H * p.dv;
@@ -1182,35 +1229,38 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     const int n = x.nchunks;
     x.grec = p.grec + (size_t)((dir * p.B + b) * p.H + h) * n * C;
 
-    // Every role walks the same periods it = -2 .. n (the last one finishes the
-    // outputs of chunk n-1), two per loop trip so that register sets alternate at
-    // compile time, with one barrier each.
+    // Every role walks the same periods it = c0 - 2 .. c1 (the last one finishes
+    // the outputs of chunk c1 - 1), two per loop trip so that register sets
+    // alternate at compile time, with one barrier each.
+    const int c0 = p.c0, c1 = p.c1;
     // out is bf16 for every input type this kernel takes
     void *out_b = reinterpret_cast<uint16_t *>(p.out) + tok0 * p.dv + dv0;
     float *part = dir ? p.partial_rev : p.partial;
     float *part_b = part ? part + tok0 * p.dv + dv0 : nullptr;
+    const float *other = dir ? p.partial : p.partial_rev;  // OUT_ADD_PARTIAL: the other direction's
+    const float *other_b = other ? other + tok0 * p.dv + dv0 : nullptr;
     if (wid < 2) {
         // Tm operands of chunk c are loaded in period c-2, right after chunk c-2
         // has used that register set.
         const int g4 = lane >> 4;
         const int col = 16 * wid + (lane & 15);
-        const size_t sbase = ((size_t)(b * p.H + h) * p.dv + dv0 + col) * DK;
+        const size_t sbase = ((size_t)(b * p.H + h) * p.dv + dv0 + col) * DK + (size_t)dir * p.state_dir_stride;
         const uint16_t *tm_head = p.tm + (size_t)((dir * p.B + b) * p.H + h) * n * TM_ELEMS;
         Chain16<DK> ch;
         ch.init(p, sm, sbase, col, g4);
-        TmOps tA = load_tm(tm_head, 0, n, lane);
-        TmOps tB = load_tm(tm_head, 1, n, lane);
+        TmOps tA = load_tm(tm_head, c0, c1, lane);
+        TmOps tB = load_tm(tm_head, c0 + 1, c1, lane);
         __syncthreads();
         f32x4_t nacc[4];
         typename Chain16<DK>::KtOps kt;
-        for (int it = -2; it < n + 1; it += 2) {
+        for (int it = c0 - 2; it < c1 + 1; it += 2) {
             const bool run0 = x.has(it), run1 = x.has(it + 1);
             if (run0) ch.step_n(sm, it, lane, col, tA, nacc, kt);
-            tA = load_tm(tm_head, it + 2, n, lane);
+            tA = load_tm(tm_head, it + 2, c1, lane);
             if (run0) ch.step_s(sm, it, lane, col, nacc, kt);
             __syncthreads();
             if (run1) ch.step_n(sm, it + 1, lane, col, tB, nacc, kt);
-            tB = load_tm(tm_head, it + 3, n, lane);
+            tB = load_tm(tm_head, it + 3, c1, lane);
             if (run1) ch.step_s(sm, it + 1, lane, col, nacc, kt);
             __syncthreads();
         }
@@ -1218,19 +1268,19 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     } else if (wid == 2) {
         OutRegs r;
         __syncthreads();
-        for (int it = -2; it < n + 1; it += 2) {
-            output_period<DK, 0, PRO>(x, sm, p, it, lane, r, out_b, part_b);
+        for (int it = c0 - 2; it < c1 + 1; it += 2) {
+            output_period<DK, 0, PRO>(x, sm, p, it, lane, r, out_b, part_b, other_b);
             __syncthreads();
-            output_period<DK, 0, PRO>(x, sm, p, it + 1, lane, r, out_b, part_b);
+            output_period<DK, 0, PRO>(x, sm, p, it + 1, lane, r, out_b, part_b, other_b);
             __syncthreads();
         }
     } else if (wid == 3) {
         OutRegs r;
         __syncthreads();
-        for (int it = -2; it < n + 1; it += 2) {
-            output_period<DK, 1, PRO>(x, sm, p, it, lane, r, out_b, part_b);
+        for (int it = c0 - 2; it < c1 + 1; it += 2) {
+            output_period<DK, 1, PRO>(x, sm, p, it, lane, r, out_b, part_b, other_b);
             __syncthreads();
-            output_period<DK, 1, PRO>(x, sm, p, it + 1, lane, r, out_b, part_b);
+            output_period<DK, 1, PRO>(x, sm, p, it + 1, lane, r, out_b, part_b, other_b);
             __syncthreads();
         }
     } else if (wid < 6) {
@@ -1246,29 +1296,41 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
             else store_rows<DK, Smem<DK>::LKK, IO>(sm.Qs[c & 1], r, lane);
         };
         Rows64<DK, IO> rA, rB;
-        rA = load_rows<DK, IO>(base, x, 0, lane);
+        rA = load_rows<DK, IO>(base, x, c0, lane);
         __syncthreads();
-        for (int it = -2; it < n + 1; it += 2) {
+        for (int it = c0 - 2; it < c1 + 1; it += 2) {
             if (x.has(it + 1)) store(it + 1, rB);
-            rB = load_rows<DK, IO>(base, x, it + 3 < n ? it + 3 : n - 1, lane);
+            rB = load_rows<DK, IO>(base, x, x.clamp(it + 3), lane);
             __syncthreads();
             if (x.has(it + 2)) store(it + 2, rA);
-            rA = load_rows<DK, IO>(base, x, it + 4 < n ? it + 4 : n - 1, lane);
+            rA = load_rows<DK, IO>(base, x, x.clamp(it + 4), lane);
             __syncthreads();
         }
     } else if (wid == 6) {
         // Gates of chunk c are computed in period c-2 from register set c&1
-        // (loaded in period c-4).
+        // (loaded in period c-4).  With OUT_ADD_PARTIAL this wave also stages the
+        // other direction's outputs of chunk c into LDS in period c (loaded in
+        // period c-2), for the output waves' stores of chunk c in period c+1.
         GateRegs gA, gB;
-        load_gates(x, 0, lane, gA);
-        load_gates(x, 1 < n ? 1 : n - 1, lane, gB);
+        load_gates(x, c0, lane, gA);
+        load_gates(x, x.clamp(c0 + 1), lane, gB);
+        const bool add = p.out_mode == OUT_ADD_PARTIAL;
+        PartRows pA, pB;
         __syncthreads();
-        for (int it = -2; it < n + 1; it += 2) {
+        for (int it = c0 - 2; it < c1 + 1; it += 2) {
             if (x.has(it + 2)) gates_store<DK, PRO>(x, sm, it + 2, lane, gA);
-            load_gates(x, it + 4 < n ? it + 4 : n - 1, lane, gA);
+            load_gates(x, x.clamp(it + 4), lane, gA);
+            if (add) {
+                if (x.has(it)) store_part(sm, it, pA, lane);
+                pA = load_part(x, other_b, x.clamp(it + 2), lane);
+            }
             __syncthreads();
             if (x.has(it + 3)) gates_store<DK, PRO>(x, sm, it + 3, lane, gB);
-            load_gates(x, it + 5 < n ? it + 5 : n - 1, lane, gB);
+            load_gates(x, x.clamp(it + 5), lane, gB);
+            if (add) {
+                if (x.has(it + 1)) store_part(sm, it + 1, pB, lane);
+                pB = load_part(x, other_b, x.clamp(it + 3), lane);
+            }
             __syncthreads();
         }
     } else {
@@ -1276,14 +1338,14 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         // (loaded in period c-3, unconditionally as for K and Q), with b_t from
         // the gate slot of chunk c.
         VRow<IO> vA, vB;
-        vA = load_v<IO>(x, 0, lane);
+        vA = load_v<IO>(x, c0, lane);
         __syncthreads();
-        for (int it = -2; it < n + 1; it += 2) {
+        for (int it = c0 - 2; it < c1 + 1; it += 2) {
             if (x.has(it + 1)) store_bv<DK, IO>(sm, it + 1, vB, lane);
-            vB = load_v<IO>(x, it + 3 < n ? it + 3 : n - 1, lane);
+            vB = load_v<IO>(x, x.clamp(it + 3), lane);
             __syncthreads();
             if (x.has(it + 2)) store_bv<DK, IO>(sm, it + 2, vA, lane);
-            vA = load_v<IO>(x, it + 4 < n ? it + 4 : n - 1, lane);
+            vA = load_v<IO>(x, x.clamp(it + 4), lane);
             __syncthreads();
         }
     }
@@ -1319,14 +1381,45 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.partial = a.partial; p.partial_rev = a.partial_rev;
     p.tm = a.tm;
     p.T = a.T; p.B = a.B; p.H = a.H; p.dv = a.dv;
+    p.state_dir_stride = 0;
     p.ntile = a.dv / DVT;
     p.nblk_dir = a.B * a.H * p.ntile;
     p.xcd_remap = (p.nblk_dir % 8) == 0;
     p.reverse = a.reverse; p.out_mode = a.out_mode; p.both_dirs = a.both_dirs;
+    p.c0 = 0; p.c1 = nchunks;
     p.scale = (float)(1.0 / __builtin_sqrt((double)DK));
     const int nblk = p.nblk_dir * dirs;
+    if (!(a.both_dirs && a.bidi_state)) {
+        hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO>), dim3(nblk), dim3(NT), 0, stream, p);
+        return hipGetLastError();
+    }
+    // Bidirectional form in two launches.  The first walks chunks [0, n1) of both
+    // directions (the forward one tokens [0, 64 n1), the reverse one the last 64 n1
+    // tokens), writes fp32 partials and keeps each direction's state; the second
+    // walks chunks [n1, n) from those states, and each direction adds the other's
+    // partial of the same token -- written by the first launch -- before rounding
+    // out once.  Tokens both first halves covered (at most 64, in the middle) are
+    // combined by a small row-range pass.
+    const int n1 = (nchunks + 1) / 2;
+    p.state_dir_stride = (long long)a.B * a.H * a.dv * DK;
+    p.state_in = nullptr;
+    p.state_out = a.bidi_state;
+    p.out_mode = OUT_PARTIAL;
+    p.c0 = 0; p.c1 = n1;
     hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO>), dim3(nblk), dim3(NT), 0, stream, p);
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (n1 < nchunks) {
+        p.state_in = a.bidi_state;
+        p.state_out = nullptr;
+        p.out_mode = OUT_ADD_PARTIAL;
+        p.c0 = n1; p.c1 = nchunks;
+        hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO>), dim3(nblk), dim3(NT), 0, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const long long half = (long long)C * n1;
+    const long long t0 = a.T - half > 0 ? a.T - half : 0, t1 = half < a.T ? half : a.T;
+    return launch_combine_rows(a.out, a.partial, a.partial_rev, a.B, a.T, (long long)a.H * a.dv, t0, t1, a.io,
+                               stream);
 }
 
 template <int DK>

@@ -22,6 +22,7 @@ __host__ __device__ constexpr int io_out_bytes(int io) { return io == IO_F32 ? 4
 enum OutMode : int {
     OUT_STORE = 0,    // out[t] = round(o_t) in the I/O dtype
     OUT_PARTIAL = 1,  // partial[t] = o_t in fp32 (one direction of the bidirectional form)
+    OUT_ADD_PARTIAL = 2,  // out[t] = round(o_t + the other direction's partial[t]) (bidirectional)
 };
 
 // One pass of the recurrence over a whole call, all (b, h) pairs.
@@ -52,6 +53,9 @@ struct PassArgs {
                             //    partial and partial_rev), from zero state
     uint16_t *tm;           // MFMA kernel only: the per-chunk scratch of the handle
     long long tm_chunks;    // chunk capacity of tm (directions x B x H x chunks)
+    float *bidi_state;      // MFMA kernel, both_dirs: [2][B,H,dv,dk] fp32 scratch; when set, the
+                            // bidirectional form is two launches split at the middle chunk and
+                            // writes out itself (no separate combine)
 };
 
 // Token-major contiguous strides for q, k [B,T,H,dk] and v [B,T,H,dv].
@@ -83,6 +87,10 @@ hipError_t launch_chunk_general(const PassArgs &a, int C, hipStream_t stream);
 // in fp32 for IO_F32 and bf16 otherwise.
 hipError_t launch_combine(void *out, const float *partial, const float *partial_rev, long long n,
                           int io, hipStream_t stream);
+// The same over the token rows [t0, t1) of every batch element of [B, T, row] tensors
+// (row % 4 == 0).
+hipError_t launch_combine_rows(void *out, const float *partial, const float *partial_rev, int B, long long T,
+                               long long row, long long t0, long long t1, int io, hipStream_t stream);
 
 // The fixed device array behind gdn_forward_noalloc (gdn_static.hip): its size,
 // and its device address on `device` (resolved on the first call for that device,

@@ -36,7 +36,8 @@
  *
  * Ownership.  The caller owns every tensor and the stream.  The library owns
  * the handle and its device scratch, allocated once in gdn_create and freed in
- * gdn_free: the two fp32 partials of gdn_forward_bidi (GDN_FLAG_BIDI), and, on
+ * gdn_free: the two fp32 partials and two fp32 states of gdn_forward_bidi
+ * (GDN_FLAG_BIDI), and, on
  * handles the bf16 MFMA chunked kernel can serve (bf16 or FP8 inputs, d_k and
  * d_v >= 32), the per-chunk triangular inverses of that kernel and each
  * token's gate record (b, log2 a and, for the packed entry points, the inverse
@@ -84,7 +85,8 @@ typedef enum {
  * arithmetic is that of the bf16 path. */
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8 = 2 } gdn_dtype;
 
-/* Request the scratch that gdn_forward_bidi needs (B * max_T * H * d_v fp32). */
+/* Request the scratch that gdn_forward_bidi needs: 2 * B * max_T * H * d_v fp32
+ * partial outputs and 2 * B * H * d_v * d_k fp32 states. */
 #define GDN_FLAG_BIDI 1u
 
 typedef struct {

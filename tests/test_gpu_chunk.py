@@ -6,7 +6,7 @@ import torch
 import oracle
 from gated_deltanet_recurrence_gdn_amd import inputs
 from gated_deltanet_recurrence_gdn_amd import binding as gb
-from gpu_util import TOL, dev, rel, reverse_tokens, slice_tokens
+from gpu_util import parity_by_head, TOL, dev, rel, reverse_tokens, slice_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -123,6 +123,27 @@ def test_bidi_chunked_and_symmetry():
     torch.cuda.synchronize()
     assert torch.equal(torch.flip(out_r, dims=[1]), out)
     g.close()
+
+
+@pytest.mark.parametrize("T", [64, 65, 127, 128, 129, 191, 192, 193, 320, 333, 449])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bidi_split_sweep(T, d):
+    """The MFMA kernel's bidirectional form walks chunks [0, n1) of both directions in
+    one launch and [n1, n) in a second (n1 = ceil(n / 2)), adding the other
+    direction's first-launch output; the middle tokens both first halves cover are
+    combined separately.  Lengths around the split points and the middle overlap,
+    against the oracle per head and per edge chunk, plus exact reversal symmetry."""
+    B, H = 2, 3
+    x, _ = make(B, T, H, d, d, seed=T + d)
+    dx = dev(x)
+    g = gb.GDN(B, H, d, d, "bf16", max_T=T, bidi=True)
+    out = g.forward_bidi(dx["q"], dx["k"], dx["v"], dx["beta"], dx["decay"], chunk_len=64)
+    r = reverse_tokens(dx)
+    out_r = g.forward_bidi(r["q"], r["k"], r["v"], r["beta"], r["decay"], chunk_len=64)
+    torch.cuda.synchronize()
+    g.close()
+    assert torch.equal(torch.flip(out_r, dims=[1]), out)
+    parity_by_head(f"bidi split T={T} d={d}", out, oracle.bidi(**x), TOL["bf16"])
 
 
 def test_state_in_untouched_and_inplace():
