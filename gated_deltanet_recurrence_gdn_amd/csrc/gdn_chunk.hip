@@ -678,10 +678,18 @@ struct __align__(16) Smem {
     // row-major reads free of bank conflicts.
     static constexpr int LOT = DVT + 4;
     float Ot[4][16][LOT];
-    // OUT_ADD_PARTIAL: the other direction's fp32 outputs of the chunk's tokens
-    // (chunk parity), staged by the gate wave
-    float Pt[2][C][LOT];
 };
+
+// OUT_ADD_PARTIAL only: the other direction's fp32 outputs of a chunk's tokens
+// (chunk parity), staged by the gate wave, in dynamic LDS that only launches of
+// that mode request.
+constexpr int LPT = DVT + 4;
+typedef float PartTile[C][LPT];
+constexpr size_t PART_LDS_BYTES = 2 * sizeof(PartTile);
+__device__ __forceinline__ PartTile *part_tiles() {
+    extern __shared__ __align__(16) float dyn_lds[];
+    return reinterpret_cast<PartTile *>(dyn_lds);
+}
 
 // Column d of bVt holds token t at position t + 16 (d / 8), mod 64: the four
 // 8-column groups that one store instruction writes then start on different
@@ -722,7 +730,7 @@ struct Chain16 {
         for (int ks = 0; ks < NKS; ++ks) sop[ks] = join_u2(w[2 * ks], w[2 * ks + 1]);
     }
 
-    __device__ __forceinline__ void init(const ChunkParams &p, Smem<DK> &sm, size_t sbase, int col, int g4) {
+    __device__ __forceinline__ void init(const ChunkParams &p, Smem<DK> &sm, size_t sbase, int col, int g4, int c0) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             sacc[db] = zero4();
@@ -731,7 +739,7 @@ struct Chain16 {
                 sacc[db][0] = s4.x; sacc[db][1] = s4.y; sacc[db][2] = s4.z; sacc[db][3] = s4.w;
             }
         }
-        publish_state(sm, p.c0 & 1, col, g4);  // the slot of the launch's first chunk
+        publish_state(sm, c0 & 1, col, g4);  // the slot of the launch's first chunk
     }
 
     // K^T as the A operands of the update: row r of block db is d_k
@@ -958,10 +966,10 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int DK, bool PRO>
+template <int DK, bool PRO, bool ADD>
 __device__ __forceinline__ void out_store(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int c, int q,
                                           int slot, int lane, const f32x4_t (&o)[2], float rq, void *out_b,
-                                          float *part_b, const float *other_b) {
+                                          float *part_b) {
     const int g4 = lane >> 4, r16 = lane & 15;
     const float sc = PRO ? p.scale * rq : p.scale;
     float(*tile)[Smem<DK>::LOT] = sm.Ot[slot];
@@ -988,11 +996,12 @@ __device__ __forceinline__ void out_store(const Ctx &x, Smem<DK> &sm, const Chun
         float4 a = *reinterpret_cast<const float4 *>(&tile[row][col]);
         float4 b = *reinterpret_cast<const float4 *>(&tile[row][col + 4]);
         if (16 * q + row < n) {
-            if (p.out_mode == OUT_ADD_PARTIAL) {
+            if constexpr (ADD) {
                 // the other direction's fp32 output of this token (written by the
                 // previous launch, staged in LDS): the sum is rounded once
-                const float4 u = *reinterpret_cast<const float4 *>(&sm.Pt[c & 1][16 * q + row][col]);
-                const float4 w = *reinterpret_cast<const float4 *>(&sm.Pt[c & 1][16 * q + row][col + 4]);
+                const PartTile &pt = part_tiles()[c & 1];
+                const float4 u = *reinterpret_cast<const float4 *>(&pt[16 * q + row][col]);
+                const float4 w = *reinterpret_cast<const float4 *>(&pt[16 * q + row][col + 4]);
                 a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
                 b.x += w.x; b.y += w.y; b.z += w.z; b.w += w.w;
             }
@@ -1028,29 +1037,42 @@ __device__ __forceinline__ void out_products_step(Smem<DK> &sm, int c, int lane,
     out_products<DK, PRO>(sm, s2, s3, QB, lane, sa, r.ob, r.pb, r.rb);
 }
 
-template <int DK, int W, bool PRO>
+template <int DK, int W, bool PRO, bool ADD>
 __device__ __forceinline__ void out_finish_step(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int c,
-                                                int lane, OutRegs &r, void *out_b, float *part_b,
-                                                const float *other_b) {
+                                                int lane, OutRegs &r, void *out_b, float *part_b) {
     constexpr int QA = W ? 1 : 0, QB = W ? 2 : 3;
     out_pn(sm, c & 1, QA, lane, r.oa, r.pa);
     out_pn(sm, c & 1, QB, lane, r.ob, r.pb);
-    out_store<DK, PRO>(x, sm, p, c, QA, 2 * W, lane, r.oa, r.ra, out_b, part_b, other_b);
-    out_store<DK, PRO>(x, sm, p, c, QB, 2 * W + 1, lane, r.ob, r.rb, out_b, part_b, other_b);
+    out_store<DK, PRO, ADD>(x, sm, p, c, QA, 2 * W, lane, r.oa, r.ra, out_b, part_b);
+    out_store<DK, PRO, ADD>(x, sm, p, c, QB, 2 * W + 1, lane, r.ob, r.rb, out_b, part_b);
 }
 
 // Period c of an output wave: finish chunk c - 1, then the products of chunk c.
-template <int DK, int W, bool PRO>
+template <int DK, int W, bool PRO, bool ADD>
 __device__ __forceinline__ void output_period(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int c, int lane,
-                                              OutRegs &r, void *out_b, float *part_b, const float *other_b) {
+                                              OutRegs &r, void *out_b, float *part_b) {
     const bool fin = x.has(c - 1), run = x.has(c);
     if (fin && run) {
-        out_finish_step<DK, W, PRO>(x, sm, p, c - 1, lane, r, out_b, part_b, other_b);
+        out_finish_step<DK, W, PRO, ADD>(x, sm, p, c - 1, lane, r, out_b, part_b);
         out_products_step<DK, W, PRO>(sm, c, lane, r);
     } else if (run) {
         out_products_step<DK, W, PRO>(sm, c, lane, r);
     } else if (fin) {
-        out_finish_step<DK, W, PRO>(x, sm, p, c - 1, lane, r, out_b, part_b, other_b);
+        out_finish_step<DK, W, PRO, ADD>(x, sm, p, c - 1, lane, r, out_b, part_b);
+    }
+}
+
+// The output waves' walk over the launch's periods.
+template <int DK, int W, bool PRO, bool ADD>
+__device__ __forceinline__ void output_role(const Ctx &x, Smem<DK> &sm, const ChunkParams &p, int lane,
+                                            void *out_b, float *part_b) {
+    OutRegs r;
+    __syncthreads();
+    for (int it = x.c0 - 2; it < x.c1 + 1; it += 2) {
+        output_period<DK, W, PRO, ADD>(x, sm, p, it, lane, r, out_b, part_b);
+        __syncthreads();
+        output_period<DK, W, PRO, ADD>(x, sm, p, it + 1, lane, r, out_b, part_b);
+        __syncthreads();
     }
 }
 
@@ -1142,11 +1164,10 @@ __device__ __forceinline__ PartRows load_part(const Ctx &x, const float *other_b
     }
     return d;
 }
-template <int DK>
-__device__ __forceinline__ void store_part(Smem<DK> &sm, int c, const PartRows &d, int lane) {
+__device__ __forceinline__ void store_part(int c, const PartRows &d, int lane) {
+    PartTile &pt = part_tiles()[c & 1];
 #pragma unroll
-    for (int s_ = 0; s_ < 8; ++s_)
-        *reinterpret_cast<float4 *>(&sm.Pt[c & 1][8 * s_ + (lane >> 3)][4 * (lane & 7)]) = d.r[s_];
+    for (int s_ = 0; s_ < 8; ++s_) *reinterpret_cast<float4 *>(&pt[8 * s_ + (lane >> 3)][4 * (lane & 7)]) = d.r[s_];
 }
 
 template <int DK, bool PRO>
@@ -1185,8 +1206,13 @@ __device__ __forceinline__ void store_bv(Smem<DK> &sm, int c, const VRow<IO> &v,
     }
 }
 
-template <int DK, int IO, bool PRO>
+// SWEEP_ALL: one launch walks every chunk.  SWEEP_FIRST / SWEEP_SECOND: the first
+// ([0, c1)) and second ([c0, n), out_mode OUT_ADD_PARTIAL) launches of the
+// bidirectional form's split sweep.
+enum Sweep : int { SWEEP_ALL = 0, SWEEP_FIRST = 1, SWEEP_SECOND = 2 };
+template <int DK, int IO, bool PRO, int SW>
 __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
+    constexpr bool ADD = SW == SWEEP_SECOND;
     constexpr int ES = io_in_bytes(IO);
     static_assert(DK % 32 == 0 && DK <= 128, "d_k must be 32, 64 or 128");
     __shared__ Smem<DK> sm;
@@ -1213,8 +1239,8 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     Ctx x;
     x.T = p.T;
     x.nchunks = (int)((p.T + C - 1) / C);
-    x.c0 = p.c0;
-    x.c1 = p.c1;
+    x.c0 = SW == SWEEP_SECOND ? p.c0 : 0;
+    x.c1 = SW == SWEEP_FIRST ? p.c1 : x.nchunks;
     x.rs = (int)(p.qk_ts * ES);
     x.rsv = (int)(p.v_ts * ES);
     x.rso = p.H * p.dv;
@@ -1232,7 +1258,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     // Every role walks the same periods it = c0 - 2 .. c1 (the last one finishes
     // the outputs of chunk c1 - 1), two per loop trip so that register sets
     // alternate at compile time, with one barrier each.
-    const int c0 = p.c0, c1 = p.c1;
+    const int c0 = x.c0, c1 = x.c1;
     // out is bf16 for every input type this kernel takes
     void *out_b = reinterpret_cast<uint16_t *>(p.out) + tok0 * p.dv + dv0;
     float *part = dir ? p.partial_rev : p.partial;
@@ -1244,10 +1270,11 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         // has used that register set.
         const int g4 = lane >> 4;
         const int col = 16 * wid + (lane & 15);
-        const size_t sbase = ((size_t)(b * p.H + h) * p.dv + dv0 + col) * DK + (size_t)dir * p.state_dir_stride;
+        size_t sbase = ((size_t)(b * p.H + h) * p.dv + dv0 + col) * DK;
+        if constexpr (SW != SWEEP_ALL) sbase += (size_t)dir * p.state_dir_stride;
         const uint16_t *tm_head = p.tm + (size_t)((dir * p.B + b) * p.H + h) * n * TM_ELEMS;
         Chain16<DK> ch;
-        ch.init(p, sm, sbase, col, g4);
+        ch.init(p, sm, sbase, col, g4, c0);
         TmOps tA = load_tm(tm_head, c0, c1, lane);
         TmOps tB = load_tm(tm_head, c0 + 1, c1, lane);
         __syncthreads();
@@ -1266,23 +1293,9 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         }
         ch.finish(p, sbase, g4);
     } else if (wid == 2) {
-        OutRegs r;
-        __syncthreads();
-        for (int it = c0 - 2; it < c1 + 1; it += 2) {
-            output_period<DK, 0, PRO>(x, sm, p, it, lane, r, out_b, part_b, other_b);
-            __syncthreads();
-            output_period<DK, 0, PRO>(x, sm, p, it + 1, lane, r, out_b, part_b, other_b);
-            __syncthreads();
-        }
+        output_role<DK, 0, PRO, ADD>(x, sm, p, lane, out_b, part_b);
     } else if (wid == 3) {
-        OutRegs r;
-        __syncthreads();
-        for (int it = c0 - 2; it < c1 + 1; it += 2) {
-            output_period<DK, 1, PRO>(x, sm, p, it, lane, r, out_b, part_b, other_b);
-            __syncthreads();
-            output_period<DK, 1, PRO>(x, sm, p, it + 1, lane, r, out_b, part_b, other_b);
-            __syncthreads();
-        }
+        output_role<DK, 1, PRO, ADD>(x, sm, p, lane, out_b, part_b);
     } else if (wid < 6) {
         // K (wave 4) or Q (wave 5) of chunk c is stored in period c-1 from register
         // set c&1, loaded in period c-3.  Memory operations only.  The loads are
@@ -1314,21 +1327,20 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         GateRegs gA, gB;
         load_gates(x, c0, lane, gA);
         load_gates(x, x.clamp(c0 + 1), lane, gB);
-        const bool add = p.out_mode == OUT_ADD_PARTIAL;
         PartRows pA, pB;
         __syncthreads();
         for (int it = c0 - 2; it < c1 + 1; it += 2) {
             if (x.has(it + 2)) gates_store<DK, PRO>(x, sm, it + 2, lane, gA);
             load_gates(x, x.clamp(it + 4), lane, gA);
-            if (add) {
-                if (x.has(it)) store_part(sm, it, pA, lane);
+            if constexpr (ADD) {
+                if (x.has(it)) store_part(it, pA, lane);
                 pA = load_part(x, other_b, x.clamp(it + 2), lane);
             }
             __syncthreads();
             if (x.has(it + 3)) gates_store<DK, PRO>(x, sm, it + 3, lane, gB);
             load_gates(x, x.clamp(it + 5), lane, gB);
-            if (add) {
-                if (x.has(it + 1)) store_part(sm, it + 1, pB, lane);
+            if constexpr (ADD) {
+                if (x.has(it + 1)) store_part(it + 1, pB, lane);
                 pB = load_part(x, other_b, x.clamp(it + 3), lane);
             }
             __syncthreads();
@@ -1390,7 +1402,7 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.scale = (float)(1.0 / __builtin_sqrt((double)DK));
     const int nblk = p.nblk_dir * dirs;
     if (!(a.both_dirs && a.bidi_state)) {
-        hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO>), dim3(nblk), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO, SWEEP_ALL>), dim3(nblk), dim3(NT), 0, stream, p);
         return hipGetLastError();
     }
     // Bidirectional form in two launches.  The first walks chunks [0, n1) of both
@@ -1406,14 +1418,15 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.state_out = a.bidi_state;
     p.out_mode = OUT_PARTIAL;
     p.c0 = 0; p.c1 = n1;
-    hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO>), dim3(nblk), dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO, SWEEP_FIRST>), dim3(nblk), dim3(NT), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (n1 < nchunks) {
         p.state_in = a.bidi_state;
         p.state_out = nullptr;
         p.out_mode = OUT_ADD_PARTIAL;
         p.c0 = n1; p.c1 = nchunks;
-        hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO>), dim3(nblk), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO, SWEEP_SECOND>), dim3(nblk), dim3(NT), PART_LDS_BYTES, stream,
+                           p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const long long half = (long long)C * n1;
