@@ -41,8 +41,7 @@
 //               l % 16, and two of them side by side are one k-step of a B
 //               operand if the k index is permuted (slots 0-3 = rows 4g .. 4g+3 of
 //               the first block, slots 4-7 = the same rows of the second); the A
-//               operand is read from LDS (or Tm from HBM) under the same
-//               permutation.  Each publishes its columns of N and a bf16 copy
+//               operand is read from LDS under the same permutation.  Each publishes its columns of N and a bf16 copy
 //               of its S columns for the outputs in double-buffered LDS slots
 //               (read after the period's barrier).
 //   waves 2, 3  outputs, query blocks {0, 3} and {1, 2} (16 queries each, the
@@ -55,7 +54,11 @@
 //               log2 a, 1/||k|| per token, written contiguously by tm_kernel
 //               from the strided [B, T, H] gates): float64 prefix sum of log2 a
 //               (DPP within 16-lane rows, then the row carries), 2^g, b 2^g,
-//               2^{g_last - g}, b.
+//               2^{g_last - g}, b.  It also stages chunk c+1's Tm operands
+//               (HBM -> registers -> LDS, loaded in period c-2), so the chain
+//               never waits on a global load (0.861 -> 0.832 ms per call), and,
+//               in the second launch of the bidirectional split, the other
+//               direction's outputs of chunk c.
 //   wave 7      b_t v_t of chunk c+1 (fp32, d_v-major) for R.
 //
 // Fused input prologue (template flag PRO): q, k, v are read in place from a
@@ -678,6 +681,8 @@ struct __align__(16) Smem {
     // row-major reads free of bank conflicts.
     static constexpr int LOT = DVT + 4;
     float Ot[4][16][LOT];
+    // Tm of a chunk in the chain's operand order (chunk parity), staged by the gate wave
+    uint16_t Tms[2][TM_ELEMS];
 };
 
 // OUT_ADD_PARTIAL only: the other direction's fp32 outputs of a chunk's tokens
@@ -841,8 +846,19 @@ struct Chain16 {
     }
 };
 
+// Tm operands of chunk c from its LDS slot.
+__device__ __forceinline__ TmOps lds_tm(const uint16_t *slot, int lane) {
+    TmOps t;
+#pragma unroll
+    for (int o = 0; o < TM_OPS; ++o) t.o[o] = lds16(slot + (size_t)o * 512 + (size_t)lane * 8);
+    return t;
+}
 // Tm operands of chunk c (clamped into range: the load is unconditional and
 // its result unused past the last chunk).
+__device__ __forceinline__ void store_tm(uint16_t *slot, const TmOps &t, int lane) {
+#pragma unroll
+    for (int o = 0; o < TM_OPS; ++o) *reinterpret_cast<bf16x8_t *>(slot + (size_t)o * 512 + (size_t)lane * 8) = t.o[o];
+}
 __device__ __forceinline__ TmOps load_tm(const uint16_t *tm_head, int c, int n, int lane) {
     const int cc = c < n ? c : n - 1;  // n: one past the last chunk of the launch
     const uint16_t *src = tm_head + (size_t)cc * TM_ELEMS + (size_t)lane * 8;
@@ -1266,29 +1282,30 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     const float *other = dir ? p.partial : p.partial_rev;  // OUT_ADD_PARTIAL: the other direction's
     const float *other_b = other ? other + tok0 * p.dv + dv0 : nullptr;
     if (wid < 2) {
-        // Tm operands of chunk c are loaded in period c-2, right after chunk c-2
-        // has used that register set.
+        // The chain reads chunk c's Tm operands from the LDS slot the gate wave
+        // filled in period c-1, so it never waits on a global load.
         const int g4 = lane >> 4;
         const int col = 16 * wid + (lane & 15);
         size_t sbase = ((size_t)(b * p.H + h) * p.dv + dv0 + col) * DK;
         if constexpr (SW != SWEEP_ALL) sbase += (size_t)dir * p.state_dir_stride;
-        const uint16_t *tm_head = p.tm + (size_t)((dir * p.B + b) * p.H + h) * n * TM_ELEMS;
         Chain16<DK> ch;
         ch.init(p, sm, sbase, col, g4, c0);
-        TmOps tA = load_tm(tm_head, c0, c1, lane);
-        TmOps tB = load_tm(tm_head, c0 + 1, c1, lane);
         __syncthreads();
         f32x4_t nacc[4];
         typename Chain16<DK>::KtOps kt;
         for (int it = c0 - 2; it < c1 + 1; it += 2) {
             const bool run0 = x.has(it), run1 = x.has(it + 1);
-            if (run0) ch.step_n(sm, it, lane, col, tA, nacc, kt);
-            tA = load_tm(tm_head, it + 2, c1, lane);
-            if (run0) ch.step_s(sm, it, lane, col, nacc, kt);
+            if (run0) {
+                const TmOps t = lds_tm(sm.Tms[it & 1], lane);
+                ch.step_n(sm, it, lane, col, t, nacc, kt);
+                ch.step_s(sm, it, lane, col, nacc, kt);
+            }
             __syncthreads();
-            if (run1) ch.step_n(sm, it + 1, lane, col, tB, nacc, kt);
-            tB = load_tm(tm_head, it + 3, c1, lane);
-            if (run1) ch.step_s(sm, it + 1, lane, col, nacc, kt);
+            if (run1) {
+                const TmOps t = lds_tm(sm.Tms[(it + 1) & 1], lane);
+                ch.step_n(sm, it + 1, lane, col, t, nacc, kt);
+                ch.step_s(sm, it + 1, lane, col, nacc, kt);
+            }
             __syncthreads();
         }
         ch.finish(p, sbase, g4);
@@ -1328,8 +1345,13 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         load_gates(x, c0, lane, gA);
         load_gates(x, x.clamp(c0 + 1), lane, gB);
         PartRows pA, pB;
+        // Tm of chunk c is stored in period c-1 from register set c&1, loaded in period c-3
+        const uint16_t *tm_head = p.tm + (size_t)((dir * p.B + b) * p.H + h) * n * TM_ELEMS;
+        TmOps mA = load_tm(tm_head, c0, c1, lane), mB;
         __syncthreads();
         for (int it = c0 - 2; it < c1 + 1; it += 2) {
+            if (x.has(it + 1)) store_tm(sm.Tms[(it + 1) & 1], mB, lane);
+            mB = load_tm(tm_head, it + 3, c1, lane);
             if (x.has(it + 2)) gates_store<DK, PRO>(x, sm, it + 2, lane, gA);
             load_gates(x, x.clamp(it + 4), lane, gA);
             if constexpr (ADD) {
@@ -1337,6 +1359,8 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
                 pA = load_part(x, other_b, x.clamp(it + 2), lane);
             }
             __syncthreads();
+            if (x.has(it + 2)) store_tm(sm.Tms[(it + 2) & 1], mA, lane);
+            mA = load_tm(tm_head, it + 4, c1, lane);
             if (x.has(it + 3)) gates_store<DK, PRO>(x, sm, it + 3, lane, gB);
             load_gates(x, x.clamp(it + 5), lane, gB);
             if constexpr (ADD) {
