@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
-FP32_VALU_PEAK_TFS = 157.3   # MI355X fp32 vector (published, packed)
+FP32_VALU_PEAK_TFS = 157.3   # MI355X fp32 vector (published; counts packed FP32)
+FP32_VALU_NOPACK_TFS = 78.6  # the same without packed FP32, which this build does not emit
 CHUNK_KERNEL = "tm_kernel + chunk_kernel"  # the two launches of one chunked gdn_forward
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -53,18 +54,44 @@ def scan_flops(B, T, H, dk, dv):
     return B * T * H * 6 * dk * dv
 
 
-def load_traffic(workload):
-    """HBM bytes per launch of the chunked kernel from the committed rocprofv3 --pmc
-    summary, if it was taken on the current kernel code (comments aside); else None."""
-    p = os.path.join(PROFILES, f"chunk_kernel_{workload}_traffic.json")
+def load_profile(name, source="gdn_chunk.hip"):
+    """A committed rocprofv3 --pmc summary (profiles/<name>.json), if it was taken on the
+    current kernel code (comments and whitespace aside); else None."""
+    p = os.path.join(PROFILES, f"{name}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
     from gated_deltanet_recurrence_gdn_amd.srchash import code_hash
-    if t.get("kernel_code_sha256_16") != code_hash("gdn_chunk.hip"):
+    if t.get("kernel_code_sha256_16") != code_hash(source):
         return None
     return t
+
+
+def load_traffic(workload):
+    """HBM bytes per launch of the chunked kernel from the committed --pmc summary."""
+    return load_profile(f"chunk_kernel_{workload}_traffic")
+
+
+def provenance(torch, x):
+    """What the numbers were measured on: input hash, software versions, host CPUs."""
+    from gated_deltanet_recurrence_gdn_amd import inputs
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"inputs_sha256": inputs.sha256(x), "torch": torch.__version__, "hip": torch.version.hip,
+            "gpu": torch.cuda.get_device_name(0), "host_cpus": os.cpu_count(), "host_cpus_usable": usable,
+            "host_cpu_model": model}
 
 
 def main():
@@ -78,6 +105,9 @@ def main():
                          "0 = every token of the workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-forms", action="store_true", help="skip the secondary forms")
+    ap.add_argument("--form", choices=["chunked", "scan"], default="chunked",
+                    help="the timed step: the chunked form (the benchmark) or, for profiling the scan "
+                         "kernel with rocprofv3, the sequential scan on the same inputs")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one plain 512 MiB device-to-device copy (a known-size "
                          "reference dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -104,11 +134,17 @@ def main():
     g = gb.GDN(B, H, dk, dv, "bf16", max_T=T)
     stream = gb.current_stream()
 
+    chunk_len = 64 if args.form == "chunked" else 1
+
     def step():
-        st = gb.gdn_forward(g.h, d["q"], d["k"], d["v"], d["beta"], d["decay"], s_in, s_out, out, T, 64,
+        st = gb.gdn_forward(g.h, d["q"], d["k"], d["v"], d["beta"], d["decay"], s_in, s_out, out, T, chunk_len,
                             stream)
         if st != gb.GDN_OK:
             raise gb.GDNError(st, gb.gdn_last_error(g.h))
+
+    # The secondary forms are measured first (each after its own untimed calls), so the
+    # headline's warm-up and timed steps follow seconds of GPU work.
+    forms = None if args.no_forms else measure_forms(torch, gb, inputs, d, g, x)
 
     for _ in range(args.warmup):
         step()
@@ -131,6 +167,7 @@ def main():
     flops = chunk_flops(B, T, H, dk, dv)
     mfma_tfs = flops / (kern_ms / 1000.0) / 1e12
     traffic = load_traffic(w.name)
+    mfma_ctr = load_profile(f"chunk_kernel_{w.name}_mfma")
 
     result = {
         "metric": "GDN tokens*heads/sec at d=128 (chunked causal form) + achieved HBM GB/s and MFMA % of peak",
@@ -145,8 +182,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; inputs.py recipe)",
-        "config": {"workload": w.name, "B": B, "H": H, "T": T, "d_k": dk, "d_v": dv, "chunk_len": 64,
-                   "form": "chunked causal, fp32 state in/out", "decay": "exp(-softplus(N(2,1)))"},
+        "config": {"workload": w.name, "B": B, "H": H, "T": T, "d_k": dk, "d_v": dv, "chunk_len": chunk_len,
+                   "form": ("chunked causal" if chunk_len == 64 else "sequential scan (profiling run)") +
+                           ", fp32 state in/out", "decay": "exp(-softplus(N(2,1)))"},
         "roofline": {
             "bound": "hbm",
             "kernel": CHUNK_KERNEL,
@@ -159,7 +197,11 @@ def main():
             "kernel_ms": kern_ms,
         },
         "mfma": {"achieved": mfma_tfs, "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
-                 "frac": mfma_tfs / BF16_MFMA_PEAK_TFS, "flops_per_launch": flops},
+                 "frac": mfma_tfs / BF16_MFMA_PEAK_TFS, "flops_per_launch": flops,
+                 "basis": "analytic dense-tile flop count over the measured time",
+                 # rocprofv3: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs), per kernel
+                 "measured_busy": (mfma_ctr["mfma_busy"] if mfma_ctr else None)},
+        "provenance": provenance(torch, x),
     }
 
     if args.calib_copy:
@@ -171,8 +213,8 @@ def main():
         result["calib_copy_bytes"] = src.numel() * src.element_size()
         del src, dst
 
-    if not args.no_forms:
-        result["forms"] = measure_forms(torch, gb, inputs, d, g, x)
+    if forms is not None:
+        result["forms"] = forms
     g.close()
 
     if not args.no_cpu:
@@ -238,10 +280,15 @@ def measure_forms(torch, gb, inputs, d, g, x):
                               stream) == 0
     ms = timed(torch, scan, 3, warm=2)
     fl = scan_flops(B, T, H, dk, dv)
+    tfs = fl / (ms / 1e3) / 1e12
+    scan_traffic = load_profile("scan_kernel_batched_bf16_d128_traffic", "gdn_scan.hip")
     forms["scan_batched_bf16_d128"] = {
         "ms": ms, "token_heads_per_s": B * H * T / (ms / 1e3), "bound": "alu",
-        "achieved_tflops": fl / (ms / 1e3) / 1e12, "peak_tflops": FP32_VALU_PEAK_TFS,
-        "hbm_gbs": algorithmic_bytes(B, T, H, dk, dv) / (ms / 1e3) / 1e9}
+        "achieved_tflops": tfs, "peak_tflops": FP32_VALU_PEAK_TFS, "frac": tfs / FP32_VALU_PEAK_TFS,
+        "peak_tflops_without_packed_fp32": FP32_VALU_NOPACK_TFS, "frac_without_packed_fp32": tfs / FP32_VALU_NOPACK_TFS,
+        "hbm_gbs_algorithmic": algorithmic_bytes(B, T, H, dk, dv) / (ms / 1e3) / 1e9,
+        # rocprofv3 FETCH_SIZE + WRITE_SIZE of scan_kernel (scaled by a plain copy), over this time
+        "hbm_gbs_measured": (scan_traffic["bytes_per_launch"] / (ms / 1e3) / 1e9 if scan_traffic else None)}
 
     # 5-call streaming (state carried) vs one call over the same 23400 tokens.
     w = inputs.WORKLOADS["streaming_bf16_d128"]

@@ -120,8 +120,10 @@ def forms_summary(d):
              "cold, 3-frame d=64 warm and cold, bidirectional, fused prologue from packed qkv, FP8 inputs)",
              "", "command (MI355X, repo root, TMPDIR=/tmp):", "  " + FORMS_CMD.format(d=rel_dir(d)),
              f"kernel code sha256[:16] (gdn_chunk.hip, comments and whitespace removed): {src_hash()}", "",
-             "template arguments: chunk_kernel<d_k, input type (1 bf16, 2 FP8), prologue>, tm_kernel<same>,",
-             "scan_kernel<d_k, state values per lane, input type (0 fp32, 1 bf16, 2 FP8), prologue>", "",
+             "template arguments: chunk_kernel<d_k, input type (1 bf16, 2 FP8), prologue, sweep (0 the whole",
+             "call; 1 and 2 the first and second launch of the bidirectional split)>, tm_kernel<d_k, input type,",
+             "prologue>, scan_kernel<d_k, state values per lane, input type (0 fp32, 1 bf16, 2 FP8), prologue>;",
+             "combine_rows_kernel: the bidirectional split's middle rows", "",
              f"  {'kernel':78s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
     for r in rows:
         name = r["Name"].replace("void gdn::(anonymous namespace)::", "")
@@ -169,6 +171,93 @@ def counters_summary(d):
     return lines
 
 
+MFMA_SETS = ["MfmaUtil", "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_MFMA"]
+MFMA_CMD = ("rocprofv3 --pmc {c} --output-format csv -d {d}/mfma_{i} -o mfma -- "
+            "python bench.py --steps 2 --warmup 1 --no-cpu --no-forms")
+SIMDS = 256 * 4  # MI355X: 256 CUs x 4 SIMDs
+
+
+def _pass_means(d, sub, kernels):
+    rows = _csv(os.path.join(d, sub, "**", "*counter_collection.csv"))
+    acc = {}
+    for r in rows:
+        for kn in kernels:
+            if kn in r["Kernel_Name"]:
+                acc.setdefault((kn, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    return {k: statistics.mean(v) for k, v in acc.items()}
+
+
+def mfma_summary(d):
+    """MFMA utilisation of tm_kernel and chunk_kernel from the DIR/mfma_<i> passes: rocprofv3's
+    derived MfmaUtil, and SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs) from the raw
+    counters as a cross-check; bf16 MFMA flops from SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512."""
+    vals = {}
+    for i in range(len(MFMA_SETS)):
+        vals.update(_pass_means(d, f"mfma_{i}", KERNELS))
+    rec = {"workload": "batched_bf16_d128", "kernel_code_sha256_16": src_hash(), "simds": SIMDS, "kernels": {}}
+    lines = ["rocprofv3 MFMA counters: chunked GDN forward (tm_kernel + chunk_kernel), workload batched_bf16_d128",
+             "(mean per dispatch)", "", "commands (MI355X, repo root, TMPDIR=/tmp), one counter set per run:"]
+    lines += ["  " + MFMA_CMD.format(c=c, d=rel_dir(d), i=i) for i, c in enumerate(MFMA_SETS)]
+    lines += [f"kernel code sha256[:16] (comments and whitespace removed): {src_hash()}", "",
+              "MfmaUtil = 100 x SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs) (rocprofv3's derived "
+              "counter); flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512", ""]
+    for kn in KERNELS:
+        g = lambda c: vals.get((kn, c))
+        util = g("MfmaUtil")
+        busy, gui, mops, ninst = (g("SQ_VALU_MFMA_BUSY_CYCLES"), g("GRBM_GUI_ACTIVE"),
+                                  g("SQ_INSTS_VALU_MFMA_MOPS_BF16"), g("SQ_INSTS_MFMA"))
+        raw = busy / (gui * SIMDS) if busy is not None and gui else None
+        rec["kernels"][kn] = {"MfmaUtil_pct": util, "SQ_VALU_MFMA_BUSY_CYCLES": busy, "GRBM_GUI_ACTIVE": gui,
+                              "busy_over_gui_x_simds": raw, "bf16_mfma_flops": (mops * 512 if mops else None),
+                              "SQ_INSTS_MFMA": ninst}
+        lines.append(f"{kn}: MfmaUtil {util}%  busy/(gui x 1024) {raw}  GRBM_GUI_ACTIVE {gui}  "
+                     f"MFMA instructions {ninst}  bf16 MFMA flops {mops * 512 if mops else None}")
+    ck = rec["kernels"][CHUNK]
+    rec["mfma_busy"] = (ck["MfmaUtil_pct"] / 100.0 if ck["MfmaUtil_pct"] is not None else ck["busy_over_gui_x_simds"])
+    lines += ["", f"chunk_kernel MFMA busy fraction reported by bench.py: {rec['mfma_busy']}"]
+    return rec, lines
+
+
+SCAN = "scan_kernel"
+SCAN_CMD = ("rocprofv3 --pmc {c} --output-format csv -d {d}/{n} -o {n} -- "
+            "python bench.py --form scan --steps 2 --warmup 1 --no-cpu --no-forms --calib-copy")
+
+
+def scan_traffic_summary(d):
+    """HBM bytes of one scan_kernel dispatch on the batched d=128 workload (DIR/scan_fetch, DIR/scan_write),
+    scaled like the chunked kernel's by the run's plain 512 MiB copy."""
+    import bench
+    from gated_deltanet_recurrence_gdn_amd import inputs
+    w = inputs.WORKLOADS["batched_bf16_d128"]
+    out = {}
+    for sub, cn in (("scan_fetch", "FETCH_SIZE"), ("scan_write", "WRITE_SIZE")):
+        rows = _csv(os.path.join(d, sub, "**", "*counter_collection.csv"))
+        ks = [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == cn and SCAN in r["Kernel_Name"]]
+        cp = [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == cn and COPY in r["Kernel_Name"]]
+        if not ks or not cp:
+            raise RuntimeError(f"{cn}: scan or copy dispatch missing in {d}/{sub}")
+        out[cn] = (statistics.mean(ks), len(ks), statistics.mean(cp))
+    f_kib, nf, f_copy = out["FETCH_SIZE"]
+    w_kib, nw, w_copy = out["WRITE_SIZE"]
+    fb = f_kib * 1024 * COPY_BYTES / (f_copy * 1024)
+    wb = w_kib * 1024 * COPY_BYTES / (w_copy * 1024)
+    abytes = bench.algorithmic_bytes(w.B, w.T, w.H, w.dk, w.dv)
+    rec = {"workload": w.name, "kernel": SCAN, "kernel_code_sha256_16": code_hash("gdn_scan.hip"),
+           "bytes_per_launch": fb + wb, "fetch_bytes": fb, "write_bytes": wb, "fetch_kib_raw": f_kib,
+           "write_kib_raw": w_kib, "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
+           "algorithmic_bytes_per_launch": abytes, "dispatches": [nf, nw]}
+    lines = [f"rocprofv3 HBM traffic counters: sequential scan (scan_kernel), workload {w.name}", "",
+             "commands (MI355X, repo root, TMPDIR=/tmp), one counter per run:",
+             "  " + SCAN_CMD.format(c="FETCH_SIZE", d=rel_dir(d), n="scan_fetch"),
+             "  " + SCAN_CMD.format(c="WRITE_SIZE", d=rel_dir(d), n="scan_write"),
+             f"kernel code sha256[:16] (gdn_scan.hip, comments and whitespace removed): {rec['kernel_code_sha256_16']}",
+             "", f"scale: the run's plain 512 MiB copy reads FETCH_SIZE {f_copy:.0f} KiB, WRITE_SIZE {w_copy:.0f} KiB",
+             f"scan_kernel per dispatch (mean of {nf} / {nw}): FETCH_SIZE {f_kib:.0f} KiB raw -> {fb / 1e9:.4f} GB, "
+             f"WRITE_SIZE {w_kib:.0f} KiB raw -> {wb / 1e9:.4f} GB",
+             f"total {(fb + wb) / 1e9:.4f} GB vs algorithmic {abytes / 1e9:.4f} GB ({(fb + wb) / abytes:.3f}x)"]
+    return rec, lines
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--counters-only", action="store_true",
@@ -177,10 +266,21 @@ def main():
     ap.add_argument("--forms-only", action="store_true",
                     help="only summarise DIR/forms (the kernel trace of a bench run with its secondary forms)")
     ap.add_argument("--workload", default="batched_bf16_d128")
+    ap.add_argument("--mfma-only", action="store_true", help="only summarise the DIR/mfma_<i> passes")
+    ap.add_argument("--scan-only", action="store_true", help="only summarise DIR/scan_fetch and DIR/scan_write")
     ap.add_argument("--algorithmic-bytes", type=float, default=None,
                     help="algorithmic bytes per launch (default: bench.py's formula for the workload)")
     a = ap.parse_args()
     os.makedirs(PROFILES, exist_ok=True)
+    if a.mfma_only or a.scan_only:
+        rec, lines = mfma_summary(a.dir) if a.mfma_only else scan_traffic_summary(a.dir)
+        name = "chunk_kernel_batched_bf16_d128_mfma" if a.mfma_only else "scan_kernel_batched_bf16_d128_traffic"
+        with open(os.path.join(PROFILES, name + ".json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        with open(os.path.join(PROFILES, name + ".txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return
     if a.counters_only:
         lines = counters_summary(a.dir)
         with open(os.path.join(PROFILES, "chunk_kernel_batched_bf16_d128_counters.txt"), "w") as f:
