@@ -29,6 +29,10 @@ struct gdn_ctx {
     size_t scratch_bytes = 0;
     uint16_t *tm = nullptr;    // per-chunk triangular inverses of the MFMA chunked kernel
     long long tm_chunks = 0;   // their capacity: directions x B x H x ceil(max_T / 64)
+    // bidirectional MFMA path: a second stream (default priority) and two events, so that
+    // the second half's inverses are formed beside the first sweep launch
+    hipStream_t side = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 };
 
 static_assert((int)GDN_F32 == (int)gdn::IO_F32 && (int)GDN_BF16 == (int)gdn::IO_BF16 &&
@@ -366,8 +370,27 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
             }
         }
     }
+    hipStream_t side = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    if (c.device >= 0 && (c.flags & GDN_FLAG_BIDI) && tm_chunks > 0) {
+        DeviceGuard g(c.device);
+        hipError_t e = hipStreamCreateWithFlags(&side, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_fork, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_join, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            if (ev_fork) (void)hipEventDestroy(ev_fork);
+            if (side) (void)hipStreamDestroy(side);
+            if (scratch) (void)hipFree(scratch);
+            if (tm) (void)hipFree(tm);
+            return fail_create(GDN_ERR_DEVICE, "creating the bidirectional side stream: %s", hipGetErrorString(e));
+        }
+    }
     gdn_ctx *h = new (std::nothrow) gdn_ctx;
     if (!h) {
+        if (ev_join) (void)hipEventDestroy(ev_join);
+        if (ev_fork) (void)hipEventDestroy(ev_fork);
+        if (side) (void)hipStreamDestroy(side);
         if (scratch) (void)hipFree(scratch);
         if (tm) (void)hipFree(tm);
         return fail_create(GDN_ERR_OOM, "out of host memory");
@@ -377,6 +400,9 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
     h->scratch_bytes = scratch_bytes;
     h->tm = tm;
     h->tm_chunks = tm ? tm_chunks : 0;
+    h->side = side;
+    h->ev_fork = ev_fork;
+    h->ev_join = ev_join;
     *out_h = h;
     g_create_err[0] = 0;
     return GDN_OK;
@@ -384,8 +410,11 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
 
 void gdn_free(gdn_handle h) {
     if (!h) return;
-    if (h->scratch || h->tm) {
+    if (h->scratch || h->tm || h->side) {
         DeviceGuard g(h->cfg.device);
+        if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+        if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+        if (h->side) (void)hipStreamDestroy(h->side);
         if (h->scratch) (void)hipFree(h->scratch);
         if (h->tm) (void)hipFree(h->tm);
     }
@@ -485,7 +514,12 @@ int run_bidi(gdn_ctx *h, const Inputs &in, void *out, size_t out_bytes, long lon
     a.both_dirs = 1;
     a.out_mode = gdn::OUT_PARTIAL;
     const bool split = C != 1 && gdn::chunk_mfma_supported(C, c.d_k, c.d_v, c.io_dtype);
-    if (split) a.bidi_state = a.partial_rev + (size_t)c.B * (size_t)c.max_T * c.H * c.d_v;
+    if (split) {
+        a.bidi_state = a.partial_rev + (size_t)c.B * (size_t)c.max_T * c.H * c.d_v;
+        a.side_stream = h->side;
+        a.ev_fork = h->ev_fork;
+        a.ev_join = h->ev_join;
+    }
     hipError_t e = (C == 1) ? gdn::launch_scan(a, s) : gdn::launch_chunk(a, C, s);
     if ((st = launch_status(h, e, "bidirectional pass"))) return st;
     if (split) return GDN_OK;

@@ -318,6 +318,7 @@ struct TmParams {
     long long T;
     long long qk_ts, qk_bs;
     int B, H, nchunks, reverse;
+    int c0, nc;       // the chunks of this launch: [c0, c0 + nc)
 };
 
 // K is dead once the Gram products are in registers, so Tm and A reuse its
@@ -530,8 +531,8 @@ __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
     long long L = blockIdx.x;
     const int h = (int)(L % p.H);
     L /= p.H;
-    const int c = (int)(L % p.nchunks);
-    L /= p.nchunks;
+    const int c = p.c0 + (int)(L % p.nc);
+    L /= p.nc;
     const int b = (int)(L % p.B);
     const int dir = (int)(L / p.B);
 
@@ -1403,9 +1404,27 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     t.grec = grec;
     t.T = a.T; t.qk_ts = a.qk_ts; t.qk_bs = a.qk_bs;
     t.B = a.B; t.H = a.H; t.nchunks = nchunks; t.reverse = a.reverse;
-    hipLaunchKernelGGL((tm_kernel<DK, IO, PRO>), dim3((unsigned)ntm), dim3(256), 0, stream, t);
+    // The bidirectional split's second launch needs the inverses of chunks [n1, n)
+    // only after the first launch, which leaves CUs idle when B H is small: given a
+    // side stream, those inverses are formed there, beside the first launch.
+    const int n1 = (nchunks + 1) / 2;
+    const bool side = a.both_dirs && a.bidi_state && a.side_stream && n1 < nchunks;
+    t.c0 = 0;
+    t.nc = side ? n1 : nchunks;
+    hipLaunchKernelGGL((tm_kernel<DK, IO, PRO>), dim3((unsigned)(dirs * a.B * a.H * t.nc)), dim3(256), 0, stream, t);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    hipStream_t s2 = static_cast<hipStream_t>(a.side_stream);
+    hipEvent_t fork = static_cast<hipEvent_t>(a.ev_fork), join = static_cast<hipEvent_t>(a.ev_join);
+    if (side) {
+        t.c0 = n1;
+        t.nc = nchunks - n1;
+        if ((e = hipEventRecord(fork, stream)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(s2, fork, 0)) != hipSuccess) return e;
+        hipLaunchKernelGGL((tm_kernel<DK, IO, PRO>), dim3((unsigned)(dirs * a.B * a.H * t.nc)), dim3(256), 0, s2, t);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = hipEventRecord(join, s2)) != hipSuccess) return e;
+    }
 
     ChunkParams p;
     p.q = static_cast<const char *>(a.q);
@@ -1436,7 +1455,6 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     // partial of the same token -- written by the first launch -- before rounding
     // out once.  Tokens both first halves covered (at most 64, in the middle) are
     // combined by a small row-range pass.
-    const int n1 = (nchunks + 1) / 2;
     p.state_dir_stride = (long long)a.B * a.H * a.dv * DK;
     p.state_in = nullptr;
     p.state_out = a.bidi_state;
@@ -1445,6 +1463,7 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO, SWEEP_FIRST>), dim3(nblk), dim3(NT), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (n1 < nchunks) {
+        if (side && (e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return e;
         p.state_in = a.bidi_state;
         p.state_out = nullptr;
         p.out_mode = OUT_ADD_PARTIAL;

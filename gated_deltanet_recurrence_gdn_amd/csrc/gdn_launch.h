@@ -56,6 +56,9 @@ struct PassArgs {
     float *bidi_state;      // MFMA kernel, both_dirs: [2][B,H,dv,dk] fp32 scratch; when set, the
                             // bidirectional form is two launches split at the middle chunk and
                             // writes out itself (no separate combine)
+    void *side_stream;      // optional (with bidi_state): a hipStream_t on which the inverses of
+    void *ev_fork;          // the second half are formed beside the first launch, ordered by
+    void *ev_join;          // these two hipEvent_t (fork: stream -> side, join: side -> stream)
 };
 
 // Token-major contiguous strides for q, k [B,T,H,dk] and v [B,T,H,dv].

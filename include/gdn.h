@@ -139,7 +139,11 @@ int gdn_forward(gdn_handle h, const void *q, const void *k, const void *v,
  * directions' outputs are summed in fp32 and rounded once to io_dtype.  The
  * reverse pass places its chunk grid from token T-1 downwards, so reversing the
  * inputs reverses the output exactly.  Needs a handle created with
- * GDN_FLAG_BIDI.  No state is read or returned.
+ * GDN_FLAG_BIDI.  No state is read or returned.  On the bf16 MFMA path the
+ * call also enqueues one kernel on a stream the handle owns (created with
+ * GDN_FLAG_BIDI, default priority), forked from and joined back into
+ * hip_stream by events: work enqueued on hip_stream after the call still runs
+ * after all of it, and the call can be captured into a HIP graph.
  */
 int gdn_forward_bidi(gdn_handle h, const void *q, const void *k, const void *v,
                      const float *beta, const float *decay, void *out,
