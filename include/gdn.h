@@ -37,7 +37,8 @@
  * Ownership.  The caller owns every tensor and the stream.  The library owns
  * the handle and its device scratch, allocated once in gdn_create and freed in
  * gdn_free: the two fp32 partials and two fp32 states of gdn_forward_bidi
- * (GDN_FLAG_BIDI), and, on
+ * (GDN_FLAG_BIDI; with them, on handles the MFMA kernel serves, a second
+ * stream of default priority and two events, see gdn_forward_bidi), and, on
  * handles the bf16 MFMA chunked kernel can serve (bf16 or FP8 inputs, d_k and
  * d_v >= 32), the per-chunk triangular inverses of that kernel and each
  * token's gate record (b, log2 a and, for the packed entry points, the inverse
