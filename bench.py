@@ -317,6 +317,19 @@ def measure_forms(torch, gb, inputs, d, g, x):
                                     "cold_per_call_median_ms": cold, "cold_sum_ms": sum(cold),
                                     "token_heads_per_s": w.B * w.H * w.T / (sum(per_call_ms) / 1e3)}
     gs.close()
+    # The same calls on a GDN_FLAG_SEGMENTS handle (token segments run concurrently).
+    gss = gb.GDN(w.B, w.H, w.dk, w.dv, "bf16", max_T=n, segments=True)
+    state.zero_()
+    seg_ms = [timed(torch, lambda: gb.gdn_forward(gss.h, parts[i]["q"], parts[i]["k"], parts[i]["v"],
+                                                  parts[i]["beta"], parts[i]["decay"], state, state, outs[i], n,
+                                                  64, stream), 5) for i in range(w.calls)]
+    seg_cold = [per_call(torch, lambda: gb.gdn_forward(gss.h, parts[i]["q"], parts[i]["k"], parts[i]["v"],
+                                                       parts[i]["beta"], parts[i]["decay"], state, state, outs[i],
+                                                       n, 64, stream), 10, warm=2, flush=flush)["median_ms"]
+                for i in range(w.calls)]
+    forms["streaming_bf16_d128"]["segmented"] = {"per_call_ms": seg_ms, "sum_ms": sum(seg_ms),
+                                                 "cold_per_call_median_ms": seg_cold, "cold_sum_ms": sum(seg_cold)}
+    gss.close()
     del xs, parts
 
     # 3 frames at d = 64 (B=1, H=16, T=4680), warm and cold.
@@ -333,6 +346,14 @@ def measure_forms(torch, gb, inputs, d, g, x):
                                 "token_heads_per_s_warm": th1 / (warm1["median_ms"] / 1e3),
                                 "token_heads_per_s_cold": th1 / (cold1["median_ms"] / 1e3)}
     g1.close()
+    g1s = gb.GDN(w1.B, w1.H, w1.dk, w1.dv, "bf16", max_T=w1.T, segments=True)
+    f1s = lambda: gb.gdn_forward(g1s.h, x1["q"], x1["k"], x1["v"], x1["beta"], x1["decay"], None, None, o1, w1.T,
+                                 64, stream)
+    warm1s = per_call(torch, f1s, 20)
+    cold1s = per_call(torch, f1s, 10, warm=2, flush=flush)
+    forms["causal_bf16_d64"]["segmented"] = {"warm": warm1s, "cold": cold1s,
+                                             "token_heads_per_s_warm": th1 / (warm1s["median_ms"] / 1e3)}
+    g1s.close()
     del x1, o1, flush_buf
 
     # Bidirectional form, 21 frames.

@@ -31,6 +31,7 @@ GDN_F32 = 0
 GDN_BF16 = 1
 GDN_FP8 = 2
 GDN_FLAG_BIDI = 1
+GDN_FLAG_SEGMENTS = 2
 
 
 class gdn_config(ctypes.Structure):
@@ -159,7 +160,7 @@ class GDN:
     on torch's current stream.  Errors raise ``GDNError`` with the library's message.
     """
 
-    def __init__(self, B, H, d_k, d_v, dtype="bf16", max_T=0, device=0, bidi=False):
+    def __init__(self, B, H, d_k, d_v, dtype="bf16", max_T=0, device=0, bidi=False, segments=False):
         self.B, self.H, self.d_k, self.d_v = B, H, d_k, d_v
         self.dtype = dtype
         self.io = {"bf16": GDN_BF16, "fp32": GDN_F32, "fp8": GDN_FP8}[dtype]
@@ -167,7 +168,8 @@ class GDN:
         self.device = device
         self.h = None
         self._free = _lib.gdn_free  # kept on the object: usable while the interpreter shuts down
-        st, h = gdn_create(device, B, H, d_k, d_v, self.io, max_T, GDN_FLAG_BIDI if bidi else 0)
+        flags = (GDN_FLAG_BIDI if bidi else 0) | (GDN_FLAG_SEGMENTS if segments else 0)
+        st, h = gdn_create(device, B, H, d_k, d_v, self.io, max_T, flags)
         if st != GDN_OK:
             raise GDNError(st, gdn_last_error(None))
         self.h = h

@@ -16,6 +16,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 #include <new>
 
 // Messages live in fixed buffers, so no call but gdn_create allocates host memory.
@@ -33,7 +34,36 @@ struct gdn_ctx {
     // the second half's inverses are formed beside the first sweep launch
     hipStream_t side = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    // segment-parallel causal form (GDN_FLAG_SEGMENTS on a handle the MFMA kernel serves):
+    // one allocation holding the buffers gdn::PassArgs describes, and the CU count that
+    // bounds the segment count
+    float *seg = nullptr;
+    int ncu = 0;
 };
+
+namespace {
+// At most this many segments per call, each of at least SEG_MIN_CHUNKS 64-token chunks.
+constexpr int SEG_MAX = 8;
+constexpr int SEG_MIN_CHUNKS = 8;
+// Element offsets of the segment buffers inside gdn_ctx::seg (all fp32 but the zero
+// row, which is sized in floats too).
+struct SegLayout {
+    size_t partial, w, sloc, phi, eye, vzero, total;
+};
+SegLayout seg_layout(const gdn_config &c) {
+    SegLayout l;
+    const size_t tok = (size_t)c.B * (size_t)c.max_T * c.H;
+    const size_t st = (size_t)c.B * c.H * c.d_v * c.d_k, tr = (size_t)c.B * c.H * c.d_k * c.d_k;
+    l.partial = 0;
+    l.w = l.partial + tok * c.d_v;
+    l.sloc = l.w + tok * c.d_k;
+    l.phi = l.sloc + SEG_MAX * st;
+    l.eye = l.phi + (SEG_MAX - 1) * tr;
+    l.vzero = l.eye + tr;
+    l.total = l.vzero + (size_t)c.H * (c.d_k > c.d_v ? c.d_k : c.d_v);
+    return l;
+}
+}  // namespace
 
 static_assert((int)GDN_F32 == (int)gdn::IO_F32 && (int)GDN_BF16 == (int)gdn::IO_BF16 &&
                   (int)GDN_FP8 == (int)gdn::IO_FP8,
@@ -317,7 +347,7 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
     if (out_h) *out_h = nullptr;
     if (!cfg || !out_h) return fail_create(GDN_ERR_ARG, "cfg and out_h must be non-NULL");
     const gdn_config c = *cfg;
-    if (int st = check_config(c, GDN_FLAG_BIDI, g_create_err)) {
+    if (int st = check_config(c, GDN_FLAG_BIDI | GDN_FLAG_SEGMENTS, g_create_err)) {
         fprintf(stderr, "gdn_create failed: %s\n", g_create_err);
         return st;
     }
@@ -335,6 +365,8 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
 
     float *scratch = nullptr;
     uint16_t *tm = nullptr;
+    float *seg = nullptr;
+    int ncu = 0;
     if (c.device >= 0) {
         int n = 0;
         hipError_t e = hipGetDeviceCount(&n);
@@ -350,6 +382,7 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
         if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
             return fail_create(GDN_ERR_DEVICE, "device %d is %s; this library is built for gfx950",
                                c.device, prop.gcnArchName);
+        ncu = prop.multiProcessorCount;
         if (scratch_bytes) {
             DeviceGuard g(c.device);
             e = hipMalloc(reinterpret_cast<void **>(&scratch), scratch_bytes);
@@ -369,6 +402,28 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
                                    hipGetErrorString(e));
             }
         }
+        // The segment buffers, only where two segments fit on the device at once; the
+        // identity matrices and the zero row are written here, once.
+        const long long bm = (long long)c.B * c.H * (c.d_v / 32), bi = (long long)c.B * c.H * (c.d_k / 32);
+        if ((c.flags & GDN_FLAG_SEGMENTS) && tm_bytes && 2 * bm + bi <= ncu) {
+            DeviceGuard g(c.device);
+            const SegLayout l = seg_layout(c);
+            e = hipMalloc(reinterpret_cast<void **>(&seg), l.total * sizeof(float));
+            if (e == hipSuccess) {
+                std::vector<float> host(l.total - l.eye, 0.0f);
+                const size_t n_rows = (size_t)c.B * c.H * c.d_k;  // row r of matrix r / d_k: 1 at column r % d_k
+                for (size_t r = 0; r < n_rows; ++r) host[r * c.d_k + r % c.d_k] = 1.0f;
+                e = hipMemcpy(seg + l.eye, host.data(), host.size() * sizeof(float), hipMemcpyHostToDevice);
+            }
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                if (seg) (void)hipFree(seg);
+                if (tm) (void)hipFree(tm);
+                if (scratch) (void)hipFree(scratch);
+                return fail_create(GDN_ERR_OOM, "the segment buffers (%zu bytes): %s", l.total * sizeof(float),
+                                   hipGetErrorString(e));
+            }
+        }
     }
     hipStream_t side = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
@@ -381,6 +436,7 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
             (void)hipGetLastError();
             if (ev_fork) (void)hipEventDestroy(ev_fork);
             if (side) (void)hipStreamDestroy(side);
+            if (seg) (void)hipFree(seg);
             if (scratch) (void)hipFree(scratch);
             if (tm) (void)hipFree(tm);
             return fail_create(GDN_ERR_DEVICE, "creating the bidirectional side stream: %s", hipGetErrorString(e));
@@ -391,6 +447,7 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
         if (ev_join) (void)hipEventDestroy(ev_join);
         if (ev_fork) (void)hipEventDestroy(ev_fork);
         if (side) (void)hipStreamDestroy(side);
+        if (seg) (void)hipFree(seg);
         if (scratch) (void)hipFree(scratch);
         if (tm) (void)hipFree(tm);
         return fail_create(GDN_ERR_OOM, "out of host memory");
@@ -403,6 +460,8 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
     h->side = side;
     h->ev_fork = ev_fork;
     h->ev_join = ev_join;
+    h->seg = seg;
+    h->ncu = ncu;
     *out_h = h;
     g_create_err[0] = 0;
     return GDN_OK;
@@ -410,8 +469,9 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
 
 void gdn_free(gdn_handle h) {
     if (!h) return;
-    if (h->scratch || h->tm || h->side) {
+    if (h->scratch || h->tm || h->side || h->seg) {
         DeviceGuard g(h->cfg.device);
+        if (h->seg) (void)hipFree(h->seg);
         if (h->ev_join) (void)hipEventDestroy(h->ev_join);
         if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
         if (h->side) (void)hipStreamDestroy(h->side);
@@ -426,6 +486,32 @@ const char *gdn_last_error(gdn_handle h) { return h ? h->err : g_create_err; }
 }  // extern "C"
 
 namespace {
+
+// Segment-parallel causal form: the largest segment count whose blocks (each
+// segment's d_v tiles, and each later segment's identity run over d_k tiles) fit on
+// the device's CUs at once, with segments of at least SEG_MIN_CHUNKS chunks.  Leaves
+// a.nseg = 0 (one sweep) when fewer than two segments fit.
+void set_segments(const gdn_ctx *h, gdn::PassArgs &a) {
+    const gdn_config &c = h->cfg;
+    const long long n = (a.T + 63) / 64;
+    const long long bm = (long long)c.B * c.H * (c.d_v / 32), bi = (long long)c.B * c.H * (c.d_k / 32);
+    int p = 1;
+    for (int q = 2; q <= SEG_MAX; ++q)
+        if (q * bm + (q - 1) * bi <= h->ncu && n / q >= SEG_MIN_CHUNKS) p = q;
+    if (p < 2) return;
+    const int len = (int)((n + p - 1) / p);
+    const int nseg = (int)((n + len - 1) / len);  // no empty segment
+    if (nseg < 2) return;
+    const SegLayout l = seg_layout(c);
+    a.nseg = nseg;
+    a.seg_len = len;
+    a.seg_partial = h->seg + l.partial;
+    a.seg_w = h->seg + l.w;
+    a.seg_sloc = h->seg + l.sloc;
+    a.seg_phi = h->seg + l.phi;
+    a.seg_eye = h->seg + l.eye;
+    a.seg_vzero = h->seg + l.vzero;
+}
 
 gdn::PassArgs pass_args(const gdn_ctx *h, const Inputs &in, long long T) {
     const gdn_config &c = h->cfg;
@@ -474,6 +560,7 @@ int run_forward(gdn_ctx *h, const Inputs &in, const float *state_in, float *stat
     gdn::PassArgs a = pass_args(h, in, T);
     a.state_in = state_in; a.state_out = state_out; a.out = out; a.partial = nullptr;
     a.reverse = 0; a.out_mode = gdn::OUT_STORE;
+    if (h->seg && tok && C != 1 && gdn::chunk_mfma_supported(C, c.d_k, c.d_v, c.io_dtype)) set_segments(h, a);
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
     // With no tokens only the state is written (state_in copied, or zeros).  The
     // scan kernel does exactly that for every shape and input type without reading

@@ -659,6 +659,14 @@ struct ChunkParams {
     int reverse, out_mode, xcd_remap, both_dirs;
     int c0, c1;                  // the chunks of this launch: [c0, c1)
     float scale;
+    // SWEEP_SEG only: block row y walks segment s = seg_base + y, chunks
+    // [s seg_len, min(n, (s + 1) seg_len)); its state_out is y seg_state_stride
+    // elements further on.  seg_zero_start: segments s > 0 start from zero (else
+    // every segment starts from state_in).  seg0_store: segment 0 stores out, the
+    // others write fp32 partials (else every segment writes partials).
+    int seg_len, seg_base, seg_zero_start, seg0_store;
+    long long seg_state_stride;
+    int seg_rows;  // block rows (y) this parameter set covers; the launch's other rows use the second set
 };
 
 template <int DK>
@@ -1225,11 +1233,28 @@ __device__ __forceinline__ void store_bv(Smem<DK> &sm, int c, const VRow<IO> &v,
 
 // SWEEP_ALL: one launch walks every chunk.  SWEEP_FIRST / SWEEP_SECOND: the first
 // ([0, c1)) and second ([c0, n), out_mode OUT_ADD_PARTIAL) launches of the
-// bidirectional form's split sweep.
-enum Sweep : int { SWEEP_ALL = 0, SWEEP_FIRST = 1, SWEEP_SECOND = 2 };
+// bidirectional form's split sweep.  SWEEP_SEG: the token segments of the
+// segment-parallel causal form, one per block row.
+enum Sweep : int { SWEEP_ALL = 0, SWEEP_FIRST = 1, SWEEP_SECOND = 2, SWEEP_SEG = 3 };
 template <int DK, int IO, bool PRO, int SW>
-__global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
+__global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p_arg, ChunkParams p_alt) {
     constexpr bool ADD = SW == SWEEP_SECOND;
+    ChunkParams p = p_arg;
+    int seg = 0;
+    if constexpr (SW == SWEEP_SEG) {
+        // block rows [0, seg_rows) use the first parameter set, the rest the second (the
+        // identity runs); a set with fewer blocks per row leaves the surplus at once
+        int y = (int)blockIdx.y;
+        if (y >= p_arg.seg_rows) {
+            p = p_alt;
+            y -= p_arg.seg_rows;
+        }
+        if ((int)blockIdx.x >= p.nblk_dir) return;
+        seg = p.seg_base + y;
+        if (p.state_out) p.state_out += (size_t)y * p.seg_state_stride;
+        if (p.seg_zero_start && seg > 0) p.state_in = nullptr;
+        p.out_mode = (p.seg0_store && seg == 0) ? OUT_STORE : OUT_PARTIAL;
+    }
     constexpr int ES = io_in_bytes(IO);
     static_assert(DK % 32 == 0 && DK <= 128, "d_k must be 32, 64 or 128");
     __shared__ Smem<DK> sm;
@@ -1256,8 +1281,9 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
     Ctx x;
     x.T = p.T;
     x.nchunks = (int)((p.T + C - 1) / C);
-    x.c0 = SW == SWEEP_SECOND ? p.c0 : 0;
+    x.c0 = SW == SWEEP_SECOND ? p.c0 : SW == SWEEP_SEG ? seg * p.seg_len : 0;
     x.c1 = SW == SWEEP_FIRST ? p.c1 : x.nchunks;
+    if constexpr (SW == SWEEP_SEG) x.c1 = min(x.nchunks, x.c0 + p.seg_len);
     x.rs = (int)(p.qk_ts * ES);
     x.rsv = (int)(p.v_ts * ES);
     x.rso = p.H * p.dv;
@@ -1288,7 +1314,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p) {
         const int g4 = lane >> 4;
         const int col = 16 * wid + (lane & 15);
         size_t sbase = ((size_t)(b * p.H + h) * p.dv + dv0 + col) * DK;
-        if constexpr (SW != SWEEP_ALL) sbase += (size_t)dir * p.state_dir_stride;
+        if constexpr (SW == SWEEP_FIRST || SW == SWEEP_SECOND) sbase += (size_t)dir * p.state_dir_stride;
         Chain16<DK> ch;
         ch.init(p, sm, sbase, col, g4, c0);
         __syncthreads();
@@ -1444,8 +1470,46 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.c0 = 0; p.c1 = nchunks;
     p.scale = (float)(1.0 / __builtin_sqrt((double)DK));
     const int nblk = p.nblk_dir * dirs;
+    if (!a.both_dirs && a.nseg > 1) {
+        // Segment-parallel causal form, one launch with a block row per segment run.
+        // Rows 0 .. nseg-1: segment 0 from state_in, storing out; segments 1 .. nseg-1
+        // from zero into fp32 partials.  Rows nseg .. 2 nseg-2: segments 1 .. nseg-1
+        // again, from the identity with v = 0 (d_v = d_k): row i of that run's state is
+        // e_i^T times the product of the segment's per-token transitions, so its
+        // outputs are w_t = (that product up to t) q_t / sqrt(d_k) and its final state
+        // is the segment's transition.  A small combine then forms the true start
+        // states and corrects the later segments' outputs.
+        if (!a.seg_partial || !a.seg_w || !a.seg_sloc || !a.seg_phi || !a.seg_eye || !a.seg_vzero ||
+            (long long)a.seg_len * (a.nseg - 1) >= nchunks)
+            return hipErrorInvalidValue;
+        ChunkParams pi = p;
+        pi.v = static_cast<const char *>(a.seg_vzero);
+        pi.v_ts = 0; pi.v_bs = 0;
+        pi.dv = DK;
+        pi.ntile = DK / DVT;
+        pi.nblk_dir = a.B * a.H * pi.ntile;
+        pi.xcd_remap = (pi.nblk_dir % 8) == 0;
+        pi.state_in = a.seg_eye;
+        pi.state_out = a.seg_phi;
+        pi.out = nullptr;
+        pi.partial = a.seg_w;
+        pi.seg_len = a.seg_len; pi.seg_base = 1; pi.seg_zero_start = 0; pi.seg0_store = 0;
+        pi.seg_state_stride = (long long)a.B * a.H * DK * DK;
+        pi.seg_rows = a.nseg - 1;
+
+        p.state_out = a.seg_sloc;
+        p.partial = a.seg_partial;
+        p.seg_len = a.seg_len; p.seg_base = 0; p.seg_zero_start = 1; p.seg0_store = 1;
+        p.seg_state_stride = (long long)a.B * a.H * a.dv * DK;
+        p.seg_rows = a.nseg;
+        const int gx = nblk > pi.nblk_dir ? nblk : pi.nblk_dir;
+        hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO, SWEEP_SEG>), dim3(gx, 2 * a.nseg - 1), dim3(NT), 0, stream,
+                           p, pi);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        return launch_seg_combine(a, stream);
+    }
     if (!(a.both_dirs && a.bidi_state)) {
-        hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO, SWEEP_ALL>), dim3(nblk), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO, SWEEP_ALL>), dim3(nblk), dim3(NT), 0, stream, p, p);
         return hipGetLastError();
     }
     // Bidirectional form in two launches.  The first walks chunks [0, n1) of both
@@ -1460,7 +1524,7 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.state_out = a.bidi_state;
     p.out_mode = OUT_PARTIAL;
     p.c0 = 0; p.c1 = n1;
-    hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO, SWEEP_FIRST>), dim3(nblk), dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO, SWEEP_FIRST>), dim3(nblk), dim3(NT), 0, stream, p, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (n1 < nchunks) {
         if (side && (e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return e;
@@ -1469,7 +1533,7 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
         p.out_mode = OUT_ADD_PARTIAL;
         p.c0 = n1; p.c1 = nchunks;
         hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO, SWEEP_SECOND>), dim3(nblk), dim3(NT), PART_LDS_BYTES, stream,
-                           p);
+                           p, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const long long half = (long long)C * n1;

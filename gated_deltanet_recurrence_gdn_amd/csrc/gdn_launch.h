@@ -59,6 +59,20 @@ struct PassArgs {
     void *side_stream;      // optional (with bidi_state): a hipStream_t on which the inverses of
     void *ev_fork;          // the second half are formed beside the first launch, ordered by
     void *ev_join;          // these two hipEvent_t (fork: stream -> side, join: side -> stream)
+    // Segment-parallel causal form (MFMA kernel, causal, nseg > 1):
+    // the call's chunks are cut into nseg segments of seg_len chunks.  Segment 0 runs
+    // from state_in and writes out; every later segment runs from zero into
+    // seg_partial, and in the same launch the same segment runs from the identity with v = 0
+    // (seg_w: its outputs w_t, seg_phi: its final state, the segment's transition);
+    // then the true start states follow segment by segment and each later token's
+    // output is corrected by S_start w_t.
+    int nseg, seg_len;
+    float *seg_partial;     // [B,T,H,dv] fp32
+    float *seg_w;           // [B,T,H,dk] fp32
+    float *seg_sloc;        // [nseg][B,H,dv,dk] fp32: final states from each segment's own start
+    float *seg_phi;         // [nseg-1][B,H,dk,dk] fp32: transitions of segments 1 .. nseg-1
+    const float *seg_eye;   // [B,H,dk,dk] fp32 identity matrices
+    const void *seg_vzero;  // H * max(dk, dv) zeros of the input type (v of the identity runs)
 };
 
 // Token-major contiguous strides for q, k [B,T,H,dk] and v [B,T,H,dv].
@@ -94,6 +108,11 @@ hipError_t launch_combine(void *out, const float *partial, const float *partial_
 // (row % 4 == 0).
 hipError_t launch_combine_rows(void *out, const float *partial, const float *partial_rev, int B, long long T,
                                long long row, long long t0, long long t1, int io, hipStream_t stream);
+
+// Segment-parallel causal form, after the sweeps: state_out and, for every token of
+// segments > 0, out = round(seg_partial + S_start w_t), with each segment's true start
+// state S_start formed from the segment states and transitions (one launch).
+hipError_t launch_seg_combine(const PassArgs &a, hipStream_t stream);
 
 // The fixed device array behind gdn_forward_noalloc (gdn_static.hip): its size,
 // and its device address on `device` (resolved on the first call for that device,

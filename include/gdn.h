@@ -90,6 +90,22 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8 = 2 } gdn_dtype;
  * partial outputs and 2 * B * H * d_v * d_k fp32 states. */
 #define GDN_FLAG_BIDI 1u
 
+/* Segment-parallel causal form, for calls whose heads leave most of the device's
+ * CUs idle (streaming calls of a few thousand tokens, few heads).  On the bf16 MFMA
+ * chunked path (chunk_len 64, bf16 or FP8 inputs, d_k and d_v >= 32) a causal call
+ * of at least 16 chunks is cut into up to 8 token segments of whole chunks that run
+ * concurrently: segment 0 from state_in, each later one from zero and, beside it,
+ * from the identity with v = 0, which gives the segment's transition; a combine
+ * then forms each segment's true start state and adds its contribution to the
+ * outputs (the recurrence is affine in the state; the correction products run on
+ * bf16 MFMA with split fp32 operands).  The segment count is the largest whose
+ * blocks fit on the device at once.  Results stay within the stated tolerances,
+ * but are not bit-identical to one sweep, nor across different splits of a
+ * sequence into calls.  Costs per handle: fp32 [B, max_T, H, d_v + d_k] plus
+ * 8 d_v x d_k states and 8 d_k x d_k matrices per (b, h).  Without this flag
+ * every call is one sweep. */
+#define GDN_FLAG_SEGMENTS 2u
+
 typedef struct {
     int device;        /* HIP device ordinal; -1 = dry run (validate only, no GPU) */
     int B, H;          /* batch (1 .. 32767) and heads (>= 1, H * max(d_k, d_v)   *

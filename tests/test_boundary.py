@@ -323,3 +323,15 @@ def test_noalloc_dry_run():
     assert noalloc(B=1, H=20, dk=128, dv=128, T=100000, chunk=64, io=gb.GDN_F32) == gb.GDN_OK
     assert gb.library().gdn_forward_noalloc(None, None, None, None, None, None, None, None, None, 0, 1,
                                             None) == gb.GDN_ERR_ARG
+
+
+def test_flags_checked():
+    """GDN_FLAG_SEGMENTS is a known flag (also with GDN_FLAG_BIDI); any other bit is
+    refused at create, and the allocation-free entry point takes no flags."""
+    for flags in (gb.GDN_FLAG_SEGMENTS, gb.GDN_FLAG_SEGMENTS | gb.GDN_FLAG_BIDI):
+        st, h = gb.gdn_create(-1, 1, 4, 128, 128, gb.GDN_BF16, 5000, flags)
+        assert st == gb.GDN_OK, gb.gdn_last_error(None)
+        gb.gdn_free(h)
+    st, h = gb.gdn_create(-1, 1, 4, 128, 128, gb.GDN_BF16, 5000, 4)
+    assert st == gb.GDN_ERR_ARG and "flags" in gb.gdn_last_error(None)
+    assert noalloc(flags=gb.GDN_FLAG_SEGMENTS) == gb.GDN_ERR_ARG
