@@ -87,7 +87,7 @@ __device__ __forceinline__ f32x4_t mfma_split(bf16x8_t ah, bf16x8_t al, bf16x8_t
 //     4 g .. 4 g + 3 of token r: out = round(partial + O), one 8-byte store.  The next
 //     group's W row and partials are loaded before the current group's products.
 //   state block: writes the chain's final state, fp32, to state_out.
-constexpr int CORR_CHUNKS = 4;
+constexpr int CORR_CHUNKS = 2;  // runs of 1 or 4 chunks measured 1-8% slower on the short workloads
 
 template <int DK, int DV>
 struct CombSmem {
@@ -121,6 +121,33 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SegParams p) {
     const size_t sstride = (size_t)p.B * p.H * DV * DK;
     const size_t pstride = (size_t)p.B * p.H * DK * DK;
 
+    // the chain over segments 1 .. seg - 1; wave w owns the 16x16 tiles i = w + 4 j of
+    // the d_v x d_k state.  Each step's transition and S^0_end values are loaded one
+    // step ahead, so that their latency overlaps the previous step's products.
+    constexpr int NCG = DK / 16;                 // column groups of the state
+    constexpr int NTW = (DV / 16) * NCG / 4;     // tiles per wave
+    constexpr int NPH = DK * DK / 4 / 256;       // float4 of a transition per thread
+    f32x4_t acc[NTW];
+    float4 v[NPH];
+    f32x4_t lo[NTW];
+    auto load_phi = [&](int s1) {
+        const float *phi = p.phi + (s1 - 1) * pstride + (size_t)head * DK * DK;
+#pragma unroll
+        for (int it = 0; it < NPH; ++it) v[it] = *reinterpret_cast<const float4 *>(phi + 4 * (size_t)(threadIdx.x + 256 * it));
+    };
+    auto load_lo = [&](int s1) {
+        const float *src = p.sloc + s1 * sstride + (size_t)head * DV * DK;
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+            const int i = wid + 4 * j, rg = i / NCG, cg = i % NCG;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) lo[j][m] = src[(size_t)(16 * rg + 4 * g4 + m) * DK + 16 * cg + r16];
+        }
+    };
+    if (seg > 1) {
+        load_phi(1);
+        load_lo(1);
+    }
     // S^0_end[0], the true state at the end of segment 0, split into LDS
     {
         const float *src = p.sloc + (size_t)head * DV * DK;
@@ -139,25 +166,15 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SegParams p) {
             const int i = threadIdx.x + 256 * it;
             if (i < DV * DK / 8) {
                 const int c = (8 * i) / DK, k0 = (8 * i) % DK;
-                bf16x8_t hi, lo;
-                split8(sv[2 * it], sv[2 * it + 1], hi, lo);
-                *reinterpret_cast<bf16x8_t *>(&sm.sh[c][k0]) = hi;
-                *reinterpret_cast<bf16x8_t *>(&sm.sl[c][k0]) = lo;
+                bf16x8_t h8, l8;
+                split8(sv[2 * it], sv[2 * it + 1], h8, l8);
+                *reinterpret_cast<bf16x8_t *>(&sm.sh[c][k0]) = h8;
+                *reinterpret_cast<bf16x8_t *>(&sm.sl[c][k0]) = l8;
             }
         }
     }
 
-    // the chain over segments 1 .. seg - 1; wave w owns the 16x16 tiles i = w + 4 j of
-    // the d_v x d_k state
-    constexpr int NCG = DK / 16;                 // column groups of the state
-    constexpr int NTW = (DV / 16) * NCG / 4;     // tiles per wave
-    f32x4_t acc[NTW];
     for (int s1 = 1; s1 < seg; ++s1) {
-        const float *phi = p.phi + (s1 - 1) * pstride + (size_t)head * DK * DK;
-        constexpr int NPH = DK * DK / 4 / 256;
-        float4 v[NPH];
-#pragma unroll
-        for (int it = 0; it < NPH; ++it) v[it] = *reinterpret_cast<const float4 *>(phi + 4 * (size_t)(threadIdx.x + 256 * it));
 #pragma unroll
         for (int it = 0; it < NPH; ++it) {
             const int i = threadIdx.x + 256 * it;
@@ -166,8 +183,8 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SegParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) split1(vv[e], sm.th[j0 + e][k], sm.tl[j0 + e][k]);
         }
+        if (s1 + 1 < seg) load_phi(s1 + 1);
         __syncthreads();  // the state and the transition are staged
-        const float *lo = p.sloc + s1 * sstride + (size_t)head * DV * DK;
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
             const int i = wid + 4 * j, rg = i / NCG, cg = i % NCG;
@@ -179,8 +196,9 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SegParams p) {
                                lds16(&sm.th[16 * cg + r16][k0]), lds16(&sm.tl[16 * cg + r16][k0]), d);
             }
 #pragma unroll
-            for (int m = 0; m < 4; ++m) acc[j][m] = d[m] + lo[(size_t)(16 * rg + 4 * g4 + m) * DK + 16 * cg + r16];
+            for (int m = 0; m < 4; ++m) acc[j][m] = d[m] + lo[j][m];
         }
+        if (s1 + 1 < seg) load_lo(s1 + 1);
         __syncthreads();  // every read of the staged state and transition is done
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
