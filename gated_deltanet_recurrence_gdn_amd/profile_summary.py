@@ -117,13 +117,15 @@ def forms_summary(d):
     """Per-kernel-instantiation stats of a bench run with its secondary forms."""
     rows = _csv(os.path.join(d, "forms", "**", "*kernel_stats.csv"))
     lines = ["rocprofv3 kernel trace: bench.py with its secondary forms (scan, 5-call streaming warm and",
-             "cold, 3-frame d=64 warm and cold, bidirectional, fused prologue from packed qkv, FP8 inputs)",
+             "cold, 3-frame d=64 warm and cold, each also segmented, bidirectional, fused prologue from",
+             "packed qkv, FP8 inputs)",
              "", "command (MI355X, repo root, TMPDIR=/tmp):", "  " + FORMS_CMD.format(d=rel_dir(d)),
              f"kernel code sha256[:16] (gdn_chunk.hip, comments and whitespace removed): {src_hash()}", "",
              "template arguments: chunk_kernel<d_k, input type (1 bf16, 2 FP8), prologue, sweep (0 the whole",
-             "call; 1 and 2 the first and second launch of the bidirectional split)>, tm_kernel<d_k, input type,",
-             "prologue>, scan_kernel<d_k, state values per lane, input type (0 fp32, 1 bf16, 2 FP8), prologue>;",
-             "combine_rows_kernel: the bidirectional split's middle rows", "",
+             "call; 1 and 2 the first and second launch of the bidirectional split; 3 the segment rows of the",
+             "segmented form)>, tm_kernel<d_k, input type, prologue>, scan_kernel<d_k, state values per lane,",
+             "input type (0 fp32, 1 bf16, 2 FP8), prologue>; combine_rows_kernel: the bidirectional split's",
+             "middle rows; seg_combine_kernel<d_k, d_v>: the segmented form's start states and corrections", "",
              f"  {'kernel':78s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
     for r in rows:
         name = r["Name"].replace("void gdn::(anonymous namespace)::", "")
