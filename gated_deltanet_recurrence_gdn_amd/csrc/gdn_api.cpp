@@ -501,7 +501,8 @@ void set_segments(const gdn_ctx *h, gdn::PassArgs &a) {
     if (p < 2) return;
     const int len = (int)((n + p - 1) / p);
     const int nseg = (int)((n + len - 1) / len);  // no empty segment
-    if (nseg < 2) return;
+    // the combine's grid rows: (nseg - 1) runs of 2 chunks per segment, plus one
+    if (nseg < 2 || (long long)(nseg - 1) * ((len + 1) / 2) + 1 > 65535) return;
     const SegLayout l = seg_layout(c);
     a.nseg = nseg;
     a.seg_len = len;

@@ -147,3 +147,19 @@ def test_graph_replay():
         torch.cuda.synchronize()
         assert torch.equal(out, eager[0]) and torch.equal(st, eager[1])
     g.close()
+
+
+@pytest.mark.parametrize("segments", [False, True])
+def test_long_sequence(segments):
+    """2^18 + 3 tokens (4,097 chunks, the last of 3 tokens) on two heads at d = 64 with a
+    start state: one sweep, and the segmented form (8 segments of 513 chunks)."""
+    T = (1 << 18) + 3
+    x = inputs.make_inputs(1, T, 2, 64, 64, "bf16", seed=21)
+    s0 = state0(1, 2, 64, 64, seed=22)
+    if segments:
+        check(f"T={T}, segments", x, s0)
+        return
+    print(f"[gpu case] T={T}, one sweep", flush=True)
+    out, st = run(x, s0, False)
+    o64, s64 = oracle.forward(**x, state_in=s0)
+    parity_by_head(f"T={T}, one sweep", out, o64, TOL["bf16"], st, s64)
