@@ -667,6 +667,7 @@ struct ChunkParams {
     int seg_len, seg_base, seg_zero_start, seg0_store;
     long long seg_state_stride;
     int seg_rows;  // block rows (y) this parameter set covers; the launch's other rows use the second set
+    int state_out_t;  // state_out written transposed ([d_k][d_v] per head)
 };
 
 template <int DK>
@@ -848,6 +849,18 @@ struct Chain16 {
 
     __device__ __forceinline__ void finish(const ChunkParams &p, size_t sbase, int g4) {
         if (!p.state_out) return;
+        if (p.state_out_t) {
+            // transposed: element (row r, column j) of the head's d_v x d_k state goes to
+            // column r of row j (d_v = d_k for the runs that ask for it)
+            const size_t head = sbase / ((size_t)p.dv * DK);
+            const int r = (int)(sbase / DK - head * p.dv);
+            float *dst = p.state_out + head * p.dv * DK + r;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) dst[(size_t)(sdk(db, g4) + m) * p.dv] = sacc[db][m];
+            return;
+        }
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
             *reinterpret_cast<float4 *>(p.state_out + sbase + sdk(db, g4)) =
@@ -1469,6 +1482,7 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.reverse = a.reverse; p.out_mode = a.out_mode; p.both_dirs = a.both_dirs;
     p.c0 = 0; p.c1 = nchunks;
     p.scale = (float)(1.0 / __builtin_sqrt((double)DK));
+    p.state_out_t = 0;
     const int nblk = p.nblk_dir * dirs;
     if (!a.both_dirs && a.nseg > 1) {
         // Segment-parallel causal form, one launch with a block row per segment run.
@@ -1496,6 +1510,7 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
         pi.seg_len = a.seg_len; pi.seg_base = 1; pi.seg_zero_start = 0; pi.seg0_store = 0;
         pi.seg_state_stride = (long long)a.B * a.H * DK * DK;
         pi.seg_rows = a.nseg - 1;
+        pi.state_out_t = 1;  // the transitions, transposed: the combine reads their columns as rows
 
         p.state_out = a.seg_sloc;
         p.partial = a.seg_partial;

@@ -70,7 +70,7 @@ struct PassArgs {
     float *seg_partial;     // [B,T,H,dv] fp32
     float *seg_w;           // [B,T,H,dk] fp32
     float *seg_sloc;        // [nseg][B,H,dv,dk] fp32: final states from each segment's own start
-    float *seg_phi;         // [nseg-1][B,H,dk,dk] fp32: transitions of segments 1 .. nseg-1
+    float *seg_phi;         // [nseg-1][B,H,dk,dk] fp32: transitions of segments 1 .. nseg-1, transposed
     const float *seg_eye;   // [B,H,dk,dk] fp32 identity matrices
     const void *seg_vzero;  // H * max(dk, dv) zeros of the input type (v of the identity runs)
 };

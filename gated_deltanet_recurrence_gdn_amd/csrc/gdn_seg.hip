@@ -93,7 +93,6 @@ template <int DK, int DV>
 struct CombSmem {
     static constexpr int P = DK + 8;
     uint16_t sh[DV][P], sl[DV][P];  // the state's rows, split bf16 (A operand)
-    uint16_t th[DK][P], tl[DK][P];  // a transition, transposed, split bf16 (B operand)
 };
 
 template <int DK, int DV>
@@ -122,18 +121,27 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SegParams p) {
     const size_t pstride = (size_t)p.B * p.H * DK * DK;
 
     // the chain over segments 1 .. seg - 1; wave w owns the 16x16 tiles i = w + 4 j of
-    // the d_v x d_k state.  Each step's transition and S^0_end values are loaded one
-    // step ahead, so that their latency overlaps the previous step's products.
+    // the d_v x d_k state.  The identity runs wrote each transition transposed, so the
+    // B operand (column j of the transition, 8 consecutive k) is a row segment of it,
+    // loaded straight into registers; each step's transition columns and S^0_end
+    // values are loaded one step ahead.
     constexpr int NCG = DK / 16;                 // column groups of the state
     constexpr int NTW = (DV / 16) * NCG / 4;     // tiles per wave
-    constexpr int NPH = DK * DK / 4 / 256;       // float4 of a transition per thread
+    constexpr int NCW = NCG > 4 ? NCG / 4 : 1;   // distinct column groups per wave: (w + 4 jj) % NCG
     f32x4_t acc[NTW];
-    float4 v[NPH];
+    float4 v[NCW][2 * NKS];
     f32x4_t lo[NTW];
     auto load_phi = [&](int s1) {
-        const float *phi = p.phi + (s1 - 1) * pstride + (size_t)head * DK * DK;
+        const float *pt = p.phi + (s1 - 1) * pstride + (size_t)head * DK * DK;
 #pragma unroll
-        for (int it = 0; it < NPH; ++it) v[it] = *reinterpret_cast<const float4 *>(phi + 4 * (size_t)(threadIdx.x + 256 * it));
+        for (int jj = 0; jj < NCW; ++jj) {
+            const float *row = pt + (size_t)(16 * ((wid + 4 * jj) % NCG) + r16) * DK + 8 * g4;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                v[jj][2 * ks] = *reinterpret_cast<const float4 *>(row + 32 * ks);
+                v[jj][2 * ks + 1] = *reinterpret_cast<const float4 *>(row + 32 * ks + 4);
+            }
+        }
     };
     auto load_lo = [&](int s1) {
         const float *src = p.sloc + s1 * sstride + (size_t)head * DV * DK;
@@ -175,31 +183,29 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SegParams p) {
     }
 
     for (int s1 = 1; s1 < seg; ++s1) {
+        bf16x8_t bh[NCW][NKS], bl[NCW][NKS];
 #pragma unroll
-        for (int it = 0; it < NPH; ++it) {
-            const int i = threadIdx.x + 256 * it;
-            const int k = (4 * i) / DK, j0 = (4 * i) % DK;
-            const float vv[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+        for (int jj = 0; jj < NCW; ++jj)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) split1(vv[e], sm.th[j0 + e][k], sm.tl[j0 + e][k]);
-        }
+            for (int ks = 0; ks < NKS; ++ks) split8(v[jj][2 * ks], v[jj][2 * ks + 1], bh[jj][ks], bl[jj][ks]);
         if (s1 + 1 < seg) load_phi(s1 + 1);
-        __syncthreads();  // the state and the transition are staged
+        __syncthreads();  // the state is staged
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
-            const int i = wid + 4 * j, rg = i / NCG, cg = i % NCG;
+            const int i = wid + 4 * j, rg = i / NCG;
+            const int jj = j % NCW;  // column group (wid + 4 j) % NCG
             f32x4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const int k0 = 32 * ks + 8 * g4;
-                d = mfma_split(lds16(&sm.sh[16 * rg + r16][k0]), lds16(&sm.sl[16 * rg + r16][k0]),
-                               lds16(&sm.th[16 * cg + r16][k0]), lds16(&sm.tl[16 * cg + r16][k0]), d);
+                d = mfma_split(lds16(&sm.sh[16 * rg + r16][k0]), lds16(&sm.sl[16 * rg + r16][k0]), bh[jj][ks],
+                               bl[jj][ks], d);
             }
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc[j][m] = d[m] + lo[j][m];
         }
         if (s1 + 1 < seg) load_lo(s1 + 1);
-        __syncthreads();  // every read of the staged state and transition is done
+        __syncthreads();  // every read of the staged state is done
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
             const int i = wid + 4 * j, rg = i / NCG, cg = i % NCG;
