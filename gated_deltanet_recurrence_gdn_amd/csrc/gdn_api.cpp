@@ -45,8 +45,10 @@ namespace {
 // At most this many segments per call, each of at least SEG_MIN_CHUNKS 64-token chunks.
 constexpr int SEG_MAX = 8;
 constexpr int SEG_MIN_CHUNKS = 8;
-// Element offsets of the segment buffers inside gdn_ctx::seg (all fp32 but the zero
-// row, which is sized in floats too).
+// Offsets, in floats, of the segment buffers inside gdn_ctx::seg: the bf16 rows
+// (partial outputs and w, two values per float slot; d_v and d_k are even), then the
+// fp32 states, transitions and identities, then the zero row of v, sized in floats
+// too.
 struct SegLayout {
     size_t partial, w, sloc, phi, eye, vzero, total;
 };
@@ -55,8 +57,8 @@ SegLayout seg_layout(const gdn_config &c) {
     const size_t tok = (size_t)c.B * (size_t)c.max_T * c.H;
     const size_t st = (size_t)c.B * c.H * c.d_v * c.d_k, tr = (size_t)c.B * c.H * c.d_k * c.d_k;
     l.partial = 0;
-    l.w = l.partial + tok * c.d_v;
-    l.sloc = l.w + tok * c.d_k;
+    l.w = l.partial + tok * c.d_v / 2;
+    l.sloc = l.w + tok * c.d_k / 2;
     l.phi = l.sloc + SEG_MAX * st;
     l.eye = l.phi + (SEG_MAX - 1) * tr;
     l.vzero = l.eye + tr;

@@ -668,6 +668,7 @@ struct ChunkParams {
     long long seg_state_stride;
     int seg_rows;  // block rows (y) this parameter set covers; the launch's other rows use the second set
     int state_out_t;  // state_out written transposed ([d_k][d_v] per head)
+    void *seg_out;    // SWEEP_SEG: bf16 [B,T,H,d_v] rows of every run but segment 0's own
 };
 
 template <int DK>
@@ -1266,7 +1267,8 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p_arg, ChunkParam
         seg = p.seg_base + y;
         if (p.state_out) p.state_out += (size_t)y * p.seg_state_stride;
         if (p.seg_zero_start && seg > 0) p.state_in = nullptr;
-        p.out_mode = (p.seg0_store && seg == 0) ? OUT_STORE : OUT_PARTIAL;
+        if (!(p.seg0_store && seg == 0)) p.out = p.seg_out;
+        p.out_mode = OUT_STORE;
     }
     constexpr int ES = io_in_bytes(IO);
     static_assert(DK % 32 == 0 && DK <= 128, "d_k must be 32, 64 or 128");
@@ -1483,11 +1485,12 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.c0 = 0; p.c1 = nchunks;
     p.scale = (float)(1.0 / __builtin_sqrt((double)DK));
     p.state_out_t = 0;
+    p.seg_out = nullptr;
     const int nblk = p.nblk_dir * dirs;
     if (!a.both_dirs && a.nseg > 1) {
         // Segment-parallel causal form, one launch with a block row per segment run.
         // Rows 0 .. nseg-1: segment 0 from state_in, storing out; segments 1 .. nseg-1
-        // from zero into fp32 partials.  Rows nseg .. 2 nseg-2: segments 1 .. nseg-1
+        // from zero, storing bf16 rows o^0.  Rows nseg .. 2 nseg-2: segments 1 .. nseg-1
         // again, from the identity with v = 0 (d_v = d_k): row i of that run's state is
         // e_i^T times the product of the segment's per-token transitions, so its
         // outputs are w_t = (that product up to t) q_t / sqrt(d_k) and its final state
@@ -1506,14 +1509,15 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
         pi.state_in = a.seg_eye;
         pi.state_out = a.seg_phi;
         pi.out = nullptr;
-        pi.partial = a.seg_w;
+        pi.partial = nullptr;
+        pi.seg_out = a.seg_w;
         pi.seg_len = a.seg_len; pi.seg_base = 1; pi.seg_zero_start = 0; pi.seg0_store = 0;
         pi.seg_state_stride = (long long)a.B * a.H * DK * DK;
         pi.seg_rows = a.nseg - 1;
         pi.state_out_t = 1;  // the transitions, transposed: the combine reads their columns as rows
 
         p.state_out = a.seg_sloc;
-        p.partial = a.seg_partial;
+        p.seg_out = a.seg_partial;
         p.seg_len = a.seg_len; p.seg_base = 0; p.seg_zero_start = 1; p.seg0_store = 1;
         p.seg_state_stride = (long long)a.B * a.H * a.dv * DK;
         p.seg_rows = a.nseg;

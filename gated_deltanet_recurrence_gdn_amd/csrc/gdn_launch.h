@@ -67,8 +67,8 @@ struct PassArgs {
     // then the true start states follow segment by segment and each later token's
     // output is corrected by S_start w_t.
     int nseg, seg_len;
-    float *seg_partial;     // [B,T,H,dv] fp32
-    float *seg_w;           // [B,T,H,dk] fp32
+    void *seg_partial;      // [B,T,H,dv] bf16
+    void *seg_w;            // [B,T,H,dk] bf16
     float *seg_sloc;        // [nseg][B,H,dv,dk] fp32: final states from each segment's own start
     float *seg_phi;         // [nseg-1][B,H,dk,dk] fp32: transitions of segments 1 .. nseg-1, transposed
     const float *seg_eye;   // [B,H,dk,dk] fp32 identity matrices

@@ -5,16 +5,18 @@
 //   S_t = S_start P_t + S_t^0,   P_t = M_first ... M_t,
 //   o_t = S_t q_t / sqrt(d_k) = S_start w_t + o_t^0,   w_t = P_t q_t / sqrt(d_k),
 // where S^0, o^0 are the same segment run from a zero state.  The chunk kernel has
-// already produced, per segment s > 0: o^0 (fp32 partials), the segment's own final
+// already produced, per segment s > 0: o^0 (bf16 rows), the segment's own final
 // state S^0_end (seg_sloc[s]), and, from a run with v = 0 started at the identity,
-// w_t (its outputs) and P_end (its final state, seg_phi[s - 1]).  Segment 0 ran from
+// w_t (its bf16 outputs) and P_end (its final state, written transposed: seg_phi[s - 1]).
+// Segment 0 ran from
 // the caller's state, so its outputs are final and seg_sloc[0] is the true state at
 // the end of segment 0.  Here:
 //   S_start[1] = seg_sloc[0],  S_start[s+1] = S_start[s] P_end[s] + seg_sloc[s],
 //   state_out = S_start[nseg-1] P_end[nseg-1] + seg_sloc[nseg-1],
 //   out_t = round(o^0_t + S_start[s] w_t) for every token t of segments s > 0,
-// all on bf16 MFMA with each fp32 operand split into a bf16 high and low part (three
-// products, ~2^-16 relative), in one launch (seg_combine_kernel).
+// all on bf16 MFMA in one launch (seg_combine_kernel).  Each fp32 state operand is
+// split into a bf16 high part and the bf16 rounding of the rest (~2^-16 relative):
+// three products per step of the chain, two per correction, whose w is bf16 already.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -24,13 +26,12 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-
 struct SegParams {
     const float *sloc;   // [nseg][B,H,dv,dk]
-    const float *phi;    // [nseg-1][B,H,dk,dk]
+    const float *phi;    // [nseg-1][B,H,dk,dk], each transition transposed
     float *state_out;    // [B,H,dv,dk] or nullptr
-    const float *w;      // [B,T,H,dk]
-    const float *part;   // [B,T,H,dv]
+    const uint16_t *w;     // [B,T,H,dk] bf16
+    const uint16_t *part;  // [B,T,H,dv] bf16
     uint16_t *out;       // [B,T,H,dv] bf16
     long long T;
     int B, H, dv, nseg, seg_len;
@@ -82,10 +83,11 @@ __device__ __forceinline__ f32x4_t mfma_split(bf16x8_t ah, bf16x8_t al, bf16x8_t
 // steps rather than wait on each other), then:
 //   correction block: O^T (columns x tokens) = S_start W^T for each 16-token group
 //     (waves take groups w, w + 4, ...) and each 16-column group of d_v; the A operand is
-//     the state's rows from LDS, the B operand the lane's token row of W (fp32 from the
-//     identity run, split in registers); the accumulator lane (16 g + r) holds columns
-//     4 g .. 4 g + 3 of token r: out = round(partial + O), one 8-byte store.  The next
-//     group's W row and partials are loaded before the current group's products.
+//     the state's rows (high and low part) from LDS, the B operand 16 bytes of the lane's
+//     token row of W straight from memory; the accumulator lane (16 g + r) holds columns
+//     4 g .. 4 g + 3 of token r: out = round(o^0 + O), one 8-byte load and one 8-byte
+//     store.  The next group's W row and o^0 are loaded before the current group's
+//     products.
 //   state block: writes the chain's final state, fp32, to state_out.
 constexpr int CORR_CHUNKS = 2;  // runs of 1 or 4 chunks measured 1-8% slower on the short workloads
 
@@ -234,26 +236,24 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SegParams p) {
     const long long t_end = 64 * c_end < p.T ? 64 * c_end : p.T;
     const int ngroups = (int)((t_end - t_begin + 15) / 16);
     constexpr int NVG = DV / 16;  // column groups of out
-    auto load = [&](int grp, float4 (&w)[2 * NKS], float4 (&z)[NVG]) {
+    auto load = [&](int grp, bf16x8_t (&w)[NKS], uint2 (&z)[NVG]) {
         long long t = t_begin + 16 * grp + r16;
         if (t >= p.T) t = p.T - 1;  // loads stay in bounds; stores only below t_end
-        const float *row = p.w + (((size_t)b * p.T + t) * p.H + h) * DK + 8 * g4;
+        const uint16_t *row = p.w + (((size_t)b * p.T + t) * p.H + h) * DK + 8 * g4;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            w[2 * ks] = *reinterpret_cast<const float4 *>(row + 32 * ks);
-            w[2 * ks + 1] = *reinterpret_cast<const float4 *>(row + 32 * ks + 4);
-        }
-        const float *zr = p.part + (((size_t)b * p.T + t) * p.H + h) * DV + 4 * g4;
+        for (int ks = 0; ks < NKS; ++ks) w[ks] = *reinterpret_cast<const bf16x8_t *>(row + 32 * ks);
+        const uint16_t *zr = p.part + (((size_t)b * p.T + t) * p.H + h) * DV + 4 * g4;
 #pragma unroll
-        for (int cg = 0; cg < NVG; ++cg) z[cg] = *reinterpret_cast<const float4 *>(zr + 16 * cg);
+        for (int cg = 0; cg < NVG; ++cg) z[cg] = *reinterpret_cast<const uint2 *>(zr + 16 * cg);
     };
-    float4 wa[2 * NKS], za[NVG];
+    bf16x8_t wa[NKS];
+    uint2 za[NVG];
     if (wid < ngroups) load(wid, wa, za);
     for (int grp = wid; grp < ngroups; grp += 4) {
-        bf16x8_t bh[NKS], bl[NKS];
+        bf16x8_t wb[NKS];
+        uint2 z[NVG];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) split8(wa[2 * ks], wa[2 * ks + 1], bh[ks], bl[ks]);
-        float4 z[NVG];
+        for (int ks = 0; ks < NKS; ++ks) wb[ks] = wa[ks];
 #pragma unroll
         for (int cg = 0; cg < NVG; ++cg) z[cg] = za[cg];
         if (grp + 4 < ngroups) load(grp + 4, wa, za);
@@ -265,11 +265,13 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SegParams p) {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const int k0 = 32 * ks + 8 * g4;
-                d = mfma_split(lds16(&sm.sh[16 * cg + r16][k0]), lds16(&sm.sl[16 * cg + r16][k0]), bh[ks], bl[ks], d);
+                d = mfma16k32(lds16(&sm.sh[16 * cg + r16][k0]), wb[ks], d);
+                d = mfma16k32(lds16(&sm.sl[16 * cg + r16][k0]), wb[ks], d);
             }
             if (t < t_end)
-                *reinterpret_cast<uint2 *>(orow + 16 * cg) = make_uint2(
-                    pack_bf16x2(z[cg].x + d[0], z[cg].y + d[1]), pack_bf16x2(z[cg].z + d[2], z[cg].w + d[3]));
+                *reinterpret_cast<uint2 *>(orow + 16 * cg) =
+                    make_uint2(pack_bf16x2(bf16_lo(z[cg].x) + d[0], bf16_hi(z[cg].x) + d[1]),
+                               pack_bf16x2(bf16_lo(z[cg].y) + d[2], bf16_hi(z[cg].y) + d[3]));
         }
     }
 }
@@ -280,8 +282,8 @@ hipError_t launch_seg_dv(const PassArgs &a, hipStream_t stream) {
     p.sloc = a.seg_sloc;
     p.phi = a.seg_phi;
     p.state_out = a.state_out;
-    p.w = a.seg_w;
-    p.part = a.seg_partial;
+    p.w = static_cast<const uint16_t *>(a.seg_w);
+    p.part = static_cast<const uint16_t *>(a.seg_partial);
     p.out = static_cast<uint16_t *>(a.out);
     p.T = a.T;
     p.B = a.B; p.H = a.H; p.dv = DV; p.nseg = a.nseg; p.seg_len = a.seg_len;

@@ -97,13 +97,14 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8 = 2 } gdn_dtype;
  * concurrently: segment 0 from state_in, each later one from zero and, beside it,
  * from the identity with v = 0, which gives the segment's transition; a combine
  * then forms each segment's true start state and adds its contribution to the
- * outputs (the recurrence is affine in the state; the correction products run on
- * bf16 MFMA with split fp32 operands).  The segment count is the largest whose
- * blocks fit on the device at once.  Results stay within the stated tolerances,
- * but are not bit-identical to one sweep, nor across different splits of a
- * sequence into calls.  Costs per handle: fp32 [B, max_T, H, d_v + d_k] plus
- * 8 d_v x d_k states and 8 d_k x d_k matrices per (b, h).  Without this flag
- * every call is one sweep. */
+ * outputs (the recurrence is affine in the state; the later segments' own outputs
+ * and the identity runs' outputs pass through bf16 rows, and the correction
+ * products run on bf16 MFMA with the fp32 states split in two bf16 parts).  The
+ * segment count is the largest whose blocks fit on the device at once.  Results
+ * stay within the stated tolerances, but are not bit-identical to one sweep, nor
+ * across different splits of a sequence into calls.  Costs per handle: bf16
+ * [B, max_T, H, d_v + d_k] plus fp32 8 d_v x d_k states and 8 d_k x d_k matrices
+ * per (b, h).  Without this flag every call is one sweep. */
 #define GDN_FLAG_SEGMENTS 2u
 
 typedef struct {
