@@ -82,12 +82,11 @@ __device__ __forceinline__ f32x4_t mfma_split(bf16x8_t ah, bf16x8_t al, bf16x8_t
 // correction block, nseg - 1 for the state block; blocks of one segment repeat the same
 // steps rather than wait on each other), then:
 //   correction block: O^T (columns x tokens) = S_start W^T for each 16-token group
-//     (waves take groups w, w + 4, ...) and each 16-column group of d_v; the A operand is
+//     (wave w takes groups w and w + 4) and each 16-column group of d_v; the A operand is
 //     the state's rows (high and low part) from LDS, the B operand 16 bytes of the lane's
 //     token row of W straight from memory; the accumulator lane (16 g + r) holds columns
 //     4 g .. 4 g + 3 of token r: out = round(o^0 + O), one 8-byte load and one 8-byte
-//     store.  The next group's W row and o^0 are loaded before the current group's
-//     products.
+//     store.
 //   state block: writes the chain's final state, fp32, to state_out.
 constexpr int CORR_CHUNKS = 2;  // runs of 1 or 4 chunks measured 1-8% slower on the short workloads
 
@@ -125,88 +124,87 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SegParams p) {
     // the chain over segments 1 .. seg - 1; wave w owns the 16x16 tiles i = w + 4 j of
     // the d_v x d_k state.  The identity runs wrote each transition transposed, so the
     // B operand (column j of the transition, 8 consecutive k) is a row segment of it,
-    // loaded straight into registers; each step's transition columns and S^0_end
-    // values are loaded one step ahead.
+    // loaded straight into registers.  The tiles are taken one column group of the
+    // transition at a time, and each group's columns are loaded while the previous
+    // group's products run, so that one group's operands are live.  Each step's
+    // S^0_end tiles are loaded into the accumulators, which the products add to.
     constexpr int NCG = DK / 16;                 // column groups of the state
     constexpr int NTW = (DV / 16) * NCG / 4;     // tiles per wave
     constexpr int NCW = NCG > 4 ? NCG / 4 : 1;   // distinct column groups per wave: (w + 4 jj) % NCG
     f32x4_t acc[NTW];
-    float4 v[NCW][2 * NKS];
-    f32x4_t lo[NTW];
-    auto load_phi = [&](int s1) {
-        const float *pt = p.phi + (s1 - 1) * pstride + (size_t)head * DK * DK;
+    float4 v[2 * NKS];
+    auto load_phi = [&](int s1, int jj) {  // column group (w + 4 jj) % NCG of step s1's transition
+        const float *row = p.phi + (s1 - 1) * pstride + (size_t)head * DK * DK +
+                           (size_t)(16 * ((wid + 4 * jj) % NCG) + r16) * DK + 8 * g4;
 #pragma unroll
-        for (int jj = 0; jj < NCW; ++jj) {
-            const float *row = pt + (size_t)(16 * ((wid + 4 * jj) % NCG) + r16) * DK + 8 * g4;
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                v[jj][2 * ks] = *reinterpret_cast<const float4 *>(row + 32 * ks);
-                v[jj][2 * ks + 1] = *reinterpret_cast<const float4 *>(row + 32 * ks + 4);
-            }
+        for (int ks = 0; ks < NKS; ++ks) {
+            v[2 * ks] = *reinterpret_cast<const float4 *>(row + 32 * ks);
+            v[2 * ks + 1] = *reinterpret_cast<const float4 *>(row + 32 * ks + 4);
         }
     };
-    auto load_lo = [&](int s1) {
+    auto load_acc = [&](int s1) {  // acc = S^0_end[s1]
         const float *src = p.sloc + s1 * sstride + (size_t)head * DV * DK;
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
             const int i = wid + 4 * j, rg = i / NCG, cg = i % NCG;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) lo[j][m] = src[(size_t)(16 * rg + 4 * g4 + m) * DK + 16 * cg + r16];
+            for (int m = 0; m < 4; ++m) acc[j][m] = src[(size_t)(16 * rg + 4 * g4 + m) * DK + 16 * cg + r16];
         }
     };
     if (seg > 1) {
-        load_phi(1);
-        load_lo(1);
+        load_phi(1, 0);
+        load_acc(1);
     }
     // S^0_end[0], the true state at the end of segment 0, split into LDS
     {
         const float *src = p.sloc + (size_t)head * DV * DK;
-        constexpr int NST = (DV * DK / 8 + 255) / 256;
-        float4 sv[2 * NST];
+        constexpr int NST = (DV * DK / 8 + 255) / 256;  // 8-value runs per thread
+        constexpr int BATCH = NST < 4 ? NST : 4;          // of which this many are in flight
 #pragma unroll
-        for (int it = 0; it < NST; ++it) {
-            const int i = threadIdx.x + 256 * it;
-            if (i < DV * DK / 8) {
-                sv[2 * it] = *reinterpret_cast<const float4 *>(src + 8 * (size_t)i);
-                sv[2 * it + 1] = *reinterpret_cast<const float4 *>(src + 8 * (size_t)i + 4);
+        for (int i0 = 0; i0 < NST; i0 += BATCH) {
+            float4 sv[2 * BATCH];
+#pragma unroll
+            for (int it = 0; it < BATCH; ++it) {
+                const int i = threadIdx.x + 256 * (i0 + it);
+                if (i < DV * DK / 8) {
+                    sv[2 * it] = *reinterpret_cast<const float4 *>(src + 8 * (size_t)i);
+                    sv[2 * it + 1] = *reinterpret_cast<const float4 *>(src + 8 * (size_t)i + 4);
+                }
             }
-        }
 #pragma unroll
-        for (int it = 0; it < NST; ++it) {
-            const int i = threadIdx.x + 256 * it;
-            if (i < DV * DK / 8) {
-                const int c = (8 * i) / DK, k0 = (8 * i) % DK;
-                bf16x8_t h8, l8;
-                split8(sv[2 * it], sv[2 * it + 1], h8, l8);
-                *reinterpret_cast<bf16x8_t *>(&sm.sh[c][k0]) = h8;
-                *reinterpret_cast<bf16x8_t *>(&sm.sl[c][k0]) = l8;
+            for (int it = 0; it < BATCH; ++it) {
+                const int i = threadIdx.x + 256 * (i0 + it);
+                if (i < DV * DK / 8) {
+                    const int c = (8 * i) / DK, k0 = (8 * i) % DK;
+                    bf16x8_t h8, l8;
+                    split8(sv[2 * it], sv[2 * it + 1], h8, l8);
+                    *reinterpret_cast<bf16x8_t *>(&sm.sh[c][k0]) = h8;
+                    *reinterpret_cast<bf16x8_t *>(&sm.sl[c][k0]) = l8;
+                }
             }
         }
     }
 
     for (int s1 = 1; s1 < seg; ++s1) {
-        bf16x8_t bh[NCW][NKS], bl[NCW][NKS];
-#pragma unroll
-        for (int jj = 0; jj < NCW; ++jj)
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) split8(v[jj][2 * ks], v[jj][2 * ks + 1], bh[jj][ks], bl[jj][ks]);
-        if (s1 + 1 < seg) load_phi(s1 + 1);
         __syncthreads();  // the state is staged
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-            const int i = wid + 4 * j, rg = i / NCG;
-            const int jj = j % NCW;  // column group (wid + 4 j) % NCG
-            f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+        for (int jj = 0; jj < NCW; ++jj) {
+            bf16x8_t bh[NKS], bl[NKS];
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const int k0 = 32 * ks + 8 * g4;
-                d = mfma_split(lds16(&sm.sh[16 * rg + r16][k0]), lds16(&sm.sl[16 * rg + r16][k0]), bh[jj][ks],
-                               bl[jj][ks], d);
+            for (int ks = 0; ks < NKS; ++ks) split8(v[2 * ks], v[2 * ks + 1], bh[ks], bl[ks]);
+            if (jj + 1 < NCW) load_phi(s1, jj + 1);
+            else if (s1 + 1 < seg) load_phi(s1 + 1, 0);
+#pragma unroll
+            for (int j = jj; j < NTW; j += NCW) {
+                const int rg = (wid + 4 * j) / NCG;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int k0 = 32 * ks + 8 * g4;
+                    acc[j] = mfma_split(lds16(&sm.sh[16 * rg + r16][k0]), lds16(&sm.sl[16 * rg + r16][k0]), bh[ks],
+                                        bl[ks], acc[j]);
+                }
             }
-#pragma unroll
-            for (int m = 0; m < 4; ++m) acc[j][m] = d[m] + lo[j][m];
         }
-        if (s1 + 1 < seg) load_lo(s1 + 1);
         __syncthreads();  // every read of the staged state is done
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
@@ -219,6 +217,7 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SegParams p) {
                 sm.sl[16 * rg + 4 * g4 + m][16 * cg + r16] = ll;
             }
         }
+        if (s1 + 1 < seg) load_acc(s1 + 1);
     }
     if (state_blk) {
 #pragma unroll
@@ -246,33 +245,37 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SegParams p) {
 #pragma unroll
         for (int cg = 0; cg < NVG; ++cg) z[cg] = *reinterpret_cast<const uint2 *>(zr + 16 * cg);
     };
-    bf16x8_t wa[NKS];
-    uint2 za[NVG];
-    if (wid < ngroups) load(wid, wa, za);
-    for (int grp = wid; grp < ngroups; grp += 4) {
-        bf16x8_t wb[NKS];
-        uint2 z[NVG];
+    // wave w corrects token groups w and w + 4 together: each A operand read from LDS
+    // serves both groups' products, and no operand is held across groups
+    static_assert(CORR_CHUNKS == 2, "the groups of a correction block are two per wave");
+    if (wid >= ngroups) return;
+    bf16x8_t w0[NKS], w1[NKS];
+    uint2 z0[NVG], z1[NVG];
+    load(wid, w0, z0);
+    load(wid + 4, w1, z1);  // clamped rows when past the end: products unused
+    const long long t0 = t_begin + 16 * wid + r16, t1 = t0 + 64;
+    uint16_t *orow0 = p.out + (((size_t)b * p.T + (t0 < p.T ? t0 : p.T - 1)) * p.H + h) * DV + 4 * g4;
+    uint16_t *orow1 = p.out + (((size_t)b * p.T + (t1 < p.T ? t1 : p.T - 1)) * p.H + h) * DV + 4 * g4;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) wb[ks] = wa[ks];
+    for (int cg = 0; cg < NVG; ++cg) {
+        f32x4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int cg = 0; cg < NVG; ++cg) z[cg] = za[cg];
-        if (grp + 4 < ngroups) load(grp + 4, wa, za);
-        const long long t = t_begin + 16 * grp + r16;
-        uint16_t *orow = p.out + (((size_t)b * p.T + (t < p.T ? t : p.T - 1)) * p.H + h) * DV + 4 * g4;
-#pragma unroll
-        for (int cg = 0; cg < NVG; ++cg) {
-            f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const int k0 = 32 * ks + 8 * g4;
-                d = mfma16k32(lds16(&sm.sh[16 * cg + r16][k0]), wb[ks], d);
-                d = mfma16k32(lds16(&sm.sl[16 * cg + r16][k0]), wb[ks], d);
-            }
-            if (t < t_end)
-                *reinterpret_cast<uint2 *>(orow + 16 * cg) =
-                    make_uint2(pack_bf16x2(bf16_lo(z[cg].x) + d[0], bf16_hi(z[cg].x) + d[1]),
-                               pack_bf16x2(bf16_lo(z[cg].y) + d[2], bf16_hi(z[cg].y) + d[3]));
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int k0 = 32 * ks + 8 * g4;
+            const bf16x8_t ah = lds16(&sm.sh[16 * cg + r16][k0]), al = lds16(&sm.sl[16 * cg + r16][k0]);
+            d0 = mfma16k32(ah, w0[ks], d0);
+            d1 = mfma16k32(ah, w1[ks], d1);
+            d0 = mfma16k32(al, w0[ks], d0);
+            d1 = mfma16k32(al, w1[ks], d1);
         }
+        if (t0 < t_end)
+            *reinterpret_cast<uint2 *>(orow0 + 16 * cg) =
+                make_uint2(pack_bf16x2(bf16_lo(z0[cg].x) + d0[0], bf16_hi(z0[cg].x) + d0[1]),
+                           pack_bf16x2(bf16_lo(z0[cg].y) + d0[2], bf16_hi(z0[cg].y) + d0[3]));
+        if (t1 < t_end)
+            *reinterpret_cast<uint2 *>(orow1 + 16 * cg) =
+                make_uint2(pack_bf16x2(bf16_lo(z1[cg].x) + d1[0], bf16_hi(z1[cg].x) + d1[1]),
+                           pack_bf16x2(bf16_lo(z1[cg].y) + d1[2], bf16_hi(z1[cg].y) + d1[3]));
     }
 }
 
