@@ -319,6 +319,7 @@ struct TmParams {
     long long qk_ts, qk_bs;
     int B, H, nchunks, reverse;
     int c0, nc;       // the chunks of this launch: [c0, c0 + nc)
+    int nblk, xcd_remap;  // the launch's block count; 1: blocks remapped so each XCD takes a contiguous range
 };
 
 // K is dead once the Gram products are in registers, so Tm and A reuse its
@@ -527,8 +528,11 @@ __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // Head fastest: blocks that run together read the same tokens of all heads,
-    // which lie next to each other in the token-major K.
-    long long L = blockIdx.x;
+    // which lie next to each other in the token-major K and the [B, T, H] gates.
+    // Blocks are dispatched round-robin over the 8 XCDs (linear id mod 8); with the
+    // remap each XCD takes a contiguous range of that order, so the gate lines that
+    // the heads of a chunk share are fetched into one XCD's L2, not into eight.
+    long long L = p.xcd_remap ? (long long)(blockIdx.x & 7) * (p.nblk >> 3) + (blockIdx.x >> 3) : blockIdx.x;
     const int h = (int)(L % p.H);
     L /= p.H;
     const int c = p.c0 + (int)(L % p.nc);
@@ -1450,19 +1454,23 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     // side stream, those inverses are formed there, beside the first launch.
     const int n1 = (nchunks + 1) / 2;
     const bool side = a.both_dirs && a.bidi_state && a.side_stream && n1 < nchunks;
-    t.c0 = 0;
-    t.nc = side ? n1 : nchunks;
-    hipLaunchKernelGGL((tm_kernel<DK, IO, PRO>), dim3((unsigned)(dirs * a.B * a.H * t.nc)), dim3(256), 0, stream, t);
+    auto set_range = [&](int c0, int nc) {
+        t.c0 = c0;
+        t.nc = nc;
+        t.nblk = dirs * a.B * a.H * nc;
+        t.xcd_remap = t.nblk % 8 == 0;
+    };
+    set_range(0, side ? n1 : nchunks);
+    hipLaunchKernelGGL((tm_kernel<DK, IO, PRO>), dim3((unsigned)t.nblk), dim3(256), 0, stream, t);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipStream_t s2 = static_cast<hipStream_t>(a.side_stream);
     hipEvent_t fork = static_cast<hipEvent_t>(a.ev_fork), join = static_cast<hipEvent_t>(a.ev_join);
     if (side) {
-        t.c0 = n1;
-        t.nc = nchunks - n1;
+        set_range(n1, nchunks - n1);
         if ((e = hipEventRecord(fork, stream)) != hipSuccess) return e;
         if ((e = hipStreamWaitEvent(s2, fork, 0)) != hipSuccess) return e;
-        hipLaunchKernelGGL((tm_kernel<DK, IO, PRO>), dim3((unsigned)(dirs * a.B * a.H * t.nc)), dim3(256), 0, s2, t);
+        hipLaunchKernelGGL((tm_kernel<DK, IO, PRO>), dim3((unsigned)t.nblk), dim3(256), 0, s2, t);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = hipEventRecord(join, s2)) != hipSuccess) return e;
     }
