@@ -127,7 +127,8 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SegParams p) {
     // loaded straight into registers.  The tiles are taken one column group of the
     // transition at a time, and each group's columns are loaded while the previous
     // group's products run, so that one group's operands are live.  Each step's
-    // S^0_end tiles are loaded into the accumulators, which the products add to.
+    // S^0_end tiles are loaded into the accumulators, which the products add to; with
+    // at most 4 tiles per wave, where registers allow, they are loaded a step ahead.
     constexpr int NCG = DK / 16;                 // column groups of the state
     constexpr int NTW = (DV / 16) * NCG / 4;     // tiles per wave
     constexpr int NCW = NCG > 4 ? NCG / 4 : 1;   // distinct column groups per wave: (w + 4 jj) % NCG
@@ -142,18 +143,22 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SegParams p) {
             v[2 * ks + 1] = *reinterpret_cast<const float4 *>(row + 32 * ks + 4);
         }
     };
-    auto load_acc = [&](int s1) {  // acc = S^0_end[s1]
+    auto load_tiles = [&](int s1, f32x4_t (&dst)[NTW]) {  // dst = this wave's tiles of S^0_end[s1]
         const float *src = p.sloc + s1 * sstride + (size_t)head * DV * DK;
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
             const int i = wid + 4 * j, rg = i / NCG, cg = i % NCG;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) acc[j][m] = src[(size_t)(16 * rg + 4 * g4 + m) * DK + 16 * cg + r16];
+            for (int m = 0; m < 4; ++m) dst[j][m] = src[(size_t)(16 * rg + 4 * g4 + m) * DK + 16 * cg + r16];
         }
     };
+    constexpr bool AHEAD = NTW <= 4;
+    f32x4_t nxt[AHEAD ? NTW : 1];
     if (seg > 1) {
         load_phi(1, 0);
-        load_acc(1);
+        load_tiles(1, acc);
+        if constexpr (AHEAD)
+            if (seg > 2) load_tiles(2, nxt);
     }
     // S^0_end[0], the true state at the end of segment 0, split into LDS
     {
@@ -217,7 +222,15 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SegParams p) {
                 sm.sl[16 * rg + 4 * g4 + m][16 * cg + r16] = ll;
             }
         }
-        if (s1 + 1 < seg) load_acc(s1 + 1);
+        if (s1 + 1 < seg) {
+            if constexpr (AHEAD) {
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) acc[j] = nxt[j];
+                if (s1 + 2 < seg) load_tiles(s1 + 2, nxt);
+            } else {
+                load_tiles(s1 + 1, acc);
+            }
+        }
     }
     if (state_blk) {
 #pragma unroll
