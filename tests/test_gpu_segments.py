@@ -57,6 +57,36 @@ def test_dims_ragged_with_state(dk, dv, T, H):
     check(f"dk={dk} dv={dv} T={T} H={H}, state_in", x, s0)
 
 
+@pytest.mark.parametrize("B,H,dk,dv,T", [(2, 4, 128, 128, 3000), (3, 2, 64, 64, 2100)])
+def test_batch_with_state(B, H, dk, dv, T):
+    """Several batch elements: every (b, h) has its own segment states, transitions and
+    start states (4 segments each)."""
+    x = inputs.make_inputs(B, T, H, dk, dv, "bf16", seed=100 * B + T)
+    s0 = state0(B, H, dv, dk, seed=T + 1)
+    check(f"B={B} H={H} dk={dk} dv={dv} T={T}, state_in", x, s0)
+
+
+def test_no_state_out():
+    """state_out NULL: the combine launches no state row (5 segments)."""
+    B, H, d, T = 2, 3, 64, 2600
+    x = inputs.make_inputs(B, T, H, d, d, "bf16", seed=31)
+    s0 = state0(B, H, d, d, seed=32)
+    d_ = dev(x)
+    outs = {}
+    for seg in (True, False):
+        g = gb.GDN(B, H, d, d, "bf16", max_T=T, segments=seg)
+        o, st = g.forward(d_["q"], d_["k"], d_["v"], d_["beta"], d_["decay"], state_in=s0.cuda(),
+                          return_state=False)
+        torch.cuda.synchronize()
+        g.close()
+        assert st is None
+        outs[seg] = o
+    print("[gpu case] no state_out, segments", flush=True)
+    assert not torch.equal(outs[True], outs[False])
+    o64, _ = oracle.forward(**x, state_in=s0)
+    parity_by_head("no state_out, segments", outs[True], o64, TOL["bf16"])
+
+
 def test_long_memory_heads():
     """Decay close to 1 (a = exp(-softplus(x)), x ~ N(-2, 1)): the start state reaches
     every later token, so the correction carries most of each output."""
