@@ -1189,28 +1189,30 @@ __device__ __forceinline__ void load_gates(const Ctx &x, int c, int lane, GateRe
     g.r = x.grec[(size_t)c * C + lane];
 }
 
-// The other direction's fp32 outputs of a chunk's tokens for this block's 32 d_v
-// columns: lane l holds row 8 s + l / 8, columns 4 (l % 8) .. + 3 (rows past the
-// end of a short final chunk re-read its last token; they are never used).
+// The other direction's outputs of a chunk's tokens for this block's 32 d_v columns,
+// bf16 rows written by the first launch: lane l holds row 8 s + l / 8, columns
+// 4 (l % 8) .. + 3 (rows past the end of a short final chunk re-read its last token;
+// they are never used).  Widened to fp32 when staged.
 struct PartRows {
-    float4 r[8];
+    uint2 r[8];
 };
-__device__ __forceinline__ PartRows load_part(const Ctx &x, const float *other_b, int c, int lane) {
+__device__ __forceinline__ PartRows load_part(const Ctx &x, const uint16_t *other_b, int c, int lane) {
     PartRows d;
     const int nt = x.ntok(c);
 #pragma unroll
     for (int s_ = 0; s_ < 8; ++s_) {
         const int j = 8 * s_ + (lane >> 3);
-        const float *src = other_b + (size_t)x.tok(c, j < nt ? j : nt - 1) * x.rso + 4 * (lane & 7);
-        const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(src));
-        d.r[s_] = make_float4(v[0], v[1], v[2], v[3]);
+        const uint16_t *src = other_b + (size_t)x.tok(c, j < nt ? j : nt - 1) * x.rso + 4 * (lane & 7);
+        d.r[s_] = *reinterpret_cast<const uint2 *>(src);
     }
     return d;
 }
 __device__ __forceinline__ void store_part(int c, const PartRows &d, int lane) {
     PartTile &pt = part_tiles()[c & 1];
 #pragma unroll
-    for (int s_ = 0; s_ < 8; ++s_) *reinterpret_cast<float4 *>(&pt[8 * s_ + (lane >> 3)][4 * (lane & 7)]) = d.r[s_];
+    for (int s_ = 0; s_ < 8; ++s_)
+        *reinterpret_cast<float4 *>(&pt[8 * s_ + (lane >> 3)][4 * (lane & 7)]) =
+            make_float4(bf16_lo(d.r[s_].x), bf16_hi(d.r[s_].x), bf16_lo(d.r[s_].y), bf16_hi(d.r[s_].y));
 }
 
 template <int DK, bool PRO>
@@ -1321,12 +1323,17 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p_arg, ChunkParam
     // the outputs of chunk c1 - 1), two per loop trip so that register sets
     // alternate at compile time, with one barrier each.
     const int c0 = x.c0, c1 = x.c1;
-    // out is bf16 for every input type this kernel takes
+    // out is bf16 for every input type this kernel takes.  The first launch of the
+    // bidirectional split stores each direction's outputs the same way, as bf16 rows of
+    // that direction's partial buffer, which the second launch reads back.
     void *out_b = reinterpret_cast<uint16_t *>(p.out) + tok0 * p.dv + dv0;
+    if constexpr (SW == SWEEP_FIRST)
+        out_b = reinterpret_cast<uint16_t *>(dir ? p.partial_rev : p.partial) + tok0 * p.dv + dv0;
     float *part = dir ? p.partial_rev : p.partial;
     float *part_b = part ? part + tok0 * p.dv + dv0 : nullptr;
-    const float *other = dir ? p.partial : p.partial_rev;  // OUT_ADD_PARTIAL: the other direction's
-    const float *other_b = other ? other + tok0 * p.dv + dv0 : nullptr;
+    // OUT_ADD_PARTIAL: the other direction's bf16 rows
+    const uint16_t *other = reinterpret_cast<const uint16_t *>(dir ? p.partial : p.partial_rev);
+    const uint16_t *other_b = other ? other + tok0 * p.dv + dv0 : nullptr;
     if (wid < 2) {
         // The chain reads chunk c's Tm operands from the LDS slot the gate wave
         // filled in period c-1, so it never waits on a global load.
@@ -1541,7 +1548,8 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     }
     // Bidirectional form in two launches.  The first walks chunks [0, n1) of both
     // directions (the forward one tokens [0, 64 n1), the reverse one the last 64 n1
-    // tokens), writes fp32 partials and keeps each direction's state; the second
+    // tokens), writes its outputs as bf16 rows of the partial buffers and keeps each
+    // direction's fp32 state; the second
     // walks chunks [n1, n) from those states, and each direction adds the other's
     // partial of the same token -- written by the first launch -- before rounding
     // out once.  Tokens both first halves covered (at most 64, in the middle) are
@@ -1549,7 +1557,7 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.state_dir_stride = (long long)a.B * a.H * a.dv * DK;
     p.state_in = nullptr;
     p.state_out = a.bidi_state;
-    p.out_mode = OUT_PARTIAL;
+    p.out_mode = OUT_STORE;  // into the direction's partial buffer (see the kernel)
     p.c0 = 0; p.c1 = n1;
     hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO, SWEEP_FIRST>), dim3(nblk), dim3(NT), 0, stream, p, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1565,8 +1573,9 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     }
     const long long half = (long long)C * n1;
     const long long t0 = a.T - half > 0 ? a.T - half : 0, t1 = half < a.T ? half : a.T;
-    return launch_combine_rows(a.out, a.partial, a.partial_rev, a.B, a.T, (long long)a.H * a.dv, t0, t1, a.io,
-                               stream);
+    return launch_combine_rows_bf16(static_cast<uint16_t *>(a.out), reinterpret_cast<const uint16_t *>(a.partial),
+                                    reinterpret_cast<const uint16_t *>(a.partial_rev), a.B, a.T,
+                                    (long long)a.H * a.dv, t0, t1, stream);
 }
 
 template <int DK>

@@ -42,8 +42,8 @@ struct PassArgs {
     const float *state_in;  // [B,H,dv,dk] or nullptr (zeros)
     float *state_out;       // [B,H,dv,dk] or nullptr; may equal state_in
     void *out;              // [B,T,H,dv] fp32 or bf16 (OUT_STORE), see IoType
-    float *partial;         // [B,T,H,dv] fp32 (OUT_PARTIAL)
-    float *partial_rev;     // [B,T,H,dv] fp32, reverse direction's partial (both_dirs)
+    float *partial;         // [B,T,H,dv] fp32 (OUT_PARTIAL); bf16 rows in the MFMA kernel's bidi split
+    float *partial_rev;     // [B,T,H,dv] the same for the reverse direction (both_dirs)
     int B, H, dk, dv;
     long long T;
     int io;                 // IoType of q, k, v
@@ -104,10 +104,11 @@ hipError_t launch_chunk_general(const PassArgs &a, int C, hipStream_t stream);
 // in fp32 for IO_F32 and bf16 otherwise.
 hipError_t launch_combine(void *out, const float *partial, const float *partial_rev, long long n,
                           int io, hipStream_t stream);
-// The same over the token rows [t0, t1) of every batch element of [B, T, row] tensors
-// (row % 4 == 0).
-hipError_t launch_combine_rows(void *out, const float *partial, const float *partial_rev, int B, long long T,
-                               long long row, long long t0, long long t1, int io, hipStream_t stream);
+// out = round(partial + partial_rev) over the token rows [t0, t1) of every batch
+// element of [B, T, row] tensors (row % 4 == 0), all three bf16: the middle rows of the
+// bidirectional MFMA split, whose first launch stores bf16 partial rows.
+hipError_t launch_combine_rows_bf16(uint16_t *out, const uint16_t *partial, const uint16_t *partial_rev, int B,
+                                    long long T, long long row, long long t0, long long t1, hipStream_t stream);
 
 // Segment-parallel causal form, after the sweeps: state_out and, for every token of
 // segments > 0, out = round(seg_partial + S_start w_t), with each segment's true start

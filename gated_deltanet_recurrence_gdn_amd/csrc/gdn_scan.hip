@@ -461,45 +461,34 @@ __global__ __launch_bounds__(256) void combine_kernel(void *out, const float4 *p
     }
 }
 
-// combine_kernel over the token rows [t0, t1) of each batch element.
-template <bool BF16>
-__global__ __launch_bounds__(256) void combine_rows_kernel(void *out, const float4 *pa, const float4 *pb, int B,
+// The bidirectional MFMA split's middle rows: out = round(a + b) over the token rows
+// [t0, t1) of each batch element, a and b bf16 rows of the two directions (4 values
+// per thread).
+__global__ __launch_bounds__(256) void combine_rows_kernel(uint16_t *out, const uint2 *pa, const uint2 *pb, int B,
                                                            long long T, long long row4, long long t0, long long t1) {
     const long long per_b = (t1 - t0) * row4;
     const long long n4 = per_b * B;
     const long long stride = (long long)gridDim.x * blockDim.x;
-    const f32x4v_t *va = reinterpret_cast<const f32x4v_t *>(pa);
-    const f32x4v_t *vb = reinterpret_cast<const f32x4v_t *>(pb);
     for (long long j = (long long)blockIdx.x * blockDim.x + threadIdx.x; j < n4; j += stride) {
         const long long b = j / per_b;
         const long long i = (b * T + t0) * row4 + (j - b * per_b);
-        const f32x4v_t x = __builtin_nontemporal_load(va + i), y = __builtin_nontemporal_load(vb + i);
-        const f32x4v_t o = x + y;
-        if constexpr (BF16) {
-            const u32x2v_t w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-            __builtin_nontemporal_store(w, reinterpret_cast<u32x2v_t *>(out) + i);
-        } else {
-            __builtin_nontemporal_store(o, reinterpret_cast<f32x4v_t *>(out) + i);
-        }
+        const uint2 x = pa[i], y = pb[i];
+        reinterpret_cast<uint2 *>(out)[i] = make_uint2(pack_bf16x2(bf16_lo(x.x) + bf16_lo(y.x), bf16_hi(x.x) + bf16_hi(y.x)),
+                                                       pack_bf16x2(bf16_lo(x.y) + bf16_lo(y.y), bf16_hi(x.y) + bf16_hi(y.y)));
     }
 }
 
 }  // namespace
 
-hipError_t launch_combine_rows(void *out, const float *partial, const float *partial_rev, int B, long long T,
-                               long long row, long long t0, long long t1, int io, hipStream_t stream) {
+hipError_t launch_combine_rows_bf16(uint16_t *out, const uint16_t *partial, const uint16_t *partial_rev, int B,
+                                    long long T, long long row, long long t0, long long t1, hipStream_t stream) {
     if (t1 <= t0 || row % 4) return t1 <= t0 ? hipSuccess : hipErrorInvalidValue;
     const long long n4 = (long long)B * (t1 - t0) * (row / 4);
     long long nb = (n4 + 255) / 256;
     if (nb > 256 * 64) nb = 256 * 64;
-    const float4 *pa = reinterpret_cast<const float4 *>(partial);
-    const float4 *pb = reinterpret_cast<const float4 *>(partial_rev);
-    if (io != IO_F32)
-        hipLaunchKernelGGL(combine_rows_kernel<true>, dim3((unsigned)nb), dim3(256), 0, stream, out, pa, pb, B, T,
-                           row / 4, t0, t1);
-    else
-        hipLaunchKernelGGL(combine_rows_kernel<false>, dim3((unsigned)nb), dim3(256), 0, stream, out, pa, pb, B, T,
-                           row / 4, t0, t1);
+    hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)nb), dim3(256), 0, stream, out,
+                       reinterpret_cast<const uint2 *>(partial), reinterpret_cast<const uint2 *>(partial_rev), B, T,
+                       row / 4, t0, t1);
     return hipGetLastError();
 }
 
