@@ -30,10 +30,10 @@ struct gdn_ctx {
     size_t scratch_bytes = 0;
     uint16_t *tm = nullptr;    // per-chunk triangular inverses of the MFMA chunked kernel
     long long tm_chunks = 0;   // their capacity: directions x B x H x ceil(max_T / 64)
-    // bidirectional MFMA path: a second stream (default priority) and two events, so that
-    // the second half's inverses are formed beside the first sweep launch
+    // bidirectional MFMA path: a second stream (default priority) and three events, so that
+    // most inverses are formed beside the first sweep launches
     hipStream_t side = nullptr;
-    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_join_mid = nullptr;
     // segment-parallel causal form (GDN_FLAG_SEGMENTS on a handle the MFMA kernel serves):
     // one allocation holding the buffers gdn::PassArgs describes, and the CU count that
     // bounds the segment count
@@ -428,14 +428,16 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
         }
     }
     hipStream_t side = nullptr;
-    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_join_mid = nullptr;
     if (c.device >= 0 && (c.flags & GDN_FLAG_BIDI) && tm_chunks > 0) {
         DeviceGuard g(c.device);
         hipError_t e = hipStreamCreateWithFlags(&side, hipStreamNonBlocking);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_fork, hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_join, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_join_mid, hipEventDisableTiming);
         if (e != hipSuccess) {
             (void)hipGetLastError();
+            if (ev_join) (void)hipEventDestroy(ev_join);
             if (ev_fork) (void)hipEventDestroy(ev_fork);
             if (side) (void)hipStreamDestroy(side);
             if (seg) (void)hipFree(seg);
@@ -446,6 +448,7 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
     }
     gdn_ctx *h = new (std::nothrow) gdn_ctx;
     if (!h) {
+        if (ev_join_mid) (void)hipEventDestroy(ev_join_mid);
         if (ev_join) (void)hipEventDestroy(ev_join);
         if (ev_fork) (void)hipEventDestroy(ev_fork);
         if (side) (void)hipStreamDestroy(side);
@@ -462,6 +465,7 @@ int gdn_create(const gdn_config *cfg, gdn_handle *out_h) {
     h->side = side;
     h->ev_fork = ev_fork;
     h->ev_join = ev_join;
+    h->ev_join_mid = ev_join_mid;
     h->seg = seg;
     h->ncu = ncu;
     *out_h = h;
@@ -474,6 +478,7 @@ void gdn_free(gdn_handle h) {
     if (h->scratch || h->tm || h->side || h->seg) {
         DeviceGuard g(h->cfg.device);
         if (h->seg) (void)hipFree(h->seg);
+        if (h->ev_join_mid) (void)hipEventDestroy(h->ev_join_mid);
         if (h->ev_join) (void)hipEventDestroy(h->ev_join);
         if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
         if (h->side) (void)hipStreamDestroy(h->side);
@@ -609,6 +614,7 @@ int run_bidi(gdn_ctx *h, const Inputs &in, void *out, size_t out_bytes, long lon
         a.side_stream = h->side;
         a.ev_fork = h->ev_fork;
         a.ev_join = h->ev_join;
+        a.ev_join_mid = h->ev_join_mid;
     }
     hipError_t e = (C == 1) ? gdn::launch_scan(a, s) : gdn::launch_chunk(a, C, s);
     if ((st = launch_status(h, e, "bidirectional pass"))) return st;

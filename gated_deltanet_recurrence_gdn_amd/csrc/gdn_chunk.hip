@@ -1302,7 +1302,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p_arg, ChunkParam
     Ctx x;
     x.T = p.T;
     x.nchunks = (int)((p.T + C - 1) / C);
-    x.c0 = SW == SWEEP_SECOND ? p.c0 : SW == SWEEP_SEG ? seg * p.seg_len : 0;
+    x.c0 = SW == SWEEP_SECOND || SW == SWEEP_FIRST ? p.c0 : SW == SWEEP_SEG ? seg * p.seg_len : 0;
     x.c1 = SW == SWEEP_FIRST ? p.c1 : x.nchunks;
     if constexpr (SW == SWEEP_SEG) x.c1 = min(x.nchunks, x.c0 + p.seg_len);
     x.rs = (int)(p.qk_ts * ES);
@@ -1461,22 +1461,33 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     // side stream, those inverses are formed there, beside the first launch.
     const int n1 = (nchunks + 1) / 2;
     const bool side = a.both_dirs && a.bidi_state && a.side_stream && n1 < nchunks;
+    // With the side stream, the first half is walked in two launches, [0, q) and
+    // [q, n1), so that only the inverses of [0, q) precede the first: those of [q, n1)
+    // and of the second half are formed on the side stream, in that order, beside it.
+    const int q = side && a.ev_join_mid && n1 >= 16 ? (n1 + 1) / 2 : n1;
     auto set_range = [&](int c0, int nc) {
         t.c0 = c0;
         t.nc = nc;
         t.nblk = dirs * a.B * a.H * nc;
         t.xcd_remap = t.nblk % 8 == 0;
     };
-    set_range(0, side ? n1 : nchunks);
+    set_range(0, side ? q : nchunks);
     hipLaunchKernelGGL((tm_kernel<DK, IO, PRO>), dim3((unsigned)t.nblk), dim3(256), 0, stream, t);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipStream_t s2 = static_cast<hipStream_t>(a.side_stream);
     hipEvent_t fork = static_cast<hipEvent_t>(a.ev_fork), join = static_cast<hipEvent_t>(a.ev_join);
+    hipEvent_t join_mid = static_cast<hipEvent_t>(a.ev_join_mid);
     if (side) {
-        set_range(n1, nchunks - n1);
         if ((e = hipEventRecord(fork, stream)) != hipSuccess) return e;
         if ((e = hipStreamWaitEvent(s2, fork, 0)) != hipSuccess) return e;
+        if (q < n1) {
+            set_range(q, n1 - q);
+            hipLaunchKernelGGL((tm_kernel<DK, IO, PRO>), dim3((unsigned)t.nblk), dim3(256), 0, s2, t);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            if ((e = hipEventRecord(join_mid, s2)) != hipSuccess) return e;
+        }
+        set_range(n1, nchunks - n1);
         hipLaunchKernelGGL((tm_kernel<DK, IO, PRO>), dim3((unsigned)t.nblk), dim3(256), 0, s2, t);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = hipEventRecord(join, s2)) != hipSuccess) return e;
@@ -1558,9 +1569,18 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     p.state_in = nullptr;
     p.state_out = a.bidi_state;
     p.out_mode = OUT_STORE;  // into the direction's partial buffer (see the kernel)
-    p.c0 = 0; p.c1 = n1;
+    p.c0 = 0; p.c1 = q;
     hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO, SWEEP_FIRST>), dim3(nblk), dim3(NT), 0, stream, p, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (q < n1) {
+        // resume from the fp32 states in place: each block reads its own columns at
+        // its start and writes them at its end
+        if ((e = hipStreamWaitEvent(stream, join_mid, 0)) != hipSuccess) return e;
+        p.state_in = a.bidi_state;
+        p.c0 = q; p.c1 = n1;
+        hipLaunchKernelGGL((chunk_kernel<DK, IO, PRO, SWEEP_FIRST>), dim3(nblk), dim3(NT), 0, stream, p, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (n1 < nchunks) {
         if (side && (e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return e;
         p.state_in = a.bidi_state;

@@ -59,6 +59,9 @@ struct PassArgs {
     void *side_stream;      // optional (with bidi_state): a hipStream_t on which the inverses of
     void *ev_fork;          // the second half are formed beside the first launch, ordered by
     void *ev_join;          // these two hipEvent_t (fork: stream -> side, join: side -> stream)
+    void *ev_join_mid;      // optional third hipEvent_t: with it the first half runs as two launches
+                            // and the inverses of its second part are formed on the side stream
+                            // too, joined back by this event before that part
     // Segment-parallel causal form (MFMA kernel, causal, nseg > 1):
     // the call's chunks are cut into nseg segments of seg_len chunks.  Segment 0 runs
     // from state_in and writes out; every later segment runs from zero into

@@ -38,7 +38,7 @@
  * the handle and its device scratch, allocated once in gdn_create and freed in
  * gdn_free: the two fp32 partials and two fp32 states of gdn_forward_bidi
  * (GDN_FLAG_BIDI; with them, on handles the MFMA kernel serves, a second
- * stream of default priority and two events, see gdn_forward_bidi), and, on
+ * stream of default priority and three events, see gdn_forward_bidi), and, on
  * handles the bf16 MFMA chunked kernel can serve (bf16 or FP8 inputs, d_k and
  * d_v >= 32), the per-chunk triangular inverses of that kernel and each
  * token's gate record (b, log2 a and, for the packed entry points, the inverse
@@ -154,14 +154,16 @@ int gdn_forward(gdn_handle h, const void *q, const void *k, const void *v,
  * Bidirectional form over one full sequence:
  *     out = fwd(x; S = 0) + R(fwd(R x; S = 0)),
  * R reversing the token axis; token t is counted by both directions.  The two
- * directions' outputs are summed in fp32 and rounded once to io_dtype.  The
- * reverse pass places its chunk grid from token T-1 downwards, so reversing the
- * inputs reverses the output exactly.  Needs a handle created with
- * GDN_FLAG_BIDI.  No state is read or returned.  On the bf16 MFMA path the
- * call also enqueues one kernel on a stream the handle owns (created with
- * GDN_FLAG_BIDI, default priority), forked from and joined back into
- * hip_stream by events: work enqueued on hip_stream after the call still runs
- * after all of it, and the call can be captured into a HIP graph.
+ * directions' outputs are summed in fp32 and rounded once to io_dtype; on the
+ * bf16 MFMA path the term a direction produced in its first half of the sweep is
+ * kept as a bf16 row until the other direction adds to it.  The reverse pass
+ * places its chunk grid from token T-1 downwards and both directions are treated
+ * alike, so reversing the inputs reverses the output exactly.  Needs a handle
+ * created with GDN_FLAG_BIDI.  No state is read or returned.  On the bf16 MFMA
+ * path the call also enqueues up to two kernels on a stream the handle owns
+ * (created with GDN_FLAG_BIDI, default priority), forked from and joined back
+ * into hip_stream by events: work enqueued on hip_stream after the call still
+ * runs after all of it, and the call can be captured into a HIP graph.
  */
 int gdn_forward_bidi(gdn_handle h, const void *q, const void *k, const void *v,
                      const float *beta, const float *decay, void *out,
