@@ -364,7 +364,7 @@ def measure_forms(torch, gb, inputs, d, g, x):
     ms = timed(torch, lambda: gb.gdn_forward_bidi(gbd.h, xb["q"], xb["k"], xb["v"], xb["beta"], xb["decay"],
                                                   ob, wb.T, 64, stream), 5)
     forms["bidi_bf16_d128"] = {"ms": ms, "token_heads_per_s": wb.B * wb.H * wb.T / (ms / 1e3),
-                               "design": "both directions concurrently, each sweep split at the middle chunk into two launches; the second half's inverses formed on a side stream beside the first launch; the second launch adds the other direction's fp32 first-half output and writes out once"}
+                               "design": "both directions concurrently; each sweep's first half in two launches and its second half in one, all but the first quarter's inverses formed on a side stream beside them; the first half's outputs kept as bf16 rows, which the second half's launch adds before writing out once"}
     gbd.close()
     del xb, ob
 
