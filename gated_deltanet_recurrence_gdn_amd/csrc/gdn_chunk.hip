@@ -105,8 +105,17 @@ constexpr int LC = C + 8; // padded bf16 row pitch of C-long rows
 // for (nb, ks) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1) -- the blocks above the
 // diagonal are zero and never stored.  Lane l of operand o holds
 // Tm[16 nb + l%16][32 ks + 4 (l/16) + 0..3] and Tm[16 nb + l%16][32 ks + 16 + 4 (l/16) + 0..3].
+// In memory (inverse pass -> gate wave) operands 0 and 3, whose second halves lie
+// above the diagonal, keep their first halves only (8 bytes per lane): 5 KiB per
+// chunk; the LDS slot holds the full operands.
 constexpr int TM_OPS = 6;
-constexpr int TM_ELEMS = TM_OPS * 64 * 8;  // bf16 per chunk
+constexpr int TM_LDS_ELEMS = TM_OPS * 64 * 8;  // bf16 per chunk in LDS
+constexpr int TM_ELEMS = 4 * 64 * 8 + 2 * 64 * 4;  // bf16 per chunk in memory
+__host__ __device__ constexpr bool tm_half(int o) { return o == 0 || o == 3; }
+__host__ __device__ constexpr int tm_off(int o) {  // element offset of operand o in memory
+    return o == 0 ? 0 : o == 1 ? 256 : o == 2 ? 768 : o == 3 ? 1280 : o == 4 ? 1536 : 2048;
+}
+static_assert(tm_off(5) + 64 * 8 == TM_ELEMS, "operand layout");
 __host__ __device__ constexpr int tm_op(int nb, int ks) { return nb < 2 ? nb : 2 + 2 * (nb - 2) + ks; }
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
@@ -176,7 +185,8 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 struct Ctx {
     const char *q, *k, *v;      // bytes; v offset to the block's d_v tile
     const float *beta, *decay;
-    const float4 *grec;         // the head's gate records (b, log2 a, 1/||k||, 0), C per chunk
+    const void *grec;           // the head's gate records, C per chunk: float4 (b, log2 a, 1/||k||, 0)
+                                // with the prologue, else float2 (b, log2 a)
     long long T;
     int nchunks;
     int c0 = 0, c1 = 0;  // the chunks this launch walks: [c0, c1) (chunk_kernel)
@@ -314,7 +324,8 @@ struct TmParams {
     const char *k;
     const float *beta, *decay;
     uint16_t *tm;     // [dirs][B][H][nchunks][TM_ELEMS]
-    float4 *grec;     // [dirs][B][H][nchunks][C] gate records (b, log2 a, 1/||k||, 0)
+    void *grec;       // [dirs][B][H][nchunks][C] gate records: float4 (b, log2 a, 1/||k||, 0) with
+                      // the prologue, else float2 (b, log2 a)
     long long T;
     long long qk_ts, qk_bs;
     int B, H, nchunks, reverse;
@@ -620,7 +631,9 @@ __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
         sm.bk[lane] = gv.bk;
         sm.xf[lane] = gv.xf;
         // the chunk's gate record, one 16-byte entry per token, contiguous for chunk_kernel
-        p.grec[((size_t)((dir * p.B + b) * p.H + h) * p.nchunks + c) * C + lane] = make_float4(bt, l2, rk, 0.f);
+        const size_t gi = ((size_t)((dir * p.B + b) * p.H + h) * p.nchunks + c) * C + lane;
+        if constexpr (PRO) static_cast<float4 *>(p.grec)[gi] = make_float4(bt, l2, rk, 0.f);
+        else static_cast<float2 *>(p.grec)[gi] = make_float2(bt, l2);
     }
     __syncthreads();  // K is read; Tm and A overwrite it
     if (wid < 2) a_diag_block(sm, g0, wid, lane);
@@ -633,15 +646,20 @@ __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
     else if (wid == 2) tm_column<2>(sm.Tb, sm.Ab, l16, g16);
     __syncthreads();
 
-    // 4. the six operand blocks, 1 KiB each, one 16-byte store per lane
+    // 4. the six operand blocks, one 16-byte store per lane (8 bytes for operands 0
+    //    and 3, whose second halves are zero)
     uint16_t *dst = p.tm + ((size_t)((dir * p.B + b) * p.H + h) * p.nchunks + c) * TM_ELEMS;
     for (int o = wid; o < TM_OPS; o += 4) {
         const int nb = o < 2 ? o : 2 + (o - 2) / 2;
         const int ks = o < 2 ? 0 : (o - 2) & 1;
         const uint16_t *row = &sm.Tb[16 * nb + l16][32 * ks + 4 * g16];
         const uint2 lo = *reinterpret_cast<const uint2 *>(row);
-        const uint2 up = *reinterpret_cast<const uint2 *>(row + 16);
-        *reinterpret_cast<uint4 *>(dst + (size_t)(o * 64 + lane) * 8) = make_uint4(lo.x, lo.y, up.x, up.y);
+        if (tm_half(o)) {
+            *reinterpret_cast<uint2 *>(dst + tm_off(o) + (size_t)lane * 4) = lo;
+        } else {
+            const uint2 up = *reinterpret_cast<const uint2 *>(row + 16);
+            *reinterpret_cast<uint4 *>(dst + tm_off(o) + (size_t)lane * 8) = make_uint4(lo.x, lo.y, up.x, up.y);
+        }
     }
 }
 
@@ -651,7 +669,7 @@ __global__ __launch_bounds__(256, 8) void tm_kernel(TmParams p) {
 struct ChunkParams {
     const char *q, *k, *v;
     long long qk_ts, qk_bs, v_ts, v_bs;  // element strides between tokens / batch elements
-    const float4 *grec;                  // gate records written by tm_kernel
+    const void *grec;                    // gate records written by tm_kernel
     const float *state_in;
     float *state_out;
     void *out;
@@ -697,7 +715,7 @@ struct __align__(16) Smem {
     static constexpr int LOT = DVT + 4;
     float Ot[4][16][LOT];
     // Tm of a chunk in the chain's operand order (chunk parity), staged by the gate wave
-    uint16_t Tms[2][TM_ELEMS];
+    uint16_t Tms[2][TM_LDS_ELEMS];
 };
 
 // OUT_ADD_PARTIAL only: the other direction's fp32 outputs of a chunk's tokens
@@ -880,18 +898,30 @@ __device__ __forceinline__ TmOps lds_tm(const uint16_t *slot, int lane) {
     for (int o = 0; o < TM_OPS; ++o) t.o[o] = lds16(slot + (size_t)o * 512 + (size_t)lane * 8);
     return t;
 }
-// Tm operands of chunk c (clamped into range: the load is unconditional and
-// its result unused past the last chunk).
-__device__ __forceinline__ void store_tm(uint16_t *slot, const TmOps &t, int lane) {
+// Tm operands of chunk c as stored in memory (operands 0 and 3 halved), loaded by
+// the gate wave (clamped into range: the load is unconditional and its result
+// unused past the last chunk) and written to the LDS slot in full.
+struct TmMem {
+    uint2 h[2];  // operands 0 and 3
+    uint4 f[4];  // operands 1, 2, 4, 5
+};
+__device__ __forceinline__ void store_tm(uint16_t *slot, const TmMem &t, int lane) {
 #pragma unroll
-    for (int o = 0; o < TM_OPS; ++o) *reinterpret_cast<bf16x8_t *>(slot + (size_t)o * 512 + (size_t)lane * 8) = t.o[o];
+    for (int o = 0; o < TM_OPS; ++o) {
+        const int i = o < 3 ? o - 1 : o - 2;
+        const uint4 v = tm_half(o) ? make_uint4(t.h[o == 3].x, t.h[o == 3].y, 0u, 0u) : t.f[i];
+        *reinterpret_cast<uint4 *>(slot + (size_t)o * 512 + (size_t)lane * 8) = v;
+    }
 }
-__device__ __forceinline__ TmOps load_tm(const uint16_t *tm_head, int c, int n, int lane) {
+__device__ __forceinline__ TmMem load_tm(const uint16_t *tm_head, int c, int n, int lane) {
     const int cc = c < n ? c : n - 1;  // n: one past the last chunk of the launch
-    const uint16_t *src = tm_head + (size_t)cc * TM_ELEMS + (size_t)lane * 8;
-    TmOps t;
+    const uint16_t *src = tm_head + (size_t)cc * TM_ELEMS;
+    TmMem t;
 #pragma unroll
-    for (int o = 0; o < TM_OPS; ++o) t.o[o] = *reinterpret_cast<const bf16x8_t *>(src + (size_t)o * 512);
+    for (int o = 0; o < TM_OPS; ++o) {
+        if (tm_half(o)) t.h[o == 3] = *reinterpret_cast<const uint2 *>(src + tm_off(o) + (size_t)lane * 4);
+        else t.f[o < 3 ? o - 1 : o - 2] = *reinterpret_cast<const uint4 *>(src + tm_off(o) + (size_t)lane * 8);
+    }
     return t;
 }
 
@@ -1181,12 +1211,19 @@ __device__ __forceinline__ VRow<IO> load_v(const Ctx &x, int c, int lane) {
     }
     return d;
 }
-// One 16-byte record per lane from a contiguous 1 KiB per chunk (the strided
-// [B, T, H] gates were read, activated and clamped by tm_kernel).  Unconditional
-// (c is clamped into range by the caller), so that the count of loads in flight
-// is the same on every path.
+// One record per lane from a contiguous run per chunk (1 KiB with the prologue, else
+// 512 bytes; the strided [B, T, H] gates were read, activated and clamped by
+// tm_kernel).  Unconditional (c is clamped into range by the caller), so that the
+// count of loads in flight is the same on every path.
+template <bool PRO>
 __device__ __forceinline__ void load_gates(const Ctx &x, int c, int lane, GateRegs &g) {
-    g.r = x.grec[(size_t)c * C + lane];
+    const size_t i = (size_t)c * C + lane;
+    if constexpr (PRO) {
+        g.r = static_cast<const float4 *>(x.grec)[i];
+    } else {
+        const float2 v = static_cast<const float2 *>(x.grec)[i];
+        g.r = make_float4(v.x, v.y, 1.f, 0.f);
+    }
 }
 
 // The other direction's outputs of a chunk's tokens for this block's 32 d_v columns,
@@ -1317,7 +1354,11 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p_arg, ChunkParam
     x.v = p.v + ((size_t)b * p.v_bs + (size_t)h * p.dv + dv0) * ES;
     x.beta = x.decay = nullptr;  // the gates arrive as tm_kernel's records (x.grec)
     const int n = x.nchunks;
-    x.grec = p.grec + (size_t)((dir * p.B + b) * p.H + h) * n * C;
+    {
+        const size_t g0 = (size_t)((dir * p.B + b) * p.H + h) * n * C;
+        x.grec = PRO ? static_cast<const void *>(static_cast<const float4 *>(p.grec) + g0)
+                     : static_cast<const void *>(static_cast<const float2 *>(p.grec) + g0);
+    }
 
     // Every role walks the same periods it = c0 - 2 .. c1 (the last one finishes
     // the outputs of chunk c1 - 1), two per loop trip so that register sets
@@ -1395,18 +1436,18 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p_arg, ChunkParam
         // other direction's outputs of chunk c into LDS in period c (loaded in
         // period c-2), for the output waves' stores of chunk c in period c+1.
         GateRegs gA, gB;
-        load_gates(x, c0, lane, gA);
-        load_gates(x, x.clamp(c0 + 1), lane, gB);
+        load_gates<PRO>(x, c0, lane, gA);
+        load_gates<PRO>(x, x.clamp(c0 + 1), lane, gB);
         PartRows pA, pB;
         // Tm of chunk c is stored in period c-1 from register set c&1, loaded in period c-3
         const uint16_t *tm_head = p.tm + (size_t)((dir * p.B + b) * p.H + h) * n * TM_ELEMS;
-        TmOps mA = load_tm(tm_head, c0, c1, lane), mB;
+        TmMem mA = load_tm(tm_head, c0, c1, lane), mB;
         __syncthreads();
         for (int it = c0 - 2; it < c1 + 1; it += 2) {
             if (x.has(it + 1)) store_tm(sm.Tms[(it + 1) & 1], mB, lane);
             mB = load_tm(tm_head, it + 3, c1, lane);
             if (x.has(it + 2)) gates_store<DK, PRO>(x, sm, it + 2, lane, gA);
-            load_gates(x, x.clamp(it + 4), lane, gA);
+            load_gates<PRO>(x, x.clamp(it + 4), lane, gA);
             if constexpr (ADD) {
                 if (x.has(it)) store_part(it, pA, lane);
                 pA = load_part(x, other_b, x.clamp(it + 2), lane);
@@ -1415,7 +1456,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p_arg, ChunkParam
             if (x.has(it + 2)) store_tm(sm.Tms[(it + 2) & 1], mA, lane);
             mA = load_tm(tm_head, it + 4, c1, lane);
             if (x.has(it + 3)) gates_store<DK, PRO>(x, sm, it + 3, lane, gB);
-            load_gates(x, x.clamp(it + 5), lane, gB);
+            load_gates<PRO>(x, x.clamp(it + 5), lane, gB);
             if constexpr (ADD) {
                 if (x.has(it + 1)) store_part(it + 1, pB, lane);
                 pB = load_part(x, other_b, x.clamp(it + 3), lane);
@@ -1447,7 +1488,7 @@ hipError_t launch_dk(const PassArgs &a, hipStream_t stream) {
     const long long ntm = (long long)dirs * a.B * a.H * nchunks;
     if (!a.tm || ntm > a.tm_chunks || ntm > 0x7fffffffLL) return hipErrorInvalidValue;
     // The gate records follow the Tm blocks of the handle's whole capacity.
-    float4 *grec = reinterpret_cast<float4 *>(a.tm + (size_t)a.tm_chunks * TM_ELEMS);
+    void *grec = a.tm + (size_t)a.tm_chunks * TM_ELEMS;
 
     TmParams t;
     t.k = static_cast<const char *>(a.k);

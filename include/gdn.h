@@ -42,7 +42,7 @@
  * handles the bf16 MFMA chunked kernel can serve (bf16 or FP8 inputs, d_k and
  * d_v >= 32), the per-chunk triangular inverses of that kernel and each
  * token's gate record (b, log2 a and, for the packed entry points, the inverse
- * k norm): 7 KiB per direction, b, h and 64-token chunk up to max_T.  The
+ * k norm): 6 KiB per direction, b, h and 64-token chunk up to max_T.  The
  * forward calls allocate nothing, never
  * synchronise and never copy between host and device: they validate, enqueue
  * kernels on the given stream and return.  Device faults surface at the
@@ -219,11 +219,11 @@ int gdn_forward_bidi_packed(gdn_handle h, const void *qkv, long long token_strid
  * handle: *cfg is a configuration as for gdn_create (flags must be 0; max_T is
  * not used).  The call allocates nothing, on the device or the host.  The
  * scratch of the bf16 / FP8 MFMA chunked kernel (chunk_len 64, d_k, d_v >= 32:
- * 7 KiB per b, h and 64-token chunk) is one fixed 64 MiB device array inside the
+ * 6 KiB per b, h and 64-token chunk) is one fixed 64 MiB device array inside the
  * library, one per GPU, held until the process ends; a call whose
- * B * H * ceil(T / 64) exceeds 9,362 chunks is refused with
+ * B * H * ceil(T / 64) exceeds 10,922 chunks is refused with
  * GDN_ERR_UNSUPPORTED before anything is launched (B = 1, H = 20 allows
- * T <= 29,952).  The other paths (scan, fp32 chunked kernel) need no scratch.
+ * T <= 34,944).  The other paths (scan, fp32 chunked kernel) need no scratch.
  * Every call on one GPU shares that GPU's array: calls that may overlap on the
  * device (streams not ordered by events) race and give wrong results.  The
  * first call on a device resolves the array's address and checks the device

@@ -313,9 +313,9 @@ def test_noalloc_dry_run():
     assert noalloc(T=-1) == gb.GDN_ERR_ARG
     assert noalloc(dk=48) == gb.GDN_ERR_UNSUPPORTED
     assert gb.gdn_last_error(None) != ""
-    # capacity: B * H * ceil(T / 64) <= 9,362 chunks on the MFMA kernel
-    assert noalloc(B=1, H=20, dk=128, dv=128, T=29952) == gb.GDN_OK
-    assert noalloc(B=1, H=20, dk=128, dv=128, T=29953) == gb.GDN_ERR_UNSUPPORTED
+    # capacity: B * H * ceil(T / 64) <= 10,922 chunks (64 MiB of 6 KiB records) on the MFMA kernel
+    assert noalloc(B=1, H=20, dk=128, dv=128, T=34944) == gb.GDN_OK
+    assert noalloc(B=1, H=20, dk=128, dv=128, T=34945) == gb.GDN_ERR_UNSUPPORTED
     assert "scratch" in gb.gdn_last_error(None)
     # the paths that use no scratch have no such limit
     assert noalloc(B=1, H=20, dk=128, dv=128, T=100000, chunk=1) == gb.GDN_OK
