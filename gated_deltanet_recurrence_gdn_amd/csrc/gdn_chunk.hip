@@ -20,8 +20,9 @@
 // tm_kernel (throughput): Tm depends only on K and the gates, so it is formed
 // once per (direction, b, h, chunk) -- one block each, all chunks in parallel --
 // and written as bf16 in exactly the register order in which the state chain
-// uses it as an MFMA operand (6 KiB per chunk), with the chunk's gate records
-// (1 KiB: b, log2 a and 1/||k|| of each token, so that chunk_kernel reads its
+// uses it as an MFMA operand (5 KiB per chunk), with the chunk's gate records
+// (b and log2 a of each token, and 1/||k|| with the prologue: 512 bytes or 1 KiB,
+// so that chunk_kernel reads its
 // gates in one coalesced load instead of two loads whose lanes all fall on
 // different cache lines).  That costs extra HBM traffic
 // (K read again, Tm written and read back) and takes the Gram products, the
@@ -51,7 +52,7 @@
 //   waves 4, 5  K and Q of chunk c+1 (HBM -> registers -> LDS), loaded in
 //               period c-2 (two register sets alternate).
 //   wave 6      gate vectors of chunk c+2 from the chunk's gate records (b,
-//               log2 a, 1/||k|| per token, written contiguously by tm_kernel
+//               log2 a and, with the prologue, 1/||k|| per token, written contiguously by tm_kernel
 //               from the strided [B, T, H] gates): float64 prefix sum of log2 a
 //               (DPP within 16-lane rows, then the row carries), 2^g, b 2^g,
 //               2^{g_last - g}, b.  It also stages chunk c+1's Tm operands
