@@ -125,14 +125,15 @@ def test_bidi_chunked_and_symmetry():
     g.close()
 
 
-@pytest.mark.parametrize("T", [64, 65, 127, 128, 129, 191, 192, 193, 320, 333, 449])
+@pytest.mark.parametrize("T", [64, 65, 127, 128, 129, 191, 192, 193, 320, 333, 449, 1920, 1921, 1984, 2049, 2113])
 @pytest.mark.parametrize("d", [64, 128])
 def test_bidi_split_sweep(T, d):
-    """The MFMA kernel's bidirectional form walks chunks [0, n1) of both directions in
-    one launch and [n1, n) in a second (n1 = ceil(n / 2)), adding the other
-    direction's first-launch output; the middle tokens both first halves cover are
-    combined separately.  Lengths around the split points and the middle overlap,
-    against the oracle per head and per edge chunk, plus exact reversal symmetry."""
+    """The MFMA kernel's bidirectional form walks chunks [0, n1) of both directions
+    (n1 = ceil(n / 2); in two launches split at ceil(n1 / 2) once n1 >= 16, i.e. from
+    T = 1921) and [n1, n) in a last one, adding the other direction's first-half
+    output; the middle tokens both first halves cover are combined separately.
+    Lengths around the split points and the middle overlap, against the oracle per
+    head and per edge chunk, plus exact reversal symmetry."""
     B, H = 2, 3
     x, _ = make(B, T, H, d, d, seed=T + d)
     dx = dev(x)
