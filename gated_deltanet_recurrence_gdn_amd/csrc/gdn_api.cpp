@@ -598,12 +598,12 @@ int run_bidi(gdn_ctx *h, const Inputs &in, void *out, size_t out_bytes, long lon
     a.partial = h->scratch;
     a.partial_rev = h->scratch + (size_t)c.B * (size_t)c.max_T * c.H * c.d_v;
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-    // Both directions run concurrently, each writing fp32 outputs (the reverse
-    // direction walks the tokens from T-1 down, chunk grid anchored there), and
-    // out = round(forward + reverse): one rounding, and fp32 addition is
-    // commutative, so reversing the inputs reverses the output exactly.  The MFMA
-    // chunked kernel splits its sweeps at the middle chunk and adds the other
-    // direction's output itself; the other kernels write both partials in one
+    // Both directions run concurrently (the reverse direction walks the tokens from
+    // T-1 down, chunk grid anchored there), and out = round(forward + reverse): one
+    // rounding, and fp32 addition is commutative, so reversing the inputs reverses
+    // the output exactly.  The MFMA chunked kernel splits its sweeps at the middle
+    // chunk, keeps the first half's outputs as bf16 rows and adds the other
+    // direction's output itself; the other kernels write both fp32 partials in one
     // launch and a combine pass adds them.
     a.reverse = 0;
     a.both_dirs = 1;

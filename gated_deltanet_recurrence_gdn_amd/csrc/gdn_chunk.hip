@@ -686,7 +686,7 @@ struct ChunkParams {
     // [s seg_len, min(n, (s + 1) seg_len)); its state_out is y seg_state_stride
     // elements further on.  seg_zero_start: segments s > 0 start from zero (else
     // every segment starts from state_in).  seg0_store: segment 0 stores out, the
-    // others write fp32 partials (else every segment writes partials).
+    // others store bf16 rows into seg_out (else every run stores into seg_out).
     int seg_len, seg_base, seg_zero_start, seg0_store;
     long long seg_state_stride;
     int seg_rows;  // block rows (y) this parameter set covers; the launch's other rows use the second set
@@ -719,9 +719,9 @@ struct __align__(16) Smem {
     uint16_t Tms[2][TM_LDS_ELEMS];
 };
 
-// OUT_ADD_PARTIAL only: the other direction's fp32 outputs of a chunk's tokens
-// (chunk parity), staged by the gate wave, in dynamic LDS that only launches of
-// that mode request.
+// OUT_ADD_PARTIAL only: the other direction's outputs of a chunk's tokens, widened
+// to fp32 (chunk parity), staged by the gate wave, in dynamic LDS that only
+// launches of that mode request.
 constexpr int LPT = DVT + 4;
 typedef float PartTile[C][LPT];
 constexpr size_t PART_LDS_BYTES = 2 * sizeof(PartTile);
