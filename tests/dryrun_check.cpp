@@ -120,8 +120,9 @@ void noalloc_cases() {
     EXPECT(na(c, 1000, 7) == GDN_ERR_UNSUPPORTED);
     EXPECT(na(c, 1000, 64, addr(0)) == GDN_ERR_ALIAS);
     gdn_config big = cfg(1, 20, 128, 128, GDN_BF16, 0, 0);
-    EXPECT(na(big, 29952, 64) == GDN_OK);
-    EXPECT(na(big, 29953, 64) == GDN_ERR_UNSUPPORTED);
+    // the fixed array holds 10,922 chunk records: 20 heads x 546 chunks fit, 547 do not
+    EXPECT(na(big, 34944, 64) == GDN_OK);
+    EXPECT(na(big, 34945, 64) == GDN_ERR_UNSUPPORTED);
     EXPECT(std::strstr(gdn_last_error(nullptr), "scratch") != nullptr);
     EXPECT(na(big, 100000, 1) == GDN_OK);
     gdn_config bidi = cfg(1, 2, 64, 64, GDN_BF16, 0, GDN_FLAG_BIDI);
