@@ -362,9 +362,12 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
         if (more) issue(st + 1);
         // every stage runs all TB tokens (padding is a no-op); token j + 1's operands
         // are read from LDS while token j is computed (the read after the last token
-        // wraps to token 0 of the same stage and is not used)
+        // wraps to token 0 of the same stage and is not used).  Fully unrolled, every
+        // LDS address is a constant offset from one base: no per-token address
+        // arithmetic and no loop branch (7.88 -> 7.02 ms at the batched d = 128 shape).
         Tok A, B;
         ld_tok(0, A);
+#pragma unroll
         for (int j = 0; j < TB; j += 2) {
             ld_tok(j + 1, B);
             step(j, A);
