@@ -101,6 +101,11 @@ struct Chunk8<IO_F32> {
 // barriers keep them there), 7.01 -> 6.67 ms at the batched d = 128 shape.
 __device__ __forceinline__ float row16_sum2(float u, float &p, bool odd, float a, const float (&s)[8],
                                             float (&as)[8]) {
+    // The wave runs at a raised priority from here until its output is stored: the
+    // row sums, nu and the update are one dependent chain, and the other wave on
+    // the SIMD (in its dot products) then yields the issue slots to it
+    // (6.67 -> 6.12 ms at the batched d = 128 shape).
+    __builtin_amdgcn_s_setprio(2);
     float t = odd ? p : u;
     const float o = odd ? u : p;
     t += dpp_mov<0xB1>(o);   // quad_perm [1,0,3,2]: the pair's other lane
@@ -378,6 +383,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
             float *dst = seg == (L == 16 ? 1 : 0) ? &of[j][rloc] : &odump[tid];
             *dst = fmaf(a, pq, nu * kq);
         }
+        if constexpr (L == 16) __builtin_amdgcn_s_setprio(0);
     };
 
     if (nst > 0) {
