@@ -1376,6 +1376,11 @@ __global__ __launch_bounds__(NT) void chunk_kernel(ChunkParams p_arg, ChunkParam
     // OUT_ADD_PARTIAL: the other direction's bf16 rows
     const uint16_t *other = reinterpret_cast<const uint16_t *>(dir ? p.partial : p.partial_rev);
     const uint16_t *other_b = other ? other + tok0 * p.dv + dv0 : nullptr;
+    // The chain and output waves run at a raised priority: each SIMD pairs one of them
+    // with a memory wave, and the compute wave then takes the issue slots first
+    // (bit-identical; 0.817 -> 0.804 ms per call at the batched d = 128 shape; the
+    // memory waves raised instead made it 9% slower).
+    if (wid < 4) __builtin_amdgcn_s_setprio(2);
     if (wid < 2) {
         // The chain reads chunk c's Tm operands from the LDS slot the gate wave
         // filled in period c-1, so it never waits on a global load.
