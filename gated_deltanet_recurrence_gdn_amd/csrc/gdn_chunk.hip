@@ -32,8 +32,9 @@
 // chunk_kernel (sequential over chunks): rows of S are independent, so a block
 // owns one (b, h) and a 32-wide tile of d_v and walks the head's chunks in
 // order.  The tiles of a head are placed on one XCD and share q/k/Tm through its
-// L2.  Eight waves with fixed roles; waves w and w + 4 share a SIMD; one
-// workgroup barrier per chunk period.  In period c:
+// L2.  Eight waves with fixed roles; waves w and w + 4 share a SIMD (w < 4, the
+// compute wave, at a raised wave priority); one workgroup barrier per chunk
+// period.  In period c:
 //   waves 0, 1  the state chain of chunk c, 16 d_v columns each.  S^T (d_k x 16)
 //               lives in fp32 accumulators of 16x16x32 MFMAs for the whole call.
 //               X = K S^T, R, N = Tm R and S^T = gam_{C-1} S^T + K^T N~ hand their
