@@ -394,19 +394,19 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
     for (long long st = 0; st < nst; ++st) {
         const bool more = st + 1 < nst;
         if (more) issue(st + 1);
-        // every stage runs all TB tokens (padding is a no-op); token j + 1's operands
-        // are read from LDS while token j is computed (the read after the last token
-        // wraps to token 0 of the same stage and is not used).  Fully unrolled, every
-        // LDS address is a constant offset from one base: no per-token address
-        // arithmetic and no loop branch (7.88 -> 7.02 ms at the batched d = 128 shape).
-        Tok A, B;
-        ld_tok(0, A);
+        // every stage runs all TB tokens (padding is a no-op); token j + 2's operands
+        // are read from LDS while token j is computed, from three rotating register
+        // sets (the reads past the last token wrap to the start of the same stage and
+        // are not used; one token ahead instead: +2%).  Fully unrolled, every LDS
+        // address is a constant offset from one base: no per-token address arithmetic
+        // and no loop branch (7.88 -> 7.02 ms at the batched d = 128 shape).
+        Tok tk[3];
+        ld_tok(0, tk[0]);
+        ld_tok(1, tk[1]);
 #pragma unroll
-        for (int j = 0; j < TB; j += 2) {
-            ld_tok(j + 1, B);
-            step(j, A);
-            ld_tok((j + 2) % TB, A);
-            step(j + 1, B);
+        for (int j = 0; j < TB; ++j) {
+            ld_tok((j + 2) % TB, tk[(j + 2) % 3]);
+            step(j, tk[j % 3]);
         }
         __syncthreads();
         // Write this stage's outputs: token j, rows [row0, row0 + rows).
