@@ -128,12 +128,17 @@ __device__ __forceinline__ float row16_sum2(float u, float &p, bool odd, float a
     return dpp_mov<0xA0>(t);  // quad_perm [0,0,2,2]: the even lane's sum
 }
 
+// Eight consecutive outputs (elem a multiple of 8): one 16-byte store of bf16, or two of fp32.
 template <int IO>
-__device__ __forceinline__ void store_out(void *out, size_t elem, float x) {
-    if constexpr (IO != IO_F32)
-        reinterpret_cast<uint16_t *>(out)[elem] = (uint16_t)f32_to_bf16_bits(x);
-    else
-        reinterpret_cast<float *>(out)[elem] = x;
+__device__ __forceinline__ void store_out8(void *out, size_t elem, const float4 &a, const float4 &b) {
+    if constexpr (IO != IO_F32) {
+        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + elem) =
+            make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
+    } else {
+        float4 *o = reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + elem);
+        o[0] = a;
+        o[1] = b;
+    }
 }
 
 // A block holds `rows` consecutive state rows of one (b, h).  A row's d_k values
@@ -155,8 +160,8 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
 
     __shared__ __align__(16) float kf[TB][DK];
     __shared__ __align__(16) float qf[TB][DK];
-    __shared__ float vf[TB][ROWS_MAX];
-    __shared__ float of[TB][ROWS_MAX];
+    __shared__ __align__(16) float vf[TB][ROWS_MAX];
+    __shared__ __align__(16) float of[TB][ROWS_MAX];
     __shared__ float odump[NT];  // the output writes of the lanes that do not own o
     __shared__ __align__(16) float gt[TB][4];  // a, b, (k . q) / sqrt(d_k) per token
 
@@ -176,8 +181,9 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
     const int H = p.H;
     const long long T = p.T;
     const int dv = p.dv;
-    const int vch = TB * rows / 8;     // 8-element v chunks per stage
-    const int vpt_tok = rows / 8;      // v chunks per token
+    const int vch = TB * rows / 8;     // 8-element v (and output) chunks per stage
+    const int vpt_tok = rows / 8;      // v chunks per token: a power of two (rows is)
+    const int lg_vpt = __builtin_ctz((unsigned)vpt_tok);
 
     // Initial state: this lane's E values of row (row0 + rloc).
     float s[E];
@@ -224,8 +230,8 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
         for (int i = 0; i < VPT; ++i) {
             const int c = tid + i * nthr;
             if (c < vch)
-                vr[i].load(p.v, (size_t)b * p.v_bs + (size_t)tok_of(st * TB + c / vpt_tok) * p.v_ts +
-                                    (size_t)h * dv + row0 + (c % vpt_tok) * 8);
+                vr[i].load(p.v, (size_t)b * p.v_bs + (size_t)tok_of(st * TB + (c >> lg_vpt)) * p.v_ts +
+                                    (size_t)h * dv + row0 + (c & (vpt_tok - 1)) * 8);
         }
 #pragma unroll
         for (int i = 0; i < GPT; ++i) {
@@ -284,12 +290,14 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
         for (int i = 0; i < VPT; ++i) {
             const int c = tid + i * nthr;
             if (c < vch) {
-                const int j = c / vpt_tok, part = c % vpt_tok;
+                const int j = c >> lg_vpt, part = c & (vpt_tok - 1);
                 const bool real = st * TB + j < T;
                 float vv[8];
                 vr[i].to_f32(vv);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) vf[j][part * 8 + e] = real ? vv[e] : 0.f;
+                for (int e = 0; e < 8; ++e) vv[e] = real ? vv[e] : 0.f;
+                *reinterpret_cast<float4 *>(&vf[j][part * 8]) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+                *reinterpret_cast<float4 *>(&vf[j][part * 8 + 4]) = make_float4(vv[4], vv[5], vv[6], vv[7]);
             }
         }
 #pragma unroll
@@ -409,16 +417,20 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p) {
             step(j, tk[j % 3]);
         }
         __syncthreads();
-        // Write this stage's outputs: token j, rows [row0, row0 + rows).
+        // Write this stage's outputs: token j, rows [row0, row0 + rows), eight rows
+        // per thread in one 16-byte store (one 2-byte store per row before, and
+        // scalar LDS stores of v: 5.98 -> 5.70 ms at the batched d = 128 shape).
         const int nvalid = (int)((T - st * TB) < TB ? (T - st * TB) : TB);
-        for (int idx = tid; idx < nvalid * rows; idx += nthr) {
-            const int j = idx / rows, r = idx % rows;
-            const size_t e = ((size_t)(b * T + tok_of(st * TB + j)) * H + h) * dv + row0 + r;
-            const float o = of[j][r];
+        for (int c = tid; c < nvalid * vpt_tok; c += nthr) {
+            const int j = c >> lg_vpt, part = c & (vpt_tok - 1);
+            const size_t e = ((size_t)(b * T + tok_of(st * TB + j)) * H + h) * dv + row0 + part * 8;
+            const float4 o0 = *reinterpret_cast<const float4 *>(&of[j][part * 8]);
+            const float4 o1 = *reinterpret_cast<const float4 *>(&of[j][part * 8 + 4]);
             if (p.out_mode == OUT_PARTIAL) {
-                partial[e] = o;
+                reinterpret_cast<float4 *>(partial + e)[0] = o0;
+                reinterpret_cast<float4 *>(partial + e)[1] = o1;
             } else {
-                store_out<IO>(p.out, e, o);
+                store_out8<IO>(p.out, e, o0, o1);
             }
         }
         if (more) commit(st + 1);
