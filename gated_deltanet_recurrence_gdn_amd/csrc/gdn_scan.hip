@@ -33,7 +33,7 @@
 namespace gdn {
 namespace {
 
-constexpr int TB = 32;       // tokens per LDS stage
+constexpr int TB = 48;       // tokens per LDS stage (32: +1% at the batched d = 128 shape)
 constexpr int NT = 256;      // max threads per block
 
 struct ScanParams {
